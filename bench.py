@@ -1,0 +1,218 @@
+"""Benchmark of the MoE layer forward (libmoe) on one MI355X.
+
+One step = one moe_forward (gate -> scatter -> expert up -> expert down ->
+combine) over one batch of T synthetic tokens, inputs resident in HBM. Layers
+rotate round-robin over several independently drawn instances so consecutive
+steps never reuse weights from the 256 MB last-level cache.
+
+Prints one JSON line: tokens/s of the main workload, the roofline of its
+dominant kernel (the expert up-projection GEMM; HIP events around each stage,
+recorded by libmoe on the stream the kernels run on), a sweep of the other token
+counts of the same layer, and the CPU oracle timed on a bounded sample.
+
+  python bench.py [--steps K] [--warmup W] [--config NAME] [--tokens T]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="mixtral_bf16")
+    ap.add_argument("--tokens", type=int, default=None, help="main workload T (default: largest of the config)")
+    ap.add_argument("--instances", type=int, default=4)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    return ap.parse_args()
+
+
+def kernel_work(cfg, counts, T):
+    """Algorithmic bytes and flops of the up and down GEMMs for one forward.
+
+    counts: per routed expert assignment counts of this batch. Shared-expert
+    slices take all T tokens. Bytes: weights (+ scales) of experts with rows,
+    the activations read and the GEMM output written."""
+    d, F, k = cfg.d_model, cfg.d_ff, cfg.top_k
+    welt = 1 if cfg.expert_dtype == "i8" else (4 if cfg.expert_dtype == "f32" else 2)
+    aelt = 4 if cfg.act_dtype == "f32" else 2
+    helt = 4 if cfg.expert_dtype == "f32" else 2
+    active = int((counts > 0).sum())
+    P = T * k
+    V = cfg.shared_d_ff // F if cfg.shared_d_ff else 0
+    rows = P + V * T
+    scale_up = active * 2 * F * 4 if welt == 1 else 0
+    scale_dn = active * d * 4 if welt == 1 else 0
+    up_w = (active + V) * 2 * d * F * welt + scale_up
+    dn_w = (active + V) * F * d * welt + scale_dn
+    up = dict(flops=2.0 * rows * d * 2 * F, bytes=up_w + T * d * aelt + rows * F * helt)
+    dn = dict(flops=2.0 * rows * F * d, bytes=dn_w + rows * F * helt + rows * d * 4)
+    layer_bytes = up_w + dn_w + d * cfg.n_experts * 4 + 2 * T * d * aelt + T * k * 8
+    layer_flops = 2.0 * T * d * cfg.n_experts + up["flops"] + dn["flops"]
+    return up, dn, dict(bytes=layer_bytes, flops=layer_flops, active=active)
+
+
+def build_instances(cfg, n, T, torch, synth, moe_tensors):
+    from harness import gpu_layer
+    insts = []
+    for i in range(n):
+        L = synth.make_layer(cfg, device="cuda", instance=i)
+        lay = gpu_layer(L, T, profile=True)
+        x = synth.make_tokens(cfg, T, device="cuda", instance=i)
+        out = lay.outputs(T, scatter=True)
+        insts.append((lay, x, out))
+        if i == 0 and moe_tensors is not None:
+            moe_tensors["layer0"] = L.to("cpu")
+        del L
+        torch.cuda.empty_cache()
+    return insts
+
+
+def run_workload(cfg, T, steps, warmup, n_inst, torch, synth, keep_layer0=False):
+    keep = {} if keep_layer0 else None
+    insts = build_instances(cfg, n_inst, T, torch, synth, keep)
+    for i in range(warmup):
+        lay, x, out = insts[i % n_inst]
+        lay.forward(x, out=out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        lay, x, out = insts[i % n_inst]
+        lay.forward(x, out=out)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # stage times of the last forward of each instance (all inside the timed loop)
+    stages = [lay.stage_times() for lay, _, _ in insts[: min(n_inst, steps)]]
+    import numpy as np
+    st = np.mean(np.array(stages), axis=0).tolist()
+    counts = insts[(steps - 1) % n_inst][2].expert_counts.cpu().numpy()
+    res = dict(T=T, ms_per_step=1e3 * wall / steps, stage_ms=st, counts=counts)
+    x0 = insts[0][1].cpu() if keep_layer0 else None
+    for lay, _, _ in insts:
+        lay.close()
+    del insts
+    torch.cuda.empty_cache()
+    return res, (keep["layer0"] if keep_layer0 else None), x0
+
+
+def summarize(cfg, res):
+    T = res["T"]
+    up, dn, layer = kernel_work(cfg, res["counts"], T)
+    gate_ms, scat_ms, up_ms, dn_ms, comb_ms = res["stage_ms"]
+    decode = T <= 256 and cfg.expert_dtype != "f32" and (2.0 * T * cfg.top_k / max(layer["active"], 1)) < 300
+    if decode:
+        rf = dict(bound="hbm", achieved=up["bytes"] / (up_ms * 1e-3) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
+    else:
+        rf = dict(bound="mfma", achieved=up["flops"] / (up_ms * 1e-3) / 1e12, peak=MFMA_BF16_PEAK_TFLOPS,
+                  unit="TFLOP/s")
+    rf["frac"] = rf["achieved"] / rf["peak"]
+    rf["traffic"] = None
+    rf["kernel"] = "expert_gemm<up>"
+    rf["avg_ms"] = up_ms
+    layer_s = res["ms_per_step"] * 1e-3
+    return dict(
+        T=T, ms_per_step=res["ms_per_step"], tokens_per_s=T / layer_s,
+        stage_ms=dict(gate=gate_ms, scatter=scat_ms, up=up_ms, down=dn_ms, combine=comb_ms),
+        layer_GBps=layer["bytes"] / layer_s / 1e9, layer_TFLOPs=layer["flops"] / layer_s / 1e12,
+        layer_hbm_frac=layer["bytes"] / layer_s / 1e9 / HBM_PEAK_GBS,
+        layer_mfma_frac=layer["flops"] / layer_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        down_frac=(dn["bytes"] / (dn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS) if decode else
+        (dn["flops"] / (dn_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS),
+        active_experts=layer["active"], roofline=rf)
+
+
+def cpu_baseline(cfg, layer_cpu, x_cpu, n_tok):
+    """The oracle as it stands, on the first n_tok tokens of the same batch."""
+    import numpy as np
+    import oracle
+    from harness import oracle_layer
+    from threadpoolctl import threadpool_info
+    olay = oracle_layer(layer_cpu)
+    xs = x_cpu[:n_tok].float().numpy()
+    t0 = time.perf_counter()
+    oracle.moe_forward(xs, olay)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return dict(value=n_tok / dt, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"{n_tok} tokens of the T={x_cpu.shape[0]} batch, whole layer forward in fp64 "
+                       f"(gate, scatter, {cfg.n_experts} experts, combine), {dt:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import synth
+    import moe_layer_forward_gate_amd as moe
+    moe.lib()
+    torch.cuda.set_device(0)
+    cfg = synth.get_config(args.config)
+    T = args.tokens or max(cfg.tokens)
+    print(f"[bench] {cfg.name} T={T} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
+    want_cpu = not args.no_cpu_baseline
+    res, layer0, x0 = run_workload(cfg, T, args.steps, args.warmup, args.instances, torch, synth,
+                                   keep_layer0=want_cpu)
+    main_s = summarize(cfg, res)
+    print(f"[bench] main {json.dumps(main_s)}", file=sys.stderr, flush=True)
+    sweep = []
+    if not args.no_sweep:
+        for Ts in cfg.tokens:
+            if Ts == T:
+                continue
+            r, _, _ = run_workload(cfg, Ts, max(args.steps, 20), args.warmup, args.instances, torch, synth)
+            s = summarize(cfg, r)
+            sweep.append(s)
+            print(f"[bench] sweep {json.dumps(s)}", file=sys.stderr, flush=True)
+    cpu = None
+    if want_cpu:
+        cpu = cpu_baseline(cfg, layer0, x0, min(args.cpu_sample_tokens, T))
+        print(f"[bench] cpu {json.dumps(cpu)}", file=sys.stderr, flush=True)
+    line = {
+        "metric": "MoE-layer tokens/s; decode HBM TB/s and prefill MFMA TFLOP/s vs roofline",
+        "value": main_s["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_s["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "f32": "f32"}[cfg.act_dtype] + ("+i8w" if cfg.expert_dtype == "i8" else ""),
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: MoE layer d_model={cfg.d_model} E={cfg.n_experts} "
+                               f"d_ff={cfg.d_ff} top-{cfg.top_k}"
+                               + (f" + shared d_ff={cfg.shared_d_ff}" if cfg.shared_d_ff else ""),
+                   "tokens": T, "instances": args.instances},
+        "roofline": {k: main_s["roofline"][k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+        "roofline_kernel": main_s["roofline"]["kernel"],
+        "stage_ms": main_s["stage_ms"],
+        "layer": {k: main_s[k] for k in ("layer_GBps", "layer_TFLOPs", "layer_hbm_frac", "layer_mfma_frac",
+                                         "down_frac", "active_experts")},
+        "sweep": [{k: s[k] for k in ("T", "tokens_per_s", "ms_per_step", "stage_ms", "layer_GBps",
+                                     "layer_hbm_frac", "layer_mfma_frac", "roofline")} for s in sweep],
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,166 @@
+/*
+ * libmoe: the MoE layer forward (Gate -> Scatter -> Expert Compute -> Gather)
+ * on one AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes. Pages are named by address: [0539edu]
+ * www.0539edu.com/news/4774449, [mhpq] www.mhpq.cn/news/563172, [hotelren]
+ * www.hotelren.com/news/4731937, [trdm] www.trdm.cn/news/555962, [pptc]
+ * www.pptc.cn/news/100465.
+ *
+ *   Gate     logits = x W_router (+ b_router)           [hotelren §3.2]
+ *            idx[t, 0..k-1]: the k largest logits of token t, slot 0 the
+ *            largest; equal logits go to the lower expert id ([mhpq §3.2],
+ *            the routing kernel's strict greater-than test);
+ *            w[t, j] = softmax of the k chosen logits    [0539edu §2.1]
+ *   Scatter  assignments a = t*k + j grouped by expert, stable in a, with an
+ *            (E+1)-entry row-offset table                [0539edu §2.2],
+ *            [hotelren §2.3] dispatch_kernel, [pptc §3.3] expert_offsets
+ *   Experts  per expert e: h = silu(X_e W_gate[e]) * (X_e W_up[e]),
+ *            o = h W_down[e]                              [hotelren §2.1 steps 4-5]
+ *   Gather   y[t] = sum_j w[t, j] * o(t, j)              [hotelren §2.3]
+ *            combine_kernel, [pptc §2.1] fused output aggregation
+ *   Shared   optional always-on expert, y[t] += sigmoid(x[t] . w_s) * S(x[t])
+ *            ([0539edu §2.2] shared-expert-augmented MoE, [trdm §8])
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are HIP device pointers, row-major, densely packed.
+ *   - The caller owns every buffer it passes. moe_layer_create copies what it
+ *     needs; the caller may free the weight buffers once it returns.
+ *   - Argument checks run before any HIP call or launch; a failed check writes
+ *     nothing and returns a negative status. moe_last_error() then holds a
+ *     message (thread-local).
+ *   - Inputs holding NaN or Inf are not supported (results unspecified).
+ *
+ * Status codes are the moe_status values below.
+ */
+#ifndef LIBMOE_MOE_H
+#define LIBMOE_MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,        /* bad argument: NULL, out of range, misaligned */
+    MOE_EUNSUPPORTED = -2,  /* valid but not implemented: dtype pair, shape */
+    MOE_ENOMEM = -3,        /* device allocation failed (create only) */
+    MOE_EHIP = -4           /* a HIP runtime call or launch failed */
+} moe_status;
+
+typedef enum moe_dtype {
+    MOE_F32 = 0,   /* IEEE binary32 */
+    MOE_BF16 = 1,  /* bfloat16, stored as 16-bit patterns */
+    MOE_I8 = 2     /* int8 with one fp32 scale per output channel */
+} moe_dtype;
+
+/* Layer shape. Supported (act_dtype, expert_dtype) pairs: (F32, F32),
+ * (BF16, BF16), (BF16, I8). Limits: 1 <= top_k <= n_experts <= 128;
+ * for BF16/I8 experts d_model % 128 == 0 and d_ff % 64 == 0; for F32 experts
+ * d_model % 64 == 0 and d_ff % 64 == 0. shared_d_ff > 0 adds a shared expert
+ * (BF16 experts only) and must be a multiple of d_ff. */
+typedef struct moe_desc {
+    int32_t d_model;
+    int32_t n_experts;
+    int32_t d_ff;
+    int32_t top_k;
+    int32_t max_tokens;     /* largest T any moe_forward call will pass */
+    int32_t act_dtype;      /* moe_dtype of x and y */
+    int32_t expert_dtype;   /* moe_dtype of the expert weights */
+    int32_t shared_d_ff;    /* 0: no shared expert */
+    int32_t profile;        /* 1: record per-stage HIP events (moe_stage_times) */
+} moe_desc;
+
+/* Layer weights (device pointers, read only during moe_layer_create).
+ * Expert matrices are stacked over experts and multiply from the right:
+ *   w_gate, w_up  [E][d_model][d_ff]     element type = expert_dtype
+ *   w_down        [E][d_ff][d_model]
+ *   s_gate, s_up  [E][d_ff]   fp32, I8 only: scale of each output column
+ *   s_down        [E][d_model] fp32, I8 only
+ *   w_router      [d_model][E] fp32 (required)
+ *   b_router      [E] fp32 or NULL (no bias)
+ *   w_shared_gate [d_model] fp32; ws_gate, ws_up [d_model][shared_d_ff] and
+ *   ws_down [shared_d_ff][d_model] bf16 (only when shared_d_ff > 0). */
+typedef struct moe_weights {
+    const float* w_router;
+    const float* b_router;
+    const void* w_gate;
+    const void* w_up;
+    const void* w_down;
+    const float* s_gate;
+    const float* s_up;
+    const float* s_down;
+    const float* w_shared_gate;
+    const void* ws_gate;
+    const void* ws_up;
+    const void* ws_down;
+} moe_weights;
+
+/* Routing results written by moe_forward (device pointers, 4-byte aligned).
+ *   topk_idx        [T][k] int32, required: expert of slot j, slot 0 largest
+ *   topk_w          [T][k] fp32, required: softmax over the chosen logits
+ *   expert_counts   [E] int32 or NULL: assignments per expert
+ *   expert_offsets  [E+1] int32 or NULL: exclusive prefix sum, [E] = T*k
+ *   sorted_assign   [T*k] int32 or NULL: assignment ids a = t*k + j grouped
+ *                   by expert, ascending a within each expert
+ *   shared_gate     [T] fp32 or NULL: sigmoid(x . w_s) (shared expert only) */
+typedef struct moe_route_out {
+    int32_t* topk_idx;
+    float* topk_w;
+    int32_t* expert_counts;
+    int32_t* expert_offsets;
+    int32_t* sorted_assign;
+    float* shared_gate;
+} moe_route_out;
+
+typedef struct moe_layer moe_layer; /* opaque */
+
+/* Create a layer on the current HIP device: checks desc and weights, allocates
+ * the packed weights and a workspace sized for desc->max_tokens, repacks the
+ * caller's weights into the kernels' tile order, and waits for that to finish.
+ * On success *out holds the layer; on failure *out is set to NULL (when out is
+ * not NULL) and nothing is leaked. Statuses: EINVAL (NULL desc/weights/out or a
+ * required weight pointer, non-positive sizes, top_k > n_experts), EUNSUPPORTED
+ * (dtype pair, shape limits), ENOMEM, EHIP. */
+MOE_API int moe_layer_create(const moe_desc* desc, const moe_weights* weights, moe_layer** out);
+
+/* Enqueue one forward pass of T tokens on `stream` (a hipStream_t; NULL is the
+ * default stream) and return without waiting. x [T][d_model] and y
+ * [T][d_model] are in act_dtype and 16-byte aligned; y is fully overwritten.
+ * Allocates nothing. T == 0 enqueues nothing and returns MOE_OK (x, y and
+ * route may then be NULL). Statuses: EINVAL (NULL layer, T < 0,
+ * T > max_tokens, and for T > 0: NULL x/y/route/topk_idx/topk_w, misaligned
+ * pointer, current device differs from the layer's), EHIP.
+ * One layer must not be used by two overlapping calls: its workspace is shared. */
+MOE_API int moe_forward(moe_layer* layer, const void* x, int32_t T, void* y,
+                const moe_route_out* route, void* stream);
+
+/* Per-stage times in milliseconds of the last moe_forward of a layer created
+ * with profile = 1: ms[0] gate, ms[1] scatter, ms[2] expert up (gate/up GEMM
+ * and SiLU), ms[3] expert down, ms[4] gather/combine. Waits for that call's
+ * last event. EINVAL if the layer does not profile or has not run. */
+MOE_API int moe_stage_times(moe_layer* layer, float ms[5]);
+
+/* Release a layer and everything it allocated. NULL-safe. Waits for the
+ * device work of the layer to finish. */
+MOE_API void moe_destroy(moe_layer* layer);
+
+/* Static text of a status code. */
+MOE_API const char* moe_status_str(int status);
+
+/* Message of the last failed call on this thread ("" if none). */
+MOE_API const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMOE_MOE_H */

@@ -1,0 +1,50 @@
+// Gather: y[t] = sum over the token's slots j of the weighted expert outputs.
+//
+// [hotelren §2.1 step 6] and [hotelren §2.3] combine_kernel: the k expert
+// outputs are summed with their gating weights; [pptc §2.1] the k outputs share
+// slices of one buffer and are accumulated into the result. The weights were
+// applied in the down-projection epilogue, which wrote slot (t, j) to row
+// t*kt + j; this pass adds the kt rows of each token in a fixed order (slot 0
+// first), so the result does not depend on scheduling, and rounds once to the
+// output dtype. Each thread handles 4 consecutive columns (d % 4 == 0).
+#include "common.h"
+
+namespace moe {
+namespace {
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ow, int T, int kt, int d,
+                                                      void* __restrict__ y) {
+    const int d4 = d / 4;
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (size_t)T * d4) return;
+    const int t = (int)(i / d4), c4 = (int)(i - (size_t)t * d4);
+    const float4* src = reinterpret_cast<const float4*>(ow + (size_t)t * kt * d) + c4;
+    float4 s = src[0];
+    for (int j = 1; j < kt; ++j) {
+        const float4 v = src[(size_t)j * d4];
+        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    if (BF16) {
+        uint2 o;
+        o.x = (uint32_t)f32_to_bf16(s.x) | ((uint32_t)f32_to_bf16(s.y) << 16);
+        o.y = (uint32_t)f32_to_bf16(s.z) | ((uint32_t)f32_to_bf16(s.w) << 16);
+        reinterpret_cast<uint2*>(y)[i] = o;
+    } else {
+        reinterpret_cast<float4*>(y)[i] = s;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float* ow, int T, int kt, int d, void* y, bool y_bf16, hipStream_t s) {
+    const size_t n = (size_t)T * (d / 4);
+    dim3 grid((unsigned)((n + 255) / 256));
+    if (y_bf16)
+        hipLaunchKernelGGL((combine_kernel<true>), grid, dim3(256), 0, s, ow, T, kt, d, y);
+    else
+        hipLaunchKernelGGL((combine_kernel<false>), grid, dim3(256), 0, s, ow, T, kt, d, y);
+    return hipGetLastError();
+}
+
+}  // namespace moe

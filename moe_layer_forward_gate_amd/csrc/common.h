@@ -1,0 +1,159 @@
+// Internal declarations shared by the libmoe HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // bfloat16 bit pattern
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16-byte chunk (a native vector, so copies stay in registers)
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 128;   // routed experts
+constexpr int kMaxTopK = 64;       // one wave lane per slot in the weight softmax
+constexpr int kXcds = 8;           // MI355X: workgroups are dealt round-robin to 8 XCDs
+
+// bf16 <-> fp32. Widening is exact; narrowing rounds to nearest, ties to even,
+// by integer rounding of the fp32 bit pattern (inputs are finite).
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// ------------------------------------------------------------------ launchers
+// Gate: router logits, top-k with (logit desc, id asc) order, softmax weights over
+// the chosen logits, and (when has_shared) the shared-expert sigmoid gate read
+// from router column E. wr_t is the router weight transposed to [Ec][d].
+hipError_t launch_gate(const void* x, bool x_bf16, const float* wr_t, const float* bias, int T, int d,
+                       int E, bool has_shared, int k, int32_t* idx, float* w, float* gs, hipStream_t s);
+
+// Scatter: counts, offsets and the stable by-expert permutation of the T*k routed
+// assignments, V shared virtual experts appended (each takes every token), and the
+// per-expert tile starts for row tiles of height bm.
+struct ScatterOut {
+    int32_t* counts;        // [Et]
+    int32_t* offsets;       // [Et+1]
+    int32_t* tile_start;    // [Et+1]
+    int32_t* sorted_c;      // [P]: combine slot c = t*kt + j of each sorted row
+    int32_t* user_counts;   // [E] or null
+    int32_t* user_offsets;  // [E+1] or null
+    int32_t* user_sorted;   // [T*k] or null: a = t*k + j
+};
+hipError_t launch_scatter(const int32_t* idx, int T, int E, int k, int V, int bm, const ScatterOut& o,
+                          hipStream_t s);
+
+// Grouped expert GEMMs on bf16 MFMA (expert weights bf16 or int8 in fragment order).
+struct GemmArgs {
+    const int32_t* tile_start;  // [Et+1]
+    const int32_t* offsets;     // [Et+1]
+    const int32_t* sorted_c;    // [P]
+    int Et, kt, k;              // experts incl. virtual, slots per token incl. virtual, routed k
+    int max_tiles;              // bound on sum_e ceil(n_e / BM)
+    // up: A = x rows gathered by token; down: A = H rows
+    const bf16_t* x;            // [T][d]
+    bf16_t* h;                  // [P][F]
+    const void* wgu;            // packed gate/up
+    const void* wdn;            // packed down
+    const float* s_gate;        // [E][F] (int8)
+    const float* s_up;          // [E][F]
+    const float* s_down;        // [E][d]
+    const float* topk_w;        // [T][k]
+    const float* gs;            // [T] shared gate or null
+    float* ow;                  // [T*kt][d] weighted expert outputs
+    int d, F;
+};
+hipError_t launch_expert_up_bf16(const GemmArgs& a, bool int8, hipStream_t s);
+hipError_t launch_expert_down_bf16(const GemmArgs& a, bool int8, hipStream_t s);
+
+// fp32 experts (VALU), weights in natural [E][K][N] layout.
+struct GemmF32Args {
+    const int32_t* tile_start;
+    const int32_t* offsets;
+    const int32_t* sorted_c;
+    int Et, kt, k, max_tiles;
+    const float* x;      // [T][d]
+    float* h;            // [P][F]
+    const float* wg;     // [E][d][F]
+    const float* wu;     // [E][d][F]
+    const float* wd;     // [E][F][d]
+    const float* topk_w;
+    const float* gs;
+    float* ow;
+    int d, F;
+};
+hipError_t launch_expert_up_f32(const GemmF32Args& a, hipStream_t s);
+hipError_t launch_expert_down_f32(const GemmF32Args& a, hipStream_t s);
+
+// Gather: y[t] = sum_{j < kt} ow[t*kt + j], written as bf16 or fp32.
+hipError_t launch_combine(const float* ow, int T, int kt, int d, void* y, bool y_bf16, hipStream_t s);
+
+// Create-time repacking into fragment order (see pack.hip).
+hipError_t pack_router(const float* wr, const float* ws_gate_vec, int d, int E, float* wr_t, hipStream_t s);
+hipError_t pack_gu_bf16(const bf16_t* wg, const bf16_t* wu, int E, int d, int F, bf16_t* dst,
+                        int64_t src_ld, hipStream_t s);
+hipError_t pack_dn_bf16(const bf16_t* wd, int E, int F, int d, bf16_t* dst, hipStream_t s);
+hipError_t pack_gu_i8(const int8_t* wg, const int8_t* wu, int E, int d, int F, int8_t* dst, hipStream_t s);
+hipError_t pack_dn_i8(const int8_t* wd, int E, int F, int d, int8_t* dst, hipStream_t s);
+
+// Row tile height used by the bf16/int8 GEMMs and by the fp32 GEMMs.
+constexpr int kBM = 128;
+constexpr int kBMf32 = 64;
+constexpr int kMaxVirtual = 63;  // shared-expert slices (scatter scan limit)
+
+// One output tile of a grouped expert GEMM: expert e, rows [seg0 + row0, seg0 +
+// row0 + rows) of the by-expert order, column tile n.
+struct Tile {
+    int e, row0, rows, seg0, n;
+};
+
+// Map this workgroup to a tile. Tiles are ordered expert by expert; inside an
+// expert, column tiles come in groups of GN, and within a group the row tiles
+// run fastest, so workgroups that share a weight tile (same n) or an activation
+// tile (same row0) run close together. Workgroup i is dealt to XCD i % 8 by the
+// hardware; the logical index is remapped so each XCD works on one contiguous
+// stretch of tiles and keeps its weight/activation tiles in its own L2.
+// tile_start[e] = sum of ceil(n_e' / bm) over e' < e; it and offsets are read
+// from device memory (the scatter just wrote them), so the grid is launched for
+// an upper bound and idle workgroups return at once.
+__device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ ts, const int32_t* __restrict__ offs,
+                                            int Et, int NT, int GN, int bm, Tile& tl) {
+    const int NTp = (NT + GN - 1) / GN * GN;
+    const int total = ts[Et] * NTp;
+    const int per = (total + kXcds - 1) / kXcds;
+    const int i = blockIdx.x;
+    const int slot = i / kXcds, xcd = i % kXcds;
+    if (slot >= per) return false;
+    const int L = xcd * per + slot;
+    if (L >= total) return false;
+    const int lane = threadIdx.x % kWave;
+    int c = 0;
+    for (int j0 = 0; j0 <= Et; j0 += kWave) {
+        const int j = j0 + lane;
+        const bool ok = j <= Et && ts[j] * NTp <= L;
+        c += __popcll(__ballot(ok));
+    }
+    const int e = c - 1;
+    const int t0 = ts[e], mt = ts[e + 1] - t0;
+    const int local = L - t0 * NTp;
+    const int grp = local / (mt * GN);
+    const int rem = local - grp * mt * GN;
+    const int m = rem / GN;
+    const int n = grp * GN + (rem - m * GN);
+    if (n >= NT) return false;
+    tl.e = e;
+    tl.n = n;
+    tl.row0 = m * bm;
+    tl.seg0 = offs[e];
+    tl.rows = min(bm, offs[e + 1] - tl.seg0 - tl.row0);
+    return true;
+}
+
+}  // namespace moe

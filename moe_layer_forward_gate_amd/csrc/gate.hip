@@ -1,0 +1,287 @@
+// Gate: router logits (fp32), wavefront top-k, softmax over the chosen logits and
+// the shared-expert sigmoid gate.
+//
+// [hotelren §3.2] the router is a linear projection of each token; [0539edu §2.1]
+// the gate yields one logit per expert and the top-k are kept; [mhpq §3.2] the
+// running-maximum selection uses a strict greater-than, so equal logits keep the
+// lower expert id and slot 0 holds the maximum; [pptc §2.1] the top-k is found
+// inside one wavefront with cross-lane shuffles and no block-wide barrier.
+//
+// Two logit paths share the same top-k code:
+//   - gate_rowdot: one workgroup per token, each wave dots the token against a
+//     group of router rows (decode: the router weights are the only real traffic);
+//   - gate_tiled: 64 tokens x all experts per workgroup, an LDS-tiled fp32 GEMM
+//     with register double-buffering (prefill).
+#include "common.h"
+
+namespace moe {
+namespace {
+
+// Order key: larger key = larger logit, then lower expert id. -0.0 is folded to
+// +0.0 so the two compare equal, as they do as floats.
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+    uint32_t u = __float_as_uint(v);
+    if (u == 0x80000000u) u = 0u;
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        uint32_t lo = __shfl_xor((uint32_t)v, off, kWave);
+        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, kWave);
+        uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// One wave: top-k of logits[0..E) (bias already added), weights, shared gate.
+// `logits` may live in LDS; E <= 128, k <= 64.
+__device__ void wave_topk_write(const float* logits, int E, int k, bool has_shared, int t, int32_t* idx,
+                                float* w, float* gs) {
+    const int lane = threadIdx.x % kWave;
+    uint64_t k0 = lane < E ? topk_key(logits[lane], lane) : 0ull;
+    uint64_t k1 = lane + kWave < E ? topk_key(logits[lane + kWave], lane + kWave) : 0ull;
+    int my_e = -1;     // lane j < k keeps slot j's expert
+    for (int j = 0; j < k; ++j) {
+        uint64_t m = wave_max_u64(k0 > k1 ? k0 : k1);
+        int e = (int)(0xFFFFFFFFu - (uint32_t)m);
+        if (k0 == m) k0 = 0ull;
+        if (k1 == m) k1 = 0ull;
+        if (lane == j) my_e = e;
+    }
+    // softmax over the chosen logits, relative to slot 0 (the maximum)
+    float l0 = __shfl(my_e >= 0 ? logits[my_e] : 0.0f, 0, kWave);
+    float ex = lane < k ? expf(logits[my_e] - l0) : 0.0f;
+    float sum = wave_sum(ex);
+    if (lane < k) {
+        idx[(size_t)t * k + lane] = my_e;
+        w[(size_t)t * k + lane] = ex / sum;
+    }
+    if (has_shared && lane == 0) {
+        float z = logits[E];
+        gs[t] = 1.0f / (1.0f + expf(-z));
+    }
+}
+
+template <typename XT>
+__device__ __forceinline__ void load8(const XT* p, float* v);
+template <>
+__device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float* v) {
+    uint4 q = *reinterpret_cast<const uint4*>(p);
+    uint32_t a[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(a[i] << 16);
+        v[2 * i + 1] = __uint_as_float(a[i] & 0xFFFF0000u);
+    }
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float* v) {
+    float4 a = reinterpret_cast<const float4*>(p)[0];
+    float4 b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// ---------------------------------------------------------------- decode path
+// grid = T workgroups of 256 threads; wave g dots the token against router rows
+// e = g*EG .. in steps of 4*EG. d % 8 == 0.
+template <typename XT, int EG>
+__global__ __launch_bounds__(256) void gate_rowdot(const XT* __restrict__ x, const float* __restrict__ wr_t,
+                                                   const float* __restrict__ bias, int d, int E, int Ec, int k,
+                                                   bool has_shared, int32_t* __restrict__ idx,
+                                                   float* __restrict__ w, float* __restrict__ gs) {
+    __shared__ float logits[kMaxExperts + 8];
+    const int t = blockIdx.x;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const XT* xr = x + (size_t)t * d;
+    for (int e0 = wave * EG; e0 < Ec; e0 += 4 * EG) {
+        float acc[EG];
+#pragma unroll
+        for (int g = 0; g < EG; ++g) acc[g] = 0.0f;
+        for (int kk = lane * 8; kk < d; kk += kWave * 8) {
+            float xv[8];
+            load8<XT>(xr + kk, xv);
+#pragma unroll
+            for (int g = 0; g < EG; ++g) {
+                if (e0 + g < Ec) {
+                    float wv[8];
+                    load8<float>(wr_t + (size_t)(e0 + g) * d + kk, wv);
+#pragma unroll
+                    for (int v = 0; v < 8; ++v) acc[g] = fmaf(xv[v], wv[v], acc[g]);
+                }
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < EG; ++g) {
+            float s = wave_sum(acc[g]);
+            if (lane == 0 && e0 + g < Ec) logits[e0 + g] = s + ((bias && e0 + g < E) ? bias[e0 + g] : 0.0f);
+        }
+    }
+    __syncthreads();
+    if (wave == 0) wave_topk_write(logits, E, k, has_shared, t, idx, w, gs);
+}
+
+// ---------------------------------------------------------------- prefill path
+// 64 tokens x (16*EJ) router columns per workgroup; thread (ty, tx) owns tokens
+// 4*ty..4*ty+3 and columns tx + 16*j. K advances in chunks of 32 with the next
+// chunk held in registers while the current one is consumed from LDS.
+constexpr int kTB = 64;
+constexpr int kKC = 32;
+
+template <typename XT, int EJ>
+__global__ __launch_bounds__(256) void gate_tiled(const XT* __restrict__ x, const float* __restrict__ wr_t,
+                                                  const float* __restrict__ bias, int T, int d, int E, int Ec,
+                                                  int k, bool has_shared, int32_t* __restrict__ idx,
+                                                  float* __restrict__ w, float* __restrict__ gs) {
+    constexpr int ECP = 16 * EJ;
+    constexpr int XP = kTB + 4;                       // padded token stride of the x tile
+    constexpr int LP = ECP + 1;                       // padded stride of the logit tile
+    constexpr int XS = 2 * kKC * XP;
+    constexpr int WS = 2 * kKC * ECP;
+    constexpr int SMEM = (XS + WS) > (kTB * LP) ? (XS + WS) : (kTB * LP);
+    __shared__ float smem[SMEM];
+    float* xs = smem;            // [2][KC][XP]   xs[k][token]
+    float* ws = smem + XS;       // [2][KC][ECP]  ws[k][col]
+
+    const int tid = threadIdx.x;
+    const int ty = tid / 16, tx = tid % 16;
+    const int t0 = blockIdx.x * kTB;
+
+    // x chunk: thread loads 8 consecutive k of token tid/4 (64 tokens x 32 k)
+    const int xl_tok = tid / 4, xl_k = (tid % 4) * 8;
+    const bool xl_ok = t0 + xl_tok < T;
+    const XT* xl_ptr = x + (size_t)(t0 + (xl_ok ? xl_tok : 0)) * d + xl_k;
+    // w chunk: ECP rows x 32 k = ECP*8 float4; thread handles float4 q = tid + 256*i
+    constexpr int WQ = (ECP * 8 + 255) / 256;
+
+    float xr[8];
+    float4 wr[WQ];
+    auto gload = [&](int kc) {
+        if (xl_ok) load8<XT>(xl_ptr + kc, xr);
+        else {
+#pragma unroll
+            for (int v = 0; v < 8; ++v) xr[v] = 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < WQ; ++i) {
+            int q = tid + 256 * i;
+            int row = q / 8, c4 = q % 8;
+            if (q < ECP * 8 && row < Ec)
+                wr[i] = *reinterpret_cast<const float4*>(wr_t + (size_t)row * d + kc + c4 * 4);
+            else
+                wr[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    auto sstore = [&](int buf) {
+        float* xb = xs + buf * kKC * XP;
+        float* wb = ws + buf * kKC * ECP;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) xb[(xl_k + v) * XP + xl_tok] = xr[v];
+#pragma unroll
+        for (int i = 0; i < WQ; ++i) {
+            int q = tid + 256 * i;
+            int row = q / 8, c4 = q % 8;
+            if (q < ECP * 8) {
+                wb[(c4 * 4 + 0) * ECP + row] = wr[i].x;
+                wb[(c4 * 4 + 1) * ECP + row] = wr[i].y;
+                wb[(c4 * 4 + 2) * ECP + row] = wr[i].z;
+                wb[(c4 * 4 + 3) * ECP + row] = wr[i].w;
+            }
+        }
+    };
+
+    float acc[4][EJ];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < EJ; ++j) acc[i][j] = 0.0f;
+
+    const int nk = d / kKC;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) gload((kt + 1) * kKC);
+        const float* xb = xs + buf * kKC * XP;
+        const float* wb = ws + buf * kKC * ECP;
+#pragma unroll 8
+        for (int kk = 0; kk < kKC; ++kk) {
+            float4 xv = *reinterpret_cast<const float4*>(xb + kk * XP + ty * 4);
+            float wv[EJ];
+#pragma unroll
+            for (int j = 0; j < EJ; ++j) wv[j] = wb[kk * ECP + tx + 16 * j];
+#pragma unroll
+            for (int j = 0; j < EJ; ++j) {
+                acc[0][j] = fmaf(xv.x, wv[j], acc[0][j]);
+                acc[1][j] = fmaf(xv.y, wv[j], acc[1][j]);
+                acc[2][j] = fmaf(xv.z, wv[j], acc[2][j]);
+                acc[3][j] = fmaf(xv.w, wv[j], acc[3][j]);
+            }
+        }
+        if (kt + 1 < nk) sstore(buf ^ 1);
+        __syncthreads();
+    }
+    // logits tile [64][LP] (reuses the staging buffers; all reads finished above)
+    float* lt = smem;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < EJ; ++j) {
+            int col = tx + 16 * j;
+            float b = (bias && col < E) ? bias[col] : 0.0f;
+            lt[(ty * 4 + i) * LP + col] = acc[i][j] + b;
+        }
+    __syncthreads();
+    const int wave = tid / kWave;
+    for (int r = wave; r < kTB; r += 4) {
+        if (t0 + r < T) wave_topk_write(lt + r * LP, E, k, has_shared, t0 + r, idx, w, gs);
+    }
+}
+
+template <typename XT>
+hipError_t launch_gate_t(const XT* x, const float* wr_t, const float* bias, int T, int d, int E, bool has_shared,
+                         int k, int32_t* idx, float* w, float* gs, hipStream_t s) {
+    const int Ec = E + (has_shared ? 1 : 0);
+    if (T <= 64) {
+        hipLaunchKernelGGL((gate_rowdot<XT, 4>), dim3(T), dim3(256), 0, s, x, wr_t, bias, d, E, Ec, k, has_shared,
+                           idx, w, gs);
+    } else {
+        const int EJ = (Ec + 15) / 16;
+        dim3 grid((T + kTB - 1) / kTB);
+        switch (EJ) {
+#define GATE_CASE(J)                                                                                          \
+    case J:                                                                                                   \
+        hipLaunchKernelGGL((gate_tiled<XT, J>), grid, dim3(256), 0, s, x, wr_t, bias, T, d, E, Ec, k,         \
+                           has_shared, idx, w, gs);                                                           \
+        break;
+            GATE_CASE(1) GATE_CASE(2) GATE_CASE(3) GATE_CASE(4) GATE_CASE(5)
+            GATE_CASE(6) GATE_CASE(7) GATE_CASE(8) GATE_CASE(9)
+#undef GATE_CASE
+            default:
+                return hipErrorInvalidValue;
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gate(const void* x, bool x_bf16, const float* wr_t, const float* bias, int T, int d, int E,
+                       bool has_shared, int k, int32_t* idx, float* w, float* gs, hipStream_t s) {
+    if (x_bf16)
+        return launch_gate_t<bf16_t>((const bf16_t*)x, wr_t, bias, T, d, E, has_shared, k, idx, w, gs, s);
+    return launch_gate_t<float>((const float*)x, wr_t, bias, T, d, E, has_shared, k, idx, w, gs, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,312 @@
+// libmoe C ABI: argument checks, layer creation (packing + workspace), the
+// forward pass as a fixed sequence of launches on the caller's stream, and
+// teardown. The host side plans launch shapes from T, k and the layer shape
+// ([hotelren §2.2]: grid, block and shared memory come from the batch and top-k,
+// computed by the host); everything that depends on the routing itself (expert
+// counts, tile lists) stays on the device, so a forward never waits on the host.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+
+#include "../../include/moe.h"
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+#define HIP_TRY(expr)                                                                                       \
+    do {                                                                                                    \
+        hipError_t e_ = (expr);                                                                             \
+        if (e_ != hipSuccess) return fail(MOE_EHIP, "%s: %s (%s:%d)", #expr, hipGetErrorString(e_), __FILE__, \
+                                          __LINE__);                                                        \
+    } while (0)
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+struct moe_layer {
+    moe_desc desc{};
+    int device = 0;
+    int E = 0, V = 0, Et = 0, kt = 0, Ec = 0;
+    bool has_bias = false;
+    // packed weights
+    float* wr_t = nullptr;
+    float* bias = nullptr;
+    void* wgu = nullptr;
+    void* wdn = nullptr;
+    float* s_gate = nullptr;
+    float* s_up = nullptr;
+    float* s_down = nullptr;
+    // workspace
+    int32_t* counts = nullptr;
+    int32_t* offsets = nullptr;
+    int32_t* tile_start = nullptr;
+    int32_t* sorted_c = nullptr;
+    float* gs = nullptr;
+    void* h = nullptr;
+    float* ow = nullptr;
+    // profiling
+    hipEvent_t ev[6] = {};
+    bool ran = false;
+};
+
+namespace {
+
+void release(moe_layer* L) {
+    if (!L) return;
+    void* bufs[] = {L->wr_t, L->bias, L->wgu, L->wdn, L->s_gate, L->s_up, L->s_down, L->counts, L->offsets,
+                    L->tile_start, L->sorted_c, L->gs, L->h, L->ow};
+    for (void* p : bufs)
+        if (p) (void)hipFree(p);
+    for (hipEvent_t e : L->ev)
+        if (e) (void)hipEventDestroy(e);
+    delete L;
+}
+
+template <typename T>
+int dev_alloc(T** p, size_t bytes) {
+    if (bytes == 0) bytes = 16;
+    hipError_t e = hipMalloc((void**)p, bytes);
+    if (e != hipSuccess) {
+        *p = nullptr;
+        (void)hipGetLastError();
+        return fail(MOE_ENOMEM, "hipMalloc(%zu bytes) failed: %s", bytes, hipGetErrorString(e));
+    }
+    return MOE_OK;
+}
+
+int check_desc(const moe_desc* d, const moe_weights* w) {
+    if (d->d_model <= 0 || d->n_experts <= 0 || d->d_ff <= 0 || d->top_k <= 0 || d->max_tokens <= 0)
+        return fail(MOE_EINVAL, "sizes must be positive (d_model=%d n_experts=%d d_ff=%d top_k=%d max_tokens=%d)",
+                    d->d_model, d->n_experts, d->d_ff, d->top_k, d->max_tokens);
+    if (d->top_k > d->n_experts) return fail(MOE_EINVAL, "top_k=%d > n_experts=%d", d->top_k, d->n_experts);
+    if (d->shared_d_ff < 0) return fail(MOE_EINVAL, "shared_d_ff < 0");
+    if (d->profile != 0 && d->profile != 1) return fail(MOE_EINVAL, "profile must be 0 or 1");
+    if (!w->w_router || !w->w_gate || !w->w_up || !w->w_down)
+        return fail(MOE_EINVAL, "w_router, w_gate, w_up and w_down are required");
+    const bool f32 = d->act_dtype == MOE_F32 && d->expert_dtype == MOE_F32;
+    const bool bf = d->act_dtype == MOE_BF16 && d->expert_dtype == MOE_BF16;
+    const bool i8 = d->act_dtype == MOE_BF16 && d->expert_dtype == MOE_I8;
+    if (!(f32 || bf || i8))
+        return fail(MOE_EUNSUPPORTED, "dtype pair (act=%d, expert=%d) not supported", d->act_dtype,
+                    d->expert_dtype);
+    if (i8 && (!w->s_gate || !w->s_up || !w->s_down))
+        return fail(MOE_EINVAL, "int8 experts need s_gate, s_up and s_down");
+    if (d->shared_d_ff > 0 && (!w->w_shared_gate || !w->ws_gate || !w->ws_up || !w->ws_down))
+        return fail(MOE_EINVAL, "shared expert needs w_shared_gate, ws_gate, ws_up and ws_down");
+    if (d->n_experts > kMaxExperts) return fail(MOE_EUNSUPPORTED, "n_experts=%d > %d", d->n_experts, kMaxExperts);
+    if (d->top_k > kMaxTopK) return fail(MOE_EUNSUPPORTED, "top_k=%d > %d", d->top_k, kMaxTopK);
+    const int dm = f32 ? 64 : 128;
+    if (d->d_model % dm || d->d_ff % 64)
+        return fail(MOE_EUNSUPPORTED, "need d_model %% %d == 0 and d_ff %% 64 == 0 (d_model=%d d_ff=%d)", dm,
+                    d->d_model, d->d_ff);
+    if (d->shared_d_ff > 0) {
+        if (!bf) return fail(MOE_EUNSUPPORTED, "a shared expert needs bf16 experts");
+        if (d->shared_d_ff % d->d_ff)
+            return fail(MOE_EUNSUPPORTED, "shared_d_ff=%d must be a multiple of d_ff=%d", d->shared_d_ff, d->d_ff);
+        if (d->shared_d_ff / d->d_ff > kMaxVirtual)
+            return fail(MOE_EUNSUPPORTED, "shared_d_ff / d_ff = %d > %d", d->shared_d_ff / d->d_ff, kMaxVirtual);
+    }
+    // all index arithmetic in the kernels is 32-bit on rows and slots
+    const long long P = (long long)d->max_tokens * (d->top_k + (d->shared_d_ff / d->d_ff));
+    if (P >= (1ll << 30)) return fail(MOE_EUNSUPPORTED, "max_tokens * slots too large (%lld)", P);
+    return MOE_OK;
+}
+
+int create_impl(const moe_desc* desc, const moe_weights* w, moe_layer* L) {
+    const moe_desc& d = *desc;
+    L->desc = d;
+    L->E = d.n_experts;
+    L->V = d.shared_d_ff / d.d_ff;
+    L->Et = L->E + L->V;
+    L->kt = d.top_k + L->V;
+    L->Ec = L->E + (d.shared_d_ff > 0 ? 1 : 0);
+    L->has_bias = w->b_router != nullptr;
+    HIP_TRY(hipGetDevice(&L->device));
+
+    const size_t dm = d.d_model, F = d.d_ff, E = L->E, Et = L->Et;
+    const bool f32 = d.expert_dtype == MOE_F32;
+    const bool i8 = d.expert_dtype == MOE_I8;
+    const size_t esz = f32 ? 4 : (i8 ? 1 : 2);
+    int rc;
+    if ((rc = dev_alloc(&L->wr_t, (size_t)L->Ec * dm * 4))) return rc;
+    if (L->has_bias && (rc = dev_alloc(&L->bias, E * 4))) return rc;
+    if ((rc = dev_alloc(&L->wgu, Et * 2 * F * dm * esz))) return rc;
+    if ((rc = dev_alloc(&L->wdn, Et * F * dm * esz))) return rc;
+    if (i8) {
+        if ((rc = dev_alloc(&L->s_gate, E * F * 4))) return rc;
+        if ((rc = dev_alloc(&L->s_up, E * F * 4))) return rc;
+        if ((rc = dev_alloc(&L->s_down, E * dm * 4))) return rc;
+    }
+    const size_t T = d.max_tokens, P = T * L->kt;
+    if ((rc = dev_alloc(&L->counts, (Et + 1) * 4))) return rc;
+    if ((rc = dev_alloc(&L->offsets, (Et + 1) * 4))) return rc;
+    if ((rc = dev_alloc(&L->tile_start, (Et + 1) * 4))) return rc;
+    if ((rc = dev_alloc(&L->sorted_c, P * 4))) return rc;
+    if ((rc = dev_alloc(&L->gs, T * 4))) return rc;
+    if ((rc = dev_alloc(&L->h, P * F * (f32 ? 4 : 2)))) return rc;
+    if ((rc = dev_alloc(&L->ow, P * dm * 4))) return rc;
+    if (d.profile)
+        for (hipEvent_t& e : L->ev) HIP_TRY(hipEventCreate(&e));
+
+    hipStream_t s = nullptr;
+    HIP_TRY(pack_router(w->w_router, d.shared_d_ff > 0 ? w->w_shared_gate : nullptr, d.d_model, L->E, L->wr_t, s));
+    if (L->has_bias) HIP_TRY(hipMemcpyAsync(L->bias, w->b_router, E * 4, hipMemcpyDeviceToDevice, s));
+    if (f32) {
+        // fp32 experts keep the natural layout: [E][d][F] gate, [E][d][F] up, [E][F][d] down
+        HIP_TRY(hipMemcpyAsync(L->wgu, w->w_gate, E * dm * F * 4, hipMemcpyDeviceToDevice, s));
+        HIP_TRY(hipMemcpyAsync((char*)L->wgu + E * dm * F * 4, w->w_up, E * dm * F * 4, hipMemcpyDeviceToDevice, s));
+        HIP_TRY(hipMemcpyAsync(L->wdn, w->w_down, E * F * dm * 4, hipMemcpyDeviceToDevice, s));
+    } else if (i8) {
+        HIP_TRY(pack_gu_i8((const int8_t*)w->w_gate, (const int8_t*)w->w_up, L->E, d.d_model, d.d_ff,
+                           (int8_t*)L->wgu, s));
+        HIP_TRY(pack_dn_i8((const int8_t*)w->w_down, L->E, d.d_ff, d.d_model, (int8_t*)L->wdn, s));
+        HIP_TRY(hipMemcpyAsync(L->s_gate, w->s_gate, E * F * 4, hipMemcpyDeviceToDevice, s));
+        HIP_TRY(hipMemcpyAsync(L->s_up, w->s_up, E * F * 4, hipMemcpyDeviceToDevice, s));
+        HIP_TRY(hipMemcpyAsync(L->s_down, w->s_down, E * dm * 4, hipMemcpyDeviceToDevice, s));
+    } else {
+        HIP_TRY(pack_gu_bf16((const bf16_t*)w->w_gate, (const bf16_t*)w->w_up, L->E, d.d_model, d.d_ff,
+                             (bf16_t*)L->wgu, d.d_ff, s));
+        HIP_TRY(pack_dn_bf16((const bf16_t*)w->w_down, L->E, d.d_ff, d.d_model, (bf16_t*)L->wdn, s));
+        // shared expert: slice v = columns [v*F, (v+1)*F) of ws_gate/ws_up and rows of ws_down
+        for (int v = 0; v < L->V; ++v) {
+            const size_t eo = (size_t)(L->E + v);
+            HIP_TRY(pack_gu_bf16((const bf16_t*)w->ws_gate + (size_t)v * F, (const bf16_t*)w->ws_up + (size_t)v * F,
+                                 1, d.d_model, d.d_ff, (bf16_t*)L->wgu + eo * 2 * F * dm, d.shared_d_ff, s));
+            HIP_TRY(pack_dn_bf16((const bf16_t*)w->ws_down + (size_t)v * F * dm, 1, d.d_ff, d.d_model,
+                                 (bf16_t*)L->wdn + eo * F * dm, s));
+        }
+    }
+    HIP_TRY(hipStreamSynchronize(s));
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(int status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+        case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: unsupported configuration";
+        case MOE_ENOMEM: return "MOE_ENOMEM: device allocation failed";
+        case MOE_EHIP: return "MOE_EHIP: HIP runtime error";
+        default: return "unknown moe status";
+    }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int moe_layer_create(const moe_desc* desc, const moe_weights* weights, moe_layer** out) {
+    g_err[0] = 0;
+    if (!out) return fail(MOE_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (!desc || !weights) return fail(MOE_EINVAL, "desc and weights are required");
+    int rc = check_desc(desc, weights);
+    if (rc) return rc;
+    moe_layer* L = new (std::nothrow) moe_layer();
+    if (!L) return fail(MOE_ENOMEM, "host allocation failed");
+    rc = create_impl(desc, weights, L);
+    if (rc) {
+        release(L);
+        return rc;
+    }
+    *out = L;
+    return MOE_OK;
+}
+
+int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route_out* r, void* stream) {
+    g_err[0] = 0;
+    if (!L) return fail(MOE_EINVAL, "layer is NULL");
+    if (T < 0 || T > L->desc.max_tokens) return fail(MOE_EINVAL, "T=%d outside [0, %d]", T, L->desc.max_tokens);
+    if (T == 0) return MOE_OK;  // nothing to read or write; buffers may be empty
+    if (!x || !y || !r || !r->topk_idx || !r->topk_w)
+        return fail(MOE_EINVAL, "x, y, route, route->topk_idx and route->topk_w are required");
+    if (!aligned(x, 16) || !aligned(y, 16)) return fail(MOE_EINVAL, "x and y must be 16-byte aligned");
+    const void* rp[] = {r->topk_idx, r->topk_w, r->expert_counts, r->expert_offsets, r->sorted_assign,
+                        r->shared_gate};
+    for (const void* p : rp)
+        if (p && !aligned(p, 4)) return fail(MOE_EINVAL, "route outputs must be 4-byte aligned");
+    int dev = -1;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev != L->device) return fail(MOE_EINVAL, "current device %d is not the layer's device %d", dev, L->device);
+
+    hipStream_t s = (hipStream_t)stream;
+    const moe_desc& d = L->desc;
+    const bool f32 = d.expert_dtype == MOE_F32;
+    const bool i8 = d.expert_dtype == MOE_I8;
+    const int k = d.top_k;
+    float* gs = r->shared_gate ? r->shared_gate : L->gs;
+    const bool prof = d.profile != 0;
+    if (prof) HIP_TRY(hipEventRecord(L->ev[0], s));
+
+    HIP_TRY(launch_gate(x, !f32, L->wr_t, L->bias, T, d.d_model, L->E, L->V > 0, k, r->topk_idx, r->topk_w, gs, s));
+    if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
+
+    const int bm = f32 ? kBMf32 : kBM;
+    ScatterOut so{L->counts, L->offsets, L->tile_start, L->sorted_c, r->expert_counts, r->expert_offsets,
+                  r->sorted_assign};
+    HIP_TRY(launch_scatter(r->topk_idx, T, L->E, k, L->V, bm, so, s));
+    if (prof) HIP_TRY(hipEventRecord(L->ev[2], s));
+
+    // upper bound on sum_e ceil(n_e / bm) over experts with rows
+    const int P = T * L->kt;
+    const int max_tiles = (P + bm - 1) / bm + std::min(L->Et, P);
+    if (f32) {
+        GemmF32Args a{L->tile_start, L->offsets, L->sorted_c, L->Et, L->kt, k, max_tiles,
+                      (const float*)x, (float*)L->h, (const float*)L->wgu,
+                      (const float*)L->wgu + (size_t)L->E * d.d_model * d.d_ff, (const float*)L->wdn,
+                      r->topk_w, gs, L->ow, d.d_model, d.d_ff};
+        HIP_TRY(launch_expert_up_f32(a, s));
+        if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));
+        HIP_TRY(launch_expert_down_f32(a, s));
+    } else {
+        GemmArgs a{L->tile_start, L->offsets, L->sorted_c, L->Et, L->kt, k, max_tiles,
+                   (const bf16_t*)x, (bf16_t*)L->h, L->wgu, L->wdn, L->s_gate, L->s_up, L->s_down,
+                   r->topk_w, gs, L->ow, d.d_model, d.d_ff};
+        HIP_TRY(launch_expert_up_bf16(a, i8, s));
+        if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));
+        HIP_TRY(launch_expert_down_bf16(a, i8, s));
+    }
+    if (prof) HIP_TRY(hipEventRecord(L->ev[4], s));
+    HIP_TRY(launch_combine(L->ow, T, L->kt, d.d_model, y, !f32, s));
+    if (prof) {
+        HIP_TRY(hipEventRecord(L->ev[5], s));
+        L->ran = true;
+    }
+    return MOE_OK;
+}
+
+int moe_stage_times(moe_layer* L, float ms[5]) {
+    g_err[0] = 0;
+    if (!L || !ms) return fail(MOE_EINVAL, "layer and ms are required");
+    if (!L->desc.profile) return fail(MOE_EINVAL, "layer was created with profile = 0");
+    if (!L->ran) return fail(MOE_EINVAL, "no profiled forward has run");
+    HIP_TRY(hipEventSynchronize(L->ev[5]));
+    for (int i = 0; i < 5; ++i) HIP_TRY(hipEventElapsedTime(&ms[i], L->ev[i], L->ev[i + 1]));
+    return MOE_OK;
+}
+
+void moe_destroy(moe_layer* L) {
+    if (!L) return;
+    (void)hipDeviceSynchronize();
+    release(L);
+}
+
+}  // extern "C"

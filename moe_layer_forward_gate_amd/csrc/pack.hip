@@ -1,0 +1,90 @@
+// Create-time repacking of the caller's weights into the kernels' layouts.
+//
+// [0539edu §3.1] weights are reorganised once, expert by expert, into one
+// contiguous block per expert, and [hotelren §3.1] transposed to output-major
+// ([out][in]) so a GEMM reads each output column's inputs contiguously. Here the
+// target is the MFMA fragment order read by the expert GEMMs:
+//   bf16 gate/up: [Et][2F/16][d/32][64 lanes][8]; packed 16-column block nb is
+//                 gate columns 16*(nb/2).. when nb is even, up columns when odd;
+//                 lane l, element v = column 16*(nb/2) + l%16, K row 32*ks + 8*(l/16) + v
+//   bf16 down:    [Et][d/16][F/32][64][8], column nb*16 + l%16 of W_down
+//   int8:         the same with 64 K rows per block and 16 bytes per lane,
+//                 bytes 0-7 from the block's first 32 rows, bytes 8-15 the next 32
+// and the router weight transposed to [Ec][d] (row E = the shared-expert gate).
+// One thread writes one 16-byte lane chunk; runs once per layer.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+__global__ void pack_router_kernel(const float* wr, const float* wsg, int d, int E, int Ec, float* out) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (size_t)Ec * d) return;
+    const int e = (int)(i / d), k = (int)(i - (size_t)e * d);
+    out[i] = e < E ? wr[(size_t)k * E + e] : wsg[k];
+}
+
+// src element (e, k, n) at src + e*K*ld + k*ld + n; for gate/up the packed column
+// block nb reads src0 (gate) or src1 (up) at column 16*(nb/2).
+template <typename T, int KPB>  // KPB: K rows per packed block (32 bf16, 64 int8)
+__global__ void pack_kernel(const T* src0, const T* src1, int E, int K, int N, int64_t ld, bool gu, T* dst) {
+    constexpr int PER = 16 / sizeof(T);  // elements per lane chunk
+    const int NB = gu ? 2 * N / 16 : N / 16;
+    const int KB = K / KPB;
+    const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t total = (size_t)E * NB * KB * 64;
+    if (q >= total) return;
+    const int ln = (int)(q % 64);
+    size_t rest = q / 64;
+    const int kb = (int)(rest % KB);
+    rest /= KB;
+    const int nb = (int)(rest % NB);
+    const int e = (int)(rest / NB);
+    const T* src = (gu && (nb & 1)) ? src1 : src0;
+    const int n = (gu ? (nb / 2) : nb) * 16 + ln % 16;
+    T v[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int k = kb * KPB + (j / 8) * 32 + 8 * (ln / 16) + (j % 8);
+        v[j] = src[(size_t)e * K * ld + (size_t)k * ld + n];
+    }
+    uint4 out;
+    __builtin_memcpy(&out, v, 16);
+    reinterpret_cast<uint4*>(dst)[q] = out;
+}
+
+template <typename T, int KPB>
+hipError_t launch_pack(const T* s0, const T* s1, int E, int K, int N, int64_t ld, bool gu, T* dst, hipStream_t s) {
+    const int NB = gu ? 2 * N / 16 : N / 16;
+    const size_t total = (size_t)E * NB * (K / KPB) * 64;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL((pack_kernel<T, KPB>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, s0, s1, E, K,
+                       N, ld, gu, dst);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t pack_router(const float* wr, const float* wsg, int d, int E, float* wr_t, hipStream_t s) {
+    const int Ec = E + (wsg ? 1 : 0);
+    const size_t n = (size_t)Ec * d;
+    hipLaunchKernelGGL(pack_router_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, wr, wsg, d, E, Ec,
+                       wr_t);
+    return hipGetLastError();
+}
+
+hipError_t pack_gu_bf16(const bf16_t* wg, const bf16_t* wu, int E, int d, int F, bf16_t* dst, int64_t src_ld,
+                        hipStream_t s) {
+    return launch_pack<bf16_t, 32>(wg, wu, E, d, F, src_ld, true, dst, s);
+}
+hipError_t pack_dn_bf16(const bf16_t* wd, int E, int F, int d, bf16_t* dst, hipStream_t s) {
+    return launch_pack<bf16_t, 32>(wd, wd, E, F, d, d, false, dst, s);
+}
+hipError_t pack_gu_i8(const int8_t* wg, const int8_t* wu, int E, int d, int F, int8_t* dst, hipStream_t s) {
+    return launch_pack<int8_t, 64>(wg, wu, E, d, F, F, true, dst, s);
+}
+hipError_t pack_dn_i8(const int8_t* wd, int E, int F, int d, int8_t* dst, hipStream_t s) {
+    return launch_pack<int8_t, 64>(wd, wd, E, F, d, d, false, dst, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,109 @@
+"""The C ABI on the CPU: libmoe loads, exports every declared symbol, and rejects
+bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_layer_forward_gate_amd as moe
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", txt)))
+
+
+def test_header_declares_binding_names():
+    assert _declared() == sorted(moe.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    assert moe.moe_status_str(0) == "MOE_OK"
+    assert moe.moe_status_str(-1).startswith("MOE_EINVAL")
+    assert moe.moe_status_str(-2).startswith("MOE_EUNSUPPORTED")
+    assert moe.moe_status_str(-3).startswith("MOE_ENOMEM")
+    assert moe.moe_status_str(-4).startswith("MOE_EHIP")
+    assert moe.moe_status_str(5) == "unknown moe status"
+
+
+def _desc(**kw):
+    base = dict(d_model=256, n_experts=8, d_ff=512, top_k=2, max_tokens=64, act_dtype=moe.MOE_BF16,
+                expert_dtype=moe.MOE_BF16, shared_d_ff=0, profile=0)
+    base.update(kw)
+    return moe.MoeDesc(**base)
+
+
+def _weights(**kw):
+    fake = 0x10000  # never dereferenced: every case below fails its checks first
+    base = dict(w_router=fake, b_router=0, w_gate=fake, w_up=fake, w_down=fake, s_gate=0, s_up=0, s_down=0,
+                w_shared_gate=0, ws_gate=0, ws_up=0, ws_down=0)
+    base.update(kw)
+    return moe.MoeWeights(**base)
+
+
+def _create(desc, weights):
+    h = ctypes.c_void_p(0xDEAD)
+    rc = moe.lib().moe_layer_create(ctypes.byref(desc) if desc is not None else None,
+                                    ctypes.byref(weights) if weights is not None else None, ctypes.byref(h))
+    return rc, h
+
+
+@pytest.mark.parametrize("desc,weights,status", [
+    (None, _weights(), moe.MOE_EINVAL),
+    (_desc(), None, moe.MOE_EINVAL),
+    (_desc(d_model=0), _weights(), moe.MOE_EINVAL),
+    (_desc(max_tokens=-1), _weights(), moe.MOE_EINVAL),
+    (_desc(top_k=9), _weights(), moe.MOE_EINVAL),
+    (_desc(top_k=0), _weights(), moe.MOE_EINVAL),
+    (_desc(profile=2), _weights(), moe.MOE_EINVAL),
+    (_desc(), _weights(w_gate=0), moe.MOE_EINVAL),
+    (_desc(), _weights(w_router=0), moe.MOE_EINVAL),
+    (_desc(expert_dtype=moe.MOE_I8), _weights(), moe.MOE_EINVAL),            # scales missing
+    (_desc(shared_d_ff=1024), _weights(), moe.MOE_EINVAL),                    # shared weights missing
+    (_desc(act_dtype=moe.MOE_F32, expert_dtype=moe.MOE_BF16), _weights(), moe.MOE_EUNSUPPORTED),
+    (_desc(act_dtype=moe.MOE_BF16, expert_dtype=moe.MOE_F32), _weights(), moe.MOE_EUNSUPPORTED),
+    (_desc(act_dtype=7), _weights(), moe.MOE_EUNSUPPORTED),
+    (_desc(d_model=192), _weights(), moe.MOE_EUNSUPPORTED),                   # bf16 needs d % 128
+    (_desc(d_ff=96), _weights(), moe.MOE_EUNSUPPORTED),
+    (_desc(n_experts=129, top_k=2), _weights(), moe.MOE_EUNSUPPORTED),
+    (_desc(n_experts=128, top_k=65), _weights(), moe.MOE_EUNSUPPORTED),
+    (_desc(shared_d_ff=700), _weights(w_shared_gate=1 << 16, ws_gate=1 << 16, ws_up=1 << 16, ws_down=1 << 16),
+     moe.MOE_EUNSUPPORTED),                                                   # not a multiple of d_ff
+    (_desc(expert_dtype=moe.MOE_I8, shared_d_ff=1024),
+     _weights(s_gate=1 << 16, s_up=1 << 16, s_down=1 << 16, w_shared_gate=1 << 16, ws_gate=1 << 16,
+              ws_up=1 << 16, ws_down=1 << 16), moe.MOE_EUNSUPPORTED),
+    (_desc(max_tokens=1 << 29, top_k=2), _weights(), moe.MOE_EUNSUPPORTED),
+])
+def test_create_rejects(desc, weights, status):
+    rc, h = _create(desc, weights)
+    assert rc == status, moe.moe_last_error()
+    assert h.value is None  # *out set to NULL
+    assert moe.moe_last_error() != ""
+
+
+def test_create_null_out():
+    rc = moe.lib().moe_layer_create(ctypes.byref(_desc()), ctypes.byref(_weights()), None)
+    assert rc == moe.MOE_EINVAL
+
+
+def test_forward_rejects_before_gpu():
+    L = moe.lib()
+    route = moe.MoeRouteOut(0x10000, 0x10000, 0, 0, 0, 0)
+    assert L.moe_forward(None, 0x10000, 4, 0x10000, ctypes.byref(route), None) == moe.MOE_EINVAL
+    assert "layer" in moe.moe_last_error()
+
+
+def test_stage_times_and_destroy_null():
+    L = moe.lib()
+    ms = (ctypes.c_float * 5)()
+    assert L.moe_stage_times(None, ms) == moe.MOE_EINVAL
+    L.moe_destroy(None)  # NULL-safe

@@ -1,0 +1,62 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (one layer, one moe_forward per batch).
+
+Routing (indices, weights, counts, offsets, permutation) is compared for every
+token; outputs for all tokens at decode sizes and for a sample of token rows at
+prefill sizes (the oracle evaluates the sampled rows one expert at a time).
+Layers are drawn on the GPU with torch's seeded generator to keep set-up short;
+the oracle gets host copies of the same tensors.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from harness import compare, gpu_layer, oracle_layer
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample(T, n=16, seed=0):
+    if T <= n:
+        return None
+    rng = np.random.default_rng(seed)
+    s = set([0, T - 1]) | set(rng.choice(T, n - 2, replace=False).tolist())
+    return sorted(s)
+
+
+def _run(name, Ts):
+    cfg = synth.get_config(name)
+    print(f"[fullsize] generating {name}", flush=True)
+    L = synth.make_layer(cfg, device="cuda")
+    olay = oracle_layer(L)
+    lay = gpu_layer(L, max(Ts))
+    out = {}
+    for T in Ts:
+        print(f"[fullsize] {name} T={T}", flush=True)
+        x = synth.make_tokens(cfg, T, device="cuda")
+        r = lay.forward(x, scatter=True)
+        torch.cuda.synchronize()
+        out[T] = compare(cfg, x, olay, r, sample=_sample(T) if T > 64 else None, label=f"{name} T={T}")
+        print(f"[fullsize] {name} T={T} {out[T]}", flush=True)
+    lay.close()
+    del L, olay
+    torch.cuda.empty_cache()
+    return out
+
+
+def test_mixtral_bf16_full():
+    _run("mixtral_bf16", [1, 8, 32, 64, 4096])
+
+
+def test_shared_fine_bf16_full():
+    _run("shared_fine_bf16", [16, 2048])
+
+
+def test_skewed_bf16_full():
+    r = _run("skewed_bf16", [8192])
+    assert r[8192]["excluded"] >= 0
+
+
+def test_int8_mixtral22b_full():
+    _run("int8_mixtral22b", [1, 16, 256])

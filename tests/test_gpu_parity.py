@@ -1,0 +1,107 @@
+"""GPU parity of libmoe against the CPU oracle, through the C ABI.
+
+Reduced-width layers keep every kernel path (fp32 VALU, bf16 MFMA, int8 MFMA,
+shared expert, skewed routing with empty and overfull experts, ragged row tiles)
+at sizes the oracle evaluates in full within seconds. Full-size layers live in
+test_gpu_fullsize.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from harness import compare, gpu_layer, oracle_layer
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(cfg, T_list, max_tokens=None, instance=0, device="cpu"):
+    L = synth.make_layer(cfg, device=device, instance=instance)
+    olay = oracle_layer(L)
+    lay = gpu_layer(L, max_tokens or max(T_list))
+    res = {}
+    for T in T_list:
+        print(f"[parity] {cfg.name} d={cfg.d_model} E={cfg.n_experts} F={cfg.d_ff} k={cfg.top_k} T={T}", flush=True)
+        x = synth.make_tokens(cfg, T, device=device, instance=instance).cuda()
+        out = lay.forward(x, scatter=True)
+        torch.cuda.synchronize()
+        res[T] = compare(cfg, x, olay, out, label=f"{cfg.name} T={T}")
+    lay.close()
+    return res
+
+
+def test_tiny_f32_full():
+    cfg = synth.get_config("tiny_f32")
+    r = _run(cfg, [64, 1, 37, 64])
+    assert r[64]["frob"] < 1e-5
+
+
+def test_mixtral_shape_reduced_bf16():
+    cfg = synth.get_config("mixtral_bf16", d_model=512, d_ff=1024)
+    _run(cfg, [1, 8, 64, 300])
+
+
+def test_shared_expert_reduced_bf16():
+    cfg = synth.get_config("shared_fine_bf16", d_model=512, d_ff=256, shared_d_ff=2048)
+    _run(cfg, [16, 200])
+
+
+def test_skewed_many_experts_reduced_bf16():
+    # 128 experts with a Zipf bias: most experts empty, a few far over one row tile
+    cfg = synth.get_config("skewed_bf16", d_model=256, d_ff=128)
+    _run(cfg, [1024])
+
+
+def test_int8_reduced():
+    cfg = synth.get_config("int8_mixtral22b", d_model=512, d_ff=1024)
+    _run(cfg, [1, 16, 256])
+
+
+def test_deterministic_and_zero_tokens():
+    cfg = synth.get_config("shared_fine_bf16", d_model=256, d_ff=128, shared_d_ff=512)
+    L = synth.make_layer(cfg)
+    lay = gpu_layer(L, 300)
+    x = synth.make_tokens(cfg, 300).cuda()
+    a = lay.forward(x, scatter=True)
+    b = lay.forward(x, scatter=True)
+    torch.cuda.synchronize()
+    for f in ("y", "topk_idx", "topk_w", "expert_counts", "expert_offsets", "sorted_assign", "shared_gate"):
+        assert torch.equal(getattr(a, f), getattr(b, f)), f
+    # T = 0 enqueues nothing and leaves the outputs alone
+    out = lay.outputs(4, scatter=True)
+    out.y.fill_(7)
+    lay.forward(x[:0], out=out)
+    torch.cuda.synchronize()
+    assert (out.y == 7).all()
+    lay.close()
+
+
+def test_zero_router_tie_rule():
+    # all logits equal: experts 0..k-1 in order, weights exactly 1/k
+    cfg = synth.get_config("mixtral_bf16", d_model=256, d_ff=128, n_experts=8, top_k=3)
+    L = synth.make_layer(cfg)
+    L.w_router.zero_()
+    lay = gpu_layer(L, 70)
+    x = synth.make_tokens(cfg, 70).cuda()
+    out = lay.forward(x, scatter=True)
+    torch.cuda.synchronize()
+    assert (out.topk_idx.cpu() == torch.arange(3, dtype=torch.int32)).all()
+    assert (out.topk_w.cpu() == 1.0 / 3.0).all()
+    compare(cfg, x, oracle_layer(L), out, label="zero router")
+    lay.close()
+
+
+def test_forward_argument_errors():
+    import moe_layer_forward_gate_amd as moe
+    cfg = synth.get_config("tiny_f32")
+    lay = gpu_layer(synth.make_layer(cfg), 16)
+    x = synth.make_tokens(cfg, 17).cuda()
+    with pytest.raises(moe.MoeError) as ei:
+        lay.forward(x)  # T > max_tokens
+    assert ei.value.status == moe.MOE_EINVAL
+    buf = torch.empty(16 * 256 + 1, dtype=torch.float32, device="cuda")
+    xm = buf[1:].view(16, 256)  # 4-byte aligned, not 16
+    with pytest.raises(moe.MoeError) as ei:
+        lay.forward(xm)
+    assert ei.value.status == moe.MOE_EINVAL
+    lay.close()
