@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device-to-device copy of 1 GiB (for HBM counter scaling)")
     return ap.parse_args()
 
 
@@ -159,6 +161,15 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_calibration:
+        # a plain copy kernel of known size: 1 GiB read + 1 GiB written per launch
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": a.numel() * 4, "copy_bytes_written": b.numel() * 4, "launches": 3}))
+        return
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import synth
     import moe_layer_forward_gate_amd as moe

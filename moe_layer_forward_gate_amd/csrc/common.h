@@ -32,8 +32,9 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z));
 // Gate: router logits, top-k with (logit desc, id asc) order, softmax weights over
 // the chosen logits, and (when has_shared) the shared-expert sigmoid gate read
 // from router column E. wr_t is the router weight transposed to [Ec][d].
-hipError_t launch_gate(const void* x, bool x_bf16, const float* wr_t, const float* bias, int T, int d,
-                       int E, bool has_shared, int k, int32_t* idx, float* w, float* gs, hipStream_t s);
+// planes: the router weight split into three bf16 planes in fragment order (bf16 tokens only).
+hipError_t launch_gate(const void* x, bool x_bf16, const float* wr_t, const void* planes, const float* bias, int T,
+                       int d, int E, bool has_shared, int k, int32_t* idx, float* w, float* gs, hipStream_t s);
 
 // Scatter: counts, offsets and the stable by-expert permutation of the T*k routed
 // assignments, V shared virtual experts appended (each takes every token), and the
@@ -56,7 +57,9 @@ struct GemmArgs {
     const int32_t* offsets;     // [Et+1]
     const int32_t* sorted_c;    // [P]
     int Et, kt, k;              // experts incl. virtual, slots per token incl. virtual, routed k
-    int max_tiles;              // bound on sum_e ceil(n_e / BM)
+    int max_tiles;              // bound on sum_e ceil(n_e / bm)
+    int bm;                     // row tile height: 256 or 128 (must match the scatter's tile list)
+    int ksplit;                 // down projection: K split into ksplit partial sums (ow rows c*ksplit + s)
     // up: A = x rows gathered by token; down: A = H rows
     const bf16_t* x;            // [T][d]
     bf16_t* h;                  // [P][F]
@@ -67,11 +70,16 @@ struct GemmArgs {
     const float* s_down;        // [E][d]
     const float* topk_w;        // [T][k]
     const float* gs;            // [T] shared gate or null
-    float* ow;                  // [T*kt][d] weighted expert outputs
+    float* ow;                  // [T*kt*ksplit][d] weighted expert outputs (partial sums)
     int d, F;
 };
 hipError_t launch_expert_up_bf16(const GemmArgs& a, bool int8, hipStream_t s);
 hipError_t launch_expert_down_bf16(const GemmArgs& a, bool int8, hipStream_t s);
+// Small-batch variants (a.bm = 16, 32 or 64 >= T, so each active expert is one row tile).
+hipError_t launch_expert_up_stream(const GemmArgs& a, bool int8, hipStream_t s);
+hipError_t launch_expert_down_stream(const GemmArgs& a, bool int8, hipStream_t s);
+constexpr int kStreamMaxT = 64;     // largest T served by the streaming kernels
+constexpr int kStreamMaxSplit = 16; // largest K split of their down projection
 
 // fp32 experts (VALU), weights in natural [E][K][N] layout.
 struct GemmF32Args {
@@ -92,19 +100,22 @@ struct GemmF32Args {
 hipError_t launch_expert_up_f32(const GemmF32Args& a, hipStream_t s);
 hipError_t launch_expert_down_f32(const GemmF32Args& a, hipStream_t s);
 
-// Gather: y[t] = sum_{j < kt} ow[t*kt + j], written as bf16 or fp32.
-hipError_t launch_combine(const float* ow, int T, int kt, int d, void* y, bool y_bf16, hipStream_t s);
+// Gather: y[t] = sum_{j < nrow} ow[t*nrow + j], written as bf16 or fp32 (nrow = slots x K splits).
+hipError_t launch_combine(const float* ow, int T, int nrow, int d, void* y, bool y_bf16, hipStream_t s);
 
 // Create-time repacking into fragment order (see pack.hip).
 hipError_t pack_router(const float* wr, const float* ws_gate_vec, int d, int E, float* wr_t, hipStream_t s);
+// Router weight [d][E] (+ shared gate column E) as three bf16 planes hi + mid + lo in MFMA
+// B-fragment order: [3][NB = ceil(Ec/16)][d/32][64 lanes][8], columns past Ec zero.
+hipError_t pack_router_planes(const float* wr, const float* ws_gate_vec, int d, int E, bf16_t* planes,
+                              hipStream_t s);
 hipError_t pack_gu_bf16(const bf16_t* wg, const bf16_t* wu, int E, int d, int F, bf16_t* dst,
                         int64_t src_ld, hipStream_t s);
 hipError_t pack_dn_bf16(const bf16_t* wd, int E, int F, int d, bf16_t* dst, hipStream_t s);
 hipError_t pack_gu_i8(const int8_t* wg, const int8_t* wu, int E, int d, int F, int8_t* dst, hipStream_t s);
 hipError_t pack_dn_i8(const int8_t* wd, int E, int F, int d, int8_t* dst, hipStream_t s);
 
-// Row tile height used by the bf16/int8 GEMMs and by the fp32 GEMMs.
-constexpr int kBM = 128;
+// Row tile height of the fp32 GEMMs (the bf16/int8 GEMMs take 256 or 128, chosen per call).
 constexpr int kBMf32 = 64;
 constexpr int kMaxVirtual = 63;  // shared-expert slices (scatter scan limit)
 
@@ -143,6 +154,43 @@ __device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ ts, cons
     const int e = c - 1;
     const int t0 = ts[e], mt = ts[e + 1] - t0;
     const int local = L - t0 * NTp;
+    const int grp = local / (mt * GN);
+    const int rem = local - grp * mt * GN;
+    const int m = rem / GN;
+    const int n = grp * GN + (rem - m * GN);
+    if (n >= NT) return false;
+    tl.e = e;
+    tl.n = n;
+    tl.row0 = m * bm;
+    tl.seg0 = offs[e];
+    tl.rows = min(bm, offs[e + 1] - tl.seg0 - tl.row0);
+    return true;
+}
+
+// decode_tile over S K-splits of every tile: logical index = tile * S + split,
+// with the XCD remap applied to the combined index.
+__device__ __forceinline__ bool decode_tile_split(const int32_t* __restrict__ ts, const int32_t* __restrict__ offs,
+                                                  int Et, int NT, int GN, int bm, int S, Tile& tl, int& split) {
+    const int NTp = (NT + GN - 1) / GN * GN;
+    const int total = ts[Et] * NTp * S;
+    const int per = (total + kXcds - 1) / kXcds;
+    const int i = blockIdx.x;
+    const int slot = i / kXcds, xcd = i % kXcds;
+    if (slot >= per) return false;
+    const int L = xcd * per + slot;
+    if (L >= total) return false;
+    const int Lt = L / S;
+    split = L - Lt * S;
+    const int lane = threadIdx.x % kWave;
+    int c = 0;
+    for (int j0 = 0; j0 <= Et; j0 += kWave) {
+        const int j = j0 + lane;
+        const bool ok = j <= Et && ts[j] * NTp <= Lt;
+        c += __popcll(__ballot(ok));
+    }
+    const int e = c - 1;
+    const int t0 = ts[e], mt = ts[e + 1] - t0;
+    const int local = Lt - t0 * NTp;
     const int grp = local / (mt * GN);
     const int rem = local - grp * mt * GN;
     const int m = rem / GN;

@@ -12,30 +12,35 @@
 //       the Gather stage is applied in this epilogue ([pptc §2.1] fused
 //       aggregation).
 //
-// Workgroup tile 128 rows x 128 columns, K step 64, 4 waves in a 2 x 2 grid of
-// 64 x 64, each wave 4 x 4 v_mfma_f32_16x16x32_bf16 accumulators. Both operands
-// are staged in LDS in MFMA fragment order (one 1 KB block = 16 rows x 32 K, lane
-// l holding row l%16, K 8*(l/16)..+7), so every fragment read is one conflict-free
-// 16-byte-per-lane ds_read. Expert weights arrive from create-time packing already
-// in that order (bf16: [Et][N/16][K/32][64][8]; int8: [E][N/16][K/64][64][16],
-// bytes 0-7 the first 32-K half and 8-15 the second), so a weight tile is a
-// straight 16-byte-per-lane copy; int8 is widened to bf16 on the way to LDS
-// (exact: |q| <= 127 fits bf16's significand) and its per-column scale is
-// applied to the fp32 accumulator in the epilogue. The next K step is loaded to
-// registers while the current one is multiplied; one barrier per K step.
+// Workgroup tile BM x 256 (BM = 256 or 128), K step 64, 8 waves; each wave owns
+// a 64 x (16*NBW) block of v_mfma_f32_16x16x32_bf16 accumulators. Operands are
+// staged in LDS in MFMA fragment order: one 1 KB block = 16 rows x 32 K, lane l
+// holding row l%16, K 8*(l/16)..+7, so every fragment read is a conflict-free
+// 16-byte-per-lane ds_read. Global -> LDS traffic uses the gfx950 LDS-DMA load
+// (global_load_lds_dwordx4): each wave instruction fills one whole 1 KB block,
+// lane l fetching its own 16 bytes, which lets the A operand be gathered
+// straight from the token rows of x (up) with no staging registers. Expert
+// weights come from create-time packing already in fragment order (bf16:
+// [Et][N/16][K/32][64][8]), so a weight block is one contiguous 1 KB read.
+// int8 weights ([E][N/16][K/64][64][16], bytes 0-7 the first 32-K half) go
+// through registers instead, widened to bf16 on the way to LDS (exact: |q| <=
+// 127 fits bf16's significand); their per-column scale multiplies the fp32
+// accumulator in the epilogue. Two LDS stages: the loads of K step kt+1 are in
+// flight while step kt is multiplied; one barrier per K step.
 // Up-projection columns are packed gate/up interleaved per 16 columns, so each
-// lane holds the gate and up accumulators of the same (row, f) and the SiLU*mul
+// lane holds the gate and up accumulators of the same (row, f) and SiLU * up
 // runs in registers.
 #include "common.h"
 
 namespace moe {
 namespace {
 
-constexpr int BM = kBM;    // 128
-constexpr int BN = 128;
-constexpr int BK = 64;
-constexpr int GN = 8;      // column tiles per group (see decode_tile)
-constexpr int kThreads = 256;
+constexpr int BN = 256;
+constexpr int GN = 4;       // column tiles per group (see decode_tile)
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / kWave;
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w, int sh) {
     // bytes sh/8 and sh/8+1 of w as two bf16 (exact widening of small integers)
@@ -45,159 +50,191 @@ __device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w, int sh) {
 }
 
 __device__ __forceinline__ u32x4 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-    u32x4 r;
-    r.x = i8x2_to_bf16x2(lo, 0);
-    r.y = i8x2_to_bf16x2(lo, 16);
-    r.z = i8x2_to_bf16x2(hi, 0);
-    r.w = i8x2_to_bf16x2(hi, 16);
-    return r;
+    return u32x4{i8x2_to_bf16x2(lo, 0), i8x2_to_bf16x2(lo, 16), i8x2_to_bf16x2(hi, 0), i8x2_to_bf16x2(hi, 16)};
 }
 
-// Global -> registers for K step kt: 4 A chunks (16 B of one row each) and the
-// weight tile's lane chunks.
-template <bool INT8, int NBQ>
-__device__ __forceinline__ void gload_tiles(u32x4 (&ra)[4], u32x4 (&rb)[NBQ], const bf16_t* const (&a_ptr)[4],
-                                            const bool (&a_ok)[4], const u32x4* b_base, int kt, int K, int tid) {
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        ra[i] = a_ok[i] ? *reinterpret_cast<const u32x4*>(a_ptr[i] + k0) : u32x4{0u, 0u, 0u, 0u};
-    if constexpr (INT8) {
-        const int KB = K / 64;
-#pragma unroll
-        for (int i = 0; i < NBQ; ++i) {
-            const int q = tid + kThreads * i;
-            const int nb = q / 64, ln = q % 64;
-            rb[i] = b_base[((size_t)nb * KB + kt) * 64 + ln];
-        }
-    } else {
-        const int KS = K / 32;
-#pragma unroll
-        for (int i = 0; i < NBQ; ++i) {
-            const int q = tid + kThreads * i;
-            const int blk = q / 64, ln = q % 64;
-            const int nb = blk / 2, ks = blk % 2;
-            rb[i] = b_base[((size_t)nb * KS + kt * 2 + ks) * 64 + ln];
-        }
-    }
+// one 16-byte LDS-DMA load per lane: LDS[block + 16*lane] = *src (block is wave-uniform)
+__device__ __forceinline__ void dma16(const void* src, u32x4* lds_block) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_block, 16, 0, 0);
 }
 
-// Registers -> LDS (fragment order); int8 weights are widened to bf16 here.
-template <bool INT8, int NBQ>
-__device__ __forceinline__ void sstore_tiles(const u32x4 (&ra)[4], const u32x4 (&rb)[NBQ], const int (&a_lds)[4],
-                                             u32x4* la, u32x4* lb, int tid) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) la[a_lds[i]] = ra[i];
-    if constexpr (INT8) {
-#pragma unroll
-        for (int i = 0; i < NBQ; ++i) {
-            const int q = tid + kThreads * i;
-            const int nb = q / 64, ln = q % 64;
-            lb[(nb * 2 + 0) * 64 + ln] = i8x8_to_bf16x8(rb[i].x, rb[i].y);
-            lb[(nb * 2 + 1) * 64 + ln] = i8x8_to_bf16x8(rb[i].z, rb[i].w);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < NBQ; ++i) lb[tid + kThreads * i] = rb[i];
-    }
+// s_waitcnt with vmcnt <= N (N < 16) and the other counters left alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vm_le() {
+    static_assert(N >= 0 && N < 16, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
 }
 
-template <bool INT8, bool UP>
-__global__ __launch_bounds__(kThreads, 2) void expert_gemm(GemmArgs a) {
+// Workgroup barrier without a memory fence (the waits above it are explicit); the
+// memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Pipeline shape: bf16 weights stream through LDS-DMA only (BK 32, 4 stages, three
+// K steps in flight); int8 weights need a register hop for the widening (BK 64,
+// 2 stages, one K step in flight).
+template <bool INT8> struct Pipe;
+template <> struct Pipe<false> { static constexpr int BK = 32, STAGES = 4; };
+template <> struct Pipe<true> { static constexpr int BK = 64, STAGES = 2; };
+
+template <int BM, bool INT8, bool UP>
+__global__ __launch_bounds__(kThreads, 1) void expert_gemm(GemmArgs a) {
+    constexpr int BK = Pipe<INT8>::BK;
+    constexpr int STAGES = Pipe<INT8>::STAGES;
+    constexpr int KH = BK / 32;               // 32-K halves per K step
+    constexpr int MBLK = BM / 16;             // 16-row blocks per tile
+    constexpr int WM = BM / 64;               // waves along M
+    constexpr int WN = kWaves / WM;           // waves along N
+    constexpr int NBW = (BN / 16) / WN;       // 16-column blocks per wave
+    constexpr int ABLK = MBLK * KH;           // A blocks per stage
+    constexpr int BBLK = (BN / 16) * KH;      // B blocks per stage
+    constexpr int STAGE = ABLK + BBLK;        // 1 KB blocks per stage
+    constexpr int AW = ABLK / kWaves;         // A block loads per wave per stage
+    constexpr int BW = INT8 ? 0 : BBLK / kWaves;  // B block loads (LDS-DMA) per wave per stage
+    constexpr int LPS = AW + BW;              // LDS-DMA loads per wave per stage
+
     const int K = UP ? a.d : a.F;
     const int N = UP ? 2 * a.F : a.d;
     const int NT = N / BN;
+    const int S = UP ? 1 : a.ksplit;
     Tile tl;
-    if (!decode_tile(a.tile_start, a.offsets, a.Et, NT, GN, BM, tl)) return;
+    int split = 0;
+    {
+        // split-K: logical tile index = tile * S + split
+        if (!decode_tile_split(a.tile_start, a.offsets, a.Et, NT, GN, BM, S, tl, split)) return;
+    }
+    const int Kpart = K / S;
+    const int kbase = split * Kpart;
 
-    __shared__ u32x4 lds[2][2][(BM / 16) * (BK / 32) * 64];  // [buf][A|B][blocks*64 lanes]
+    extern __shared__ u32x4 lds[];  // [STAGES][STAGE blocks][64 lanes]
 
     const int tid = threadIdx.x;
     const int wave = tid / kWave, lane = tid % kWave;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
 
-    // ---- A rows: thread loads rows tid/8 + 32*i, 16 B at K offset (tid%8)*8
-    const int a_kc = tid % 8;
-    const bf16_t* a_ptr[4];
-    bool a_ok[4];
+    // ---- A: wave loads stage blocks b = wave + 8*i: m-block b / KH, K half b % KH
+    const bf16_t* a_row[AW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = tid / 8 + 32 * i;
-        a_ok[i] = r < tl.rows;
-        const int p = tl.seg0 + tl.row0 + (a_ok[i] ? r : 0);
-        if (UP) {
-            const int c = a.sorted_c[p];
-            a_ptr[i] = a.x + (size_t)(c / a.kt) * a.d + a_kc * 8;
-        } else {
-            a_ptr[i] = a.h + (size_t)p * a.F + a_kc * 8;
-        }
+    for (int i = 0; i < AW; ++i) {
+        const int b = wave + kWaves * i;
+        const int r = (b / KH) * 16 + lane % 16;
+        const int rr = r < tl.rows ? r : 0;  // rows past the segment load row 0 (their outputs are dropped)
+        const int p = tl.seg0 + tl.row0 + rr;
+        const bf16_t* base = UP ? a.x + (size_t)(a.sorted_c[p] / a.kt) * a.d : a.h + (size_t)p * a.F;
+        a_row[i] = base + kbase + (b % KH) * 32 + 8 * (lane / 16);
     }
-    // LDS slot of each A chunk: block (r/16, kc/4), lane (r%16) + 16*(kc%4)
-    int a_lds[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = tid / 8 + 32 * i;
-        a_lds[i] = ((r / 16) * 2 + a_kc / 4) * 64 + (r % 16) + 16 * (a_kc % 4);
-    }
-
-    // ---- B tile
-    const u32x4* b_base;
-    if (INT8) {
-        const int KB = K / 64;
+    // ---- B
+    const int KS = K / 32;
+    const u32x4* b_src;
+    if constexpr (INT8) {
         const int8_t* wb = (const int8_t*)(UP ? a.wgu : a.wdn) + (size_t)tl.e * N * K;
-        b_base = reinterpret_cast<const u32x4*>(wb) + (size_t)(tl.n * 8) * KB * 64;
+        b_src = reinterpret_cast<const u32x4*>(wb) + (size_t)(tl.n * (BN / 16)) * (K / 64) * 64 + kbase / 64 * 64;
     } else {
-        const int KS = K / 32;
         const bf16_t* wb = (const bf16_t*)(UP ? a.wgu : a.wdn) + (size_t)tl.e * N * K;
-        b_base = reinterpret_cast<const u32x4*>(wb) + (size_t)(tl.n * 8) * KS * 64;
+        b_src = reinterpret_cast<const u32x4*>(wb) + (size_t)(tl.n * (BN / 16)) * KS * 64 + kbase / 32 * 64;
     }
+    // int8: thread loads lane chunks q = tid + 512*i of the (BN/16) x 1 KB int8 blocks
+    constexpr int NQ8 = INT8 ? (BN / 16) * 64 / kThreads : 1;
+    u32x4 r8[NQ8];
 
-    constexpr int NBQ = INT8 ? 2 : 4;
-    u32x4 ra[4], rb[NBQ];
-    const int KT = K / BK;
-    gload_tiles<INT8, NBQ>(ra, rb, a_ptr, a_ok, b_base, 0, K, tid);
-    sstore_tiles<INT8, NBQ>(ra, rb, a_lds, lds[0][0], lds[0][1], tid);
-    __syncthreads();
+    auto issue = [&](int kt, int stage) {
+        u32x4* st = lds + (size_t)stage * STAGE * 64;
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int i = 0; i < AW; ++i) dma16(a_row[i] + k0, st + (wave + kWaves * i) * 64);
+        if constexpr (INT8) {
+#pragma unroll
+            for (int i = 0; i < NQ8; ++i) {
+                const int q = tid + kThreads * i;
+                r8[i] = b_src[((size_t)(q / 64) * (K / 64) + kt) * 64 + q % 64];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < BW; ++j) {
+                const int blk = wave * BW + j;  // stage B block: n-block blk / KH, K half blk % KH
+                const int nb = blk / KH, kh = blk % KH;
+                dma16(b_src + ((size_t)nb * KS + kt * KH + kh) * 64 + lane, st + (ABLK + blk) * 64);
+            }
+        }
+    };
+    auto store_b8 = [&](int stage) {
+        if constexpr (INT8) {
+            u32x4* lb = lds + (size_t)stage * STAGE * 64 + ABLK * 64;
+#pragma unroll
+            for (int i = 0; i < NQ8; ++i) {
+                const int q = tid + kThreads * i;
+                const int nb = q / 64, ln = q % 64;
+                lb[(nb * 2 + 0) * 64 + ln] = i8x8_to_bf16x8(r8[i].x, r8[i].y);
+                lb[(nb * 2 + 1) * 64 + ln] = i8x8_to_bf16x8(r8[i].z, r8[i].w);
+            }
+        }
+    };
 
-    f32x4 acc[4][4];
+    f32x4 acc[4][NBW];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NBW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < KT) gload_tiles<INT8, NBQ>(ra, rb, a_ptr, a_ok, b_base, kt + 1, K, tid);
-        const u32x4* la = lds[buf][0];
-        const u32x4* lb = lds[buf][1];
+    auto compute = [&](int stage) {
+        const u32x4* la = lds + (size_t)stage * STAGE * 64;
+        const u32x4* lb = la + ABLK * 64;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 af[4], bfg[4];
+        for (int kh = 0; kh < KH; ++kh) {
+            bf16x8 af[4], bfg[NBW];
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb)
-                af[mb] = __builtin_bit_cast(bf16x8, la[((wm * 4 + mb) * 2 + ks) * 64 + lane]);
+                af[mb] = __builtin_bit_cast(bf16x8, la[((wm * 4 + mb) * KH + kh) * 64 + lane]);
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-                bfg[nb] = __builtin_bit_cast(bf16x8, lb[((wn * 4 + nb) * 2 + ks) * 64 + lane]);
+            for (int nb = 0; nb < NBW; ++nb)
+                bfg[nb] = __builtin_bit_cast(bf16x8, lb[((wn * NBW + nb) * KH + kh) * 64 + lane]);
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb)
+                for (int nb = 0; nb < NBW; ++nb)
                     acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], bfg[nb], acc[mb][nb], 0, 0, 0);
         }
-        if (kt + 1 < KT) sstore_tiles<INT8, NBQ>(ra, rb, a_lds, lds[buf ^ 1][0], lds[buf ^ 1][1], tid);
+    };
+
+    const int KT = Kpart / BK;
+    if constexpr (INT8) {
+        issue(0, 0);
+        store_b8(0);
+        wait_vm_le<0>();
         __syncthreads();
+        for (int kt = 0; kt < KT; ++kt) {
+            const int stage = kt & 1;
+            if (kt + 1 < KT) issue(kt + 1, stage ^ 1);
+            compute(stage);
+            if (kt + 1 < KT) store_b8(stage ^ 1);
+            wait_vm_le<0>();
+            __syncthreads();
+        }
+    } else {
+        // prologue: stages 0 .. STAGES-2 in flight
+#pragma unroll
+        for (int s0 = 0; s0 < STAGES - 1; ++s0)
+            if (s0 < KT) issue(s0, s0);
+        for (int kt = 0; kt < KT; ++kt) {
+            // stage kt has landed once at most the loads of the STAGES-2 later stages are outstanding
+            if (kt + STAGES - 2 < KT) wait_vm_le<(STAGES - 2) * LPS>();
+            else wait_vm_le<0>();
+            // every wave's loads of stage kt are in LDS; stage kt-1 is no longer read. A bare
+            // s_barrier: __syncthreads() would also drain the later stages' loads (vmcnt(0)).
+            lds_barrier();
+            if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+            compute(kt % STAGES);
+        }
     }
 
     // ---- epilogue: lane holds column lane%16 of each 16x16 block, rows 4*(lane/16)+i
     const int col16 = lane % 16;
     const int rq = 4 * (lane / 16);
-    if (UP) {
+    if constexpr (UP) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int f = (tl.n * 4 + wn * 2 + q) * 16 + col16;
+        for (int q = 0; q < NBW / 2; ++q) {
+            const int f = ((tl.n * (BN / 16) + wn * NBW) / 2 + q) * 16 + col16;
             float sg = 1.f, su = 1.f;
-            if (INT8) {
+            if constexpr (INT8) {
                 sg = a.s_gate[(size_t)tl.e * a.F + f];
                 su = a.s_up[(size_t)tl.e * a.F + f];
             }
@@ -224,12 +261,13 @@ __global__ __launch_bounds__(kThreads, 2) void expert_gemm(GemmArgs a) {
                     const int c = a.sorted_c[tl.seg0 + tl.row0 + r];
                     const int t = c / a.kt, j = c - t * a.kt;
                     const float wgt = j < a.k ? a.topk_w[(size_t)t * a.k + j] : a.gs[t];
-                    float* orow = a.ow + (size_t)c * a.d;
+                    // partial sum `split` of slot c: row c*S + split of the combine buffer
+                    float* orow = a.ow + ((size_t)c * S + split) * a.d;
 #pragma unroll
-                    for (int nb = 0; nb < 4; ++nb) {
-                        const int n = tl.n * BN + wn * 64 + nb * 16 + col16;
+                    for (int nb = 0; nb < NBW; ++nb) {
+                        const int n = tl.n * BN + (wn * NBW + nb) * 16 + col16;
                         float v = acc[mb][nb][i] * wgt;
-                        if (INT8) v *= a.s_down[(size_t)tl.e * a.d + n];
+                        if constexpr (INT8) v *= a.s_down[(size_t)tl.e * a.d + n];
                         orow[n] = v;
                     }
                 }
@@ -237,29 +275,43 @@ __global__ __launch_bounds__(kThreads, 2) void expert_gemm(GemmArgs a) {
     }
 }
 
-}  // namespace
-
-hipError_t launch_expert_up_bf16(const GemmArgs& a, bool int8, hipStream_t s) {
-    const int NT = 2 * a.F / BN;
-    const int NTp = (NT + GN - 1) / GN * GN;
+template <int BM, bool INT8, bool UP>
+hipError_t launch(const GemmArgs& a, hipStream_t s) {
+    constexpr int KH = Pipe<INT8>::BK / 32;
+    constexpr int STAGE = (BM / 16) * KH + (BN / 16) * KH;
+    const size_t lds_bytes = (size_t)Pipe<INT8>::STAGES * STAGE * 64 * 16;
+    auto kern = expert_gemm<BM, INT8, UP>;
+    static bool attr_set = false;  // one-time opt-in above the default dynamic LDS limit
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)lds_bytes);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int N = UP ? 2 * a.F : a.d;
+    const int S = UP ? 1 : a.ksplit;
+    const int NTp = (N / BN + GN - 1) / GN * GN;
     // a multiple of 8 workgroups, so every XCD gets ceil(tiles / 8) slots
-    dim3 grid((unsigned)((a.max_tiles * NTp + kXcds - 1) / kXcds * kXcds));
-    if (int8)
-        hipLaunchKernelGGL((expert_gemm<true, true>), grid, dim3(kThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL((expert_gemm<false, true>), grid, dim3(kThreads), 0, s, a);
+    dim3 grid((unsigned)(((size_t)a.max_tiles * NTp * S + kXcds - 1) / kXcds * kXcds));
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds_bytes, s, a);
     return hipGetLastError();
 }
 
+template <bool UP>
+hipError_t launch_dispatch(const GemmArgs& a, bool int8, hipStream_t s) {
+    if (a.bm == 256) return int8 ? launch<256, true, UP>(a, s) : launch<256, false, UP>(a, s);
+    if (a.bm == 128) return int8 ? launch<128, true, UP>(a, s) : launch<128, false, UP>(a, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_expert_up_bf16(const GemmArgs& a, bool int8, hipStream_t s) {
+    return launch_dispatch<true>(a, int8, s);
+}
+
 hipError_t launch_expert_down_bf16(const GemmArgs& a, bool int8, hipStream_t s) {
-    const int NT = a.d / BN;
-    const int NTp = (NT + GN - 1) / GN * GN;
-    dim3 grid((unsigned)((a.max_tiles * NTp + kXcds - 1) / kXcds * kXcds));
-    if (int8)
-        hipLaunchKernelGGL((expert_gemm<true, false>), grid, dim3(kThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL((expert_gemm<false, false>), grid, dim3(kThreads), 0, s, a);
-    return hipGetLastError();
+    return launch_dispatch<false>(a, int8, s);
 }
 
 }  // namespace moe

@@ -1,0 +1,219 @@
+// Expert compute for small batches (decode): weight-streaming grouped GEMMs.
+//
+// With a handful of tokens the expert weights are the only real traffic
+// ([hotelren §2.1]: the bottleneck is moving data, not arithmetic), so this path
+// is built to stream each active expert's packed weights from HBM exactly once
+// at full width, with every weight byte fetched by exactly one wave:
+//   - every wave owns NBW 16-column weight blocks and a K range; it reads them
+//     as contiguous 1 KB fragment blocks (16 B per lane) straight into MFMA
+//     operand registers, U K-steps at a time so many loads are in flight;
+//   - the few token rows (<= 16*MB) come in as MFMA A fragments from L2;
+//   - the down projection splits K over S workgroups when the active experts
+//     alone would leave the GPU idle; each split writes its own partial row of
+//     the combine buffer (row c*S + s) and the Gather pass adds them, so the
+//     result does not depend on scheduling.
+// Work item = (active expert, group of 4*NBW column blocks, K split); experts
+// without rows get no work items (the item count is read from the scatter's tile
+// table on the device).
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint32_t i8x2_bf16(uint32_t w, int sh) {
+    const float f0 = (float)(int)(int8_t)(w >> sh);
+    const float f1 = (float)(int)(int8_t)(w >> (sh + 8));
+    return (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+}
+
+template <int MB, int NBW, bool INT8, bool UP, int U>
+__global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
+    constexpr int KSTEP = INT8 ? 64 : 32;  // K covered by one 16-byte weight chunk per lane
+    constexpr int KH = KSTEP / 32;
+    const int K = UP ? a.d : a.F;
+    const int N = UP ? 2 * a.F : a.d;
+    const int NG = N / (16 * NBW * 4);  // column groups per expert
+    // ---- work item
+    const int total = a.tile_start[a.Et] * NG * S;
+    const int L = blockIdx.x;
+    if (L >= total) return;
+    const int tile = L / (NG * S);
+    const int rem = L - tile * NG * S;
+    const int ng = rem / S, split = rem - (rem / S) * S;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    int c = 0;
+    for (int j0 = 0; j0 <= a.Et; j0 += kWave) {
+        const int j = j0 + lane;
+        c += __popcll(__ballot(j <= a.Et && a.tile_start[j] <= tile));
+    }
+    const int e = c - 1;
+    const int seg0 = a.offsets[e] + (tile - a.tile_start[e]) * a.bm;
+    const int rows = min(a.bm, a.offsets[e + 1] - seg0);
+    const int mb_act = (rows + 15) / 16;  // <= MB by construction of the launch
+
+    const int Kp = K / S;
+    const int kbase = split * Kp;
+    const int nsteps = Kp / KSTEP;
+    const int nb0 = (ng * 4 + wave) * NBW;
+
+    // weight stream of each owned column block: contiguous 1 KB chunks along K
+    const u32x4* bptr[NBW];
+    {
+        const int KB = K / KSTEP;
+        const u32x4* wb = reinterpret_cast<const u32x4*>(INT8 ? (const void*)((const int8_t*)(UP ? a.wgu : a.wdn) +
+                                                                                (size_t)e * N * K)
+                                                              : (const void*)((const bf16_t*)(UP ? a.wgu : a.wdn) +
+                                                                              (size_t)e * N * K));
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) bptr[j] = wb + ((size_t)(nb0 + j) * KB + kbase / KSTEP) * 64 + lane;
+    }
+    // token rows as A fragments: lane holds row 16*mb + lane%16, K 8*(lane/16)..+7
+    const bf16_t* aptr[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int r = mb * 16 + lane % 16;
+        const int p = seg0 + (r < rows ? r : 0);
+        const bf16_t* base = UP ? a.x + (size_t)(a.sorted_c[p] / a.kt) * a.d : a.h + (size_t)p * a.F;
+        aptr[mb] = base + kbase + 8 * (lane / 16);
+    }
+
+    f32x4 acc[MB][NBW];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto step = [&](const u32x4 (&bb)[NBW], const u32x4 (&aa)[MB][KH]) {
+#pragma unroll
+        for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) {
+                u32x4 bw;
+                if constexpr (INT8) {
+                    const uint32_t lo = kh ? bb[j].z : bb[j].x, hi = kh ? bb[j].w : bb[j].y;
+                    bw = u32x4{i8x2_bf16(lo, 0), i8x2_bf16(lo, 16), i8x2_bf16(hi, 0), i8x2_bf16(hi, 16)};
+                } else {
+                    bw = bb[j];
+                }
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    if (mb < mb_act)
+                        acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, aa[mb][kh]), __builtin_bit_cast(bf16x8, bw), acc[mb][j], 0, 0,
+                            0);
+            }
+    };
+
+    int s = 0;
+    for (; s + U <= nsteps; s += U) {
+        u32x4 bb[U][NBW];
+        u32x4 aa[U][MB][KH];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) bb[u][j] = bptr[j][(size_t)(s + u) * 64];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int kh = 0; kh < KH; ++kh)
+                    aa[u][mb][kh] = mb < mb_act ? *reinterpret_cast<const u32x4*>(aptr[mb] + (s + u) * KSTEP + kh * 32)
+                                                : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int u = 0; u < U; ++u) step(bb[u], aa[u]);
+    }
+    for (; s < nsteps; ++s) {
+        u32x4 bb[NBW];
+        u32x4 aa[MB][KH];
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) bb[j] = bptr[j][(size_t)s * 64];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int kh = 0; kh < KH; ++kh)
+                aa[mb][kh] = mb < mb_act ? *reinterpret_cast<const u32x4*>(aptr[mb] + s * KSTEP + kh * 32)
+                                         : u32x4{0u, 0u, 0u, 0u};
+        step(bb, aa);
+    }
+
+    // ---- epilogue (same fragment layout as the prefill kernels)
+    const int col16 = lane % 16, rq = 4 * (lane / 16);
+    if constexpr (UP) {
+#pragma unroll
+        for (int q = 0; q < NBW / 2; ++q) {
+            const int f = (nb0 / 2 + q) * 16 + col16;
+            float sg = 1.f, su = 1.f;
+            if constexpr (INT8) {
+                sg = a.s_gate[(size_t)e * a.F + f];
+                su = a.s_up[(size_t)e * a.F + f];
+            }
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = mb * 16 + rq + i;
+                    if (r < rows) {
+                        const float g = acc[mb][2 * q][i] * sg, u = acc[mb][2 * q + 1][i] * su;
+                        a.h[(size_t)(seg0 + r) * a.F + f] = f32_to_bf16(silu(g) * u);
+                    }
+                }
+        }
+    } else {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = mb * 16 + rq + i;
+                if (r < rows) {
+                    const int cs = a.sorted_c[seg0 + r];
+                    const int t = cs / a.kt, j = cs - t * a.kt;
+                    const float wgt = j < a.k ? a.topk_w[(size_t)t * a.k + j] : a.gs[t];
+                    float* orow = a.ow + ((size_t)cs * S + split) * a.d;
+#pragma unroll
+                    for (int jn = 0; jn < NBW; ++jn) {
+                        const int n = (nb0 + jn) * 16 + col16;
+                        float v = acc[mb][jn][i] * wgt;
+                        if constexpr (INT8) v *= a.s_down[(size_t)e * a.d + n];
+                        orow[n] = v;
+                    }
+                }
+            }
+    }
+}
+
+template <int MB, bool INT8, bool UP>
+hipError_t launch_mb(const GemmArgs& a, int S, hipStream_t s) {
+    constexpr int NBW = 2;
+    constexpr int U = INT8 ? 4 : (MB <= 2 ? 8 : 4);
+    const int N = UP ? 2 * a.F : a.d;
+    const int NG = N / (16 * NBW * 4);
+    dim3 grid((unsigned)((size_t)a.max_tiles * NG * S));
+    hipLaunchKernelGGL((expert_stream<MB, NBW, INT8, UP, U>), grid, dim3(kThreads), 0, s, a, S);
+    return hipGetLastError();
+}
+
+template <bool INT8, bool UP>
+hipError_t launch_t(const GemmArgs& a, int S, hipStream_t s) {
+    switch ((a.bm + 15) / 16) {
+        case 1: return launch_mb<1, INT8, UP>(a, S, s);
+        case 2: return launch_mb<2, INT8, UP>(a, S, s);
+        case 3:
+        case 4: return launch_mb<4, INT8, UP>(a, S, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_expert_up_stream(const GemmArgs& a, bool int8, hipStream_t s) {
+    return int8 ? launch_t<true, true>(a, 1, s) : launch_t<false, true>(a, 1, s);
+}
+
+hipError_t launch_expert_down_stream(const GemmArgs& a, bool int8, hipStream_t s) {
+    return int8 ? launch_t<true, false>(a, a.ksplit, s) : launch_t<false, false>(a, a.ksplit, s);
+}
+
+}  // namespace moe

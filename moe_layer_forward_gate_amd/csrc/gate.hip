@@ -7,11 +7,16 @@
 // lower expert id and slot 0 holds the maximum; [pptc §2.1] the top-k is found
 // inside one wavefront with cross-lane shuffles and no block-wide barrier.
 //
-// Two logit paths share the same top-k code:
-//   - gate_rowdot: one workgroup per token, each wave dots the token against a
-//     group of router rows (decode: the router weights are the only real traffic);
-//   - gate_tiled: 64 tokens x all experts per workgroup, an LDS-tiled fp32 GEMM
-//     with register double-buffering (prefill).
+// Three logit paths share the same top-k code:
+//   - gate_rowdot (T <= 64): one workgroup per token; the 256 threads split K and
+//     take the router rows eight at a time, so every load of the token and of the
+//     router weights is in flight at once (decode: latency is what counts);
+//   - gate_mfma (T > 64, bf16 tokens): 16 tokens per workgroup on bf16 MFMA. The
+//     fp32 router weight is carried as three bf16 planes w = hi + mid + lo (an
+//     exact split: each plane takes the next 8 significant bits), and a bf16
+//     token times a bf16 plane is exact in the fp32 accumulator, so the three
+//     products summed in fp32 give the fp32 router GEMM;
+//   - gate_tiled (T > 64, fp32 tokens): LDS-tiled fp32 FMA.
 #include "common.h"
 
 namespace moe {
@@ -93,45 +98,116 @@ __device__ __forceinline__ void load8<float>(const float* p, float* v) {
 }
 
 // ---------------------------------------------------------------- decode path
-// grid = T workgroups of 256 threads; wave g dots the token against router rows
-// e = g*EG .. in steps of 4*EG. d % 8 == 0.
-template <typename XT, int EG>
+// grid = T workgroups of 256 threads. Thread tid owns K chunks tid*8 + 2048*c
+// (c < XC, d <= 2048*XC); router rows are taken 8 at a time, each thread forms 8
+// partial dots, a wave butterfly folds them and the 4 wave partials meet in LDS.
+constexpr int kRowXC = 4;
+template <typename XT>
 __global__ __launch_bounds__(256) void gate_rowdot(const XT* __restrict__ x, const float* __restrict__ wr_t,
                                                    const float* __restrict__ bias, int d, int E, int Ec, int k,
                                                    bool has_shared, int32_t* __restrict__ idx,
                                                    float* __restrict__ w, float* __restrict__ gs) {
+    __shared__ float part[4][kMaxExperts + 8];
     __shared__ float logits[kMaxExperts + 8];
     const int t = blockIdx.x;
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const XT* xr = x + (size_t)t * d;
-    for (int e0 = wave * EG; e0 < Ec; e0 += 4 * EG) {
-        float acc[EG];
+    float xv[kRowXC][8];
 #pragma unroll
-        for (int g = 0; g < EG; ++g) acc[g] = 0.0f;
-        for (int kk = lane * 8; kk < d; kk += kWave * 8) {
-            float xv[8];
-            load8<XT>(xr + kk, xv);
+    for (int c = 0; c < kRowXC; ++c) {
+        const int kk = tid * 8 + 2048 * c;
+        if (kk < d) load8<XT>(xr + kk, xv[c]);
+        else {
 #pragma unroll
-            for (int g = 0; g < EG; ++g) {
-                if (e0 + g < Ec) {
-                    float wv[8];
-                    load8<float>(wr_t + (size_t)(e0 + g) * d + kk, wv);
+            for (int v = 0; v < 8; ++v) xv[c][v] = 0.0f;
+        }
+    }
+    for (int e0 = 0; e0 < Ec; e0 += 8) {
+        float acc[8];
 #pragma unroll
-                    for (int v = 0; v < 8; ++v) acc[g] = fmaf(xv[v], wv[v], acc[g]);
+        for (int g = 0; g < 8; ++g) acc[g] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < kRowXC; ++c) {
+            const int kk = tid * 8 + 2048 * c;
+            if (kk < d) {
+#pragma unroll
+                for (int g = 0; g < 8; ++g) {
+                    if (e0 + g < Ec) {
+                        float wv[8];
+                        load8<float>(wr_t + (size_t)(e0 + g) * d + kk, wv);
+#pragma unroll
+                        for (int v = 0; v < 8; ++v) acc[g] = fmaf(xv[c][v], wv[v], acc[g]);
+                    }
                 }
             }
         }
 #pragma unroll
-        for (int g = 0; g < EG; ++g) {
-            float s = wave_sum(acc[g]);
-            if (lane == 0 && e0 + g < Ec) logits[e0 + g] = s + ((bias && e0 + g < E) ? bias[e0 + g] : 0.0f);
+        for (int g = 0; g < 8; ++g) {
+            const float sum = wave_sum(acc[g]);
+            if (lane == 0 && e0 + g < Ec) part[wave][e0 + g] = sum;
         }
+    }
+    __syncthreads();
+    if (tid < Ec) {
+        const float b = (bias && tid < E) ? bias[tid] : 0.0f;
+        logits[tid] = (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]) + b;
     }
     __syncthreads();
     if (wave == 0) wave_topk_write(logits, E, k, has_shared, t, idx, w, gs);
 }
 
-// ---------------------------------------------------------------- prefill path
+// ---------------------------------------------------------------- prefill path, bf16 tokens
+// 16 tokens per workgroup; wave v takes the K quarter [v*d/4, (v+1)*d/4) and all
+// 16-column router blocks (NB = ceil(Ec/16) <= 9). A fragments come straight from
+// the token rows, B fragments from the three packed planes ([plane][NB][d/32][64]
+// lanes x 16 B, fragment order). The four wave partials are added in LDS.
+template <int NB>
+__global__ __launch_bounds__(256) void gate_mfma(const bf16_t* __restrict__ x, const u32x4* __restrict__ planes,
+                                                 const float* __restrict__ bias, int T, int d, int E, int k,
+                                                 bool has_shared, int32_t* __restrict__ idx, float* __restrict__ w,
+                                                 float* __restrict__ gs) {
+    constexpr int LP = NB * 16 + 1;
+    __shared__ float part[4][16 * LP];
+    const int t0 = blockIdx.x * 16;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int KS = d / 32;
+    const int ks0 = wave * (KS / 4), ks1 = (wave == 3) ? KS : ks0 + KS / 4;
+    const int tok = min(t0 + lane % 16, T - 1);  // rows past T repeat the last token (dropped below)
+    const bf16_t* xr = x + (size_t)tok * d + 8 * (lane / 16);
+    const size_t plane_stride = (size_t)NB * KS * 64;
+    f32x4 acc[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = ks0; ks < ks1; ++ks) {
+        const bf16x8 af = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xr + ks * 32));
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const u32x4* pb = planes + ((size_t)j * KS + ks) * 64 + lane;
+#pragma unroll
+            for (int pl = 2; pl >= 0; --pl)  // smallest plane first
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    af, __builtin_bit_cast(bf16x8, pb[pl * plane_stride]), acc[j], 0, 0, 0);
+        }
+    }
+    // lane holds column 16*j + lane%16, tokens 4*(lane/16) + i
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[wave][(4 * (lane / 16) + i) * LP + 16 * j + lane % 16] = acc[j][i];
+    __syncthreads();
+    const int Ec = E + (has_shared ? 1 : 0);
+    for (int q = tid; q < 16 * Ec; q += 256) {
+        const int r = q / Ec, col = q - r * Ec;
+        const float b = (bias && col < E) ? bias[col] : 0.0f;
+        const int o = r * LP + col;
+        part[0][o] = (part[0][o] + part[1][o]) + (part[2][o] + part[3][o]) + b;
+    }
+    __syncthreads();
+    for (int r = wave; r < 16; r += 4)
+        if (t0 + r < T) wave_topk_write(part[0] + r * LP, E, k, has_shared, t0 + r, idx, w, gs);
+}
+
+// ---------------------------------------------------------------- prefill path, fp32 tokens
 // 64 tokens x (16*EJ) router columns per workgroup; thread (ty, tx) owns tokens
 // 4*ty..4*ty+3 and columns tx + 16*j. K advances in chunks of 32 with the next
 // chunk held in registers while the current one is consumed from LDS.
@@ -250,12 +326,27 @@ __global__ __launch_bounds__(256) void gate_tiled(const XT* __restrict__ x, cons
 }
 
 template <typename XT>
-hipError_t launch_gate_t(const XT* x, const float* wr_t, const float* bias, int T, int d, int E, bool has_shared,
-                         int k, int32_t* idx, float* w, float* gs, hipStream_t s) {
+hipError_t launch_gate_t(const XT* x, const float* wr_t, const u32x4* planes, const float* bias, int T, int d, int E,
+                         bool has_shared, int k, int32_t* idx, float* w, float* gs, hipStream_t s) {
     const int Ec = E + (has_shared ? 1 : 0);
-    if (T <= 64) {
-        hipLaunchKernelGGL((gate_rowdot<XT, 4>), dim3(T), dim3(256), 0, s, x, wr_t, bias, d, E, Ec, k, has_shared,
-                           idx, w, gs);
+    if (T <= 64 && d <= 2048 * kRowXC) {
+        hipLaunchKernelGGL((gate_rowdot<XT>), dim3(T), dim3(256), 0, s, x, wr_t, bias, d, E, Ec, k, has_shared, idx, w,
+                           gs);
+    } else if (planes != nullptr && (d / 32) >= 4) {
+        const int NB = (Ec + 15) / 16;
+        dim3 grid((T + 15) / 16);
+        switch (NB) {
+#define GATE_MFMA_CASE(J)                                                                                     \
+    case J:                                                                                                   \
+        hipLaunchKernelGGL((gate_mfma<J>), grid, dim3(256), 0, s, (const bf16_t*)x, planes, bias, T, d, E, k, \
+                           has_shared, idx, w, gs);                                                           \
+        break;
+            GATE_MFMA_CASE(1) GATE_MFMA_CASE(2) GATE_MFMA_CASE(3) GATE_MFMA_CASE(4) GATE_MFMA_CASE(5)
+            GATE_MFMA_CASE(6) GATE_MFMA_CASE(7) GATE_MFMA_CASE(8) GATE_MFMA_CASE(9)
+#undef GATE_MFMA_CASE
+            default:
+                return hipErrorInvalidValue;
+        }
     } else {
         const int EJ = (Ec + 15) / 16;
         dim3 grid((T + kTB - 1) / kTB);
@@ -277,11 +368,12 @@ hipError_t launch_gate_t(const XT* x, const float* wr_t, const float* bias, int 
 
 }  // namespace
 
-hipError_t launch_gate(const void* x, bool x_bf16, const float* wr_t, const float* bias, int T, int d, int E,
-                       bool has_shared, int k, int32_t* idx, float* w, float* gs, hipStream_t s) {
+hipError_t launch_gate(const void* x, bool x_bf16, const float* wr_t, const void* planes, const float* bias, int T,
+                       int d, int E, bool has_shared, int k, int32_t* idx, float* w, float* gs, hipStream_t s) {
     if (x_bf16)
-        return launch_gate_t<bf16_t>((const bf16_t*)x, wr_t, bias, T, d, E, has_shared, k, idx, w, gs, s);
-    return launch_gate_t<float>((const float*)x, wr_t, bias, T, d, E, has_shared, k, idx, w, gs, s);
+        return launch_gate_t<bf16_t>((const bf16_t*)x, wr_t, (const u32x4*)planes, bias, T, d, E, has_shared, k, idx,
+                                     w, gs, s);
+    return launch_gate_t<float>((const float*)x, wr_t, nullptr, bias, T, d, E, has_shared, k, idx, w, gs, s);
 }
 
 }  // namespace moe

@@ -46,6 +46,7 @@ struct moe_layer {
     bool has_bias = false;
     // packed weights
     float* wr_t = nullptr;
+    bf16_t* wr_planes = nullptr;  // router as three bf16 planes (bf16 activations)
     float* bias = nullptr;
     void* wgu = nullptr;
     void* wdn = nullptr;
@@ -60,6 +61,7 @@ struct moe_layer {
     float* gs = nullptr;
     void* h = nullptr;
     float* ow = nullptr;
+    size_t ow_rows = 0;
     // profiling
     hipEvent_t ev[6] = {};
     bool ran = false;
@@ -69,7 +71,7 @@ namespace {
 
 void release(moe_layer* L) {
     if (!L) return;
-    void* bufs[] = {L->wr_t, L->bias, L->wgu, L->wdn, L->s_gate, L->s_up, L->s_down, L->counts, L->offsets,
+    void* bufs[] = {L->wr_t, L->wr_planes, L->bias, L->wgu, L->wdn, L->s_gate, L->s_up, L->s_down, L->counts, L->offsets,
                     L->tile_start, L->sorted_c, L->gs, L->h, L->ow};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
@@ -145,6 +147,7 @@ int create_impl(const moe_desc* desc, const moe_weights* w, moe_layer* L) {
     const size_t esz = f32 ? 4 : (i8 ? 1 : 2);
     int rc;
     if ((rc = dev_alloc(&L->wr_t, (size_t)L->Ec * dm * 4))) return rc;
+    if (!f32 && (rc = dev_alloc(&L->wr_planes, (size_t)3 * ((L->Ec + 15) / 16) * 16 * dm * 2))) return rc;
     if (L->has_bias && (rc = dev_alloc(&L->bias, E * 4))) return rc;
     if ((rc = dev_alloc(&L->wgu, Et * 2 * F * dm * esz))) return rc;
     if ((rc = dev_alloc(&L->wdn, Et * F * dm * esz))) return rc;
@@ -160,12 +163,18 @@ int create_impl(const moe_desc* desc, const moe_weights* w, moe_layer* L) {
     if ((rc = dev_alloc(&L->sorted_c, P * 4))) return rc;
     if ((rc = dev_alloc(&L->gs, T * 4))) return rc;
     if ((rc = dev_alloc(&L->h, P * F * (f32 ? 4 : 2)))) return rc;
-    if ((rc = dev_alloc(&L->ow, P * dm * 4))) return rc;
+    // combine buffer: one row per (token, slot, K split): 2 splits for large batches,
+    // up to kStreamMaxSplit for batches the streaming kernels serve
+    L->ow_rows = std::max(P * 2, std::min(T, (size_t)kStreamMaxT) * L->kt * kStreamMaxSplit);
+    if ((rc = dev_alloc(&L->ow, L->ow_rows * dm * 4))) return rc;
     if (d.profile)
         for (hipEvent_t& e : L->ev) HIP_TRY(hipEventCreate(&e));
 
     hipStream_t s = nullptr;
     HIP_TRY(pack_router(w->w_router, d.shared_d_ff > 0 ? w->w_shared_gate : nullptr, d.d_model, L->E, L->wr_t, s));
+    if (L->wr_planes)
+        HIP_TRY(pack_router_planes(w->w_router, d.shared_d_ff > 0 ? w->w_shared_gate : nullptr, d.d_model, L->E,
+                                   L->wr_planes, s));
     if (L->has_bias) HIP_TRY(hipMemcpyAsync(L->bias, w->b_router, E * 4, hipMemcpyDeviceToDevice, s));
     if (f32) {
         // fp32 experts keep the natural layout: [E][d][F] gate, [E][d][F] up, [E][F][d] down
@@ -256,10 +265,30 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
     const bool prof = d.profile != 0;
     if (prof) HIP_TRY(hipEventRecord(L->ev[0], s));
 
-    HIP_TRY(launch_gate(x, !f32, L->wr_t, L->bias, T, d.d_model, L->E, L->V > 0, k, r->topk_idx, r->topk_w, gs, s));
+    HIP_TRY(launch_gate(x, !f32, L->wr_t, L->wr_planes, L->bias, T, d.d_model, L->E, L->V > 0, k, r->topk_idx, r->topk_w, gs, s));
     if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
 
-    const int bm = f32 ? kBMf32 : kBM;
+    // Launch plan (host side, from T, k and the layer shape only):
+    //  - small batches (T <= 64) stream the weights: one row tile per active
+    //    expert (bm >= T), the down projection's K split so ~1024 workgroups run;
+    //  - larger batches use the LDS-tiled MFMA GEMMs, with tall 256-row tiles
+    //    when experts are expected to hold many rows and a 2-way K split of the
+    //    down projection when its column tiles alone would leave the GPU idle.
+    const bool streaming = !f32 && T <= kStreamMaxT;
+    const int avg_rows = (T * k) / L->E;
+    int bm, ksplit = 1;
+    if (f32) {
+        bm = kBMf32;
+    } else if (streaming) {
+        bm = T <= 16 ? 16 : (T <= 32 ? 32 : 64);
+        const int active = std::min(L->E, T * k) + L->V;
+        const int groups = active * (d.d_model / 128);
+        while (ksplit < kStreamMaxSplit && groups * ksplit < 1024 && d.d_ff % (ksplit * 2 * 64) == 0) ksplit *= 2;
+    } else {
+        bm = (avg_rows >= 768 || T >= 8192) ? 256 : 128;
+        if (T >= 1024 && d.d_ff % (2 * 64) == 0) ksplit = 2;
+    }
+    if ((size_t)T * L->kt * ksplit > L->ow_rows) ksplit = 1;  // never past the combine buffer
     ScatterOut so{L->counts, L->offsets, L->tile_start, L->sorted_c, r->expert_counts, r->expert_offsets,
                   r->sorted_assign};
     HIP_TRY(launch_scatter(r->topk_idx, T, L->E, k, L->V, bm, so, s));
@@ -267,7 +296,7 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
 
     // upper bound on sum_e ceil(n_e / bm) over experts with rows
     const int P = T * L->kt;
-    const int max_tiles = (P + bm - 1) / bm + std::min(L->Et, P);
+    const int max_tiles = streaming ? std::min(L->Et, P) : (P + bm - 1) / bm + std::min(L->Et, P);
     if (f32) {
         GemmF32Args a{L->tile_start, L->offsets, L->sorted_c, L->Et, L->kt, k, max_tiles,
                       (const float*)x, (float*)L->h, (const float*)L->wgu,
@@ -277,15 +306,21 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
         if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));
         HIP_TRY(launch_expert_down_f32(a, s));
     } else {
-        GemmArgs a{L->tile_start, L->offsets, L->sorted_c, L->Et, L->kt, k, max_tiles,
+        GemmArgs a{L->tile_start, L->offsets, L->sorted_c, L->Et, L->kt, k, max_tiles, bm, ksplit,
                    (const bf16_t*)x, (bf16_t*)L->h, L->wgu, L->wdn, L->s_gate, L->s_up, L->s_down,
                    r->topk_w, gs, L->ow, d.d_model, d.d_ff};
-        HIP_TRY(launch_expert_up_bf16(a, i8, s));
-        if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));
-        HIP_TRY(launch_expert_down_bf16(a, i8, s));
+        if (streaming) {
+            HIP_TRY(launch_expert_up_stream(a, i8, s));
+            if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));
+            HIP_TRY(launch_expert_down_stream(a, i8, s));
+        } else {
+            HIP_TRY(launch_expert_up_bf16(a, i8, s));
+            if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));
+            HIP_TRY(launch_expert_down_bf16(a, i8, s));
+        }
     }
     if (prof) HIP_TRY(hipEventRecord(L->ev[4], s));
-    HIP_TRY(launch_combine(L->ow, T, L->kt, d.d_model, y, !f32, s));
+    HIP_TRY(launch_combine(L->ow, T, L->kt * ksplit, d.d_model, y, !f32, s));
     if (prof) {
         HIP_TRY(hipEventRecord(L->ev[5], s));
         L->ran = true;

@@ -24,6 +24,33 @@ __global__ void pack_router_kernel(const float* wr, const float* wsg, int d, int
     out[i] = e < E ? wr[(size_t)k * E + e] : wsg[k];
 }
 
+// Exact three-way split of an fp32 value into bf16 planes (round to nearest at each
+// step; the remainders are exact in fp32 and the last one fits 8 bits).
+__device__ __forceinline__ void split3(float v, bf16_t& hi, bf16_t& mid, bf16_t& lo) {
+    hi = f32_to_bf16(v);
+    const float r1 = v - bf16_to_f32(hi);
+    mid = f32_to_bf16(r1);
+    const float r2 = r1 - bf16_to_f32(mid);
+    lo = f32_to_bf16(r2);
+}
+
+__global__ void pack_router_planes_kernel(const float* wr, const float* wsg, int d, int E, int Ec, int NB,
+                                          bf16_t* out) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;  // one per (column, k)
+    if (i >= (size_t)NB * 16 * d) return;
+    const int col = (int)(i / d), k = (int)(i - (size_t)col * d);
+    const float v = col < E ? wr[(size_t)k * E + col] : (col < Ec ? wsg[k] : 0.0f);
+    bf16_t p[3];
+    split3(v, p[0], p[1], p[2]);
+    const int nb = col / 16, ks = k / 32, kin = k % 32;
+    const int lane = col % 16 + 16 * (kin / 8);
+    const size_t plane = (size_t)NB * (d / 32) * 64 * 8;
+    const size_t off = (((size_t)nb * (d / 32) + ks) * 64 + lane) * 8 + kin % 8;
+    out[off] = p[0];
+    out[plane + off] = p[1];
+    out[2 * plane + off] = p[2];
+}
+
 // src element (e, k, n) at src + e*K*ld + k*ld + n; for gate/up the packed column
 // block nb reads src0 (gate) or src1 (up) at column 16*(nb/2).
 template <typename T, int KPB>  // KPB: K rows per packed block (32 bf16, 64 int8)
@@ -70,6 +97,15 @@ hipError_t pack_router(const float* wr, const float* wsg, int d, int E, float* w
     const size_t n = (size_t)Ec * d;
     hipLaunchKernelGGL(pack_router_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, wr, wsg, d, E, Ec,
                        wr_t);
+    return hipGetLastError();
+}
+
+hipError_t pack_router_planes(const float* wr, const float* wsg, int d, int E, bf16_t* planes, hipStream_t s) {
+    const int Ec = E + (wsg ? 1 : 0);
+    const int NB = (Ec + 15) / 16;
+    const size_t n = (size_t)NB * 16 * d;
+    hipLaunchKernelGGL(pack_router_planes_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, wr, wsg, d, E,
+                       Ec, NB, planes);
     return hipGetLastError();
 }
 

@@ -37,13 +37,14 @@ def test_tiny_f32_full():
 
 
 def test_mixtral_shape_reduced_bf16():
+    # T = 1024 splits the down projection's K in two; T = 3072 also switches to 256-row tiles
     cfg = synth.get_config("mixtral_bf16", d_model=512, d_ff=1024)
-    _run(cfg, [1, 8, 64, 300])
+    _run(cfg, [1, 8, 64, 300, 1024, 3072])
 
 
 def test_shared_expert_reduced_bf16():
     cfg = synth.get_config("shared_fine_bf16", d_model=512, d_ff=256, shared_d_ff=2048)
-    _run(cfg, [16, 200])
+    _run(cfg, [16, 200, 1100])
 
 
 def test_skewed_many_experts_reduced_bf16():
@@ -54,7 +55,7 @@ def test_skewed_many_experts_reduced_bf16():
 
 def test_int8_reduced():
     cfg = synth.get_config("int8_mixtral22b", d_model=512, d_ff=1024)
-    _run(cfg, [1, 16, 256])
+    _run(cfg, [1, 16, 256, 1024, 3072])
 
 
 def test_deterministic_and_zero_tokens():
