@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--peaks", action="store_true",
+                    help="only measure achievable peaks with torch/hipBLASLt: a large read-only "
+                         "reduction (HBM) and bf16 GEMMs of the per-expert shape (MFMA)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of 1 GiB (for HBM counter scaling)")
     return ap.parse_args()
@@ -154,6 +157,37 @@ def cpu_baseline(cfg, layer_cpu, x_cpu, n_tok):
                        f"(gate, scatter, {cfg.n_experts} experts, combine), {dt:.1f} s")
 
 
+def measure_peaks(torch):
+    """Achievable rates on this GPU with library kernels (context for the roofline fractions)."""
+    out = {}
+    a = torch.empty(1 << 31, dtype=torch.bfloat16, device="cuda").normal_()  # 4 GiB
+    for _ in range(2):
+        a.sum(dtype=torch.float32)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    n = 10
+    for _ in range(n):
+        a.sum(dtype=torch.float32)
+    ev[1].record()
+    torch.cuda.synchronize()
+    out["read_GBps"] = a.numel() * 2 * n / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
+    del a
+    for M, K, N in ((8192, 8192, 8192), (1024, 4096, 28672), (1024, 14336, 4096)):
+        A = torch.randn(M, K, dtype=torch.bfloat16, device="cuda")
+        B = torch.randn(K, N, dtype=torch.bfloat16, device="cuda")
+        for _ in range(3):
+            A @ B
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(n):
+            A @ B
+        ev[1].record()
+        torch.cuda.synchronize()
+        out[f"gemm_{M}x{K}x{N}_TFLOPs"] = 2.0 * M * N * K * n / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e12
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -169,6 +203,9 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": a.numel() * 4, "copy_bytes_written": b.numel() * 4, "launches": 3}))
+        return
+    if args.peaks:
+        print(json.dumps(measure_peaks(torch)), flush=True)
         return
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import synth

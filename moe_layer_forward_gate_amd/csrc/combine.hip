@@ -20,8 +20,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     if (i >= (size_t)T * d4) return;
     const int t = (int)(i / d4), c4 = (int)(i - (size_t)t * d4);
     const float4* src = reinterpret_cast<const float4*>(ow + (size_t)t * kt * d) + c4;
-    float4 s = src[0];
-    for (int j = 1; j < kt; ++j) {
+    // rows are added in order 0, 1, 2, ...; loads go out 8 rows at a time
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    int j = 0;
+    for (; j + 8 <= kt; j += 8) {
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(j + u) * d4];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
+        }
+    }
+    for (; j < kt; ++j) {
         const float4 v = src[(size_t)j * d4];
         s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
     }

@@ -210,19 +210,51 @@ __global__ __launch_bounds__(kThreads, 1) void expert_gemm(GemmArgs a) {
             __syncthreads();
         }
     } else {
-        // prologue: stages 0 .. STAGES-2 in flight
+        // Fragments are double-buffered in registers: the LDS reads of K step kt+1 are
+        // issued before the MFMAs of step kt, so LDS latency hides under the MFMAs.
+        // Stage (kt-1) % STAGES is refilled in iteration kt: its fragments were read
+        // in iteration kt-2 and consumed in kt-1, before this iteration's barrier.
+        static_assert(STAGES >= 3 && KH == 1, "pipeline shape");
+        bf16x8 fa[2][4], fb[2][NBW];
+        auto read_frags = [&](int stage, bf16x8 (&af)[4], bf16x8 (&bf)[NBW]) {
+            const u32x4* la = lds + (size_t)stage * STAGE * 64;
+            const u32x4* lb = la + ABLK * 64;
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) af[mb] = __builtin_bit_cast(bf16x8, la[(wm * 4 + mb) * 64 + lane]);
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) bf[nb] = __builtin_bit_cast(bf16x8, lb[(wn * NBW + nb) * 64 + lane]);
+        };
+        auto mfma_frags = [&](const bf16x8 (&af)[4], const bf16x8 (&bf)[NBW]) {
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb)
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], bf[nb], acc[mb][nb], 0, 0, 0);
+        };
+        // prologue: stages 0 .. STAGES-2 in flight, then stage 0's fragments
 #pragma unroll
         for (int s0 = 0; s0 < STAGES - 1; ++s0)
             if (s0 < KT) issue(s0, s0);
-        for (int kt = 0; kt < KT; ++kt) {
-            // stage kt has landed once at most the loads of the STAGES-2 later stages are outstanding
-            if (kt + STAGES - 2 < KT) wait_vm_le<(STAGES - 2) * LPS>();
-            else wait_vm_le<0>();
-            // every wave's loads of stage kt are in LDS; stage kt-1 is no longer read. A bare
-            // s_barrier: __syncthreads() would also drain the later stages' loads (vmcnt(0)).
-            lds_barrier();
-            if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-            compute(kt % STAGES);
+        if (STAGES - 2 < KT) wait_vm_le<(STAGES - 2) * LPS>();
+        else wait_vm_le<0>();
+        lds_barrier();
+        read_frags(0, fa[0], fb[0]);
+        for (int kt = 0; kt < KT; kt += 2) {
+            // even step: compute kt from buffer 0, fetch kt+1 into buffer 1
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int k = kt + h;
+                if (k >= KT) break;
+                if (k + 1 < KT) {
+                    // stage k+1 has landed once only the later stages' loads are outstanding
+                    if (k + STAGES - 2 < KT) wait_vm_le<(STAGES - 3) * LPS>();
+                    else wait_vm_le<0>();
+                    lds_barrier();
+                    if (k + STAGES - 1 < KT) issue(k + STAGES - 1, (k + STAGES - 1) % STAGES);
+                    read_frags((k + 1) % STAGES, fa[h ^ 1], fb[h ^ 1]);
+                }
+                mfma_frags(fa[h], fb[h]);
+            }
         }
     }
 

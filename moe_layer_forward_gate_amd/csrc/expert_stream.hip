@@ -106,25 +106,43 @@ __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
             }
     };
 
-    int s = 0;
-    for (; s + U <= nsteps; s += U) {
+    // rounds of U K-steps, double-buffered: the loads of round r+1 are issued before the
+    // MFMAs of round r, so every wave always has a round of weight loads in flight
+    struct Round {
         u32x4 bb[U][NBW];
         u32x4 aa[U][MB][KH];
+    };
+    auto load_round = [&](Round& R, int s0) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int j = 0; j < NBW; ++j) bb[u][j] = bptr[j][(size_t)(s + u) * 64];
+            for (int j = 0; j < NBW; ++j) R.bb[u][j] = bptr[j][(size_t)(s0 + u) * 64];
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                 for (int kh = 0; kh < KH; ++kh)
-                    aa[u][mb][kh] = mb < mb_act ? *reinterpret_cast<const u32x4*>(aptr[mb] + (s + u) * KSTEP + kh * 32)
-                                                : u32x4{0u, 0u, 0u, 0u};
+                    R.aa[u][mb][kh] = mb < mb_act
+                                          ? *reinterpret_cast<const u32x4*>(aptr[mb] + (s0 + u) * KSTEP + kh * 32)
+                                          : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto compute_round = [&](const Round& R) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) step(bb[u], aa[u]);
+        for (int u = 0; u < U; ++u) step(R.bb[u], R.aa[u]);
+    };
+    const int nround = nsteps / U;
+    Round r0, r1;
+    if (nround > 0) load_round(r0, 0);
+    for (int r = 0; r < nround; r += 2) {
+        if (r + 1 < nround) load_round(r1, (r + 1) * U);
+        compute_round(r0);
+        if (r + 1 < nround) {
+            if (r + 2 < nround) load_round(r0, (r + 2) * U);
+            compute_round(r1);
+        }
     }
+    int s = nround * U;
     for (; s < nsteps; ++s) {
         u32x4 bb[NBW];
         u32x4 aa[MB][KH];
@@ -187,7 +205,8 @@ __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
 template <int MB, bool INT8, bool UP>
 hipError_t launch_mb(const GemmArgs& a, int S, hipStream_t s) {
     constexpr int NBW = 2;
-    constexpr int U = INT8 ? 4 : (MB <= 2 ? 8 : 4);
+    // K-steps per round (two rounds are in flight per wave)
+    constexpr int U = INT8 ? 2 : (MB <= 2 ? 4 : 2);
     const int N = UP ? 2 * a.F : a.d;
     const int NG = N / (16 * NBW * 4);
     dim3 grid((unsigned)((size_t)a.max_tiles * NG * S));

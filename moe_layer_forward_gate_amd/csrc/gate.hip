@@ -17,6 +17,8 @@
 //     token times a bf16 plane is exact in the fp32 accumulator, so the three
 //     products summed in fp32 give the fp32 router GEMM;
 //   - gate_tiled (T > 64, fp32 tokens): LDS-tiled fp32 FMA.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -112,14 +114,31 @@ __global__ __launch_bounds__(256) void gate_rowdot(const XT* __restrict__ x, con
     const int t = blockIdx.x;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const XT* xr = x + (size_t)t * d;
-    float xv[kRowXC][8];
+    // every load is unconditional (out-of-range chunks and rows read a valid address and are
+    // zeroed or dropped), so the compiler can keep all of them in flight at once
+    constexpr int XQ = sizeof(XT) / 2;  // 16-byte chunks per 8 elements
+    u32x4 xq[kRowXC][XQ];
 #pragma unroll
     for (int c = 0; c < kRowXC; ++c) {
         const int kk = tid * 8 + 2048 * c;
-        if (kk < d) load8<XT>(xr + kk, xv[c]);
-        else {
+        const u32x4* p = reinterpret_cast<const u32x4*>(xr + (kk < d ? kk : 0));
 #pragma unroll
-            for (int v = 0; v < 8; ++v) xv[c][v] = 0.0f;
+        for (int q = 0; q < XQ; ++q) xq[c][q] = p[q];
+    }
+    float xv[kRowXC][8];
+#pragma unroll
+    for (int c = 0; c < kRowXC; ++c) {
+        const bool ok = tid * 8 + 2048 * c < d;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            float f;
+            if constexpr (XQ == 1) {
+                const uint32_t wv = xq[c][0][v / 2];
+                f = __uint_as_float((v & 1) ? (wv & 0xFFFF0000u) : (wv << 16));
+            } else {
+                f = __uint_as_float(xq[c][v / 4][v % 4]);
+            }
+            xv[c][v] = ok ? f : 0.0f;
         }
     }
     for (int e0 = 0; e0 < Ec; e0 += 8) {
@@ -129,16 +148,14 @@ __global__ __launch_bounds__(256) void gate_rowdot(const XT* __restrict__ x, con
 #pragma unroll
         for (int c = 0; c < kRowXC; ++c) {
             const int kk = tid * 8 + 2048 * c;
-            if (kk < d) {
+            const int kc = kk < d ? kk : 0;
 #pragma unroll
-                for (int g = 0; g < 8; ++g) {
-                    if (e0 + g < Ec) {
-                        float wv[8];
-                        load8<float>(wr_t + (size_t)(e0 + g) * d + kk, wv);
+            for (int g = 0; g < 8; ++g) {
+                const int e = e0 + g < Ec ? e0 + g : 0;
+                float wv[8];
+                load8<float>(wr_t + (size_t)e * d + kc, wv);
 #pragma unroll
-                        for (int v = 0; v < 8; ++v) acc[g] = fmaf(xv[c][v], wv[v], acc[g]);
-                    }
-                }
+                for (int v = 0; v < 8; ++v) acc[g] = fmaf(xv[c][v], wv[v], acc[g]);
             }
         }
 #pragma unroll
@@ -178,17 +195,33 @@ __global__ __launch_bounds__(256) void gate_mfma(const bf16_t* __restrict__ x, c
     f32x4 acc[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int ks = ks0; ks < ks1; ++ks) {
-        const bf16x8 af = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xr + ks * 32));
+    // U K-steps per round, every load of the round issued before the first MFMA
+    constexpr int U = NB <= 2 ? 8 : (NB <= 4 ? 4 : 2);
+    auto round = [&](int ks, auto uconst) {
+        constexpr int UU = decltype(uconst)::value;
+        u32x4 av[UU], bv[UU][NB][3];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const u32x4* pb = planes + ((size_t)j * KS + ks) * 64 + lane;
+        for (int u = 0; u < UU; ++u) {
+            av[u] = *reinterpret_cast<const u32x4*>(xr + (ks + u) * 32);
 #pragma unroll
-            for (int pl = 2; pl >= 0; --pl)  // smallest plane first
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    af, __builtin_bit_cast(bf16x8, pb[pl * plane_stride]), acc[j], 0, 0, 0);
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int pl = 0; pl < 3; ++pl) bv[u][j][pl] = planes[pl * plane_stride + ((size_t)j * KS + ks + u) * 64 + lane];
         }
-    }
+        __builtin_amdgcn_sched_barrier(0);  // keep the whole round's loads ahead of its MFMAs
+#pragma unroll
+        for (int u = 0; u < UU; ++u)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int pl = 2; pl >= 0; --pl)  // smallest plane first
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u]),
+                                                                     __builtin_bit_cast(bf16x8, bv[u][j][pl]), acc[j],
+                                                                     0, 0, 0);
+    };
+    int ks = ks0;
+    for (; ks + U <= ks1; ks += U) round(ks, std::integral_constant<int, U>{});
+    for (; ks < ks1; ++ks) round(ks, std::integral_constant<int, 1>{});
     // lane holds column 16*j + lane%16, tokens 4*(lane/16) + i
 #pragma unroll
     for (int j = 0; j < NB; ++j)
