@@ -26,6 +26,38 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 
+# HBM traffic per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (scaled by a
+# plain-copy calibration), keyed by kernel and workload, valid only while the kernel's
+# sources hash to the recorded value.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "expert_gemm": ["expert_gemm.hip", "common.h"],
+    "expert_stream": ["expert_stream.hip", "common.h"],
+}
+
+
+def kernel_sources_sha(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "moe_layer_forward_gate_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def lookup_traffic(kernel, key):
+    """Measured HBM bytes per launch of `kernel` on workload `key`, or None when not measured
+    or measured on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            tab = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    ent = tab.get("kernels", {}).get(f"{kernel}|{key}")
+    if not ent or ent.get("source_sha") != kernel_sources_sha(kernel):
+        return None
+    return ent.get("bytes_per_launch")
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -118,15 +150,18 @@ def summarize(cfg, res):
     T = res["T"]
     up, dn, layer = kernel_work(cfg, res["counts"], T)
     gate_ms, scat_ms, up_ms, dn_ms, comb_ms = res["stage_ms"]
-    decode = T <= 256 and cfg.expert_dtype != "f32" and (2.0 * T * cfg.top_k / max(layer["active"], 1)) < 300
+    # the up kernel's own roofline: bandwidth-bound below the ridge point (peak flops / peak bytes)
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    decode = up["flops"] / up["bytes"] < ridge
     if decode:
         rf = dict(bound="hbm", achieved=up["bytes"] / (up_ms * 1e-3) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
     else:
         rf = dict(bound="mfma", achieved=up["flops"] / (up_ms * 1e-3) / 1e12, peak=MFMA_BF16_PEAK_TFLOPS,
                   unit="TFLOP/s")
     rf["frac"] = rf["achieved"] / rf["peak"]
-    rf["traffic"] = None
-    rf["kernel"] = "expert_gemm<up>"
+    kern = "expert_stream" if (T <= 64 and cfg.expert_dtype != "f32") else "expert_gemm"
+    rf["kernel"] = f"{kern}<up>"
+    rf["traffic"] = lookup_traffic(kern, f"up|{cfg.name}|T={T}")
     rf["avg_ms"] = up_ms
     layer_s = res["ms_per_step"] * 1e-3
     return dict(

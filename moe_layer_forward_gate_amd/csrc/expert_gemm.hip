@@ -231,31 +231,31 @@ __global__ __launch_bounds__(kThreads, 1) void expert_gemm(GemmArgs a) {
                 for (int nb = 0; nb < NBW; ++nb)
                     acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], bf[nb], acc[mb][nb], 0, 0, 0);
         };
-        // prologue: stages 0 .. STAGES-2 in flight, then stage 0's fragments
+        // Branch-free steady state (a join in the loop would make the compiler drain every
+        // LDS read before the MFMAs): every step issues one stage of LDS-DMA loads -- past
+        // the last stage it re-loads the last stage into the free slot, which is never
+        // read -- and every step but the last reads the next step's fragments. K/32 is
+        // even, so the step pairs below always end with the buffer parity known.
+        auto step = [&](int k, bf16x8 (&ca)[4], bf16x8 (&cb)[NBW], bf16x8 (&na)[4], bf16x8 (&nb)[NBW]) {
+            wait_vm_le<(STAGES - 3) * LPS>();  // stage k+1 has landed
+            lds_barrier();                     // ... for every wave; stage k-1 is free
+            issue(min(k + STAGES - 1, KT - 1), (k + STAGES - 1) % STAGES);
+            read_frags((k + 1) % STAGES, na, nb);
+            mfma_frags(ca, cb);
+        };
 #pragma unroll
-        for (int s0 = 0; s0 < STAGES - 1; ++s0)
-            if (s0 < KT) issue(s0, s0);
-        if (STAGES - 2 < KT) wait_vm_le<(STAGES - 2) * LPS>();
-        else wait_vm_le<0>();
+        for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(min(s0, KT - 1), s0);
+        wait_vm_le<(STAGES - 2) * LPS>();
         lds_barrier();
         read_frags(0, fa[0], fb[0]);
-        for (int kt = 0; kt < KT; kt += 2) {
-            // even step: compute kt from buffer 0, fetch kt+1 into buffer 1
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int k = kt + h;
-                if (k >= KT) break;
-                if (k + 1 < KT) {
-                    // stage k+1 has landed once only the later stages' loads are outstanding
-                    if (k + STAGES - 2 < KT) wait_vm_le<(STAGES - 3) * LPS>();
-                    else wait_vm_le<0>();
-                    lds_barrier();
-                    if (k + STAGES - 1 < KT) issue(k + STAGES - 1, (k + STAGES - 1) % STAGES);
-                    read_frags((k + 1) % STAGES, fa[h ^ 1], fb[h ^ 1]);
-                }
-                mfma_frags(fa[h], fb[h]);
-            }
+        int k = 0;
+        for (; k < KT - 2; k += 2) {
+            step(k, fa[0], fb[0], fa[1], fb[1]);
+            step(k + 1, fa[1], fb[1], fa[0], fb[0]);
         }
+        step(k, fa[0], fb[0], fa[1], fb[1]);
+        mfma_frags(fa[1], fb[1]);
+        wait_vm_le<0>();  // no LDS-DMA write may outlive the workgroup
     }
 
     // ---- epilogue: lane holds column lane%16 of each 16x16 block, rows 4*(lane/16)+i
@@ -322,6 +322,8 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
     }
     const int N = UP ? 2 * a.F : a.d;
     const int S = UP ? 1 : a.ksplit;
+    const int Kpart = (UP ? a.d : a.F) / S;
+    if (Kpart % 64 != 0 || Kpart < 64) return hipErrorInvalidValue;  // the pipeline takes K steps in pairs
     const int NTp = (N / BN + GN - 1) / GN * GN;
     // a multiple of 8 workgroups, so every XCD gets ceil(tiles / 8) slots
     dim3 grid((unsigned)(((size_t)a.max_tiles * NTp * S + kXcds - 1) / kXcds * kXcds));
