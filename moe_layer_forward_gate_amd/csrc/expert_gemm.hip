@@ -36,9 +36,8 @@ namespace moe {
 namespace {
 
 constexpr int BN = 256;
+constexpr int kBf16Waves = 8;
 constexpr int GN = 4;       // column tiles per group (see decode_tile)
-constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / kWave;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -58,11 +57,12 @@ __device__ __forceinline__ void dma16(const void* src, u32x4* lds_block) {
     __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_block, 16, 0, 0);
 }
 
-// s_waitcnt with vmcnt <= N (N < 16) and the other counters left alone (gfx9 encoding)
+// s_waitcnt with vmcnt <= N (N < 64) and the other counters left alone (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 template <int N>
 __device__ __forceinline__ void wait_vm_le() {
-    static_assert(N >= 0 && N < 16, "vmcnt immediate");
-    __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
+    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 // Workgroup barrier without a memory fence (the waits above it are explicit); the
@@ -76,15 +76,29 @@ template <bool INT8> struct Pipe;
 template <> struct Pipe<false> { static constexpr int BK = 32, STAGES = 4; };
 template <> struct Pipe<true> { static constexpr int BK = 64, STAGES = 2; };
 
-template <int BM, bool INT8, bool UP>
-__global__ __launch_bounds__(kThreads, 1) void expert_gemm(GemmArgs a) {
+// Wave layout: NW waves; 8 waves tile the block 4 x 2 (BM 256) or 2 x 4 (BM 128) with
+// 64-row wave tiles; 4 waves would tile it 2 x 2 with (BM/2)-row x 128-column wave tiles
+// (fewer LDS fragment reads per MFMA, accumulators in AGPRs, one wave per SIMD).
+template <int BM, int NW>
+struct WaveShape {
+    static constexpr int WM = NW == 8 ? BM / 64 : 2;  // waves along M
+    static constexpr int WN = NW / WM;                // waves along N
+    static constexpr int MWB = BM / 16 / WM;          // 16-row blocks per wave
+    static constexpr int NBW = (BN / 16) / WN;        // 16-column blocks per wave
+};
+
+template <int BM, int NW, bool INT8, bool UP>
+__global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
+    constexpr int kThreads = NW * 64;
+    constexpr int kWaves = NW;
     constexpr int BK = Pipe<INT8>::BK;
     constexpr int STAGES = Pipe<INT8>::STAGES;
     constexpr int KH = BK / 32;               // 32-K halves per K step
     constexpr int MBLK = BM / 16;             // 16-row blocks per tile
-    constexpr int WM = BM / 64;               // waves along M
-    constexpr int WN = kWaves / WM;           // waves along N
-    constexpr int NBW = (BN / 16) / WN;       // 16-column blocks per wave
+    constexpr int WM = WaveShape<BM, NW>::WM;
+    constexpr int WN = WaveShape<BM, NW>::WN;
+    constexpr int MWB = WaveShape<BM, NW>::MWB;
+    constexpr int NBW = WaveShape<BM, NW>::NBW;
     constexpr int ABLK = MBLK * KH;           // A blocks per stage
     constexpr int BBLK = (BN / 16) * KH;      // B blocks per stage
     constexpr int STAGE = ABLK + BBLK;        // 1 KB blocks per stage
@@ -169,9 +183,9 @@ __global__ __launch_bounds__(kThreads, 1) void expert_gemm(GemmArgs a) {
         }
     };
 
-    f32x4 acc[4][NBW];
+    f32x4 acc[MWB][NBW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MWB; ++i)
 #pragma unroll
         for (int j = 0; j < NBW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -180,15 +194,15 @@ __global__ __launch_bounds__(kThreads, 1) void expert_gemm(GemmArgs a) {
         const u32x4* lb = la + ABLK * 64;
 #pragma unroll
         for (int kh = 0; kh < KH; ++kh) {
-            bf16x8 af[4], bfg[NBW];
+            bf16x8 af[MWB], bfg[NBW];
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-                af[mb] = __builtin_bit_cast(bf16x8, la[((wm * 4 + mb) * KH + kh) * 64 + lane]);
+            for (int mb = 0; mb < MWB; ++mb)
+                af[mb] = __builtin_bit_cast(bf16x8, la[((wm * MWB + mb) * KH + kh) * 64 + lane]);
 #pragma unroll
             for (int nb = 0; nb < NBW; ++nb)
                 bfg[nb] = __builtin_bit_cast(bf16x8, lb[((wn * NBW + nb) * KH + kh) * 64 + lane]);
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
+            for (int mb = 0; mb < MWB; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < NBW; ++nb)
                     acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], bfg[nb], acc[mb][nb], 0, 0, 0);
@@ -215,18 +229,18 @@ __global__ __launch_bounds__(kThreads, 1) void expert_gemm(GemmArgs a) {
         // Stage (kt-1) % STAGES is refilled in iteration kt: its fragments were read
         // in iteration kt-2 and consumed in kt-1, before this iteration's barrier.
         static_assert(STAGES >= 3 && KH == 1, "pipeline shape");
-        bf16x8 fa[2][4], fb[2][NBW];
-        auto read_frags = [&](int stage, bf16x8 (&af)[4], bf16x8 (&bf)[NBW]) {
+        bf16x8 fa[2][MWB], fb[2][NBW];
+        auto read_frags = [&](int stage, bf16x8 (&af)[MWB], bf16x8 (&bf)[NBW]) {
             const u32x4* la = lds + (size_t)stage * STAGE * 64;
             const u32x4* lb = la + ABLK * 64;
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) af[mb] = __builtin_bit_cast(bf16x8, la[(wm * 4 + mb) * 64 + lane]);
+            for (int mb = 0; mb < MWB; ++mb) af[mb] = __builtin_bit_cast(bf16x8, la[(wm * MWB + mb) * 64 + lane]);
 #pragma unroll
             for (int nb = 0; nb < NBW; ++nb) bf[nb] = __builtin_bit_cast(bf16x8, lb[(wn * NBW + nb) * 64 + lane]);
         };
-        auto mfma_frags = [&](const bf16x8 (&af)[4], const bf16x8 (&bf)[NBW]) {
+        auto mfma_frags = [&](const bf16x8 (&af)[MWB], const bf16x8 (&bf)[NBW]) {
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
+            for (int mb = 0; mb < MWB; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < NBW; ++nb)
                     acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], bf[nb], acc[mb][nb], 0, 0, 0);
@@ -236,7 +250,7 @@ __global__ __launch_bounds__(kThreads, 1) void expert_gemm(GemmArgs a) {
         // the last stage it re-loads the last stage into the free slot, which is never
         // read -- and every step but the last reads the next step's fragments. K/32 is
         // even, so the step pairs below always end with the buffer parity known.
-        auto step = [&](int k, bf16x8 (&ca)[4], bf16x8 (&cb)[NBW], bf16x8 (&na)[4], bf16x8 (&nb)[NBW]) {
+        auto step = [&](int k, bf16x8 (&ca)[MWB], bf16x8 (&cb)[NBW], bf16x8 (&na)[MWB], bf16x8 (&nb)[NBW]) {
             wait_vm_le<(STAGES - 3) * LPS>();  // stage k+1 has landed
             lds_barrier();                     // ... for every wave; stage k-1 is free
             issue(min(k + STAGES - 1, KT - 1), (k + STAGES - 1) % STAGES);
@@ -271,10 +285,10 @@ __global__ __launch_bounds__(kThreads, 1) void expert_gemm(GemmArgs a) {
                 su = a.s_up[(size_t)tl.e * a.F + f];
             }
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
+            for (int mb = 0; mb < MWB; ++mb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = wm * 64 + mb * 16 + rq + i;
+                    const int r = (wm * MWB + mb) * 16 + rq + i;
                     if (r < tl.rows) {
                         const float g = acc[mb][2 * q][i] * sg;
                         const float u = acc[mb][2 * q + 1][i] * su;
@@ -285,10 +299,10 @@ __global__ __launch_bounds__(kThreads, 1) void expert_gemm(GemmArgs a) {
         }
     } else {
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < MWB; ++mb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = wm * 64 + mb * 16 + rq + i;
+                const int r = (wm * MWB + mb) * 16 + rq + i;
                 if (r < tl.rows) {
                     const int c = a.sorted_c[tl.seg0 + tl.row0 + r];
                     const int t = c / a.kt, j = c - t * a.kt;
@@ -307,12 +321,12 @@ __global__ __launch_bounds__(kThreads, 1) void expert_gemm(GemmArgs a) {
     }
 }
 
-template <int BM, bool INT8, bool UP>
+template <int BM, int NW, bool INT8, bool UP>
 hipError_t launch(const GemmArgs& a, hipStream_t s) {
     constexpr int KH = Pipe<INT8>::BK / 32;
     constexpr int STAGE = (BM / 16) * KH + (BN / 16) * KH;
     const size_t lds_bytes = (size_t)Pipe<INT8>::STAGES * STAGE * 64 * 16;
-    auto kern = expert_gemm<BM, INT8, UP>;
+    auto kern = expert_gemm<BM, NW, INT8, UP>;
     static bool attr_set = false;  // one-time opt-in above the default dynamic LDS limit
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -327,14 +341,16 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
     const int NTp = (N / BN + GN - 1) / GN * GN;
     // a multiple of 8 workgroups, so every XCD gets ceil(tiles / 8) slots
     dim3 grid((unsigned)(((size_t)a.max_tiles * NTp * S + kXcds - 1) / kXcds * kXcds));
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds_bytes, s, a);
+    hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds_bytes, s, a);
     return hipGetLastError();
 }
 
 template <bool UP>
 hipError_t launch_dispatch(const GemmArgs& a, bool int8, hipStream_t s) {
-    if (a.bm == 256) return int8 ? launch<256, true, UP>(a, s) : launch<256, false, UP>(a, s);
-    if (a.bm == 128) return int8 ? launch<128, true, UP>(a, s) : launch<128, false, UP>(a, s);
+    // 8 waves (two per SIMD): the 4-wave layout with 128 x 128 wave tiles reads less LDS per
+    // MFMA but leaves one wave per SIMD to hide every latency, and measured 25% slower
+    if (a.bm == 256) return int8 ? launch<256, 8, true, UP>(a, s) : launch<256, kBf16Waves, false, UP>(a, s);
+    if (a.bm == 128) return int8 ? launch<128, 8, true, UP>(a, s) : launch<128, kBf16Waves, false, UP>(a, s);
     return hipErrorInvalidValue;
 }
 
