@@ -5,10 +5,12 @@ combine) over one batch of T synthetic tokens, inputs resident in HBM. Layers
 rotate round-robin over several independently drawn instances so consecutive
 steps never reuse weights from the 256 MB last-level cache.
 
-Prints one JSON line: tokens/s of the main workload, the roofline of its
-dominant kernel (the expert up-projection GEMM; HIP events around each stage,
-recorded by libmoe on the stream the kernels run on), a sweep of the other token
-counts of the same layer, and the CPU oracle timed on a bounded sample.
+Prints one JSON line: tokens/s of the main workload (timed with libmoe's stage
+events off), the roofline of its dominant kernel (the expert up-projection GEMM;
+its average duration comes from libmoe's per-stage HIP events, recorded on the
+stream the kernels run on over a second pass of the same steps), a sweep of the
+other token counts of the same layer, and the CPU oracle timed on a bounded
+sample.
 
   python bench.py [--steps K] [--warmup W] [--config NAME] [--tokens T]
 """
@@ -68,6 +70,7 @@ def parse():
     ap.add_argument("--tokens", type=int, default=None, help="main workload T (default: largest of the config)")
     ap.add_argument("--instances", type=int, default=4)
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--peaks", action="store_true",
@@ -108,7 +111,7 @@ def build_instances(cfg, n, T, torch, synth, moe_tensors):
     insts = []
     for i in range(n):
         L = synth.make_layer(cfg, device="cuda", instance=i)
-        lay = gpu_layer(L, T, profile=True)
+        lay = gpu_layer(L, T, profile=False)
         x = synth.make_tokens(cfg, T, device="cuda", instance=i)
         out = lay.outputs(T, scatter=True)
         insts.append((lay, x, out))
@@ -119,26 +122,51 @@ def build_instances(cfg, n, T, torch, synth, moe_tensors):
     return insts
 
 
-def run_workload(cfg, T, steps, warmup, n_inst, torch, synth, keep_layer0=False):
+def run_workload(cfg, T, steps, warmup, n_inst, torch, synth, keep_layer0=False, graph=False):
+    """Time `steps` forwards (rotating over n_inst layers) with per-stage events off, then run
+    the same steps again with libmoe's per-stage HIP events on and average the stage times."""
+    import numpy as np
     keep = {} if keep_layer0 else None
     insts = build_instances(cfg, n_inst, T, torch, synth, keep)
     for i in range(warmup):
         lay, x, out = insts[i % n_inst]
         lay.forward(x, out=out)
     torch.cuda.synchronize()
+    graphs = None
+    if graph:
+        # one HIP graph per layer instance, each replaying that instance's moe_forward
+        graphs = []
+        s = torch.cuda.Stream()
+        for lay, x, out in insts:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                lay.forward(x, out=out)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for i in range(steps):
+        if graphs is not None:
+            graphs[i % n_inst].replay()
+        else:
+            lay, x, out = insts[i % n_inst]
+            lay.forward(x, out=out)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stages = []
+    for lay, _, _ in insts:
+        lay.set_profiling(True)
     for i in range(steps):
         lay, x, out = insts[i % n_inst]
         lay.forward(x, out=out)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # stage times of the last forward of each instance (all inside the timed loop)
-    stages = [lay.stage_times() for lay, _, _ in insts[: min(n_inst, steps)]]
-    import numpy as np
+        stages.append(lay.stage_times())
     st = np.mean(np.array(stages), axis=0).tolist()
     counts = insts[(steps - 1) % n_inst][2].expert_counts.cpu().numpy()
     res = dict(T=T, ms_per_step=1e3 * wall / steps, stage_ms=st, counts=counts)
     x0 = insts[0][1].cpu() if keep_layer0 else None
+    del graphs
     for lay, _, _ in insts:
         lay.close()
     del insts
@@ -252,7 +280,7 @@ def main():
     print(f"[bench] {cfg.name} T={T} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
     want_cpu = not args.no_cpu_baseline
     res, layer0, x0 = run_workload(cfg, T, args.steps, args.warmup, args.instances, torch, synth,
-                                   keep_layer0=want_cpu)
+                                   keep_layer0=want_cpu, graph=args.graph)
     main_s = summarize(cfg, res)
     print(f"[bench] main {json.dumps(main_s)}", file=sys.stderr, flush=True)
     sweep = []
@@ -260,7 +288,8 @@ def main():
         for Ts in cfg.tokens:
             if Ts == T:
                 continue
-            r, _, _ = run_workload(cfg, Ts, max(args.steps, 20), args.warmup, args.instances, torch, synth)
+            r, _, _ = run_workload(cfg, Ts, max(args.steps, 20), args.warmup, args.instances, torch, synth,
+                                   graph=args.graph)
             s = summarize(cfg, r)
             sweep.append(s)
             print(f"[bench] sweep {json.dumps(s)}", file=sys.stderr, flush=True)
@@ -284,7 +313,7 @@ def main():
         "config": {"workload": f"{cfg.name}: MoE layer d_model={cfg.d_model} E={cfg.n_experts} "
                                f"d_ff={cfg.d_ff} top-{cfg.top_k}"
                                + (f" + shared d_ff={cfg.shared_d_ff}" if cfg.shared_d_ff else ""),
-                   "tokens": T, "instances": args.instances},
+                   "tokens": T, "instances": args.instances, "hip_graph": bool(args.graph)},
         "roofline": {k: main_s["roofline"][k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
         "roofline_kernel": main_s["roofline"]["kernel"],
         "stage_ms": main_s["stage_ms"],

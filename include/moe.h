@@ -76,7 +76,7 @@ typedef struct moe_desc {
     int32_t act_dtype;      /* moe_dtype of x and y */
     int32_t expert_dtype;   /* moe_dtype of the expert weights */
     int32_t shared_d_ff;    /* 0: no shared expert */
-    int32_t profile;        /* 1: record per-stage HIP events (moe_stage_times) */
+    int32_t profile;        /* 1: start with per-stage HIP events on (moe_set_profiling) */
 } moe_desc;
 
 /* Layer weights (device pointers, read only during moe_layer_create).
@@ -143,10 +143,18 @@ MOE_API int moe_layer_create(const moe_desc* desc, const moe_weights* weights, m
 MOE_API int moe_forward(moe_layer* layer, const void* x, int32_t T, void* y,
                 const moe_route_out* route, void* stream);
 
-/* Per-stage times in milliseconds of the last moe_forward of a layer created
- * with profile = 1: ms[0] gate, ms[1] scatter, ms[2] expert up (gate/up GEMM
- * and SiLU), ms[3] expert down, ms[4] gather/combine. Waits for that call's
- * last event. EINVAL if the layer does not profile or has not run. */
+/* Turn per-stage HIP event timing on (1) or off (0) for the following
+ * moe_forward calls on this layer ([0539edu §3.3]: profiling is a per-call
+ * switch of the inference config). The initial state is desc->profile. Events
+ * are recorded on the call's stream between the stages, so timing adds a few
+ * microseconds per stage. Statuses: EINVAL (NULL layer, enable not 0 or 1),
+ * EHIP (event creation failed). */
+MOE_API int moe_set_profiling(moe_layer* layer, int enable);
+
+/* Per-stage times in milliseconds of the last moe_forward that ran with
+ * profiling on: ms[0] gate, ms[1] scatter, ms[2] expert up (gate/up GEMM and
+ * SiLU), ms[3] expert down, ms[4] gather/combine. Waits for that call's last
+ * event. EINVAL if no forward has run with profiling on. */
 MOE_API int moe_stage_times(moe_layer* layer, float ms[5]);
 
 /* Release a layer and everything it allocated. NULL-safe. Waits for the

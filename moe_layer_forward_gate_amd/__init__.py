@@ -2,7 +2,8 @@
 
 Argument marshalling only: every step of the forward runs in libmoe's HIP
 kernels. The raw C entry points keep their C names (moe_layer_create,
-moe_forward, moe_stage_times, moe_destroy, moe_status_str, moe_last_error);
+moe_forward, moe_set_profiling, moe_stage_times, moe_destroy, moe_status_str,
+moe_last_error);
 MoeLayer wraps them for torch device tensors. PyTorch supplies device memory and
 streams. If libmoe.so has not been built, loading raises: there is no fallback.
 """
@@ -15,8 +16,8 @@ from typing import Optional
 
 __all__ = [
     "MoeError", "lib", "MOE_F32", "MOE_BF16", "MOE_I8", "MoeDesc", "MoeWeights", "MoeRouteOut",
-    "moe_layer_create", "moe_forward", "moe_stage_times", "moe_destroy", "moe_status_str",
-    "moe_last_error", "MoeLayer", "LIB_PATH", "EXPORTED",
+    "moe_layer_create", "moe_forward", "moe_set_profiling", "moe_stage_times", "moe_destroy",
+    "moe_status_str", "moe_last_error", "MoeLayer", "LIB_PATH", "EXPORTED",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
@@ -25,8 +26,8 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOMEM, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_I8 = 0, 1, 2
 
 # every symbol include/moe.h declares
-EXPORTED = ("moe_layer_create", "moe_forward", "moe_stage_times", "moe_destroy", "moe_status_str",
-            "moe_last_error")
+EXPORTED = ("moe_layer_create", "moe_forward", "moe_set_profiling", "moe_stage_times", "moe_destroy",
+            "moe_status_str", "moe_last_error")
 
 
 class MoeError(RuntimeError):
@@ -69,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.moe_forward.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                   ctypes.POINTER(MoeRouteOut), ctypes.c_void_p]
         L.moe_forward.restype = ctypes.c_int
+        L.moe_set_profiling.argtypes = [ctypes.c_void_p, ctypes.c_int]
+        L.moe_set_profiling.restype = ctypes.c_int
         L.moe_stage_times.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]
         L.moe_stage_times.restype = ctypes.c_int
         L.moe_destroy.argtypes = [ctypes.c_void_p]
@@ -105,6 +108,10 @@ def moe_layer_create(desc: MoeDesc, weights: MoeWeights) -> ctypes.c_void_p:
 def moe_forward(handle, x_ptr: int, T: int, y_ptr: int, route: MoeRouteOut, stream_ptr: int = 0) -> None:
     """Raw forward on device pointers; enqueues on the given HIP stream."""
     _check(lib().moe_forward(handle, x_ptr, T, y_ptr, ctypes.byref(route), stream_ptr), "moe_forward")
+
+
+def moe_set_profiling(handle, enable: bool) -> None:
+    _check(lib().moe_set_profiling(handle, 1 if enable else 0), "moe_set_profiling")
 
 
 def moe_stage_times(handle):
@@ -207,6 +214,10 @@ class MoeLayer:
         moe_forward(self._h, _ptr(x), T, _ptr(out.y), route, int(s.cuda_stream))
         return out
 
+    def set_profiling(self, enable: bool) -> None:
+        """Record per-stage HIP events in the following forwards (or stop)."""
+        moe_set_profiling(self._h, enable)
+
     def stage_times(self):
-        """[gate, scatter, up, down, combine] ms of the last forward (profile=True layers)."""
+        """[gate, scatter, up, down, combine] ms of the last forward run with profiling on."""
         return moe_stage_times(self._h)

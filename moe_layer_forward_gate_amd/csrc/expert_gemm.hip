@@ -30,6 +30,8 @@
 // Up-projection columns are packed gate/up interleaved per 16 columns, so each
 // lane holds the gate and up accumulators of the same (row, f) and SiLU * up
 // runs in registers.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -250,37 +252,55 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
         // the last stage it re-loads the last stage into the free slot, which is never
         // read -- and every step but the last reads the next step's fragments. K/32 is
         // even, so the step pairs below always end with the buffer parity known.
-        auto step = [&](int k, bf16x8 (&ca)[MWB], bf16x8 (&cb)[NBW], bf16x8 (&na)[MWB], bf16x8 (&nb)[NBW]) {
-            wait_vm_le<(STAGES - 3) * LPS>();  // stage k+1 has landed
-            lds_barrier();                     // ... for every wave; stage k-1 is free
-            issue(min(k + STAGES - 1, KT - 1), (k + STAGES - 1) % STAGES);
-            read_frags((k + 1) % STAGES, na, nb);
-            mfma_frags(ca, cb);
-        };
+        // A wave whose 64 rows all lie past the expert's last row (the ragged last row
+        // tile) runs the same loop without fragment reads or MFMAs: it still loads its
+        // share of the tiles and meets every barrier.
+        auto run = [&](auto compute) {
+            constexpr bool C = decltype(compute)::value;
+            auto step = [&](int k, bf16x8 (&ca)[MWB], bf16x8 (&cb)[NBW], bf16x8 (&na)[MWB],
+                            bf16x8 (&nb)[NBW]) {
+                wait_vm_le<(STAGES - 3) * LPS>();  // stage k+1 has landed
+                lds_barrier();                     // ... for every wave; stage k-1 is free
+                issue(min(k + STAGES - 1, KT - 1), (k + STAGES - 1) % STAGES);
+                if constexpr (C) {
+                    read_frags((k + 1) % STAGES, na, nb);
+                    mfma_frags(ca, cb);
+                }
+            };
 #pragma unroll
-        for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(min(s0, KT - 1), s0);
-        wait_vm_le<(STAGES - 2) * LPS>();
-        lds_barrier();
-        read_frags(0, fa[0], fb[0]);
-        int k = 0;
-        for (; k < KT - 2; k += 2) {
+            for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(min(s0, KT - 1), s0);
+            wait_vm_le<(STAGES - 2) * LPS>();
+            lds_barrier();
+            if constexpr (C) read_frags(0, fa[0], fb[0]);
+            int k = 0;
+            for (; k < KT - 2; k += 2) {
+                step(k, fa[0], fb[0], fa[1], fb[1]);
+                step(k + 1, fa[1], fb[1], fa[0], fb[0]);
+            }
             step(k, fa[0], fb[0], fa[1], fb[1]);
-            step(k + 1, fa[1], fb[1], fa[0], fb[0]);
-        }
-        step(k, fa[0], fb[0], fa[1], fb[1]);
-        mfma_frags(fa[1], fb[1]);
+            if constexpr (C) mfma_frags(fa[1], fb[1]);
+        };
+        if (wm * MWB * 16 < tl.rows) run(std::true_type{});
+        else run(std::false_type{});
         wait_vm_le<0>();  // no LDS-DMA write may outlive the workgroup
     }
 
-    // ---- epilogue: lane holds column lane%16 of each 16x16 block, rows 4*(lane/16)+i
+    // ---- epilogue. Lane holds column lane%16 of each 16x16 block, rows 4*(lane/16)+i;
+    // results go through a per-wave LDS patch so that global stores are 16 bytes per lane
+    // along output rows.
     const int col16 = lane % 16;
     const int rq = 4 * (lane / 16);
+    const int rw0 = wm * MWB * 16;  // first tile row of this wave
+    __syncthreads();                // every wave is done with the operand stages
     if constexpr (UP) {
+        // H patch: 16*MWB rows x 8*NBW bf16 columns (the wave's NBW/2 gate/up pairs)
+        constexpr int PW = 8 * NBW;
+        bf16_t* patch = reinterpret_cast<bf16_t*>(lds) + (size_t)wave * (16 * MWB) * PW;
 #pragma unroll
         for (int q = 0; q < NBW / 2; ++q) {
-            const int f = ((tl.n * (BN / 16) + wn * NBW) / 2 + q) * 16 + col16;
             float sg = 1.f, su = 1.f;
             if constexpr (INT8) {
+                const int f = ((tl.n * (BN / 16) + wn * NBW) / 2 + q) * 16 + col16;
                 sg = a.s_gate[(size_t)tl.e * a.F + f];
                 su = a.s_up[(size_t)tl.e * a.F + f];
             }
@@ -288,36 +308,50 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
             for (int mb = 0; mb < MWB; ++mb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = (wm * MWB + mb) * 16 + rq + i;
-                    if (r < tl.rows) {
-                        const float g = acc[mb][2 * q][i] * sg;
-                        const float u = acc[mb][2 * q + 1][i] * su;
-                        const size_t p = (size_t)tl.seg0 + tl.row0 + r;
-                        a.h[p * a.F + f] = f32_to_bf16(silu(g) * u);
-                    }
+                    const float g = acc[mb][2 * q][i] * sg;
+                    const float u = acc[mb][2 * q + 1][i] * su;
+                    patch[(mb * 16 + rq + i) * PW + q * 16 + col16] = f32_to_bf16(silu(g) * u);
                 }
         }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the patch is written
+        const int f0 = ((tl.n * (BN / 16) + wn * NBW) / 2) * 16;
+        constexpr int CPR = PW / 8;  // 16-byte chunks per patch row
+#pragma unroll
+        for (int c = lane; c < 16 * MWB * CPR; c += kWave) {
+            const int r = c / CPR, c8 = (c % CPR) * 8;
+            if (rw0 + r < tl.rows) {
+                const size_t p = (size_t)tl.seg0 + tl.row0 + rw0 + r;
+                *reinterpret_cast<u32x4*>(a.h + p * a.F + f0 + c8) = *reinterpret_cast<const u32x4*>(patch + r * PW + c8);
+            }
+        }
     } else {
+        // output patch: 16*MWB rows x 32 fp32 columns, two 16-column blocks at a time
+        float* patch = reinterpret_cast<float*>(lds) + (size_t)wave * (16 * MWB) * 32;
 #pragma unroll
-        for (int mb = 0; mb < MWB; ++mb)
+        for (int nh = 0; nh < NBW / 2; ++nh) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = (wm * MWB + mb) * 16 + rq + i;
-                if (r < tl.rows) {
-                    const int c = a.sorted_c[tl.seg0 + tl.row0 + r];
-                    const int t = c / a.kt, j = c - t * a.kt;
+            for (int mb = 0; mb < MWB; ++mb)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) patch[(mb * 16 + rq + i) * 32 + j * 16 + col16] = acc[mb][2 * nh + j][i];
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+            const int n0 = tl.n * BN + (wn * NBW + 2 * nh) * 16;
+#pragma unroll
+            for (int c = lane; c < 16 * MWB * 8; c += kWave) {
+                const int r = c / 8, c4 = (c % 8) * 4;
+                if (rw0 + r < tl.rows) {
+                    const int cs = a.sorted_c[tl.seg0 + tl.row0 + rw0 + r];
+                    const int t = cs / a.kt, j = cs - t * a.kt;
                     const float wgt = j < a.k ? a.topk_w[(size_t)t * a.k + j] : a.gs[t];
-                    // partial sum `split` of slot c: row c*S + split of the combine buffer
-                    float* orow = a.ow + ((size_t)c * S + split) * a.d;
-#pragma unroll
-                    for (int nb = 0; nb < NBW; ++nb) {
-                        const int n = tl.n * BN + (wn * NBW + nb) * 16 + col16;
-                        float v = acc[mb][nb][i] * wgt;
-                        if constexpr (INT8) v *= a.s_down[(size_t)tl.e * a.d + n];
-                        orow[n] = v;
-                    }
+                    f32x4 v = *reinterpret_cast<const f32x4*>(patch + r * 32 + c4) * wgt;
+                    if constexpr (INT8) v *= *reinterpret_cast<const f32x4*>(a.s_down + (size_t)tl.e * a.d + n0 + c4);
+                    // partial sum `split` of slot cs: row cs*S + split of the combine buffer
+                    *reinterpret_cast<f32x4*>(a.ow + ((size_t)cs * S + split) * a.d + n0 + c4) = v;
                 }
             }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // patch reads done before the next half overwrites it
+        }
     }
 }
 

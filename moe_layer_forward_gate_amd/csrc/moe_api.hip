@@ -63,6 +63,7 @@ struct moe_layer {
     float* ow = nullptr;
     size_t ow_rows = 0;
     // profiling
+    bool profiling = false;
     hipEvent_t ev[6] = {};
     bool ran = false;
 };
@@ -167,8 +168,10 @@ int create_impl(const moe_desc* desc, const moe_weights* w, moe_layer* L) {
     // up to kStreamMaxSplit for batches the streaming kernels serve
     L->ow_rows = std::max(P * 2, std::min(T, (size_t)kStreamMaxT) * L->kt * kStreamMaxSplit);
     if ((rc = dev_alloc(&L->ow, L->ow_rows * dm * 4))) return rc;
-    if (d.profile)
+    if (d.profile) {
         for (hipEvent_t& e : L->ev) HIP_TRY(hipEventCreate(&e));
+        L->profiling = true;
+    }
 
     hipStream_t s = nullptr;
     HIP_TRY(pack_router(w->w_router, d.shared_d_ff > 0 ? w->w_shared_gate : nullptr, d.d_model, L->E, L->wr_t, s));
@@ -262,11 +265,9 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
     const bool i8 = d.expert_dtype == MOE_I8;
     const int k = d.top_k;
     float* gs = r->shared_gate ? r->shared_gate : L->gs;
-    const bool prof = d.profile != 0;
+    const bool prof = L->profiling;
     if (prof) HIP_TRY(hipEventRecord(L->ev[0], s));
 
-    HIP_TRY(launch_gate(x, !f32, L->wr_t, L->wr_planes, L->bias, T, d.d_model, L->E, L->V > 0, k, r->topk_idx, r->topk_w, gs, s));
-    if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
 
     // Launch plan (host side, from T, k and the layer shape only):
     //  - small batches (T <= 64) stream the weights: one row tile per active
@@ -286,11 +287,17 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
         while (ksplit < kStreamMaxSplit && groups * ksplit < 1024 && d.d_ff % (ksplit * 2 * 64) == 0) ksplit *= 2;
     } else {
         bm = (avg_rows >= 768 || T >= 8192) ? 256 : 128;
-        if (T >= 1024 && d.d_ff % (2 * 64) == 0) ksplit = 2;
+        // split the down projection's K in two when its tiles alone fill the GPU less than
+        // ~8 workgroups per CU and K is long enough for both halves to stay efficient
+        const int est_tiles = (T * L->kt + bm - 1) / bm + std::min(L->Et, T * L->kt);
+        if (est_tiles * (d.d_model / 256) < 2048 && d.d_ff >= 4096 && d.d_ff % (2 * 64) == 0) ksplit = 2;
     }
     if ((size_t)T * L->kt * ksplit > L->ow_rows) ksplit = 1;  // never past the combine buffer
     ScatterOut so{L->counts, L->offsets, L->tile_start, L->sorted_c, r->expert_counts, r->expert_offsets,
                   r->sorted_assign};
+    HIP_TRY(launch_gate(x, !f32, L->wr_t, L->wr_planes, L->bias, T, d.d_model, L->E, L->V > 0, k, r->topk_idx,
+                        r->topk_w, gs, s));
+    if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
     HIP_TRY(launch_scatter(r->topk_idx, T, L->E, k, L->V, bm, so, s));
     if (prof) HIP_TRY(hipEventRecord(L->ev[2], s));
 
@@ -328,11 +335,20 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
     return MOE_OK;
 }
 
+int moe_set_profiling(moe_layer* L, int enable) {
+    g_err[0] = 0;
+    if (!L) return fail(MOE_EINVAL, "layer is NULL");
+    if (enable != 0 && enable != 1) return fail(MOE_EINVAL, "enable must be 0 or 1");
+    if (enable && !L->ev[0])
+        for (hipEvent_t& e : L->ev) HIP_TRY(hipEventCreate(&e));
+    L->profiling = enable != 0;
+    return MOE_OK;
+}
+
 int moe_stage_times(moe_layer* L, float ms[5]) {
     g_err[0] = 0;
     if (!L || !ms) return fail(MOE_EINVAL, "layer and ms are required");
-    if (!L->desc.profile) return fail(MOE_EINVAL, "layer was created with profile = 0");
-    if (!L->ran) return fail(MOE_EINVAL, "no profiled forward has run");
+    if (!L->ran) return fail(MOE_EINVAL, "no forward has run with profiling on");
     HIP_TRY(hipEventSynchronize(L->ev[5]));
     for (int i = 0; i < 5; ++i) HIP_TRY(hipEventElapsedTime(&ms[i], L->ev[i], L->ev[i + 1]));
     return MOE_OK;

@@ -1,131 +1,15 @@
-// Scatter: group the T*k routed assignments by expert.
-//
-// [0539edu §2.2] Scatter stage; [hotelren §2.3] dispatch_kernel sends each token
-// to its k experts' input buffers; [mhpq §2.1] tokens of one expert form one
-// contiguous batch for a single GEMM; [pptc §3.3] expert_offsets is a prefix sum.
-//
-// One workgroup of 16 waves. Assignment a = t*k + j. Wave w owns the contiguous
-// range of assignments [w*chunk, (w+1)*chunk):
-//   1. per-wave expert histograms (LDS atomics; counts do not depend on order);
-//   2. per-expert exclusive scan over waves, then over experts -> offsets;
-//   3. each wave walks its range 64 assignments at a time; lanes holding the same
-//      expert are found with 7 ballots over the expert-id bits, the rank of a lane
-//      among them is a popcount of the lower lanes, and the group's lowest lane
-//      advances the wave's running cursor for that expert.
-// The result is the unique stable order (ascending a within each expert); no
-// global atomics are used, so it is the same on every run.
-//
-// Shared virtual experts (the shared FFN split into V slices of d_ff columns)
-// are appended as experts E..E+V-1, each holding every token in order.
-#include "common.h"
+// Scatter kernel: one workgroup of 16 waves runs scatter_block (scatter.h).
+#include "scatter.h"
 
 namespace moe {
 namespace {
 
 constexpr int kScatterWaves = 16;
-constexpr int kMaxEt = kMaxExperts + kMaxVirtual;  // <= 191: the scan covers 192 entries
-
-// exclusive scan of v[0..n) (n <= 191) by one wave; writes out[0..n], out[n] = total
-__device__ void wave_exclusive_scan(const int* v, int n, int* out) {
-    const int lane = threadIdx.x % kWave;
-    int a[3];
-    int s = 0;
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-        int e = lane * 3 + i;
-        a[i] = e < n ? v[e] : 0;
-        s += a[i];
-    }
-    int incl = s;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        int o = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += o;
-    }
-    int run = incl - s;
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-        int e = lane * 3 + i;
-        if (e <= n) out[e] = run;
-        run += a[i];
-    }
-}
 
 __global__ __launch_bounds__(1024) void scatter_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
                                                       int V, int bm, ScatterOut o) {
-    __shared__ int hist[kScatterWaves * kMaxExperts];  // per-wave counts, then cursors
-    __shared__ int cnt[kMaxEt];
-    __shared__ int offs[kMaxEt + 1];
-    __shared__ int tiles[kMaxEt];
-    __shared__ int tstart[kMaxEt + 1];
-
-    const int tid = threadIdx.x;
-    const int wave = tid / kWave, lane = tid % kWave;
-    const int N = T * k;
-    const int kt = k + V;
-    const int Et = E + V;
-    const int chunk = (N + kScatterWaves - 1) / kScatterWaves;
-    const int a0 = min(N, wave * chunk), a1 = min(N, a0 + chunk);
-
-    for (int i = tid; i < kScatterWaves * E; i += blockDim.x) hist[i] = 0;
-    __syncthreads();
-    for (int a = a0 + lane; a < a1; a += kWave) atomicAdd(&hist[wave * E + idx[a]], 1);
-    __syncthreads();
-    if (tid < E) {
-        int c = 0;
-        for (int w = 0; w < kScatterWaves; ++w) {
-            int h = hist[w * E + tid];
-            hist[w * E + tid] = c;  // assignments of this expert in earlier waves
-            c += h;
-        }
-        cnt[tid] = c;
-    } else if (tid < Et) {
-        cnt[tid] = T;
-    }
-    __syncthreads();
-    if (wave == 0) wave_exclusive_scan(cnt, Et, offs);
-    if (wave == 1) {
-        for (int e = lane; e < Et; e += kWave) tiles[e] = (cnt[e] + bm - 1) / bm;
-    }
-    __syncthreads();
-    if (wave == 1) wave_exclusive_scan(tiles, Et, tstart);
-    for (int i = tid; i < kScatterWaves * E; i += blockDim.x) hist[i] += offs[i % E];
-    __syncthreads();
-
-    // stable ranks
-    const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (kWave - lane));
-    for (int base = a0; base < a1; base += kWave) {
-        const int a = base + lane;
-        const bool valid = a < a1;
-        const int e = valid ? idx[a] : 0;
-        uint64_t same = __ballot(valid);
-#pragma unroll
-        for (int b = 0; b < 7; ++b) {
-            const bool bit = (e >> b) & 1;
-            const uint64_t bb = __ballot(valid && bit);
-            same &= bit ? bb : ~bb;
-        }
-        if (valid) {
-            const int rank = __popcll(same & lt_mask);
-            const int pos = hist[wave * E + e] + rank;
-            const int t = a / k, j = a - t * k;
-            o.sorted_c[pos] = t * kt + j;
-            if (o.user_sorted) o.user_sorted[pos] = a;
-            if (rank == 0) hist[wave * E + e] += __popcll(same);
-        }
-    }
-    // shared virtual experts: every token, in order
-    for (int i = tid; i < V * T; i += blockDim.x) {
-        const int v = i / T, t = i - v * T;
-        o.sorted_c[N + i] = t * kt + k + v;
-    }
-    for (int e = tid; e <= Et; e += blockDim.x) {
-        if (e < Et) o.counts[e] = cnt[e];
-        o.offsets[e] = offs[e];
-        o.tile_start[e] = tstart[e];
-        if (e < E && o.user_counts) o.user_counts[e] = cnt[e];
-        if (e <= E && o.user_offsets) o.user_offsets[e] = offs[e];
-    }
+    __shared__ ScatterSmem<kScatterWaves> sm;
+    scatter_block<kScatterWaves>(idx, T, E, k, V, bm, o, sm);
 }
 
 }  // namespace

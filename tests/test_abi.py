@@ -102,8 +102,9 @@ def test_forward_rejects_before_gpu():
     assert "layer" in moe.moe_last_error()
 
 
-def test_stage_times_and_destroy_null():
+def test_stage_times_profiling_and_destroy_null():
     L = moe.lib()
     ms = (ctypes.c_float * 5)()
     assert L.moe_stage_times(None, ms) == moe.MOE_EINVAL
+    assert L.moe_set_profiling(None, 1) == moe.MOE_EINVAL
     L.moe_destroy(None)  # NULL-safe

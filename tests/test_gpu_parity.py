@@ -42,6 +42,13 @@ def test_mixtral_shape_reduced_bf16():
     _run(cfg, [1, 8, 64, 300, 1024, 3072])
 
 
+def test_down_ksplit_reduced_bf16():
+    # d_ff >= 4096 and few row tiles: the down projection's K is split in two (partial rows
+    # added by the Gather pass)
+    cfg = synth.get_config("mixtral_bf16", d_model=256, d_ff=4096)
+    _run(cfg, [1024, 2000])
+
+
 def test_shared_expert_reduced_bf16():
     cfg = synth.get_config("shared_fine_bf16", d_model=512, d_ff=256, shared_d_ff=2048)
     _run(cfg, [16, 200, 1100])
@@ -62,12 +69,13 @@ def test_deterministic_and_zero_tokens():
     cfg = synth.get_config("shared_fine_bf16", d_model=256, d_ff=128, shared_d_ff=512)
     L = synth.make_layer(cfg)
     lay = gpu_layer(L, 300)
-    x = synth.make_tokens(cfg, 300).cuda()
-    a = lay.forward(x, scatter=True)
-    b = lay.forward(x, scatter=True)
-    torch.cuda.synchronize()
-    for f in ("y", "topk_idx", "topk_w", "expert_counts", "expert_offsets", "sorted_assign", "shared_gate"):
-        assert torch.equal(getattr(a, f), getattr(b, f)), f
+    for T in (300, 16):  # separate launches, and the fused small-batch path (arrival counters)
+        x = synth.make_tokens(cfg, T).cuda()
+        a = lay.forward(x, scatter=True)
+        b = lay.forward(x, scatter=True)
+        torch.cuda.synchronize()
+        for f in ("y", "topk_idx", "topk_w", "expert_counts", "expert_offsets", "sorted_assign", "shared_gate"):
+            assert torch.equal(getattr(a, f), getattr(b, f)), (T, f)
     # T = 0 enqueues nothing and leaves the outputs alone
     out = lay.outputs(4, scatter=True)
     out.y.fill_(7)
