@@ -72,10 +72,13 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="tokens of the batch the oracle runs on (0: the whole batch)")
+    ap.add_argument("--cpu-min-seconds", type=float, default=10.0,
+                    help="repeat the oracle's pass over the sample until this much time has passed")
     ap.add_argument("--peaks", action="store_true",
-                    help="only measure achievable peaks with torch/hipBLASLt: a large read-only "
-                         "reduction (HBM) and bf16 GEMMs of the per-expert shape (MFMA)")
+                    help="only measure achievable rates: streaming HBM read and bf16 MFMA issue "
+                         "microbenchmarks, and hipBLASLt bf16 GEMMs of the expert shapes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of 1 GiB (for HBM counter scaling)")
     return ap.parse_args()
@@ -203,39 +206,43 @@ def summarize(cfg, res):
         active_experts=layer["active"], roofline=rf)
 
 
-def cpu_baseline(cfg, layer_cpu, x_cpu, n_tok):
-    """The oracle as it stands, on the first n_tok tokens of the same batch."""
+def cpu_baseline(cfg, layer_cpu, x_cpu, n_tok, min_s):
+    """The oracle as it stands, on the first n_tok tokens of the same batch, repeated (at most
+    4 passes) until min_s seconds have passed."""
     import numpy as np
     import oracle
     from harness import oracle_layer
     from threadpoolctl import threadpool_info
     olay = oracle_layer(layer_cpu)
     xs = x_cpu[:n_tok].float().numpy()
+    passes = 0
     t0 = time.perf_counter()
-    oracle.moe_forward(xs, olay)
-    dt = time.perf_counter() - t0
+    while True:
+        oracle.moe_forward(xs, olay)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_s or passes == 4:
+            break
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    return dict(value=n_tok / dt, unit="tokens/s", cores=int(threads), kind="oracle",
-                sample=f"{n_tok} tokens of the T={x_cpu.shape[0]} batch, whole layer forward in fp64 "
-                       f"(gate, scatter, {cfg.n_experts} experts, combine), {dt:.1f} s")
+    return dict(value=passes * n_tok / dt, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"{passes} pass(es) over {n_tok} tokens of the T={x_cpu.shape[0]} batch, whole layer "
+                       f"forward in fp64 (gate, scatter, {cfg.n_experts} experts, combine), {dt:.1f} s")
 
 
 def measure_peaks(torch):
-    """Achievable rates on this GPU with library kernels (context for the roofline fractions)."""
+    """Achievable rates on this GPU: libmoe_peaks microbenchmarks (streaming HBM read, bf16
+    MFMA issue from registers) and, for comparison, hipBLASLt bf16 GEMMs of the expert shapes."""
+    import ctypes
     out = {}
-    a = torch.empty(1 << 31, dtype=torch.bfloat16, device="cuda").normal_()  # 4 GiB
-    for _ in range(2):
-        a.sum(dtype=torch.float32)
-    torch.cuda.synchronize()
+    P = ctypes.CDLL(os.path.join(ROOT, "moe_layer_forward_gate_amd", "libmoe_peaks.so"))
+    P.moe_peak_read_gbps.restype = ctypes.c_double
+    P.moe_peak_read_gbps.argtypes = [ctypes.c_size_t, ctypes.c_int, ctypes.c_int]
+    P.moe_peak_mfma_tflops.restype = ctypes.c_double
+    P.moe_peak_mfma_tflops.argtypes = [ctypes.c_int, ctypes.c_int]
+    out["read_stream_GBps"] = {w: P.moe_peak_read_gbps(4 << 30, w, 5) for w in (2048, 4096, 8192)}
+    out["mfma_bf16_TFLOPs"] = {w: P.moe_peak_mfma_tflops(w, 20000) for w in (256, 512)}
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev[0].record()
     n = 10
-    for _ in range(n):
-        a.sum(dtype=torch.float32)
-    ev[1].record()
-    torch.cuda.synchronize()
-    out["read_GBps"] = a.numel() * 2 * n / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
-    del a
     for M, K, N in ((8192, 8192, 8192), (1024, 4096, 28672), (1024, 14336, 4096)):
         A = torch.randn(M, K, dtype=torch.bfloat16, device="cuda")
         B = torch.randn(K, N, dtype=torch.bfloat16, device="cuda")
@@ -247,7 +254,7 @@ def measure_peaks(torch):
             A @ B
         ev[1].record()
         torch.cuda.synchronize()
-        out[f"gemm_{M}x{K}x{N}_TFLOPs"] = 2.0 * M * N * K * n / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e12
+        out[f"hipblaslt_gemm_{M}x{K}x{N}_TFLOPs"] = 2.0 * M * N * K * n / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e12
     return out
 
 
@@ -295,7 +302,8 @@ def main():
             print(f"[bench] sweep {json.dumps(s)}", file=sys.stderr, flush=True)
     cpu = None
     if want_cpu:
-        cpu = cpu_baseline(cfg, layer0, x0, min(args.cpu_sample_tokens, T))
+        n_tok = T if args.cpu_sample_tokens <= 0 else min(args.cpu_sample_tokens, T)
+        cpu = cpu_baseline(cfg, layer0, x0, n_tok, args.cpu_min_seconds)
         print(f"[bench] cpu {json.dumps(cpu)}", file=sys.stderr, flush=True)
     line = {
         "metric": "MoE-layer tokens/s; decode HBM TB/s and prefill MFMA TFLOP/s vs roofline",

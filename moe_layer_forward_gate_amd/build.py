@@ -18,6 +18,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmoe.so")
+PEAKS_SRC = os.path.join(PKG, "peaks", "peaks.hip")
+PEAKS_OUT = os.path.join(PKG, "libmoe_peaks.so")
 BUILD = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -50,8 +52,14 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     shutil.move(tmp, OUT)
+    # the peak-rate microbenchmarks used by bench.py --peaks (a separate library)
+    tmp = PEAKS_OUT + ".tmp"
+    r = subprocess.run([HIPCC, *FLAGS, "-shared", PEAKS_SRC, "-o", tmp], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PEAKS_SRC}:\n{r.stderr}")
+    shutil.move(tmp, PEAKS_OUT)
     if verbose:
-        print(f"built {OUT} from {len(srcs)} sources")
+        print(f"built {OUT} from {len(srcs)} sources, and {PEAKS_OUT}")
     return OUT
 
 
