@@ -60,9 +60,13 @@ struct GemmArgs {
     int max_tiles;              // bound on sum_e ceil(n_e / bm)
     int bm;                     // row tile height: 256 or 128 (must match the scatter's tile list)
     int ksplit;                 // down projection: K split into ksplit partial sums (ow rows c*ksplit + s)
-    // up: A = x rows gathered by token; down: A = H rows
+    // Streaming kernels: A = x rows gathered by token (up), H rows [P][F] (down).
+    // Tiled kernels: A in fragment order over padded rows (tile g owns padded rows
+    // [g*bm, (g+1)*bm)): xp = the gathered tokens [R/16][d/32][64][8] written by
+    // launch_pack_a, h = H as [R/16][F/32][64][8] written by the up kernel.
     const bf16_t* x;            // [T][d]
-    bf16_t* h;                  // [P][F]
+    bf16_t* xp;                 // tiled up operand (see above)
+    bf16_t* h;                  // [P][F] or packed [R/16][F/32][64][8]
     const void* wgu;            // packed gate/up
     const void* wdn;            // packed down
     const float* s_gate;        // [E][F] (int8)
@@ -75,6 +79,11 @@ struct GemmArgs {
 };
 hipError_t launch_expert_up_bf16(const GemmArgs& a, bool int8, hipStream_t s);
 hipError_t launch_expert_down_bf16(const GemmArgs& a, bool int8, hipStream_t s);
+// Token rows into the tiled up operand a.xp (padded rows past an expert's last row are
+// zero; shared virtual experts after the first are not written, the up kernel reads the
+// first one's rows for them). Reads the scatter's tile list on the device; writes
+// max_tiles*bm rows at most.
+hipError_t launch_pack_a(const GemmArgs& a, hipStream_t s);
 // Small-batch variants (a.bm = 16, 32 or 64 >= T, so each active expert is one row tile).
 hipError_t launch_expert_up_stream(const GemmArgs& a, bool int8, hipStream_t s);
 hipError_t launch_expert_down_stream(const GemmArgs& a, bool int8, hipStream_t s);
@@ -120,9 +129,10 @@ constexpr int kBMf32 = 64;
 constexpr int kMaxVirtual = 63;  // shared-expert slices (scatter scan limit)
 
 // One output tile of a grouped expert GEMM: expert e, rows [seg0 + row0, seg0 +
-// row0 + rows) of the by-expert order, column tile n.
+// row0 + rows) of the by-expert order, column tile n; g = tile_start[e] + row0/bm is
+// the tile's index in the padded row space of the tiled operands.
 struct Tile {
-    int e, row0, rows, seg0, n;
+    int e, row0, rows, seg0, n, g;
 };
 
 // Map this workgroup to a tile. Tiles are ordered expert by expert; inside an
@@ -161,6 +171,7 @@ __device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ ts, cons
     if (n >= NT) return false;
     tl.e = e;
     tl.n = n;
+    tl.g = t0 + m;
     tl.row0 = m * bm;
     tl.seg0 = offs[e];
     tl.rows = min(bm, offs[e + 1] - tl.seg0 - tl.row0);
@@ -198,6 +209,7 @@ __device__ __forceinline__ bool decode_tile_split(const int32_t* __restrict__ ts
     if (n >= NT) return false;
     tl.e = e;
     tl.n = n;
+    tl.g = t0 + m;
     tl.row0 = m * bm;
     tl.seg0 = offs[e];
     tl.rows = min(bm, offs[e + 1] - tl.seg0 - tl.row0);

@@ -18,10 +18,13 @@
 // holding row l%16, K 8*(l/16)..+7, so every fragment read is a conflict-free
 // 16-byte-per-lane ds_read. Global -> LDS traffic uses the gfx950 LDS-DMA load
 // (global_load_lds_dwordx4): each wave instruction fills one whole 1 KB block,
-// lane l fetching its own 16 bytes, which lets the A operand be gathered
-// straight from the token rows of x (up) with no staging registers. Expert
-// weights come from create-time packing already in fragment order (bf16:
-// [Et][N/16][K/32][64][8]), so a weight block is one contiguous 1 KB read.
+// lane l fetching its own 16 bytes. Both operands are stored in that fragment
+// order in HBM, so every block is one contiguous 1 KB read (sixteen separate
+// 64-byte row pieces per block, as a gather from token rows would need, keep the
+// vector memory pipe busy for about twice as long per byte): the A operand of the
+// up projection is packed by launch_pack_a after the scatter, the up kernel's
+// epilogue writes H in the down projection's A order, and expert weights are
+// packed at create time (bf16: [Et][N/16][K/32][64][8]).
 // int8 weights ([E][N/16][K/64][64][16], bytes 0-7 the first 32-K half) go
 // through registers instead, widened to bf16 on the way to LDS (exact: |q| <=
 // 127 fits bf16's significand); their per-column scale multiplies the fp32
@@ -127,16 +130,20 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
     const int wave = tid / kWave, lane = tid % kWave;
     const int wm = wave / WN, wn = wave % WN;
 
-    // ---- A: wave loads stage blocks b = wave + 8*i: m-block b / KH, K half b % KH
-    const bf16_t* a_row[AW];
+    // ---- A: wave loads stage blocks b = wave + 8*i: m-block b / KH, K half b % KH. The
+    // operand is in fragment order over padded rows (tile g owns row blocks g*BM/16 ..),
+    // so every block is one contiguous 1 KB; rows past the expert's last row are zeros.
+    // Shared virtual experts past the first read the first one's token rows (the same
+    // tokens in the same order).
+    const int KA = K / 32;  // 32-K blocks per row block
+    const int e0 = a.Et - a.kt + a.k;  // first shared virtual expert (== Et without one)
+    const int ga = (UP && tl.e > e0) ? tl.g - a.tile_start[tl.e] + a.tile_start[e0] : tl.g;
+    const bf16_t* a_blk[AW];
 #pragma unroll
     for (int i = 0; i < AW; ++i) {
         const int b = wave + kWaves * i;
-        const int r = (b / KH) * 16 + lane % 16;
-        const int rr = r < tl.rows ? r : 0;  // rows past the segment load row 0 (their outputs are dropped)
-        const int p = tl.seg0 + tl.row0 + rr;
-        const bf16_t* base = UP ? a.x + (size_t)(a.sorted_c[p] / a.kt) * a.d : a.h + (size_t)p * a.F;
-        a_row[i] = base + kbase + (b % KH) * 32 + 8 * (lane / 16);
+        const size_t mbg = (size_t)ga * (BM / 16) + b / KH;
+        a_blk[i] = (UP ? a.xp : a.h) + ((mbg * KA + kbase / 32 + b % KH) * 64 + lane) * 8;
     }
     // ---- B
     const int KS = K / 32;
@@ -154,9 +161,8 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
 
     auto issue = [&](int kt, int stage) {
         u32x4* st = lds + (size_t)stage * STAGE * 64;
-        const int k0 = kt * BK;
 #pragma unroll
-        for (int i = 0; i < AW; ++i) dma16(a_row[i] + k0, st + (wave + kWaves * i) * 64);
+        for (int i = 0; i < AW; ++i) dma16(a_blk[i] + (size_t)kt * KH * 512, st + (wave + kWaves * i) * 64);
         if constexpr (INT8) {
 #pragma unroll
             for (int i = 0; i < NQ8; ++i) {
@@ -314,16 +320,22 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
                 }
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the patch is written
-        const int f0 = ((tl.n * (BN / 16) + wn * NBW) / 2) * 16;
-        constexpr int CPR = PW / 8;  // 16-byte chunks per patch row
+        // H in the down kernel's fragment order: block (row block, 32-column block), lane l
+        // holding row l%16, columns 8*(l/16)..+7. Every row of the tile is written (rows past
+        // the expert's last row come out zero from their zero inputs), so the down kernel
+        // never reads memory this forward did not write.
+        const int fb0 = ((tl.n * (BN / 16) + wn * NBW) / 2) * 16 / 32;
+        constexpr int FB = PW / 32;  // 32-column blocks per patch
+        static_assert(PW % 32 == 0, "patch width");
 #pragma unroll
-        for (int c = lane; c < 16 * MWB * CPR; c += kWave) {
-            const int r = c / CPR, c8 = (c % CPR) * 8;
-            if (rw0 + r < tl.rows) {
-                const size_t p = (size_t)tl.seg0 + tl.row0 + rw0 + r;
-                *reinterpret_cast<u32x4*>(a.h + p * a.F + f0 + c8) = *reinterpret_cast<const u32x4*>(patch + r * PW + c8);
+        for (int mb = 0; mb < MWB; ++mb)
+#pragma unroll
+            for (int fb = 0; fb < FB; ++fb) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(patch + (mb * 16 + lane % 16) * PW + fb * 32 +
+                                                                8 * (lane / 16));
+                const size_t blk = ((size_t)tl.g * (BM / 16) + wm * MWB + mb) * (a.F / 32) + fb0 + fb;
+                *reinterpret_cast<u32x4*>(a.h + (blk * 64 + lane) * 8) = v;
             }
-        }
     } else {
         // output patch: 16*MWB rows x 32 fp32 columns, two 16-column blocks at a time
         float* patch = reinterpret_cast<float*>(lds) + (size_t)wave * (16 * MWB) * 32;

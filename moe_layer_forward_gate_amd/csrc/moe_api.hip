@@ -59,6 +59,7 @@ struct moe_layer {
     int32_t* tile_start = nullptr;
     int32_t* sorted_c = nullptr;
     float* gs = nullptr;
+    bf16_t* xp = nullptr;  // tiled up operand (bf16/int8 experts)
     void* h = nullptr;
     float* ow = nullptr;
     size_t ow_rows = 0;
@@ -73,7 +74,7 @@ namespace {
 void release(moe_layer* L) {
     if (!L) return;
     void* bufs[] = {L->wr_t, L->wr_planes, L->bias, L->wgu, L->wdn, L->s_gate, L->s_up, L->s_down, L->counts, L->offsets,
-                    L->tile_start, L->sorted_c, L->gs, L->h, L->ow};
+                    L->tile_start, L->sorted_c, L->gs, L->xp, L->h, L->ow};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
     for (hipEvent_t e : L->ev)
@@ -163,7 +164,10 @@ int create_impl(const moe_desc* desc, const moe_weights* w, moe_layer* L) {
     if ((rc = dev_alloc(&L->tile_start, (Et + 1) * 4))) return rc;
     if ((rc = dev_alloc(&L->sorted_c, P * 4))) return rc;
     if ((rc = dev_alloc(&L->gs, T * 4))) return rc;
-    if ((rc = dev_alloc(&L->h, P * F * (f32 ? 4 : 2)))) return rc;
+    // the tiled GEMMs work on padded rows: at most P + (bm - 1) + Et*bm of them for bm <= 256
+    const size_t R = P + (size_t)256 * (Et + 1);
+    if (!f32 && (rc = dev_alloc(&L->xp, R * dm * 2))) return rc;
+    if ((rc = dev_alloc(&L->h, (f32 ? P : R) * F * (f32 ? 4 : 2)))) return rc;
     // combine buffer: one row per (token, slot, K split): 2 splits for large batches,
     // up to kStreamMaxSplit for batches the streaming kernels serve
     L->ow_rows = std::max(P * 2, std::min(T, (size_t)kStreamMaxT) * L->kt * kStreamMaxSplit);
@@ -295,15 +299,20 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
     if ((size_t)T * L->kt * ksplit > L->ow_rows) ksplit = 1;  // never past the combine buffer
     ScatterOut so{L->counts, L->offsets, L->tile_start, L->sorted_c, r->expert_counts, r->expert_offsets,
                   r->sorted_assign};
+    // upper bound on sum_e ceil(n_e / bm) over experts with rows
+    const int P = T * L->kt;
+    const int max_tiles = streaming ? std::min(L->Et, P) : (P + bm - 1) / bm + std::min(L->Et, P);
+    const GemmArgs a{L->tile_start, L->offsets, L->sorted_c, L->Et, L->kt, k, max_tiles, bm, ksplit,
+                     (const bf16_t*)x, L->xp, (bf16_t*)L->h, L->wgu, L->wdn, L->s_gate, L->s_up, L->s_down,
+                     r->topk_w, gs, L->ow, d.d_model, d.d_ff};
     HIP_TRY(launch_gate(x, !f32, L->wr_t, L->wr_planes, L->bias, T, d.d_model, L->E, L->V > 0, k, r->topk_idx,
                         r->topk_w, gs, s));
     if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
     HIP_TRY(launch_scatter(r->topk_idx, T, L->E, k, L->V, bm, so, s));
+    // the tiled GEMMs take the token rows already gathered into fragment order
+    if (!f32 && !streaming) HIP_TRY(launch_pack_a(a, s));
     if (prof) HIP_TRY(hipEventRecord(L->ev[2], s));
 
-    // upper bound on sum_e ceil(n_e / bm) over experts with rows
-    const int P = T * L->kt;
-    const int max_tiles = streaming ? std::min(L->Et, P) : (P + bm - 1) / bm + std::min(L->Et, P);
     if (f32) {
         GemmF32Args a{L->tile_start, L->offsets, L->sorted_c, L->Et, L->kt, k, max_tiles,
                       (const float*)x, (float*)L->h, (const float*)L->wgu,
@@ -313,9 +322,6 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
         if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));
         HIP_TRY(launch_expert_down_f32(a, s));
     } else {
-        GemmArgs a{L->tile_start, L->offsets, L->sorted_c, L->Et, L->kt, k, max_tiles, bm, ksplit,
-                   (const bf16_t*)x, (bf16_t*)L->h, L->wgu, L->wdn, L->s_gate, L->s_up, L->s_down,
-                   r->topk_w, gs, L->ow, d.d_model, d.d_ff};
         if (streaming) {
             HIP_TRY(launch_expert_up_stream(a, i8, s));
             if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));
