@@ -50,6 +50,12 @@ struct ScatterOut {
 };
 hipError_t launch_scatter(const int32_t* idx, int T, int E, int k, int V, int bm, const ScatterOut& o,
                           hipStream_t s);
+// Gate then Scatter in a single workgroup, for tiny batches: up to 4 tokens,
+// d_model <= 8192, at most 16 router columns (experts + shared gate).
+bool gate_scatter_small_fits(int T, int d, int E, bool has_shared, bool x_bf16);
+hipError_t launch_gate_scatter_small(const void* x, bool x_bf16, const float* wr_t, const float* bias, int T, int d,
+                                     int E, bool has_shared, int k, int32_t* idx, float* w, float* gs, int V,
+                                     int bm, const ScatterOut& o, hipStream_t s);
 
 // Grouped expert GEMMs on bf16 MFMA (expert weights bf16 or int8 in fragment order).
 struct GemmArgs {
@@ -58,7 +64,7 @@ struct GemmArgs {
     const int32_t* sorted_c;    // [P]
     int Et, kt, k;              // experts incl. virtual, slots per token incl. virtual, routed k
     int max_tiles;              // bound on sum_e ceil(n_e / bm)
-    int bm;                     // row tile height: 256 or 128 (must match the scatter's tile list)
+    int bm;                     // row tile height: 256, or 128 for int8 (must match the scatter's tile list)
     int ksplit;                 // down projection: K split into ksplit partial sums (ow rows c*ksplit + s)
     // Streaming kernels: A = x rows gathered by token (up), H rows [P][F] (down).
     // Tiled kernels: A in fragment order over padded rows (tile g owns padded rows

@@ -12,8 +12,10 @@
 //       the Gather stage is applied in this epilogue ([pptc §2.1] fused
 //       aggregation).
 //
-// Workgroup tile BM x 256 (BM = 256 or 128), K step 64, 8 waves; each wave owns
-// a 64 x (16*NBW) block of v_mfma_f32_16x16x32_bf16 accumulators. Operands are
+// Workgroup tile BM x 256 (BM = 256; 128 for int8 experts holding few rows), 8
+// waves; each wave owns a 64 x (16*NBW) block of v_mfma_f32_16x16x32_bf16
+// accumulators. bf16 weights: K step 32, four LDS stages, three K steps of loads in
+// flight, one barrier per step; int8 weights: K step 64, two stages. Operands are
 // staged in LDS in MFMA fragment order: one 1 KB block = 16 rows x 32 K, lane l
 // holding row l%16, K 8*(l/16)..+7, so every fragment read is a conflict-free
 // 16-byte-per-lane ds_read. Global -> LDS traffic uses the gfx950 LDS-DMA load
@@ -28,8 +30,8 @@
 // int8 weights ([E][N/16][K/64][64][16], bytes 0-7 the first 32-K half) go
 // through registers instead, widened to bf16 on the way to LDS (exact: |q| <=
 // 127 fits bf16's significand); their per-column scale multiplies the fp32
-// accumulator in the epilogue. Two LDS stages: the loads of K step kt+1 are in
-// flight while step kt is multiplied; one barrier per K step.
+// accumulator in the epilogue; the loads of K step kt+1 are in flight while step
+// kt is multiplied.
 // Up-projection columns are packed gate/up interleaved per 16 columns, so each
 // lane holds the gate and up accumulators of the same (row, f) and SiLU * up
 // runs in registers.
@@ -396,7 +398,7 @@ hipError_t launch_dispatch(const GemmArgs& a, bool int8, hipStream_t s) {
     // 8 waves (two per SIMD): the 4-wave layout with 128 x 128 wave tiles reads less LDS per
     // MFMA but leaves one wave per SIMD to hide every latency, and measured 25% slower
     if (a.bm == 256) return int8 ? launch<256, 8, true, UP>(a, s) : launch<256, kBf16Waves, false, UP>(a, s);
-    if (a.bm == 128) return int8 ? launch<128, 8, true, UP>(a, s) : launch<128, kBf16Waves, false, UP>(a, s);
+    if (a.bm == 128 && int8) return launch<128, 8, true, UP>(a, s);
     return hipErrorInvalidValue;
 }
 

@@ -20,6 +20,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "scatter.h"
 
 namespace moe {
 namespace {
@@ -53,7 +54,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 // One wave: top-k of logits[0..E) (bias already added), weights, shared gate.
 // `logits` may live in LDS; E <= 128, k <= 64.
 __device__ void wave_topk_write(const float* logits, int E, int k, bool has_shared, int t, int32_t* idx,
-                                float* w, float* gs) {
+                                float* w, float* gs, int32_t* ids_copy = nullptr) {
     const int lane = threadIdx.x % kWave;
     uint64_t k0 = lane < E ? topk_key(logits[lane], lane) : 0ull;
     uint64_t k1 = lane + kWave < E ? topk_key(logits[lane + kWave], lane + kWave) : 0ull;
@@ -72,6 +73,7 @@ __device__ void wave_topk_write(const float* logits, int E, int k, bool has_shar
     if (lane < k) {
         idx[(size_t)t * k + lane] = my_e;
         w[(size_t)t * k + lane] = ex / sum;
+        if (ids_copy) ids_copy[t * k + lane] = my_e;
     }
     if (has_shared && lane == 0) {
         float z = logits[E];
@@ -358,6 +360,91 @@ __global__ __launch_bounds__(256) void gate_tiled(const XT* __restrict__ x, cons
     }
 }
 
+// ---------------------------------------------------------------- tiny batches, fused
+// Gate and Scatter in one workgroup of 16 waves for up to four tokens: thread tid owns
+// the K chunk [8*tid, 8*tid + 8) (d <= 8192); the chunks of every token and of eight
+// router columns are loaded at once (a decode step is a chain of memory latencies, so
+// one round trip instead of two or three), each wave folds its 64 partial dots with a
+// butterfly, the 16 wave partials are added in LDS in a fixed order, one wave per token
+// takes the top-k, and the same workgroup then runs the scatter ([0539edu §2.2], the
+// two stages back to back with no launch between them).
+template <typename XT>
+struct SmallGate {
+    static constexpr int T = 4;  // tokens (register budget at 1024 threads)
+    static constexpr int EC = 16;                      // router columns (experts + shared gate)
+    static constexpr int EG = 8;                       // columns per load round
+};
+
+template <typename XT>
+__global__ __launch_bounds__(1024) void gate_scatter_small(const XT* __restrict__ x, const float* __restrict__ wr_t,
+                                                           const float* __restrict__ bias, int T, int d, int E,
+                                                           int Ec, int k, bool has_shared, int32_t* __restrict__ idx,
+                                                           float* __restrict__ w, float* __restrict__ gs, int V,
+                                                           int bm, ScatterOut o) {
+    constexpr int MT = SmallGate<XT>::T, EC = SmallGate<XT>::EC, EG = SmallGate<XT>::EG;
+    constexpr int NW = 16;
+    __shared__ float part[NW][MT * EC];
+    __shared__ float logits[MT][EC + 1];
+    __shared__ ScatterSmem<NW> sm;
+    __shared__ int32_t ids[MT * kMaxTopK];  // the top-k ids again, for the scatter to read from LDS
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const bool has = tid * 8 < d;
+    const int kc = has ? tid * 8 : 0;
+    constexpr int XQ = sizeof(XT) / 2;  // 16-byte chunks per 8 elements
+    u32x4 xq[MT][XQ];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(x + (size_t)(t < T ? t : 0) * d + kc);
+#pragma unroll
+        for (int q = 0; q < XQ; ++q) xq[t][q] = p[q];
+    }
+    for (int e0 = 0; e0 < Ec; e0 += EG) {
+        u32x4 wq[EG][2];
+#pragma unroll
+        for (int g = 0; g < EG; ++g) {
+            const u32x4* p = reinterpret_cast<const u32x4*>(wr_t + (size_t)(e0 + g < Ec ? e0 + g : 0) * d + kc);
+            wq[g][0] = p[0];
+            wq[g][1] = p[1];
+        }
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            if (t < T) {
+#pragma unroll
+                for (int g = 0; g < EG; ++g) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int v = 0; v < 8; ++v) {
+                        float f;
+                        if constexpr (XQ == 1) {
+                            const uint32_t u = xq[t][0][v / 2];
+                            f = __uint_as_float((v & 1) ? (u & 0xFFFF0000u) : (u << 16));
+                        } else {
+                            f = __uint_as_float(xq[t][v / 4][v % 4]);
+                        }
+                        acc = fmaf(f, __uint_as_float(wq[g][v / 4][v % 4]), acc);
+                    }
+                    const float sum = wave_sum(has ? acc : 0.0f);
+                    if (lane == 0 && e0 + g < Ec) part[wave][t * EC + e0 + g] = sum;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < T * EC) {
+        const int t = tid / EC, e = tid - (tid / EC) * EC;
+        if (e < Ec) {
+            float v = 0.0f;
+#pragma unroll
+            for (int q = 0; q < NW; ++q) v += part[q][tid];
+            logits[t][e] = v + ((bias && e < E) ? bias[e] : 0.0f);
+        }
+    }
+    __syncthreads();
+    if (wave < T) wave_topk_write(logits[wave], E, k, has_shared, wave, idx, w, gs, ids);
+    __syncthreads();
+    scatter_block<NW>(ids, T, E, k, V, bm, o, sm);
+}
+
 template <typename XT>
 hipError_t launch_gate_t(const XT* x, const float* wr_t, const u32x4* planes, const float* bias, int T, int d, int E,
                          bool has_shared, int k, int32_t* idx, float* w, float* gs, hipStream_t s) {
@@ -400,6 +487,25 @@ hipError_t launch_gate_t(const XT* x, const float* wr_t, const u32x4* planes, co
 }
 
 }  // namespace
+
+bool gate_scatter_small_fits(int T, int d, int E, bool has_shared, bool x_bf16) {
+    const int mt = x_bf16 ? SmallGate<bf16_t>::T : SmallGate<float>::T;
+    return T >= 1 && T <= mt && d <= 8 * 1024 && d % 8 == 0 && E + (has_shared ? 1 : 0) <= SmallGate<float>::EC;
+}
+
+hipError_t launch_gate_scatter_small(const void* x, bool x_bf16, const float* wr_t, const float* bias, int T, int d,
+                                     int E, bool has_shared, int k, int32_t* idx, float* w, float* gs, int V,
+                                     int bm, const ScatterOut& o, hipStream_t s) {
+    if (!gate_scatter_small_fits(T, d, E, has_shared, x_bf16) || E + V > kMaxEt) return hipErrorInvalidValue;
+    const int Ec = E + (has_shared ? 1 : 0);
+    if (x_bf16)
+        hipLaunchKernelGGL(gate_scatter_small<bf16_t>, dim3(1), dim3(1024), 0, s, (const bf16_t*)x, wr_t, bias, T, d,
+                           E, Ec, k, has_shared, idx, w, gs, V, bm, o);
+    else
+        hipLaunchKernelGGL(gate_scatter_small<float>, dim3(1), dim3(1024), 0, s, (const float*)x, wr_t, bias, T, d,
+                           E, Ec, k, has_shared, idx, w, gs, V, bm, o);
+    return hipGetLastError();
+}
 
 hipError_t launch_gate(const void* x, bool x_bf16, const float* wr_t, const void* planes, const float* bias, int T,
                        int d, int E, bool has_shared, int k, int32_t* idx, float* w, float* gs, hipStream_t s) {

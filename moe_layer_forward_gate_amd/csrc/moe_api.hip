@@ -290,7 +290,11 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
         const int groups = active * (d.d_model / 128);
         while (ksplit < kStreamMaxSplit && groups * ksplit < 1024 && d.d_ff % (ksplit * 2 * 64) == 0) ksplit *= 2;
     } else {
-        bm = (avg_rows >= 768 || T >= 8192) ? 256 : 128;
+        // 256-row tiles: the 256 x 256 workgroup tile reads the least LDS and L2 per MFMA and
+        // outruns 128-row tiles even when most experts leave their last tile half empty; int8
+        // weights (widened through registers, one K step in flight) keep 128-row tiles while
+        // experts hold few rows, where the kernel is bound by the weight stream
+        bm = (i8 && avg_rows < 768 && T < 8192) ? 128 : 256;
         // split the down projection's K in two when its tiles alone fill the GPU less than
         // ~8 workgroups per CU and K is long enough for both halves to stay efficient
         const int est_tiles = (T * L->kt + bm - 1) / bm + std::min(L->Et, T * L->kt);
@@ -305,10 +309,17 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
     const GemmArgs a{L->tile_start, L->offsets, L->sorted_c, L->Et, L->kt, k, max_tiles, bm, ksplit,
                      (const bf16_t*)x, L->xp, (bf16_t*)L->h, L->wgu, L->wdn, L->s_gate, L->s_up, L->s_down,
                      r->topk_w, gs, L->ow, d.d_model, d.d_ff};
-    HIP_TRY(launch_gate(x, !f32, L->wr_t, L->wr_planes, L->bias, T, d.d_model, L->E, L->V > 0, k, r->topk_idx,
-                        r->topk_w, gs, s));
-    if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
-    HIP_TRY(launch_scatter(r->topk_idx, T, L->E, k, L->V, bm, so, s));
+    if (gate_scatter_small_fits(T, d.d_model, L->E, L->V > 0, !f32)) {
+        // tiny batch: both stages in one workgroup (the scatter stage then times as empty)
+        HIP_TRY(launch_gate_scatter_small(x, !f32, L->wr_t, L->bias, T, d.d_model, L->E, L->V > 0, k, r->topk_idx,
+                                          r->topk_w, gs, L->V, bm, so, s));
+        if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
+    } else {
+        HIP_TRY(launch_gate(x, !f32, L->wr_t, L->wr_planes, L->bias, T, d.d_model, L->E, L->V > 0, k, r->topk_idx,
+                            r->topk_w, gs, s));
+        if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
+        HIP_TRY(launch_scatter(r->topk_idx, T, L->E, k, L->V, bm, so, s));
+    }
     // the tiled GEMMs take the token rows already gathered into fragment order
     if (!f32 && !streaming) HIP_TRY(launch_pack_a(a, s));
     if (prof) HIP_TRY(hipEventRecord(L->ev[2], s));

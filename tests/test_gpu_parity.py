@@ -65,11 +65,20 @@ def test_int8_reduced():
     _run(cfg, [1, 16, 256, 1024, 3072])
 
 
+def test_tiny_batches_single_workgroup_route():
+    # T <= 4 with at most 16 router columns: gate and scatter run in one workgroup
+    _run(synth.get_config("mixtral_bf16", d_model=512, d_ff=1024), [1, 2, 3, 4, 5])
+    _run(synth.get_config("shared_fine_bf16", d_model=256, d_ff=128, n_experts=8, top_k=2, shared_d_ff=512),
+         [1, 3, 4])
+    _run(synth.get_config("tiny_f32"), [1, 4])
+    _run(synth.get_config("int8_mixtral22b", d_model=512, d_ff=1024), [2, 4])
+
+
 def test_deterministic_and_zero_tokens():
     cfg = synth.get_config("shared_fine_bf16", d_model=256, d_ff=128, shared_d_ff=512)
     L = synth.make_layer(cfg)
     lay = gpu_layer(L, 300)
-    for T in (300, 16):  # separate launches, and the fused small-batch path (arrival counters)
+    for T in (300, 16):  # tiled GEMMs, and the streaming kernels
         x = synth.make_tokens(cfg, T).cuda()
         a = lay.forward(x, scatter=True)
         b = lay.forward(x, scatter=True)
