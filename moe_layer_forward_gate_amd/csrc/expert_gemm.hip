@@ -115,7 +115,12 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
 
     const int K = UP ? a.d : a.F;
     const int N = UP ? 2 * a.F : a.d;
-    const int NT = N / BN;
+    // column tiles; the last one is partial when N % 256 == 128 (N is a multiple of 128):
+    // its missing 16-column blocks load the expert's last block and are never stored, and
+    // since they come in whole wave shares (multiples of 8 blocks), a wave is either all
+    // valid or all skipped
+    const int NT = (N + BN - 1) / BN;
+    const int NB16 = N / 16;  // valid 16-column blocks
     const int S = UP ? 1 : a.ksplit;
     Tile tl;
     int split = 0;
@@ -152,10 +157,10 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
     const u32x4* b_src;
     if constexpr (INT8) {
         const int8_t* wb = (const int8_t*)(UP ? a.wgu : a.wdn) + (size_t)tl.e * N * K;
-        b_src = reinterpret_cast<const u32x4*>(wb) + (size_t)(tl.n * (BN / 16)) * (K / 64) * 64 + kbase / 64 * 64;
+        b_src = reinterpret_cast<const u32x4*>(wb) + kbase / 64 * 64;
     } else {
         const bf16_t* wb = (const bf16_t*)(UP ? a.wgu : a.wdn) + (size_t)tl.e * N * K;
-        b_src = reinterpret_cast<const u32x4*>(wb) + (size_t)(tl.n * (BN / 16)) * KS * 64 + kbase / 32 * 64;
+        b_src = reinterpret_cast<const u32x4*>(wb) + kbase / 32 * 64;
     }
     // int8: thread loads lane chunks q = tid + 512*i of the (BN/16) x 1 KB int8 blocks
     constexpr int NQ8 = INT8 ? (BN / 16) * 64 / kThreads : 1;
@@ -169,14 +174,16 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
 #pragma unroll
             for (int i = 0; i < NQ8; ++i) {
                 const int q = tid + kThreads * i;
-                r8[i] = b_src[((size_t)(q / 64) * (K / 64) + kt) * 64 + q % 64];
+                const int nbg = min(tl.n * (BN / 16) + q / 64, NB16 - 1);
+                r8[i] = b_src[((size_t)nbg * (K / 64) + kt) * 64 + q % 64];
             }
         } else {
 #pragma unroll
             for (int j = 0; j < BW; ++j) {
                 const int blk = wave * BW + j;  // stage B block: n-block blk / KH, K half blk % KH
                 const int nb = blk / KH, kh = blk % KH;
-                dma16(b_src + ((size_t)nb * KS + kt * KH + kh) * 64 + lane, st + (ABLK + blk) * 64);
+                const int nbg = min(tl.n * (BN / 16) + nb, NB16 - 1);
+                dma16(b_src + ((size_t)nbg * KS + kt * KH + kh) * 64 + lane, st + (ABLK + blk) * 64);
             }
         }
     };
@@ -300,6 +307,7 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
     const int rq = 4 * (lane / 16);
     const int rw0 = wm * MWB * 16;  // first tile row of this wave
     __syncthreads();                // every wave is done with the operand stages
+    if (tl.n * (BN / 16) + wn * NBW >= NB16) return;  // columns past N (partial last tile): nothing to store
     if constexpr (UP) {
         // H patch: 16*MWB rows x 8*NBW bf16 columns (the wave's NBW/2 gate/up pairs)
         constexpr int PW = 8 * NBW;
@@ -386,7 +394,7 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
     const int S = UP ? 1 : a.ksplit;
     const int Kpart = (UP ? a.d : a.F) / S;
     if (Kpart % 64 != 0 || Kpart < 64) return hipErrorInvalidValue;  // the pipeline takes K steps in pairs
-    const int NTp = (N / BN + GN - 1) / GN * GN;
+    const int NTp = ((N + BN - 1) / BN + GN - 1) / GN * GN;
     // a multiple of 8 workgroups, so every XCD gets ceil(tiles / 8) slots
     dim3 grid((unsigned)(((size_t)a.max_tiles * NTp * S + kXcds - 1) / kXcds * kXcds));
     hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds_bytes, s, a);

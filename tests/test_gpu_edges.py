@@ -1,0 +1,81 @@
+"""GPU parity on edge shapes and degenerate routings, at sizes the oracle evaluates in full.
+
+Covers: k = 1 and k = E, expert counts that are not multiples of 8 or 16 (up to the
+128-expert limit), the smallest supported widths, T at the max_tokens bound and on
+both sides of the streaming / tiled switch, every token routed to one expert, a
+shared expert of one and of sixteen d_ff slices, and int8 output channels whose
+scale is zero.
+"""
+import pytest
+import torch
+
+import synth
+from harness import compare, gpu_layer, oracle_layer
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(cfg, Ts, max_tokens=None, mutate=None):
+    L = synth.make_layer(cfg)
+    if mutate is not None:
+        mutate(L)
+    olay = oracle_layer(L)
+    lay = gpu_layer(L, max_tokens or max(Ts))
+    for T in Ts:
+        print(f"[edge] {cfg.name} d={cfg.d_model} E={cfg.n_experts} F={cfg.d_ff} k={cfg.top_k} "
+              f"Fs={cfg.shared_d_ff} T={T}", flush=True)
+        x = synth.make_tokens(cfg, T).cuda()
+        out = lay.forward(x, scatter=True)
+        torch.cuda.synchronize()
+        compare(cfg, x, olay, out, label=f"{cfg.name} E={cfg.n_experts} k={cfg.top_k} T={T}")
+    lay.close()
+
+
+@pytest.mark.parametrize("k", [1, 8])
+def test_top_k_extremes(k):
+    # k = 1: every weight is exactly 1; k = E = 8: the dense softmax mixture
+    _run(synth.get_config("mixtral_bf16", d_model=256, d_ff=128, top_k=k), [1, 5, 70, 600])
+
+
+@pytest.mark.parametrize("E,k", [(5, 2), (13, 3), (127, 4), (128, 1)])
+def test_odd_expert_counts(E, k):
+    _run(synth.get_config("mixtral_bf16", d_model=128, d_ff=64, n_experts=E, top_k=k), [3, 64, 65, 700])
+
+
+def test_smallest_widths():
+    _run(synth.get_config("mixtral_bf16", d_model=128, d_ff=64), [1, 2, 64, 65, 513])
+    _run(synth.get_config("tiny_f32", d_model=64, d_ff=64), [1, 64, 200])
+    _run(synth.get_config("int8_mixtral22b", d_model=128, d_ff=64), [1, 100])
+
+
+def test_max_tokens_bound():
+    # T == max_tokens on both sides of the streaming / tiled switch (T <= 64 streams)
+    cfg = synth.get_config("mixtral_bf16", d_model=256, d_ff=256)
+    _run(cfg, [64], max_tokens=64)
+    _run(cfg, [65, 300], max_tokens=300)
+
+
+def test_every_token_on_one_expert():
+    # a large bias on expert 3 puts it in slot 0 of every token: one expert holds T rows
+    def bias(L):
+        b = torch.zeros(L.cfg.n_experts, dtype=torch.float32)
+        b[3] = 50.0
+        L.b_router = b
+    _run(synth.get_config("mixtral_bf16", d_model=256, d_ff=128), [1, 64, 1000], mutate=bias)
+
+
+@pytest.mark.parametrize("slices", [1, 16])
+def test_shared_expert_slices(slices):
+    cfg = synth.get_config("shared_fine_bf16", d_model=256, d_ff=64, n_experts=8, top_k=2,
+                           shared_d_ff=64 * slices)
+    _run(cfg, [1, 16, 300])
+
+
+def test_int8_zero_scale_channels():
+    # output channels quantised from all-zero weights have s = 0 and q = 0
+    def zero(L):
+        L.w_gate[2, :, 5] = 0
+        L.s_gate[2, 5] = 0
+        L.w_down[1, :, 7] = 0
+        L.s_down[1, 7] = 0
+    _run(synth.get_config("int8_mixtral22b", d_model=256, d_ff=128), [1, 300], mutate=zero)
