@@ -50,6 +50,14 @@ struct ScatterOut {
 };
 hipError_t launch_scatter(const int32_t* idx, int T, int E, int k, int V, int bm, const ScatterOut& o,
                           hipStream_t s);
+// Gate then Scatter for decode batches (T <= 64, k <= 8) in two launches: partial router
+// dots over (16-column block, 128-wide K slice) workgroups into `part`
+// (gate_split_workspace bytes), then one workgroup for the sums, top-k and scatter.
+bool gate_split_fits(int T, int k);
+size_t gate_split_workspace(int T, int d, int E, bool has_shared);
+hipError_t launch_gate_split(const void* x, bool x_bf16, const float* wr_t, const float* bias, int T, int d, int E,
+                             bool has_shared, int k, int32_t* idx, float* w, float* gs, int V, int bm,
+                             const ScatterOut& o, float* part, hipStream_t s);
 // Gate then Scatter in a single workgroup, for tiny batches: up to 4 tokens,
 // d_model <= 8192, at most 16 router columns (experts + shared gate).
 bool gate_scatter_small_fits(int T, int d, int E, bool has_shared, bool x_bf16);

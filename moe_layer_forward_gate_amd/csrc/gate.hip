@@ -445,6 +445,103 @@ __global__ __launch_bounds__(1024) void gate_scatter_small(const XT* __restrict_
     scatter_block<NW>(ids, T, E, k, V, bm, o, sm);
 }
 
+// ---------------------------------------------------------------- decode batches, split
+// For T <= 64 the router GEMM is spread over many workgroups, each one 16-column block
+// times one 128-wide K slice for every token (a decode step is a chain of memory
+// latencies: every load of a workgroup is issued at once, and many CUs pull the router):
+//   gate_partial: lane (column e = lane%16, 32-wide sub-slice c = lane/16) keeps its 32
+//     router weights in registers; wave w (of 16) takes tokens w, w+16, w+32, w+48, all
+//     their loads first; one fp32 dot per token, the four sub-slices folded with two
+//     butterflies, written to part[slice][t][column];
+//   gate_finish: one workgroup adds the slices in order (+ bias), takes the top-k of every
+//     token and then runs the scatter, so the routing is done in two launches.
+constexpr int kPartK = 128;  // K slice per gate_partial workgroup
+
+template <typename XT>
+__global__ __launch_bounds__(1024) void gate_partial(const XT* __restrict__ x, const float* __restrict__ wr_t, int T,
+                                                     int d, int Ec, float* __restrict__ part) {
+    constexpr int XQ = sizeof(XT) / 2;   // 16-byte chunks per 8 elements
+    constexpr int U = XQ == 1 ? 4 : 2;   // tokens per wave per round (register budget)
+    const int nb = blockIdx.x, ks = blockIdx.y, NC = gridDim.x * 16;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int e = nb * 16 + lane % 16;
+    const int k0 = ks * kPartK + (lane / 16) * 32;
+    const bool kin = k0 < d;  // d % 32 == 0: a sub-slice is all inside or all outside
+    const int kc = kin ? k0 : 0;
+    float wv[32];
+    {
+        const float4* p = reinterpret_cast<const float4*>(wr_t + (size_t)(e < Ec ? e : 0) * d + kc);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float4 q = p[i];
+            wv[4 * i] = q.x;
+            wv[4 * i + 1] = q.y;
+            wv[4 * i + 2] = q.z;
+            wv[4 * i + 3] = q.w;
+        }
+    }
+    for (int t0 = wave; t0 < T; t0 += 16 * U) {
+        u32x4 xq[U][4 * XQ];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = t0 + 16 * u;
+            const u32x4* px = reinterpret_cast<const u32x4*>(x + (size_t)(t < T ? t : 0) * d + kc);
+#pragma unroll
+            for (int i = 0; i < 4 * XQ; ++i) xq[u][i] = px[i];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = t0 + 16 * u;
+            float acc = 0.0f;
+#pragma unroll
+            for (int v = 0; v < 32; ++v) {
+                float f;
+                if constexpr (XQ == 1) {
+                    const uint32_t q = xq[u][v / 8][(v % 8) / 2];
+                    f = __uint_as_float((v & 1) ? (q & 0xFFFF0000u) : (q << 16));
+                } else {
+                    f = __uint_as_float(xq[u][v / 4][v % 4]);
+                }
+                acc = fmaf(f, wv[v], acc);
+            }
+            acc = kin ? acc : 0.0f;
+            acc += __shfl_xor(acc, 16, kWave);
+            acc += __shfl_xor(acc, 32, kWave);
+            if (lane < 16 && t < T) part[((size_t)ks * T + t) * NC + e] = acc;
+        }
+    }
+}
+
+constexpr int kFinishT = 64;  // tokens per gate_finish (the decode bound)
+
+__global__ __launch_bounds__(1024) void gate_finish(const float* __restrict__ part, int KS, int NC, int T, int E,
+                                                    int Ec, const float* __restrict__ bias, int k, bool has_shared,
+                                                    int32_t* __restrict__ idx, float* __restrict__ w,
+                                                    float* __restrict__ gs, int V, int bm, ScatterOut o) {
+    constexpr int NW = 16;
+    __shared__ float logits[kFinishT][kMaxExperts + 2];
+    __shared__ int32_t ids[kFinishT * 8];  // top-k ids (k <= 8 here) for the scatter to read from LDS
+    __shared__ ScatterSmem<NW> sm;
+    const int tid = threadIdx.x, wave = tid / kWave;
+    for (int i = tid; i < T * Ec; i += NW * kWave) {
+        const int t = i / Ec, e = i - (i / Ec) * Ec;
+        // slices added in order; their loads are issued 16 at a time (not one round trip each)
+        float v = 0.0f;
+        for (int q0 = 0; q0 < KS; q0 += 16) {
+            float pv[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) pv[q] = q0 + q < KS ? part[((size_t)(q0 + q) * T + t) * NC + e] : 0.0f;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) v += pv[q];
+        }
+        logits[t][e] = v + ((bias && e < E) ? bias[e] : 0.0f);
+    }
+    __syncthreads();
+    for (int t = wave; t < T; t += NW) wave_topk_write(logits[t], E, k, has_shared, t, idx, w, gs, ids);
+    __syncthreads();
+    scatter_block<NW>(ids, T, E, k, V, bm, o, sm);
+}
+
 template <typename XT>
 hipError_t launch_gate_t(const XT* x, const float* wr_t, const u32x4* planes, const float* bias, int T, int d, int E,
                          bool has_shared, int k, int32_t* idx, float* w, float* gs, hipStream_t s) {
@@ -487,6 +584,32 @@ hipError_t launch_gate_t(const XT* x, const float* wr_t, const u32x4* planes, co
 }
 
 }  // namespace
+
+bool gate_split_fits(int T, int k) { return T >= 1 && T <= kFinishT && k <= 8; }
+
+size_t gate_split_workspace(int T, int d, int E, bool has_shared) {
+    const int NC = (E + (has_shared ? 1 : 0) + 15) / 16 * 16;
+    return (size_t)((d + kPartK - 1) / kPartK) * T * NC * sizeof(float);
+}
+
+hipError_t launch_gate_split(const void* x, bool x_bf16, const float* wr_t, const float* bias, int T, int d, int E,
+                             bool has_shared, int k, int32_t* idx, float* w, float* gs, int V, int bm,
+                             const ScatterOut& o, float* part, hipStream_t s) {
+    if (!gate_split_fits(T, k) || d % 32 || E > kMaxExperts || E + V > kMaxEt) return hipErrorInvalidValue;
+    const int Ec = E + (has_shared ? 1 : 0);
+    const int NB = (Ec + 15) / 16, KS = (d + kPartK - 1) / kPartK;
+    if (x_bf16)
+        hipLaunchKernelGGL(gate_partial<bf16_t>, dim3(NB, KS), dim3(1024), 0, s, (const bf16_t*)x, wr_t, T, d, Ec,
+                           part);
+    else
+        hipLaunchKernelGGL(gate_partial<float>, dim3(NB, KS), dim3(1024), 0, s, (const float*)x, wr_t, T, d, Ec,
+                           part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gate_finish, dim3(1), dim3(1024), 0, s, (const float*)part, KS, NB * 16, T, E, Ec, bias, k,
+                       has_shared, idx, w, gs, V, bm, o);
+    return hipGetLastError();
+}
 
 bool gate_scatter_small_fits(int T, int d, int E, bool has_shared, bool x_bf16) {
     const int mt = x_bf16 ? SmallGate<bf16_t>::T : SmallGate<float>::T;

@@ -59,6 +59,7 @@ struct moe_layer {
     int32_t* tile_start = nullptr;
     int32_t* sorted_c = nullptr;
     float* gs = nullptr;
+    float* gate_part = nullptr;  // partial router dots of the split decode gate
     bf16_t* xp = nullptr;  // tiled up operand (bf16/int8 experts)
     void* h = nullptr;
     float* ow = nullptr;
@@ -74,7 +75,7 @@ namespace {
 void release(moe_layer* L) {
     if (!L) return;
     void* bufs[] = {L->wr_t, L->wr_planes, L->bias, L->wgu, L->wdn, L->s_gate, L->s_up, L->s_down, L->counts, L->offsets,
-                    L->tile_start, L->sorted_c, L->gs, L->xp, L->h, L->ow};
+                    L->tile_start, L->sorted_c, L->gs, L->gate_part, L->xp, L->h, L->ow};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
     for (hipEvent_t e : L->ev)
@@ -164,6 +165,9 @@ int create_impl(const moe_desc* desc, const moe_weights* w, moe_layer* L) {
     if ((rc = dev_alloc(&L->tile_start, (Et + 1) * 4))) return rc;
     if ((rc = dev_alloc(&L->sorted_c, P * 4))) return rc;
     if ((rc = dev_alloc(&L->gs, T * 4))) return rc;
+    if ((rc = dev_alloc(&L->gate_part, gate_split_workspace((int)std::min(T, (size_t)64), d.d_model, L->E,
+                                                             d.shared_d_ff > 0))))
+        return rc;
     // the tiled GEMMs work on padded rows: at most P + (bm - 1) + Et*bm of them for bm <= 256
     const size_t R = P + (size_t)256 * (Et + 1);
     if (!f32 && (rc = dev_alloc(&L->xp, R * dm * 2))) return rc;
@@ -309,10 +313,20 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
     const GemmArgs a{L->tile_start, L->offsets, L->sorted_c, L->Et, L->kt, k, max_tiles, bm, ksplit,
                      (const bf16_t*)x, L->xp, (bf16_t*)L->h, L->wgu, L->wdn, L->s_gate, L->s_up, L->s_down,
                      r->topk_w, gs, L->ow, d.d_model, d.d_ff};
-    if (gate_scatter_small_fits(T, d.d_model, L->E, L->V > 0, !f32)) {
+    // Routing for decode batches: up to 16 router columns, one workgroup reads the whole
+    // router quickly enough (tiny batches fuse gate and scatter; larger ones run one gate
+    // workgroup per token, then the scatter); more columns spread the router over many
+    // workgroups (split gate, whose last launch also runs the scatter).
+    const bool wide_router = L->E + (L->V > 0 ? 1 : 0) > 16;
+    if (!wide_router && gate_scatter_small_fits(T, d.d_model, L->E, L->V > 0, !f32)) {
         // tiny batch: both stages in one workgroup (the scatter stage then times as empty)
         HIP_TRY(launch_gate_scatter_small(x, !f32, L->wr_t, L->bias, T, d.d_model, L->E, L->V > 0, k, r->topk_idx,
                                           r->topk_w, gs, L->V, bm, so, s));
+        if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
+    } else if (wide_router && gate_split_fits(T, k)) {
+        // decode batch: router dots on many workgroups, then top-k and scatter in one
+        HIP_TRY(launch_gate_split(x, !f32, L->wr_t, L->bias, T, d.d_model, L->E, L->V > 0, k, r->topk_idx,
+                                  r->topk_w, gs, L->V, bm, so, L->gate_part, s));
         if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
     } else {
         HIP_TRY(launch_gate(x, !f32, L->wr_t, L->wr_planes, L->bias, T, d.d_model, L->E, L->V > 0, k, r->topk_idx,

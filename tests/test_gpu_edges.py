@@ -3,8 +3,8 @@
 Covers: k = 1 and k = E, expert counts that are not multiples of 8 or 16 (up to the
 128-expert limit), the smallest supported widths, T at the max_tokens bound and on
 both sides of the streaming / tiled switch, every token routed to one expert, a
-shared expert of one and of sixteen d_ff slices, and int8 output channels whose
-scale is zero.
+shared expert of one and of sixteen d_ff slices, int8 output channels whose
+scale is zero, and the decode routing paths for routers wider than 16 columns.
 """
 import pytest
 import torch
@@ -79,3 +79,10 @@ def test_int8_zero_scale_channels():
         L.w_down[1, :, 7] = 0
         L.s_down[1, 7] = 0
     _run(synth.get_config("int8_mixtral22b", d_model=256, d_ff=128), [1, 300], mutate=zero)
+
+
+def test_wide_router_decode_paths():
+    # more than 16 router columns at T <= 64: the split gate (k <= 8), fp32 tokens included,
+    # and the per-token gate kernel when k > 8
+    _run(synth.get_config("tiny_f32", d_model=64, d_ff=64, n_experts=32, top_k=4), [1, 8, 64])
+    _run(synth.get_config("mixtral_bf16", d_model=128, d_ff=64, n_experts=32, top_k=10), [1, 8, 64])
