@@ -72,7 +72,7 @@ struct GemmArgs {
     const int32_t* sorted_c;    // [P]
     int Et, kt, k;              // experts incl. virtual, slots per token incl. virtual, routed k
     int max_tiles;              // bound on sum_e ceil(n_e / bm)
-    int bm;                     // row tile height: 256, or 128 for int8 (must match the scatter's tile list)
+    int bm;                     // row tile height: 256 (bf16) or 128 (int8); must match the scatter's tile list
     int ksplit;                 // down projection: K split into ksplit partial sums (ow rows c*ksplit + s)
     // Streaming kernels: A = x rows gathered by token (up), H rows [P][F] (down).
     // Tiled kernels: A in fragment order over padded rows (tile g owns padded rows

@@ -12,10 +12,10 @@
 //       the Gather stage is applied in this epilogue ([pptc §2.1] fused
 //       aggregation).
 //
-// Workgroup tile BM x 256 (BM = 256; 128 for int8 experts holding few rows), 8
+// Workgroup tile BM x 256 (BM = 256 for bf16 weights, 128 for int8), 8
 // waves; each wave owns a 64 x (16*NBW) block of v_mfma_f32_16x16x32_bf16
-// accumulators. bf16 weights: K step 32, four LDS stages, three K steps of loads in
-// flight, one barrier per step; int8 weights: K step 64, two stages. Operands are
+// accumulators. K step 32 (bf16 weights) or 64 (int8), four LDS stages, three K
+// steps of loads in flight, one barrier per step. Operands are
 // staged in LDS in MFMA fragment order: one 1 KB block = 16 rows x 32 K, lane l
 // holding row l%16, K 8*(l/16)..+7, so every fragment read is a conflict-free
 // 16-byte-per-lane ds_read. Global -> LDS traffic uses the gfx950 LDS-DMA load
@@ -27,11 +27,10 @@
 // up projection is packed by launch_pack_a after the scatter, the up kernel's
 // epilogue writes H in the down projection's A order, and expert weights are
 // packed at create time (bf16: [Et][N/16][K/32][64][8]).
-// int8 weights ([E][N/16][K/64][64][16], bytes 0-7 the first 32-K half) go
-// through registers instead, widened to bf16 on the way to LDS (exact: |q| <=
-// 127 fits bf16's significand); their per-column scale multiplies the fp32
-// accumulator in the epilogue; the loads of K step kt+1 are in flight while step
-// kt is multiplied.
+// int8 weights ([E][N/16][K/64][64][16], bytes 0-7 the first 32-K half) are staged
+// in LDS as int8 by the same LDS-DMA (half the bytes of bf16) and widened to bf16 in
+// registers right before their MFMAs (exact: |q| <= 127 fits bf16's significand);
+// their per-column scale multiplies the fp32 accumulator in the epilogue.
 // Up-projection columns are packed gate/up interleaved per 16 columns, so each
 // lane holds the gate and up accumulators of the same (row, f) and SiLU * up
 // runs in registers.
@@ -76,12 +75,12 @@ __device__ __forceinline__ void wait_vm_le() {
 // memory clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Pipeline shape: bf16 weights stream through LDS-DMA only (BK 32, 4 stages, three
-// K steps in flight); int8 weights need a register hop for the widening (BK 64,
-// 2 stages, one K step in flight).
+// Pipeline shape: both operands stream through LDS-DMA, four stages (three K steps of
+// loads in flight). bf16: K step 32. int8: K step 64 (one 1 KB int8 block holds 16
+// columns x 64 K), widened to bf16 when the wave reads its B fragments from LDS.
 template <bool INT8> struct Pipe;
 template <> struct Pipe<false> { static constexpr int BK = 32, STAGES = 4; };
-template <> struct Pipe<true> { static constexpr int BK = 64, STAGES = 2; };
+template <> struct Pipe<true> { static constexpr int BK = 64, STAGES = 4; };
 
 // Wave layout: NW waves; 8 waves tile the block 4 x 2 (BM 256) or 2 x 4 (BM 128) with
 // 64-row wave tiles; 4 waves would tile it 2 x 2 with (BM/2)-row x 128-column wave tiles
@@ -107,10 +106,10 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
     constexpr int MWB = WaveShape<BM, NW>::MWB;
     constexpr int NBW = WaveShape<BM, NW>::NBW;
     constexpr int ABLK = MBLK * KH;           // A blocks per stage
-    constexpr int BBLK = (BN / 16) * KH;      // B blocks per stage
+    constexpr int BBLK = INT8 ? BN / 16 : (BN / 16) * KH;  // B blocks per stage (an int8 block spans 64 K)
     constexpr int STAGE = ABLK + BBLK;        // 1 KB blocks per stage
     constexpr int AW = ABLK / kWaves;         // A block loads per wave per stage
-    constexpr int BW = INT8 ? 0 : BBLK / kWaves;  // B block loads (LDS-DMA) per wave per stage
+    constexpr int BW = BBLK / kWaves;         // B block loads per wave per stage
     constexpr int LPS = AW + BW;              // LDS-DMA loads per wave per stage
 
     const int K = UP ? a.d : a.F;
@@ -162,40 +161,20 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
         const bf16_t* wb = (const bf16_t*)(UP ? a.wgu : a.wdn) + (size_t)tl.e * N * K;
         b_src = reinterpret_cast<const u32x4*>(wb) + kbase / 32 * 64;
     }
-    // int8: thread loads lane chunks q = tid + 512*i of the (BN/16) x 1 KB int8 blocks
-    constexpr int NQ8 = INT8 ? (BN / 16) * 64 / kThreads : 1;
-    u32x4 r8[NQ8];
-
     auto issue = [&](int kt, int stage) {
         u32x4* st = lds + (size_t)stage * STAGE * 64;
 #pragma unroll
         for (int i = 0; i < AW; ++i) dma16(a_blk[i] + (size_t)kt * KH * 512, st + (wave + kWaves * i) * 64);
-        if constexpr (INT8) {
 #pragma unroll
-            for (int i = 0; i < NQ8; ++i) {
-                const int q = tid + kThreads * i;
-                const int nbg = min(tl.n * (BN / 16) + q / 64, NB16 - 1);
-                r8[i] = b_src[((size_t)nbg * (K / 64) + kt) * 64 + q % 64];
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < BW; ++j) {
-                const int blk = wave * BW + j;  // stage B block: n-block blk / KH, K half blk % KH
+        for (int j = 0; j < BW; ++j) {
+            const int blk = wave * BW + j;  // bf16: n-block blk / KH, K half blk % KH; int8: n-block blk
+            if constexpr (INT8) {
+                const int nbg = min(tl.n * (BN / 16) + blk, NB16 - 1);
+                dma16(b_src + ((size_t)nbg * (K / 64) + kt) * 64 + lane, st + (ABLK + blk) * 64);
+            } else {
                 const int nb = blk / KH, kh = blk % KH;
                 const int nbg = min(tl.n * (BN / 16) + nb, NB16 - 1);
                 dma16(b_src + ((size_t)nbg * KS + kt * KH + kh) * 64 + lane, st + (ABLK + blk) * 64);
-            }
-        }
-    };
-    auto store_b8 = [&](int stage) {
-        if constexpr (INT8) {
-            u32x4* lb = lds + (size_t)stage * STAGE * 64 + ABLK * 64;
-#pragma unroll
-            for (int i = 0; i < NQ8; ++i) {
-                const int q = tid + kThreads * i;
-                const int nb = q / 64, ln = q % 64;
-                lb[(nb * 2 + 0) * 64 + ln] = i8x8_to_bf16x8(r8[i].x, r8[i].y);
-                lb[(nb * 2 + 1) * 64 + ln] = i8x8_to_bf16x8(r8[i].z, r8[i].w);
             }
         }
     };
@@ -206,74 +185,61 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < NBW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int stage) {
-        const u32x4* la = lds + (size_t)stage * STAGE * 64;
-        const u32x4* lb = la + ABLK * 64;
-#pragma unroll
-        for (int kh = 0; kh < KH; ++kh) {
-            bf16x8 af[MWB], bfg[NBW];
-#pragma unroll
-            for (int mb = 0; mb < MWB; ++mb)
-                af[mb] = __builtin_bit_cast(bf16x8, la[((wm * MWB + mb) * KH + kh) * 64 + lane]);
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb)
-                bfg[nb] = __builtin_bit_cast(bf16x8, lb[((wn * NBW + nb) * KH + kh) * 64 + lane]);
-#pragma unroll
-            for (int mb = 0; mb < MWB; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < NBW; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], bfg[nb], acc[mb][nb], 0, 0, 0);
-        }
-    };
-
     const int KT = Kpart / BK;
-    if constexpr (INT8) {
-        issue(0, 0);
-        store_b8(0);
-        wait_vm_le<0>();
-        __syncthreads();
-        for (int kt = 0; kt < KT; ++kt) {
-            const int stage = kt & 1;
-            if (kt + 1 < KT) issue(kt + 1, stage ^ 1);
-            compute(stage);
-            if (kt + 1 < KT) store_b8(stage ^ 1);
-            wait_vm_le<0>();
-            __syncthreads();
-        }
-    } else {
+    {
         // Fragments are double-buffered in registers: the LDS reads of K step kt+1 are
         // issued before the MFMAs of step kt, so LDS latency hides under the MFMAs.
         // Stage (kt-1) % STAGES is refilled in iteration kt: its fragments were read
         // in iteration kt-2 and consumed in kt-1, before this iteration's barrier.
-        static_assert(STAGES >= 3 && KH == 1, "pipeline shape");
-        bf16x8 fa[2][MWB], fb[2][NBW];
-        auto read_frags = [&](int stage, bf16x8 (&af)[MWB], bf16x8 (&bf)[NBW]) {
+        // B fragments are kept as loaded (int8 bytes are widened right before their MFMAs).
+        static_assert(STAGES >= 3, "pipeline shape");
+        using BFrag = std::conditional_t<INT8, u32x4, bf16x8>;  // int8 bytes are widened at use
+        bf16x8 fa[2][MWB][KH];
+        BFrag fb[2][NBW];
+        auto read_frags = [&](int stage, bf16x8 (&af)[MWB][KH], BFrag (&bq)[NBW]) {
             const u32x4* la = lds + (size_t)stage * STAGE * 64;
             const u32x4* lb = la + ABLK * 64;
 #pragma unroll
-            for (int mb = 0; mb < MWB; ++mb) af[mb] = __builtin_bit_cast(bf16x8, la[(wm * MWB + mb) * 64 + lane]);
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) bf[nb] = __builtin_bit_cast(bf16x8, lb[(wn * NBW + nb) * 64 + lane]);
-        };
-        auto mfma_frags = [&](const bf16x8 (&af)[MWB], const bf16x8 (&bf)[NBW]) {
-#pragma unroll
             for (int mb = 0; mb < MWB; ++mb)
 #pragma unroll
-                for (int nb = 0; nb < NBW; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], bf[nb], acc[mb][nb], 0, 0, 0);
+                for (int kh = 0; kh < KH; ++kh)
+                    af[mb][kh] = __builtin_bit_cast(bf16x8, la[((wm * MWB + mb) * KH + kh) * 64 + lane]);
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) bq[nb] = __builtin_bit_cast(BFrag, lb[(wn * NBW + nb) * 64 + lane]);
+        };
+        auto mfma_frags = [&](const bf16x8 (&af)[MWB][KH], const BFrag (&bq)[NBW]) {
+            if constexpr (INT8) {
+                // column block outermost: each widened B fragment serves every row block
+#pragma unroll
+                for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+                    for (int nb = 0; nb < NBW; ++nb) {
+                        // int8 lane bytes 0-7: K half 0, bytes 8-15: K half 1
+                        const bf16x8 bw = __builtin_bit_cast(bf16x8, kh ? i8x8_to_bf16x8(bq[nb].z, bq[nb].w)
+                                                                        : i8x8_to_bf16x8(bq[nb].x, bq[nb].y));
+#pragma unroll
+                        for (int mb = 0; mb < MWB; ++mb)
+                            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb][kh], bw, acc[mb][nb], 0, 0, 0);
+                    }
+            } else {
+#pragma unroll
+                for (int mb = 0; mb < MWB; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < NBW; ++nb)
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb][0], bq[nb], acc[mb][nb], 0, 0, 0);
+            }
         };
         // Branch-free steady state (a join in the loop would make the compiler drain every
         // LDS read before the MFMAs): every step issues one stage of LDS-DMA loads -- past
         // the last stage it re-loads the last stage into the free slot, which is never
-        // read -- and every step but the last reads the next step's fragments. K/32 is
-        // even, so the step pairs below always end with the buffer parity known.
+        // read -- and reads the next step's fragments. Steps run in pairs so the register
+        // buffer parity is static; one or two steps remain after the pairs.
         // A wave whose 64 rows all lie past the expert's last row (the ragged last row
         // tile) runs the same loop without fragment reads or MFMAs: it still loads its
         // share of the tiles and meets every barrier.
         auto run = [&](auto compute) {
             constexpr bool C = decltype(compute)::value;
-            auto step = [&](int k, bf16x8 (&ca)[MWB], bf16x8 (&cb)[NBW], bf16x8 (&na)[MWB],
-                            bf16x8 (&nb)[NBW]) {
+            auto step = [&](int k, auto& ca, auto& cb, auto& na, auto& nb) {
                 wait_vm_le<(STAGES - 3) * LPS>();  // stage k+1 has landed
                 lds_barrier();                     // ... for every wave; stage k-1 is free
                 issue(min(k + STAGES - 1, KT - 1), (k + STAGES - 1) % STAGES);
@@ -288,12 +254,17 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
             lds_barrier();
             if constexpr (C) read_frags(0, fa[0], fb[0]);
             int k = 0;
-            for (; k < KT - 2; k += 2) {
+            for (; k + 2 < KT; k += 2) {
                 step(k, fa[0], fb[0], fa[1], fb[1]);
                 step(k + 1, fa[1], fb[1], fa[0], fb[0]);
             }
+            // one or two steps left (bf16: always two, K/32 is even): the last pair step runs
+            // in either case (with one step left its fragment read is of a stage that does
+            // not exist and is dropped)
             step(k, fa[0], fb[0], fa[1], fb[1]);
-            if constexpr (C) mfma_frags(fa[1], fb[1]);
+            if constexpr (C) {
+                if (!INT8 || KT - k == 2) mfma_frags(fa[1], fb[1]);
+            }
         };
         if (wm * MWB * 16 < tl.rows) run(std::true_type{});
         else run(std::false_type{});
@@ -380,7 +351,8 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
 template <int BM, int NW, bool INT8, bool UP>
 hipError_t launch(const GemmArgs& a, hipStream_t s) {
     constexpr int KH = Pipe<INT8>::BK / 32;
-    constexpr int STAGE = (BM / 16) * KH + (BN / 16) * KH;
+    constexpr int STAGE = (BM / 16) * KH + (INT8 ? BN / 16 : (BN / 16) * KH);  // as in the kernel
+    static_assert(Pipe<INT8>::STAGES * STAGE * 1024 <= 160 * 1024, "LDS");
     const size_t lds_bytes = (size_t)Pipe<INT8>::STAGES * STAGE * 64 * 16;
     auto kern = expert_gemm<BM, NW, INT8, UP>;
     static bool attr_set = false;  // one-time opt-in above the default dynamic LDS limit
@@ -393,7 +365,7 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
     const int N = UP ? 2 * a.F : a.d;
     const int S = UP ? 1 : a.ksplit;
     const int Kpart = (UP ? a.d : a.F) / S;
-    if (Kpart % 64 != 0 || Kpart < 64) return hipErrorInvalidValue;  // the pipeline takes K steps in pairs
+    if (Kpart % 64 != 0 || Kpart < 64) return hipErrorInvalidValue;  // whole K steps of 64 (int8) or 2 x 32
     const int NTp = ((N + BN - 1) / BN + GN - 1) / GN * GN;
     // a multiple of 8 workgroups, so every XCD gets ceil(tiles / 8) slots
     dim3 grid((unsigned)(((size_t)a.max_tiles * NTp * S + kXcds - 1) / kXcds * kXcds));
@@ -405,8 +377,10 @@ template <bool UP>
 hipError_t launch_dispatch(const GemmArgs& a, bool int8, hipStream_t s) {
     // 8 waves (two per SIMD): the 4-wave layout with 128 x 128 wave tiles reads less LDS per
     // MFMA but leaves one wave per SIMD to hide every latency, and measured 25% slower
-    if (a.bm == 256) return int8 ? launch<256, 8, true, UP>(a, s) : launch<256, kBf16Waves, false, UP>(a, s);
-    if (a.bm == 128 && int8) return launch<128, 8, true, UP>(a, s);
+    // bf16 weights: 256-row tiles; int8: 128-row tiles (the 64 x 128 wave tiles of 256-row
+    // tiles leave no registers for the int8 fragments of two K halves)
+    if (!int8 && a.bm == 256) return launch<256, kBf16Waves, false, UP>(a, s);
+    if (int8 && a.bm == 128) return launch<128, 8, true, UP>(a, s);
     return hipErrorInvalidValue;
 }
 

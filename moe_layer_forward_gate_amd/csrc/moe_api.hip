@@ -284,7 +284,6 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
     //    when experts are expected to hold many rows and a 2-way K split of the
     //    down projection when its column tiles alone would leave the GPU idle.
     const bool streaming = !f32 && T <= kStreamMaxT;
-    const int avg_rows = (T * k) / L->E;
     int bm, ksplit = 1;
     if (f32) {
         bm = kBMf32;
@@ -294,11 +293,10 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
         const int groups = active * (d.d_model / 128);
         while (ksplit < kStreamMaxSplit && groups * ksplit < 1024 && d.d_ff % (ksplit * 2 * 64) == 0) ksplit *= 2;
     } else {
-        // 256-row tiles: the 256 x 256 workgroup tile reads the least LDS and L2 per MFMA and
-        // outruns 128-row tiles even when most experts leave their last tile half empty; int8
-        // weights (widened through registers, one K step in flight) keep 128-row tiles while
-        // experts hold few rows, where the kernel is bound by the weight stream
-        bm = (i8 && avg_rows < 768 && T < 8192) ? 128 : 256;
+        // bf16: 256-row tiles (the 256 x 256 workgroup tile reads the least LDS and L2 per MFMA
+        // and outruns 128-row tiles even when most experts leave their last tile half empty);
+        // int8: 128-row tiles (see the GEMM launcher)
+        bm = i8 ? 128 : 256;
         // split the down projection's K in two when its tiles alone fill the GPU less than
         // ~8 workgroups per CU and K is long enough for both halves to stay efficient
         const int est_tiles = (T * L->kt + bm - 1) / bm + std::min(L->Et, T * L->kt);
