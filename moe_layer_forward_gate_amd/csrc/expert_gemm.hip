@@ -161,10 +161,16 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
         const bf16_t* wb = (const bf16_t*)(UP ? a.wgu : a.wdn) + (size_t)tl.e * N * K;
         b_src = reinterpret_cast<const u32x4*>(wb) + kbase / 32 * 64;
     }
-    auto issue = [&](int kt, int stage) {
+    // HALF: the tile holds at most BM/2 rows, so the A blocks of its lower half (load i >=
+    // AW/2 of every wave) are not loaded; no wave reads them (the waves that would are the
+    // ones without rows, which skip their MFMAs)
+    static_assert(AW % 2 == 0, "A loads split in halves");
+    auto issue = [&](int kt, int stage, auto half) {
+        constexpr bool HALF = decltype(half)::value;
         u32x4* st = lds + (size_t)stage * STAGE * 64;
 #pragma unroll
-        for (int i = 0; i < AW; ++i) dma16(a_blk[i] + (size_t)kt * KH * 512, st + (wave + kWaves * i) * 64);
+        for (int i = 0; i < (HALF ? AW / 2 : AW); ++i)
+            dma16(a_blk[i] + (size_t)kt * KH * 512, st + (wave + kWaves * i) * 64);
 #pragma unroll
         for (int j = 0; j < BW; ++j) {
             const int blk = wave * BW + j;  // bf16: n-block blk / KH, K half blk % KH; int8: n-block blk
@@ -237,20 +243,21 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
         // A wave whose 64 rows all lie past the expert's last row (the ragged last row
         // tile) runs the same loop without fragment reads or MFMAs: it still loads its
         // share of the tiles and meets every barrier.
-        auto run = [&](auto compute) {
+        auto run = [&](auto compute, auto half) {
             constexpr bool C = decltype(compute)::value;
+            constexpr int L = decltype(half)::value ? LPS - AW / 2 : LPS;  // LDS-DMA loads per stage
             auto step = [&](int k, auto& ca, auto& cb, auto& na, auto& nb) {
-                wait_vm_le<(STAGES - 3) * LPS>();  // stage k+1 has landed
+                wait_vm_le<(STAGES - 3) * L>();    // stage k+1 has landed
                 lds_barrier();                     // ... for every wave; stage k-1 is free
-                issue(min(k + STAGES - 1, KT - 1), (k + STAGES - 1) % STAGES);
+                issue(min(k + STAGES - 1, KT - 1), (k + STAGES - 1) % STAGES, half);
                 if constexpr (C) {
                     read_frags((k + 1) % STAGES, na, nb);
                     mfma_frags(ca, cb);
                 }
             };
 #pragma unroll
-            for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(min(s0, KT - 1), s0);
-            wait_vm_le<(STAGES - 2) * LPS>();
+            for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(min(s0, KT - 1), s0, half);
+            wait_vm_le<(STAGES - 2) * L>();
             lds_barrier();
             if constexpr (C) read_frags(0, fa[0], fb[0]);
             int k = 0;
@@ -266,8 +273,14 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
                 if (!INT8 || KT - k == 2) mfma_frags(fa[1], fb[1]);
             }
         };
-        if (wm * MWB * 16 < tl.rows) run(std::true_type{});
-        else run(std::false_type{});
+        const bool has_rows = wm * MWB * 16 < tl.rows;
+        if (tl.rows <= BM / 2) {
+            if (has_rows) run(std::true_type{}, std::true_type{});
+            else run(std::false_type{}, std::true_type{});
+        } else {
+            if (has_rows) run(std::true_type{}, std::false_type{});
+            else run(std::false_type{}, std::false_type{});
+        }
         wait_vm_le<0>();  // no LDS-DMA write may outlive the workgroup
     }
 
