@@ -87,7 +87,7 @@ template <> struct Pipe<true> { static constexpr int BK = 64, STAGES = 4; };
 // (fewer LDS fragment reads per MFMA, accumulators in AGPRs, one wave per SIMD).
 template <int BM, int NW>
 struct WaveShape {
-    static constexpr int WM = NW == 8 ? BM / 64 : 2;  // waves along M
+    static constexpr int WM = NW >= 8 ? BM / 64 : 2;  // waves along M
     static constexpr int WN = NW / WM;                // waves along N
     static constexpr int MWB = BM / 16 / WM;          // 16-row blocks per wave
     static constexpr int NBW = (BN / 16) / WN;        // 16-column blocks per wave
@@ -161,16 +161,15 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
         const bf16_t* wb = (const bf16_t*)(UP ? a.wgu : a.wdn) + (size_t)tl.e * N * K;
         b_src = reinterpret_cast<const u32x4*>(wb) + kbase / 32 * 64;
     }
-    // HALF: the tile holds at most BM/2 rows, so the A blocks of its lower half (load i >=
-    // AW/2 of every wave) are not loaded; no wave reads them (the waves that would are the
-    // ones without rows, which skip their MFMAs)
-    static_assert(AW % 2 == 0, "A loads split in halves");
-    auto issue = [&](int kt, int stage, auto half) {
-        constexpr bool HALF = decltype(half)::value;
+    // NA: how many of this wave's A block loads are made. Load i fills row block
+    // (wave + NW*i) / KH, read only by the waves of row group (that block) / MWB; a block
+    // whose readers hold no rows (past the expert's last row) is not loaded. Blocks grow
+    // with i, so the loads made are always a prefix.
+    auto issue = [&](int kt, int stage, auto na) {
+        constexpr int NA = decltype(na)::value;
         u32x4* st = lds + (size_t)stage * STAGE * 64;
 #pragma unroll
-        for (int i = 0; i < (HALF ? AW / 2 : AW); ++i)
-            dma16(a_blk[i] + (size_t)kt * KH * 512, st + (wave + kWaves * i) * 64);
+        for (int i = 0; i < NA; ++i) dma16(a_blk[i] + (size_t)kt * KH * 512, st + (wave + kWaves * i) * 64);
 #pragma unroll
         for (int j = 0; j < BW; ++j) {
             const int blk = wave * BW + j;  // bf16: n-block blk / KH, K half blk % KH; int8: n-block blk
@@ -243,20 +242,20 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
         // A wave whose 64 rows all lie past the expert's last row (the ragged last row
         // tile) runs the same loop without fragment reads or MFMAs: it still loads its
         // share of the tiles and meets every barrier.
-        auto run = [&](auto compute, auto half) {
+        auto run = [&](auto compute, auto nac) {
             constexpr bool C = decltype(compute)::value;
-            constexpr int L = decltype(half)::value ? LPS - AW / 2 : LPS;  // LDS-DMA loads per stage
+            constexpr int L = decltype(nac)::value + BW;  // LDS-DMA loads per stage of this wave
             auto step = [&](int k, auto& ca, auto& cb, auto& na, auto& nb) {
                 wait_vm_le<(STAGES - 3) * L>();    // stage k+1 has landed
                 lds_barrier();                     // ... for every wave; stage k-1 is free
-                issue(min(k + STAGES - 1, KT - 1), (k + STAGES - 1) % STAGES, half);
+                issue(min(k + STAGES - 1, KT - 1), (k + STAGES - 1) % STAGES, nac);
                 if constexpr (C) {
                     read_frags((k + 1) % STAGES, na, nb);
                     mfma_frags(ca, cb);
                 }
             };
 #pragma unroll
-            for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(min(s0, KT - 1), s0, half);
+            for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(min(s0, KT - 1), s0, nac);
             wait_vm_le<(STAGES - 2) * L>();
             lds_barrier();
             if constexpr (C) read_frags(0, fa[0], fb[0]);
@@ -274,12 +273,22 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
             }
         };
         const bool has_rows = wm * MWB * 16 < tl.rows;
-        if (tl.rows <= BM / 2) {
-            if (has_rows) run(std::true_type{}, std::true_type{});
-            else run(std::false_type{}, std::true_type{});
+        int nA = 0;
+#pragma unroll
+        for (int i = 0; i < AW; ++i)
+            if (((wave + kWaves * i) / KH / MWB) * MWB * 16 < tl.rows) nA = i + 1;
+        static_assert(AW >= 1 && AW <= 2, "A loads per wave");
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, AW>;  // == 2 when AW == 2
+        if (has_rows) {
+            if (nA == AW) run(std::true_type{}, I2{});
+            else if (nA == 1) run(std::true_type{}, I1{});
+            else run(std::true_type{}, I0{});
         } else {
-            if (has_rows) run(std::true_type{}, std::false_type{});
-            else run(std::false_type{}, std::false_type{});
+            if (nA == AW) run(std::false_type{}, I2{});
+            else if (nA == 1) run(std::false_type{}, I1{});
+            else run(std::false_type{}, I0{});
         }
         wait_vm_le<0>();  // no LDS-DMA write may outlive the workgroup
     }
