@@ -12,8 +12,8 @@
 //       the Gather stage is applied in this epilogue ([pptc §2.1] fused
 //       aggregation).
 //
-// Workgroup tile BM x 256 (BM = 256 for bf16 weights, 128 for int8), 8
-// waves; each wave owns a 64 x (16*NBW) block of v_mfma_f32_16x16x32_bf16
+// Workgroup tile BM x 256 (BM = 256 on 16 waves for bf16 weights, 128 on 8 waves
+// for int8); each wave owns a 64 x 64 block of v_mfma_f32_16x16x32_bf16
 // accumulators. K step 32 (bf16 weights) or 64 (int8), four LDS stages, three K
 // steps of loads in flight, one barrier per step. Operands are
 // staged in LDS in MFMA fragment order: one 1 KB block = 16 rows x 32 K, lane l
@@ -42,7 +42,7 @@ namespace moe {
 namespace {
 
 constexpr int BN = 256;
-constexpr int kBf16Waves = 8;
+constexpr int kBf16Waves = 16;
 constexpr int GN = 4;       // column tiles per group (see decode_tile)
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -82,9 +82,10 @@ template <bool INT8> struct Pipe;
 template <> struct Pipe<false> { static constexpr int BK = 32, STAGES = 4; };
 template <> struct Pipe<true> { static constexpr int BK = 64, STAGES = 4; };
 
-// Wave layout: NW waves; 8 waves tile the block 4 x 2 (BM 256) or 2 x 4 (BM 128) with
-// 64-row wave tiles; 4 waves would tile it 2 x 2 with (BM/2)-row x 128-column wave tiles
-// (fewer LDS fragment reads per MFMA, accumulators in AGPRs, one wave per SIMD).
+// Wave layout: NW waves with 64-row wave tiles: 16 waves tile a 256-row block 4 x 4
+// (64 x 64 wave tiles, four waves per SIMD, 128 registers each); 8 waves tile a 128-row
+// block 2 x 4 (64 x 64) or a 256-row block 4 x 2 (64 x 128); 4 waves would tile it 2 x 2
+// with (BM/2)-row x 128-column wave tiles.
 template <int BM, int NW>
 struct WaveShape {
     static constexpr int WM = NW >= 8 ? BM / 64 : 2;  // waves along M
@@ -397,10 +398,11 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
 
 template <bool UP>
 hipError_t launch_dispatch(const GemmArgs& a, bool int8, hipStream_t s) {
-    // 8 waves (two per SIMD): the 4-wave layout with 128 x 128 wave tiles reads less LDS per
-    // MFMA but leaves one wave per SIMD to hide every latency, and measured 25% slower
-    // bf16 weights: 256-row tiles; int8: 128-row tiles (the 64 x 128 wave tiles of 256-row
-    // tiles leave no registers for the int8 fragments of two K halves)
+    // bf16 weights: 256-row tiles on 16 waves (four per SIMD hide more latency than two
+    // waves with 64 x 128 tiles, though they read a third more LDS per MFMA); int8: 128-row
+    // tiles on 8 waves (two K halves of int8 fragments need the registers of two waves per
+    // SIMD). Measured slower: 4 waves with 128 x 128 wave tiles (one wave per SIMD hides
+    // nothing), 128-row bf16 tiles (more operand traffic per MFMA).
     if (!int8 && a.bm == 256) return launch<256, kBf16Waves, false, UP>(a, s);
     if (int8 && a.bm == 128) return launch<128, 8, true, UP>(a, s);
     return hipErrorInvalidValue;
