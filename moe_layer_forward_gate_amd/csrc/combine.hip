@@ -3,23 +3,25 @@
 // [hotelren §2.1 step 6] and [hotelren §2.3] combine_kernel: the k expert
 // outputs are summed with their gating weights; [pptc §2.1] the k outputs share
 // slices of one buffer and are accumulated into the result. The weights were
-// applied in the down-projection epilogue, which wrote slot (t, j) to row
-// t*kt + j; this pass adds the kt rows of each token in a fixed order (slot 0
-// first), so the result does not depend on scheduling, and rounds once to the
-// output dtype. Each thread handles 4 consecutive columns (d % 4 == 0).
+// applied in the down-projection epilogue, which wrote slot (t, j), K split s to row
+// (t*kt + j)*S + s; this pass adds the first nrow rows of each token's stride rows in
+// a fixed order (slot 0 first), so the result does not depend on scheduling, and
+// rounds once to the output dtype. (With the shared slices merged into one sum only
+// the first k+1 slots of a token are written.) Each thread handles 4 consecutive
+// columns (d % 4 == 0).
 #include "common.h"
 
 namespace moe {
 namespace {
 
 template <bool BF16>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ow, int T, int kt, int d,
-                                                      void* __restrict__ y) {
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ow, int T, int kt, int stride,
+                                                      int d, void* __restrict__ y) {
     const int d4 = d / 4;
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (size_t)T * d4) return;
     const int t = (int)(i / d4), c4 = (int)(i - (size_t)t * d4);
-    const float4* src = reinterpret_cast<const float4*>(ow + (size_t)t * kt * d) + c4;
+    const float4* src = reinterpret_cast<const float4*>(ow + (size_t)t * stride * d) + c4;
     // rows are added in order 0, 1, 2, ...; loads go out 8 rows at a time
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     int j = 0;
@@ -48,13 +50,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_combine(const float* ow, int T, int kt, int d, void* y, bool y_bf16, hipStream_t s) {
+hipError_t launch_combine(const float* ow, int T, int nrow, int stride, int d, void* y, bool y_bf16,
+                          hipStream_t s) {
+    if (nrow > stride) return hipErrorInvalidValue;
     const size_t n = (size_t)T * (d / 4);
     dim3 grid((unsigned)((n + 255) / 256));
     if (y_bf16)
-        hipLaunchKernelGGL((combine_kernel<true>), grid, dim3(256), 0, s, ow, T, kt, d, y);
+        hipLaunchKernelGGL((combine_kernel<true>), grid, dim3(256), 0, s, ow, T, nrow, stride, d, y);
     else
-        hipLaunchKernelGGL((combine_kernel<false>), grid, dim3(256), 0, s, ow, T, kt, d, y);
+        hipLaunchKernelGGL((combine_kernel<false>), grid, dim3(256), 0, s, ow, T, nrow, stride, d, y);
     return hipGetLastError();
 }
 

@@ -74,6 +74,7 @@ struct GemmArgs {
     int max_tiles;              // bound on sum_e ceil(n_e / bm)
     int bm;                     // row tile height: 256 (bf16) or 128 (int8); must match the scatter's tile list
     int ksplit;                 // down projection: K split into ksplit partial sums (ow rows c*ksplit + s)
+    int merge_shared;           // tiled down projection: shared slices summed as one K = V*F tile (ksplit 1)
     // Streaming kernels: A = x rows gathered by token (up), H rows [P][F] (down).
     // Tiled kernels: A in fragment order over padded rows (tile g owns padded rows
     // [g*bm, (g+1)*bm)): xp = the gathered tokens [R/16][d/32][64][8] written by
@@ -123,8 +124,10 @@ struct GemmF32Args {
 hipError_t launch_expert_up_f32(const GemmF32Args& a, hipStream_t s);
 hipError_t launch_expert_down_f32(const GemmF32Args& a, hipStream_t s);
 
-// Gather: y[t] = sum_{j < nrow} ow[t*nrow + j], written as bf16 or fp32 (nrow = slots x K splits).
-hipError_t launch_combine(const float* ow, int T, int nrow, int d, void* y, bool y_bf16, hipStream_t s);
+// Gather: y[t] = sum_{j < nrow} ow[t*stride + j], written as bf16 or fp32 (rows: slots x K
+// splits; stride >= nrow rows per token).
+hipError_t launch_combine(const float* ow, int T, int nrow, int stride, int d, void* y, bool y_bf16,
+                          hipStream_t s);
 
 // Create-time repacking into fragment order (see pack.hip).
 hipError_t pack_router(const float* wr, const float* ws_gate_vec, int d, int E, float* wr_t, hipStream_t s);
@@ -158,48 +161,14 @@ struct Tile {
 // tile_start[e] = sum of ceil(n_e' / bm) over e' < e; it and offsets are read
 // from device memory (the scatter just wrote them), so the grid is launched for
 // an upper bound and idle workgroups return at once.
-__device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ ts, const int32_t* __restrict__ offs,
-                                            int Et, int NT, int GN, int bm, Tile& tl) {
+__device__ __forceinline__ bool decode_tile_at(const int32_t* __restrict__ ts, const int32_t* __restrict__ offs,
+                                               int Ecount, int NT, int GN, int bm, int S, int i, Tile& tl,
+                                               int& split) {
+    // i: the workgroup's index in the launch, dealt to XCD i % 8; S K-splits of every tile
+    // (logical index = tile * S + split), the XCD remap applied to the combined index
     const int NTp = (NT + GN - 1) / GN * GN;
-    const int total = ts[Et] * NTp;
+    const int total = ts[Ecount] * NTp * S;
     const int per = (total + kXcds - 1) / kXcds;
-    const int i = blockIdx.x;
-    const int slot = i / kXcds, xcd = i % kXcds;
-    if (slot >= per) return false;
-    const int L = xcd * per + slot;
-    if (L >= total) return false;
-    const int lane = threadIdx.x % kWave;
-    int c = 0;
-    for (int j0 = 0; j0 <= Et; j0 += kWave) {
-        const int j = j0 + lane;
-        const bool ok = j <= Et && ts[j] * NTp <= L;
-        c += __popcll(__ballot(ok));
-    }
-    const int e = c - 1;
-    const int t0 = ts[e], mt = ts[e + 1] - t0;
-    const int local = L - t0 * NTp;
-    const int grp = local / (mt * GN);
-    const int rem = local - grp * mt * GN;
-    const int m = rem / GN;
-    const int n = grp * GN + (rem - m * GN);
-    if (n >= NT) return false;
-    tl.e = e;
-    tl.n = n;
-    tl.g = t0 + m;
-    tl.row0 = m * bm;
-    tl.seg0 = offs[e];
-    tl.rows = min(bm, offs[e + 1] - tl.seg0 - tl.row0);
-    return true;
-}
-
-// decode_tile over S K-splits of every tile: logical index = tile * S + split,
-// with the XCD remap applied to the combined index.
-__device__ __forceinline__ bool decode_tile_split(const int32_t* __restrict__ ts, const int32_t* __restrict__ offs,
-                                                  int Et, int NT, int GN, int bm, int S, Tile& tl, int& split) {
-    const int NTp = (NT + GN - 1) / GN * GN;
-    const int total = ts[Et] * NTp * S;
-    const int per = (total + kXcds - 1) / kXcds;
-    const int i = blockIdx.x;
     const int slot = i / kXcds, xcd = i % kXcds;
     if (slot >= per) return false;
     const int L = xcd * per + slot;
@@ -208,9 +177,9 @@ __device__ __forceinline__ bool decode_tile_split(const int32_t* __restrict__ ts
     split = L - Lt * S;
     const int lane = threadIdx.x % kWave;
     int c = 0;
-    for (int j0 = 0; j0 <= Et; j0 += kWave) {
+    for (int j0 = 0; j0 <= Ecount; j0 += kWave) {
         const int j = j0 + lane;
-        const bool ok = j <= Et && ts[j] * NTp <= Lt;
+        const bool ok = j <= Ecount && ts[j] * NTp <= Lt;
         c += __popcll(__ballot(ok));
     }
     const int e = c - 1;
@@ -228,6 +197,47 @@ __device__ __forceinline__ bool decode_tile_split(const int32_t* __restrict__ ts
     tl.seg0 = offs[e];
     tl.rows = min(bm, offs[e + 1] - tl.seg0 - tl.row0);
     return true;
+}
+
+__device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ ts, const int32_t* __restrict__ offs,
+                                            int Et, int NT, int GN, int bm, Tile& tl) {
+    int split;
+    return decode_tile_at(ts, offs, Et, NT, GN, bm, 1, blockIdx.x, tl, split);
+}
+
+// decode_tile over S K-splits of every tile.
+__device__ __forceinline__ bool decode_tile_split(const int32_t* __restrict__ ts, const int32_t* __restrict__ offs,
+                                                  int Et, int NT, int GN, int bm, int S, Tile& tl, int& split) {
+    return decode_tile_at(ts, offs, Et, NT, GN, bm, S, blockIdx.x, tl, split);
+}
+
+// Down projection with the shared expert's V slices merged into one K = V*F sum per
+// tile: workgroups 0 .. mtv*NT-1 take the row tiles of the first slice (expert E0, all
+// slices hold the same rows), one per XCD in turn and launched first (each runs V times
+// longer than a routed tile); the rest, from the next multiple of 8, take the routed
+// experts' tiles through decode_tile_at. *kv = V for a merged tile, 1 otherwise.
+__device__ __forceinline__ bool decode_tile_down_merged(const int32_t* __restrict__ ts,
+                                                        const int32_t* __restrict__ offs, int E0, int V, int NT,
+                                                        int GN, int bm, Tile& tl, int& kv) {
+    const int mtv = ts[E0 + 1] - ts[E0];
+    const int nlong = mtv * NT;
+    const int i = blockIdx.x;
+    if (i < nlong) {
+        const int m = i / NT;
+        tl.e = E0;
+        tl.n = i - m * NT;
+        tl.g = ts[E0] + m;
+        tl.row0 = m * bm;
+        tl.seg0 = offs[E0];
+        tl.rows = min(bm, offs[E0 + 1] - tl.seg0 - tl.row0);
+        kv = V;
+        return true;
+    }
+    const int first = (nlong + kXcds - 1) / kXcds * kXcds;  // keeps i % 8 the XCD of the remap
+    if (i < first) return false;
+    int split;
+    kv = 1;
+    return decode_tile_at(ts, offs, E0, NT, GN, bm, 1, i - first, tl, split);
 }
 
 }  // namespace moe

@@ -124,7 +124,11 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
     const int S = UP ? 1 : a.ksplit;
     Tile tl;
     int split = 0;
-    {
+    int kv = 1;  // shared slices this tile sums as one K (merged shared down projection)
+    if (!UP && a.merge_shared) {
+        if (!decode_tile_down_merged(a.tile_start, a.offsets, a.Et - (a.kt - a.k), a.kt - a.k, NT, GN, BM, tl, kv))
+            return;
+    } else {
         // split-K: logical tile index = tile * S + split
         if (!decode_tile_split(a.tile_start, a.offsets, a.Et, NT, GN, BM, S, tl, split)) return;
     }
@@ -162,6 +166,17 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
         const bf16_t* wb = (const bf16_t*)(UP ? a.wgu : a.wdn) + (size_t)tl.e * N * K;
         b_src = reinterpret_cast<const u32x4*>(wb) + kbase / 32 * 64;
     }
+    // A merged tile runs kv * KBv K steps: step kt is step kt % KBv of slice kt / KBv, whose
+    // A rows (the same tokens) and weights lie a fixed stride further on (slices are
+    // consecutive virtual experts with equal row-tile counts). kt / KBv by a multiply with
+    // ceil(2^32 / KBv), exact for kt * KBv < 2^32.
+    const uint32_t KBv = Kpart / BK;
+    const uint64_t kb_magic = ((1ull << 32) + KBv - 1) / KBv;
+    size_t strideA = 0, strideB = 0;
+    if (!UP && kv > 1) {
+        strideA = (size_t)(a.tile_start[tl.e + 1] - a.tile_start[tl.e]) * (BM / 16) * KA * 512;
+        strideB = (size_t)N * K / 8;  // one expert's weights in 16-byte units (bf16)
+    }
     // NA: how many of this wave's A block loads are made. Load i fills row block
     // (wave + NW*i) / KH, read only by the waves of row group (that block) / MWB; a block
     // whose readers hold no rows (past the expert's last row) is not loaded. Blocks grow
@@ -169,18 +184,25 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
     auto issue = [&](int kt, int stage, auto na) {
         constexpr int NA = decltype(na)::value;
         u32x4* st = lds + (size_t)stage * STAGE * 64;
+        size_t oa = 0, ob = 0;
+        if constexpr (!UP) {
+            const uint32_t v = (uint32_t)(((uint64_t)(uint32_t)kt * kb_magic) >> 32);
+            kt -= (int)(v * KBv);
+            oa = v * strideA;
+            ob = v * strideB;
+        }
 #pragma unroll
-        for (int i = 0; i < NA; ++i) dma16(a_blk[i] + (size_t)kt * KH * 512, st + (wave + kWaves * i) * 64);
+        for (int i = 0; i < NA; ++i) dma16(a_blk[i] + oa + (size_t)kt * KH * 512, st + (wave + kWaves * i) * 64);
 #pragma unroll
         for (int j = 0; j < BW; ++j) {
             const int blk = wave * BW + j;  // bf16: n-block blk / KH, K half blk % KH; int8: n-block blk
             if constexpr (INT8) {
                 const int nbg = min(tl.n * (BN / 16) + blk, NB16 - 1);
-                dma16(b_src + ((size_t)nbg * (K / 64) + kt) * 64 + lane, st + (ABLK + blk) * 64);
+                dma16(b_src + ob + ((size_t)nbg * (K / 64) + kt) * 64 + lane, st + (ABLK + blk) * 64);
             } else {
                 const int nb = blk / KH, kh = blk % KH;
                 const int nbg = min(tl.n * (BN / 16) + nb, NB16 - 1);
-                dma16(b_src + ((size_t)nbg * KS + kt * KH + kh) * 64 + lane, st + (ABLK + blk) * 64);
+                dma16(b_src + ob + ((size_t)nbg * KS + kt * KH + kh) * 64 + lane, st + (ABLK + blk) * 64);
             }
         }
     };
@@ -191,7 +213,7 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < NBW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int KT = Kpart / BK;
+    const int KT = kv * (Kpart / BK);
     {
         // Fragments are double-buffered in registers: the LDS reads of K step kt+1 are
         // issued before the MFMAs of step kt, so LDS latency hides under the MFMAs.
@@ -390,8 +412,10 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
     const int Kpart = (UP ? a.d : a.F) / S;
     if (Kpart % 64 != 0 || Kpart < 64) return hipErrorInvalidValue;  // whole K steps of 64 (int8) or 2 x 32
     const int NTp = ((N + BN - 1) / BN + GN - 1) / GN * GN;
-    // a multiple of 8 workgroups, so every XCD gets ceil(tiles / 8) slots
-    dim3 grid((unsigned)(((size_t)a.max_tiles * NTp * S + kXcds - 1) / kXcds * kXcds));
+    // a multiple of 8 workgroups, so every XCD gets ceil(tiles / 8) slots (a merged shared
+    // down projection starts its routed tiles at the next multiple of 8 after its own)
+    const size_t blocks = (size_t)a.max_tiles * NTp * S + (!UP && a.merge_shared ? 2 * kXcds : 0);
+    dim3 grid((unsigned)((blocks + kXcds - 1) / kXcds * kXcds));
     hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds_bytes, s, a);
     return hipGetLastError();
 }

@@ -308,7 +308,10 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
     // upper bound on sum_e ceil(n_e / bm) over experts with rows
     const int P = T * L->kt;
     const int max_tiles = streaming ? std::min(L->Et, P) : (P + bm - 1) / bm + std::min(L->Et, P);
-    const GemmArgs a{L->tile_start, L->offsets, L->sorted_c, L->Et, L->kt, k, max_tiles, bm, ksplit,
+    // tiled down projection of a shared expert in several slices: the slices of a row tile
+    // are summed in one K loop (one partial row per token instead of one per slice)
+    const bool merge = !f32 && !streaming && !i8 && L->V > 1 && ksplit == 1;
+    const GemmArgs a{L->tile_start, L->offsets, L->sorted_c, L->Et, L->kt, k, max_tiles, bm, ksplit, merge ? 1 : 0,
                      (const bf16_t*)x, L->xp, (bf16_t*)L->h, L->wgu, L->wdn, L->s_gate, L->s_up, L->s_down,
                      r->topk_w, gs, L->ow, d.d_model, d.d_ff};
     // Routing for decode batches: up to 16 router columns, one workgroup reads the whole
@@ -356,7 +359,7 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
         }
     }
     if (prof) HIP_TRY(hipEventRecord(L->ev[4], s));
-    HIP_TRY(launch_combine(L->ow, T, L->kt * ksplit, d.d_model, y, !f32, s));
+    HIP_TRY(launch_combine(L->ow, T, (merge ? k + 1 : L->kt) * ksplit, L->kt * ksplit, d.d_model, y, !f32, s));
     if (prof) {
         HIP_TRY(hipEventRecord(L->ev[5], s));
         L->ran = true;
