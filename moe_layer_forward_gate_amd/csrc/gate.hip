@@ -176,35 +176,45 @@ __global__ __launch_bounds__(256) void gate_rowdot(const XT* __restrict__ x, con
 }
 
 // ---------------------------------------------------------------- prefill path, bf16 tokens
-// 16 tokens per workgroup; wave v takes the K quarter [v*d/4, (v+1)*d/4) and all
-// 16-column router blocks (NB = ceil(Ec/16) <= 9). A fragments come straight from
-// the token rows, B fragments from the three packed planes ([plane][NB][d/32][64]
-// lanes x 16 B, fragment order). The four wave partials are added in LDS.
-template <int NB>
+// 16*TB tokens per workgroup; wave v takes the K quarter [v*d/4, (v+1)*d/4) and all
+// 16-column router blocks (NB = ceil(Ec/16) <= 9) for all TB token blocks, so every
+// router fragment it loads serves TB MFMAs (the router is re-read once per workgroup:
+// TB sets how many tokens share that read). A fragments come straight from the token
+// rows, B fragments from the three packed planes ([plane][NB][d/32][64] lanes x 16 B,
+// fragment order). The four wave partials are added in LDS one token block at a time.
+template <int NB, int TB>
 __global__ __launch_bounds__(256) void gate_mfma(const bf16_t* __restrict__ x, const u32x4* __restrict__ planes,
                                                  const float* __restrict__ bias, int T, int d, int E, int k,
                                                  bool has_shared, int32_t* __restrict__ idx, float* __restrict__ w,
                                                  float* __restrict__ gs) {
     constexpr int LP = NB * 16 + 1;
     __shared__ float part[4][16 * LP];
-    const int t0 = blockIdx.x * 16;
+    __shared__ float logits[16 * TB * LP];
+    const int t0 = blockIdx.x * 16 * TB;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int KS = d / 32;
     const int ks0 = wave * (KS / 4), ks1 = (wave == 3) ? KS : ks0 + KS / 4;
-    const int tok = min(t0 + lane % 16, T - 1);  // rows past T repeat the last token (dropped below)
-    const bf16_t* xr = x + (size_t)tok * d + 8 * (lane / 16);
-    const size_t plane_stride = (size_t)NB * KS * 64;
-    f32x4 acc[NB];
+    const bf16_t* xr[TB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tb = 0; tb < TB; ++tb) {
+        const int tok = min(t0 + 16 * tb + lane % 16, T - 1);  // rows past T repeat the last token (dropped)
+        xr[tb] = x + (size_t)tok * d + 8 * (lane / 16);
+    }
+    const size_t plane_stride = (size_t)NB * KS * 64;
+    f32x4 acc[TB][NB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[tb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     // U K-steps per round, every load of the round issued before the first MFMA
-    constexpr int U = NB <= 2 ? 8 : (NB <= 4 ? 4 : 2);
+    constexpr int U = NB * TB <= 2 ? 8 : (NB * TB <= 4 ? 4 : (NB * TB <= 12 ? 2 : 1));
     auto round = [&](int ks, auto uconst) {
         constexpr int UU = decltype(uconst)::value;
-        u32x4 av[UU], bv[UU][NB][3];
+        u32x4 av[UU][TB], bv[UU][NB][3];
 #pragma unroll
         for (int u = 0; u < UU; ++u) {
-            av[u] = *reinterpret_cast<const u32x4*>(xr + (ks + u) * 32);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) av[u][tb] = *reinterpret_cast<const u32x4*>(xr[tb] + (ks + u) * 32);
 #pragma unroll
             for (int j = 0; j < NB; ++j)
 #pragma unroll
@@ -214,32 +224,37 @@ __global__ __launch_bounds__(256) void gate_mfma(const bf16_t* __restrict__ x, c
 #pragma unroll
         for (int u = 0; u < UU; ++u)
 #pragma unroll
-            for (int j = 0; j < NB; ++j)
+            for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-                for (int pl = 2; pl >= 0; --pl)  // smallest plane first
-                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u]),
-                                                                     __builtin_bit_cast(bf16x8, bv[u][j][pl]), acc[j],
-                                                                     0, 0, 0);
+                for (int j = 0; j < NB; ++j)
+#pragma unroll
+                    for (int pl = 2; pl >= 0; --pl)  // smallest plane first
+                        acc[tb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, av[u][tb]), __builtin_bit_cast(bf16x8, bv[u][j][pl]),
+                            acc[tb][j], 0, 0, 0);
     };
     int ks = ks0;
     for (; ks + U <= ks1; ks += U) round(ks, std::integral_constant<int, U>{});
     for (; ks < ks1; ++ks) round(ks, std::integral_constant<int, 1>{});
-    // lane holds column 16*j + lane%16, tokens 4*(lane/16) + i
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) part[wave][(4 * (lane / 16) + i) * LP + 16 * j + lane % 16] = acc[j][i];
-    __syncthreads();
+    // lane holds column 16*j + lane%16, tokens 4*(lane/16) + i of each token block
     const int Ec = E + (has_shared ? 1 : 0);
-    for (int q = tid; q < 16 * Ec; q += 256) {
-        const int r = q / Ec, col = q - r * Ec;
-        const float b = (bias && col < E) ? bias[col] : 0.0f;
-        const int o = r * LP + col;
-        part[0][o] = (part[0][o] + part[1][o]) + (part[2][o] + part[3][o]) + b;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part[wave][(4 * (lane / 16) + i) * LP + 16 * j + lane % 16] = acc[tb][j][i];
+        __syncthreads();
+        for (int q = tid; q < 16 * Ec; q += 256) {
+            const int r = q / Ec, col = q - r * Ec;
+            const float b = (bias && col < E) ? bias[col] : 0.0f;
+            const int o = r * LP + col;
+            logits[tb * 16 * LP + o] = (part[0][o] + part[1][o]) + (part[2][o] + part[3][o]) + b;
+        }
+        __syncthreads();
     }
-    __syncthreads();
-    for (int r = wave; r < 16; r += 4)
-        if (t0 + r < T) wave_topk_write(part[0] + r * LP, E, k, has_shared, t0 + r, idx, w, gs);
+    for (int r = wave; r < 16 * TB; r += 4)
+        if (t0 + r < T) wave_topk_write(logits + r * LP, E, k, has_shared, t0 + r, idx, w, gs);
 }
 
 // ---------------------------------------------------------------- prefill path, fp32 tokens
@@ -542,6 +557,32 @@ __global__ __launch_bounds__(1024) void gate_finish(const float* __restrict__ pa
     scatter_block<NW>(ids, T, E, k, V, bm, o, sm);
 }
 
+template <int TB>
+hipError_t launch_gate_mfma_tb(int NB, const bf16_t* x, const u32x4* planes, const float* bias, int T, int d, int E,
+                               int k, bool has_shared, int32_t* idx, float* w, float* gs, hipStream_t s) {
+    dim3 grid((T + 16 * TB - 1) / (16 * TB));
+    switch (NB) {
+#define GATE_MFMA_CASE(J)                                                                                          \
+    case J:                                                                                                        \
+        hipLaunchKernelGGL((gate_mfma<J, TB>), grid, dim3(256), 0, s, x, planes, bias, T, d, E, k, has_shared, idx, \
+                           w, gs);                                                                                 \
+        break;
+        GATE_MFMA_CASE(1) GATE_MFMA_CASE(2) GATE_MFMA_CASE(3) GATE_MFMA_CASE(4) GATE_MFMA_CASE(5)
+        GATE_MFMA_CASE(6) GATE_MFMA_CASE(7) GATE_MFMA_CASE(8) GATE_MFMA_CASE(9)
+#undef GATE_MFMA_CASE
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gate_mfma_nb(int TB, int NB, const bf16_t* x, const u32x4* planes, const float* bias, int T, int d,
+                               int E, int k, bool has_shared, int32_t* idx, float* w, float* gs, hipStream_t s) {
+    if (TB == 4) return launch_gate_mfma_tb<4>(NB, x, planes, bias, T, d, E, k, has_shared, idx, w, gs, s);
+    if (TB == 2) return launch_gate_mfma_tb<2>(NB, x, planes, bias, T, d, E, k, has_shared, idx, w, gs, s);
+    return launch_gate_mfma_tb<1>(NB, x, planes, bias, T, d, E, k, has_shared, idx, w, gs, s);
+}
+
 template <typename XT>
 hipError_t launch_gate_t(const XT* x, const float* wr_t, const u32x4* planes, const float* bias, int T, int d, int E,
                          bool has_shared, int k, int32_t* idx, float* w, float* gs, hipStream_t s) {
@@ -550,20 +591,14 @@ hipError_t launch_gate_t(const XT* x, const float* wr_t, const u32x4* planes, co
         hipLaunchKernelGGL((gate_rowdot<XT>), dim3(T), dim3(256), 0, s, x, wr_t, bias, d, E, Ec, k, has_shared, idx, w,
                            gs);
     } else if (planes != nullptr && (d / 32) >= 4) {
-        const int NB = (Ec + 15) / 16;
-        dim3 grid((T + 15) / 16);
-        switch (NB) {
-#define GATE_MFMA_CASE(J)                                                                                     \
-    case J:                                                                                                   \
-        hipLaunchKernelGGL((gate_mfma<J>), grid, dim3(256), 0, s, (const bf16_t*)x, planes, bias, T, d, E, k, \
-                           has_shared, idx, w, gs);                                                           \
-        break;
-            GATE_MFMA_CASE(1) GATE_MFMA_CASE(2) GATE_MFMA_CASE(3) GATE_MFMA_CASE(4) GATE_MFMA_CASE(5)
-            GATE_MFMA_CASE(6) GATE_MFMA_CASE(7) GATE_MFMA_CASE(8) GATE_MFMA_CASE(9)
-#undef GATE_MFMA_CASE
-            default:
-                return hipErrorInvalidValue;
-        }
+        // token blocks per workgroup: as many as keep >= 256 workgroups (up to 4)
+#ifdef MOE_GATE_TB
+        const int TB = MOE_GATE_TB;
+#else
+        const int TB = T >= 16 * 4 * 256 ? 4 : (T >= 16 * 2 * 256 ? 2 : 1);
+#endif
+        return launch_gate_mfma_nb(TB, (Ec + 15) / 16, (const bf16_t*)x, planes, bias, T, d, E, k, has_shared, idx, w,
+                                   gs, s);
     } else {
         const int EJ = (Ec + 15) / 16;
         dim3 grid((T + kTB - 1) / kTB);
