@@ -50,6 +50,11 @@ struct ScatterOut {
 };
 hipError_t launch_scatter(const int32_t* idx, int T, int E, int k, int V, int bm, const ScatterOut& o,
                           hipStream_t s);
+// The same scatter over many workgroups (three launches), for large T*k; `work` holds
+// scatter_wide_workspace(T*k, E) bytes.
+size_t scatter_wide_workspace(int N, int E);
+hipError_t launch_scatter_wide(const int32_t* idx, int T, int E, int k, int V, int bm, const ScatterOut& o,
+                               int32_t* work, hipStream_t s);
 // Gate then Scatter for decode batches (T <= 64, k <= 8) in two launches: partial router
 // dots over (16-column block, 128-wide K slice) workgroups into `part`
 // (gate_split_workspace bytes), then one workgroup for the sums, top-k and scatter.

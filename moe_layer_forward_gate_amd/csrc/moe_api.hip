@@ -60,6 +60,7 @@ struct moe_layer {
     int32_t* sorted_c = nullptr;
     float* gs = nullptr;
     float* gate_part = nullptr;  // partial router dots of the split decode gate
+    int32_t* scatter_work = nullptr;  // chunk counts and ranks of the multi-workgroup scatter
     bf16_t* xp = nullptr;  // tiled up operand (bf16/int8 experts)
     void* h = nullptr;
     float* ow = nullptr;
@@ -75,7 +76,7 @@ namespace {
 void release(moe_layer* L) {
     if (!L) return;
     void* bufs[] = {L->wr_t, L->wr_planes, L->bias, L->wgu, L->wdn, L->s_gate, L->s_up, L->s_down, L->counts, L->offsets,
-                    L->tile_start, L->sorted_c, L->gs, L->gate_part, L->xp, L->h, L->ow};
+                    L->tile_start, L->sorted_c, L->gs, L->gate_part, L->scatter_work, L->xp, L->h, L->ow};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
     for (hipEvent_t e : L->ev)
@@ -168,6 +169,7 @@ int create_impl(const moe_desc* desc, const moe_weights* w, moe_layer* L) {
     if ((rc = dev_alloc(&L->gate_part, gate_split_workspace((int)std::min(T, (size_t)64), d.d_model, L->E,
                                                              d.shared_d_ff > 0))))
         return rc;
+    if ((rc = dev_alloc(&L->scatter_work, scatter_wide_workspace((int)(T * d.top_k), L->E)))) return rc;
     // the tiled GEMMs work on padded rows: at most P + (bm - 1) + Et*bm of them for bm <= 256
     const size_t R = P + (size_t)256 * (Et + 1);
     if (!f32 && (rc = dev_alloc(&L->xp, R * dm * 2))) return rc;
@@ -333,7 +335,14 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
         HIP_TRY(launch_gate(x, !f32, L->wr_t, L->wr_planes, L->bias, T, d.d_model, L->E, L->V > 0, k, r->topk_idx,
                             r->topk_w, gs, s));
         if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
-        HIP_TRY(launch_scatter(r->topk_idx, T, L->E, k, L->V, bm, so, s));
+#ifndef MOE_SCATTER_WIDE_MIN
+#define MOE_SCATTER_WIDE_MIN 4095
+#endif
+        // many assignments: the scatter over many workgroups (three launches)
+        if (T * k > MOE_SCATTER_WIDE_MIN)
+            HIP_TRY(launch_scatter_wide(r->topk_idx, T, L->E, k, L->V, bm, so, L->scatter_work, s));
+        else
+            HIP_TRY(launch_scatter(r->topk_idx, T, L->E, k, L->V, bm, so, s));
     }
     // the tiled GEMMs take the token rows already gathered into fragment order
     if (!f32 && !streaming) HIP_TRY(launch_pack_a(a, s));

@@ -54,7 +54,133 @@ __global__ __launch_bounds__(256) void pack_a_kernel(GemmArgs a) {
     for (int i = 0; i < 4; ++i) dst[i * 64] = v[i];
 }
 
+// ---- the scatter over many workgroups, for large batches: three launches
+// count: chunk c (kChunk assignments, one per lane of 16 waves) -- per-wave ranks from
+//   ballots over the expert-id bits, per-wave counts, their prefix over the chunk's
+//   waves; writes cnt[c][e] and each assignment's rank inside its chunk;
+// scan: one workgroup turns cnt[.][e] into each chunk's offset within expert e (in place,
+//   chunk order), and builds counts, offsets and the tile table as scatter_block does;
+// place: sorted position = offsets[e] + chunk offset + rank inside the chunk.
+// The result is the same unique stable order.
+constexpr int kChunk = 1024;
+
+__global__ __launch_bounds__(1024) void scatter_count(const int32_t* __restrict__ idx, int N, int E,
+                                                     int32_t* __restrict__ cnt, int32_t* __restrict__ lrank) {
+    __shared__ int hist[16][kMaxExperts];
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    for (int i = tid; i < 16 * E; i += 1024) hist[i / E][i % E] = 0;
+    const int a = blockIdx.x * kChunk + tid;
+    const bool valid = a < N;
+    const int e = valid ? idx[a] : 0;
+    __syncthreads();
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 7; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t bb = __ballot(valid && bit);
+        same &= bit ? bb : ~bb;
+    }
+    const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (kWave - lane));
+    const int rank = __popcll(same & lt_mask);
+    if (valid && rank == 0) hist[wave][e] = __popcll(same);  // the group's lowest lane
+    __syncthreads();
+    if (tid < E) {
+        int run = 0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+            const int h = hist[w][tid];
+            hist[w][tid] = run;
+            run += h;
+        }
+        cnt[(size_t)blockIdx.x * E + tid] = run;
+    }
+    __syncthreads();
+    if (valid) lrank[a] = hist[wave][e] + rank;
+}
+
+__global__ __launch_bounds__(1024) void scatter_scan(int N, int T, int E, int V, int bm, int C,
+                                                    int32_t* __restrict__ cnt, ScatterOut o) {
+    __shared__ int ecnt[kMaxEt];
+    __shared__ int offs[kMaxEt + 1];
+    __shared__ int tiles[kMaxEt];
+    __shared__ int tstart[kMaxEt + 1];
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int Et = E + V;
+    if (tid < E) {
+        // chunk offsets within expert tid, in chunk order; loads go out 16 at a time
+        int run = 0;
+        for (int c0 = 0; c0 < C; c0 += 16) {
+            int v[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) v[q] = c0 + q < C ? cnt[(size_t)(c0 + q) * E + tid] : 0;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                if (c0 + q < C) cnt[(size_t)(c0 + q) * E + tid] = run;
+                run += v[q];
+            }
+        }
+        ecnt[tid] = run;
+    } else if (tid < Et) {
+        ecnt[tid] = T;  // shared virtual experts hold every token
+    }
+    __syncthreads();
+    if (wave == 0) wave_exclusive_scan(ecnt, Et, offs);
+    if (wave == 1)
+        for (int e = lane; e < Et; e += kWave) tiles[e] = (ecnt[e] + bm - 1) / bm;
+    __syncthreads();
+    if (wave == 1) wave_exclusive_scan(tiles, Et, tstart);
+    __syncthreads();
+    for (int e = tid; e <= Et; e += 1024) {
+        if (e < Et) o.counts[e] = ecnt[e];
+        o.offsets[e] = offs[e];
+        o.tile_start[e] = tstart[e];
+        if (e < E && o.user_counts) o.user_counts[e] = ecnt[e];
+        if (e <= E && o.user_offsets) o.user_offsets[e] = offs[e];
+    }
+}
+
+__global__ __launch_bounds__(256) void scatter_place(const int32_t* __restrict__ idx, int N, int T, int E, int k,
+                                                     int V, const int32_t* __restrict__ cnt,
+                                                     const int32_t* __restrict__ lrank, ScatterOut o) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    const int kt = k + V;
+    if (i < N) {
+        const int e = idx[i];
+        const int pos = o.offsets[e] + cnt[(size_t)(i / kChunk) * E + e] + lrank[i];
+        const int t = i / k, j = i - t * k;
+        o.sorted_c[pos] = t * kt + j;
+        if (o.user_sorted) o.user_sorted[pos] = i;
+    } else if (i < N + V * T) {
+        // shared virtual experts: every token, in order
+        const int q = i - N, v = q / T, t = q - v * T;
+        o.sorted_c[i] = t * kt + k + v;
+    }
+}
+
 }  // namespace
+
+size_t scatter_wide_workspace(int N, int E) {
+    const size_t C = ((size_t)N + kChunk - 1) / kChunk;
+    return (C * E + (size_t)N) * sizeof(int32_t);
+}
+
+hipError_t launch_scatter_wide(const int32_t* idx, int T, int E, int k, int V, int bm, const ScatterOut& o,
+                               int32_t* work, hipStream_t s) {
+    if (E > kMaxExperts || E + V > kMaxEt) return hipErrorInvalidValue;
+    const int N = T * k;
+    const int C = (N + kChunk - 1) / kChunk;
+    int32_t* cnt = work;
+    int32_t* lrank = work + (size_t)C * E;
+    hipLaunchKernelGGL(scatter_count, dim3(C), dim3(1024), 0, s, idx, N, E, cnt, lrank);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(scatter_scan, dim3(1), dim3(1024), 0, s, N, T, E, V, bm, C, cnt, o);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const int tot = N + V * T;
+    hipLaunchKernelGGL(scatter_place, dim3((tot + 255) / 256), dim3(256), 0, s, idx, N, T, E, k, V,
+                       (const int32_t*)cnt, (const int32_t*)lrank, o);
+    return hipGetLastError();
+}
 
 hipError_t launch_pack_a(const GemmArgs& a, hipStream_t s) {
     if (a.d % 128 || a.bm % 16) return hipErrorInvalidValue;
