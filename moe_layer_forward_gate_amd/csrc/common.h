@@ -104,7 +104,8 @@ hipError_t launch_expert_down_bf16(const GemmArgs& a, bool int8, hipStream_t s);
 // first one's rows for them). Reads the scatter's tile list on the device; writes
 // max_tiles*bm rows at most.
 hipError_t launch_pack_a(const GemmArgs& a, hipStream_t s);
-// Small-batch variants (a.bm = 16, 32 or 64 >= T, so each active expert is one row tile).
+// Small-batch variants (a.bm = 16, 32 or 64: an active expert usually fits one row tile;
+// one that does not takes several, each streaming the weights again).
 hipError_t launch_expert_up_stream(const GemmArgs& a, bool int8, hipStream_t s);
 hipError_t launch_expert_down_stream(const GemmArgs& a, bool int8, hipStream_t s);
 constexpr int kStreamMaxT = 64;     // largest T served by the streaming kernels

@@ -280,17 +280,21 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
 
 
     // Launch plan (host side, from T, k and the layer shape only):
-    //  - small batches (T <= 64) stream the weights: one row tile per active
-    //    expert (bm >= T), the down projection's K split so ~1024 workgroups run;
-    //  - larger batches use the LDS-tiled MFMA GEMMs, with tall 256-row tiles
-    //    when experts are expected to hold many rows and a 2-way K split of the
-    //    down projection when its column tiles alone would leave the GPU idle.
+    //  - small batches (T <= 64) stream the weights: row tiles of 16, 32 or 64 rows,
+    //    sized so an active expert almost always fits one tile, the down projection's K
+    //    split so ~1024 workgroups run;
+    //  - larger batches use the LDS-tiled MFMA GEMMs (256-row tiles for bf16 weights,
+    //    128 for int8), with a 2-way K split of the down projection when its tiles alone
+    //    would leave the GPU short of work.
     const bool streaming = !f32 && T <= kStreamMaxT;
     int bm, ksplit = 1;
     if (f32) {
         bm = kBMf32;
     } else if (streaming) {
-        bm = T <= 16 ? 16 : (T <= 32 ? 32 : 64);
+        // row tile: expected rows of the busiest expert (shared slices hold all T rows; routed
+        // experts about twice their average), so an expert rarely needs a second tile
+        const int need = L->V > 0 ? T : std::min(T, 2 * ((T * k + L->E - 1) / L->E));
+        bm = need <= 16 ? 16 : (need <= 32 ? 32 : 64);
         const int active = std::min(L->E, T * k) + L->V;
         const int groups = active * (d.d_model / 128);
         while (ksplit < kStreamMaxSplit && groups * ksplit < 1024 && d.d_ff % (ksplit * 2 * 64) == 0) ksplit *= 2;
