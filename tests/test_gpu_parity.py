@@ -123,3 +123,33 @@ def test_forward_argument_errors():
         lay.forward(xm)
     assert ei.value.status == moe.MOE_EINVAL
     lay.close()
+
+
+def test_hip_graph_replays_match_eager():
+    # moe_forward only enqueues kernels (no allocation, no host sync, no memset nodes), so it
+    # can be captured in a HIP graph; every replay, with eager work and synchronisations in
+    # between, must reproduce the eager result bit for bit (prefill and decode plans)
+    cfg = synth.get_config("shared_fine_bf16", d_model=256, d_ff=128, shared_d_ff=512)
+    L = synth.make_layer(cfg)
+    lay = gpu_layer(L, 300)
+    for T in (300, 3, 16):
+        x = synth.make_tokens(cfg, T).cuda()
+        ref = lay.forward(x, scatter=True)
+        torch.cuda.synchronize()
+        out = lay.outputs(T, scatter=True)
+        s = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            lay.forward(x, out=out, stream=s)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            for f in ("y", "topk_idx", "topk_w", "expert_counts", "expert_offsets", "sorted_assign", "shared_gate"):
+                getattr(out, f).fill_(-1) if getattr(out, f).dtype != torch.bfloat16 else getattr(out, f).fill_(7)
+            g.replay()
+            torch.cuda.synchronize()
+            for f in ("y", "topk_idx", "topk_w", "expert_counts", "expert_offsets", "sorted_assign", "shared_gate"):
+                assert torch.equal(getattr(out, f), getattr(ref, f)), (T, rep, f)
+            lay.forward(x[: max(1, T // 2)], scatter=True)  # eager work between replays
+            torch.cuda.synchronize()
+        del g
+    lay.close()
