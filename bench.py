@@ -105,7 +105,8 @@ def kernel_work(cfg, counts, T):
     up = dict(flops=2.0 * rows * d * 2 * F, bytes=up_w + T * d * aelt + rows * F * helt)
     dn = dict(flops=2.0 * rows * F * d, bytes=dn_w + rows * F * helt + rows * d * 4)
     layer_bytes = up_w + dn_w + d * cfg.n_experts * 4 + 2 * T * d * aelt + T * k * 8
-    layer_flops = 2.0 * T * d * cfg.n_experts + up["flops"] + dn["flops"]
+    # router GEMM (+ the shared gate's dot per token) and the two expert GEMMs
+    layer_flops = 2.0 * T * d * (cfg.n_experts + (1 if V else 0)) + up["flops"] + dn["flops"]
     return up, dn, dict(bytes=layer_bytes, flops=layer_flops, active=active)
 
 

@@ -1,0 +1,56 @@
+"""bench.py host logic on the CPU: the algorithmic work it prices the kernels with, and its
+single-GPU contract."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_decode_bytes_are_the_active_experts_weights():
+    # Mixtral-shaped layer, one token on two experts: 2 x 3 x 4096 x 14336 bf16 weights, plus
+    # the router (fp32), x and y, and the routing outputs
+    cfg = synth.get_config("mixtral_bf16")
+    counts = np.array([1, 0, 0, 1, 0, 0, 0, 0])
+    up, dn, layer = bench.kernel_work(cfg, counts, 1)
+    w = 2 * 3 * 4096 * 14336 * 2
+    assert layer["active"] == 2
+    assert layer["bytes"] == w + 4096 * 8 * 4 + 2 * 4096 * 2 + 2 * 8
+    assert up["bytes"] == 2 * 2 * 4096 * 14336 * 2 + 4096 * 2 + 2 * 14336 * 2
+    assert abs(layer["bytes"] / 1e9 - 0.705) < 1e-3
+
+
+def test_flops_match_the_closed_form():
+    # T (2 k 3 d F + 2 d E) routed, + T (6 d Fs + 2 d) for the shared expert
+    for name, T in (("mixtral_bf16", 4096), ("shared_fine_bf16", 2048), ("skewed_bf16", 8192)):
+        cfg = synth.get_config(name)
+        d, F, k, E, Fs = cfg.d_model, cfg.d_ff, cfg.top_k, cfg.n_experts, cfg.shared_d_ff
+        counts = np.ones(E, dtype=np.int64)
+        _, _, layer = bench.kernel_work(cfg, counts, T)
+        want = T * (2 * k * 3 * d * F + 2 * d * E) + (T * (6 * d * Fs + 2 * d) if Fs else 0)
+        assert layer["flops"] == want, name
+    cfg = synth.get_config("mixtral_bf16")
+    _, _, layer = bench.kernel_work(cfg, np.ones(8, dtype=np.int64), 4096)
+    assert abs(layer["flops"] / 1e12 - 2.886) < 1e-3
+
+
+def test_int8_bytes_count_scales():
+    cfg = synth.get_config("int8_mixtral22b")
+    counts = np.array([0, 1, 0, 0, 0, 0, 1, 0])
+    up, dn, _ = bench.kernel_work(cfg, counts, 1)
+    d, F = 6144, 16384
+    assert up["bytes"] == 2 * (2 * d * F * 1 + 2 * F * 4) + d * 2 + 2 * F * 2
+    assert dn["bytes"] == 2 * (F * d * 1 + d * 4) + 2 * F * 2 + 2 * d * 4
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=60)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
