@@ -154,9 +154,10 @@ MOE_API int moe_set_profiling(moe_layer* layer, int enable);
 /* Per-stage times in milliseconds of the last moe_forward that ran with
  * profiling on: ms[0] gate, ms[1] scatter (with the gathering of token rows
  * for the large-batch GEMMs), ms[2] expert up (gate/up GEMM and SiLU), ms[3]
- * expert down, ms[4] gather/combine. Where one kernel runs two stages (tiny
- * and decode batches route in the gate's launches), the time is booked on the
- * first and the next reads as the event overhead alone. Waits for that call's
+ * expert down, ms[4] gather/combine. Where the gate's launches also run the
+ * scatter (batches of up to four tokens; batches of up to 64 tokens with more
+ * than 16 router columns), its time is booked on the gate and the scatter
+ * reads as the event overhead alone. Waits for that call's
  * last event. EINVAL if no forward has run with profiling on. */
 MOE_API int moe_stage_times(moe_layer* layer, float ms[5]);
 
