@@ -51,6 +51,33 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Wave sums of N = 2^M values at once (a transposed butterfly: at each of the first M
+// steps a lane keeps half of its values and adds its partner's copy of them, then the
+// last 6-M steps fold single values): N - 1 + 6 - M shuffles instead of 6 N. Lane l
+// returns the sum of value l >> (6 - M).
+template <int N>
+__device__ __forceinline__ float wave_sum_many(float (&v)[N]) {
+    constexpr int M = N == 1 ? 0 : N == 2 ? 1 : N == 4 ? 2 : N == 8 ? 3 : N == 16 ? 4 : 5;
+    static_assert((1 << M) == N && N <= 32, "power of two up to 32");
+    const int lane = threadIdx.x % kWave;
+#pragma unroll
+    for (int s = 0; s < M; ++s) {
+        const int off = 32 >> s;
+        const bool upper = lane & off;
+#pragma unroll
+        for (int i = 0; i < (N >> (s + 1)); ++i) {
+            const int h = N >> (s + 1);
+            const float send = upper ? v[i] : v[i + h];
+            const float keep = upper ? v[i + h] : v[i];
+            v[i] = keep + __shfl_xor(send, off, kWave);
+        }
+    }
+    float r = v[0];
+#pragma unroll
+    for (int off = 32 >> M; off > 0; off >>= 1) r += __shfl_xor(r, off, kWave);
+    return r;
+}
+
 // One wave: top-k of logits[0..E) (bias already added), weights, shared gate.
 // `logits` may live in LDS; E <= 128, k <= 64.
 __device__ void wave_topk_write(const float* logits, int E, int k, bool has_shared, int t, int32_t* idx,
@@ -421,25 +448,33 @@ __global__ __launch_bounds__(1024) void gate_scatter_small(const XT* __restrict_
             wq[g][0] = p[0];
             wq[g][1] = p[1];
         }
+        // per token, RG dots at a time, each group folded with one transposed butterfly
+        constexpr int RG = 4;  // register budget at 1024 threads
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
             if (t < T) {
 #pragma unroll
-                for (int g = 0; g < EG; ++g) {
-                    float acc = 0.0f;
+                for (int g0 = 0; g0 < EG; g0 += RG) {
+                    float acc[RG];
 #pragma unroll
-                    for (int v = 0; v < 8; ++v) {
-                        float f;
-                        if constexpr (XQ == 1) {
-                            const uint32_t u = xq[t][0][v / 2];
-                            f = __uint_as_float((v & 1) ? (u & 0xFFFF0000u) : (u << 16));
-                        } else {
-                            f = __uint_as_float(xq[t][v / 4][v % 4]);
+                    for (int r = 0; r < RG; ++r) {
+                        float a = 0.0f;
+#pragma unroll
+                        for (int v = 0; v < 8; ++v) {
+                            float f;
+                            if constexpr (XQ == 1) {
+                                const uint32_t u = xq[t][0][v / 2];
+                                f = __uint_as_float((v & 1) ? (u & 0xFFFF0000u) : (u << 16));
+                            } else {
+                                f = __uint_as_float(xq[t][v / 4][v % 4]);
+                            }
+                            a = fmaf(f, __uint_as_float(wq[g0 + r][v / 4][v % 4]), a);
                         }
-                        acc = fmaf(f, __uint_as_float(wq[g][v / 4][v % 4]), acc);
+                        acc[r] = has ? a : 0.0f;
                     }
-                    const float sum = wave_sum(has ? acc : 0.0f);
-                    if (lane == 0 && e0 + g < Ec) part[wave][t * EC + e0 + g] = sum;
+                    const float sum = wave_sum_many<RG>(acc);  // lane l: column e0 + g0 + l / (64 / RG)
+                    const int g = g0 + lane / (64 / RG);
+                    if (lane % (64 / RG) == 0 && e0 + g < Ec) part[wave][t * EC + e0 + g] = sum;
                 }
             }
         }
