@@ -311,9 +311,11 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
     if ((size_t)T * L->kt * ksplit > L->ow_rows) ksplit = 1;  // never past the combine buffer
     ScatterOut so{L->counts, L->offsets, L->tile_start, L->sorted_c, r->expert_counts, r->expert_offsets,
                   r->sorted_assign};
-    // upper bound on sum_e ceil(n_e / bm) over experts with rows
+    // upper bound on sum_e ceil(n_e / bm) over experts with rows: one tile per active
+    // expert, plus sum_e floor((n_e - 1) / bm) <= floor((P - 1) / bm) more for experts past
+    // one tile (the streaming tile is sized to the expected busiest expert, not a bound)
     const int P = T * L->kt;
-    const int max_tiles = streaming ? std::min(L->Et, P) : (P + bm - 1) / bm + std::min(L->Et, P);
+    const int max_tiles = std::min(L->Et, P) + (P - 1) / bm;
     // tiled down projection of a shared expert in several slices: the slices of a row tile
     // are summed in one K loop (one partial row per token instead of one per slice)
     const bool merge = !f32 && !streaming && !i8 && L->V > 1 && ksplit == 1;

@@ -2,7 +2,8 @@
 
 Covers: k = 1 and k = E, expert counts that are not multiples of 8 or 16 (up to the
 128-expert limit), the smallest supported widths, T at the max_tokens bound and on
-both sides of the streaming / tiled switch, every token routed to one expert, a
+both sides of the streaming / tiled switch, every token routed to one expert, an
+expert holding more rows than the streaming row tile (more tiles than active experts), a
 shared expert of one and of sixteen d_ff slices, int8 output channels whose
 scale is zero, and the decode routing paths for routers wider than 16 columns.
 """
@@ -62,6 +63,18 @@ def test_every_token_on_one_expert():
         b[3] = 50.0
         L.b_router = b
     _run(synth.get_config("mixtral_bf16", d_model=256, d_ff=128), [1, 64, 1000], mutate=bias)
+
+
+@pytest.mark.parametrize("name", ["mixtral_bf16", "int8_mixtral22b"])
+def test_streaming_expert_past_one_tile(name):
+    # a bias of 2 on expert 3 puts it in slot 0 of (nearly) every token while the slot-1
+    # weights stay near 0.2: at T = 32 and 64 expert 3 holds T rows, twice the streaming
+    # row tile, so the tiles outnumber the active experts (9 against 8 for this draw)
+    def bias(L):
+        b = torch.zeros(L.cfg.n_experts, dtype=torch.float32)
+        b[3] = 2.0
+        L.b_router = b
+    _run(synth.get_config(name, d_model=256, d_ff=128), [32, 64], mutate=bias)
 
 
 @pytest.mark.parametrize("slices", [1, 16])
