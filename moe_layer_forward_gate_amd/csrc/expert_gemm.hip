@@ -224,18 +224,22 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
         using BFrag = std::conditional_t<INT8, u32x4, bf16x8>;  // int8 bytes are widened at use
         bf16x8 fa[2][MWB][KH];
         BFrag fb[2][NBW];
-        auto read_frags = [&](int stage, bf16x8 (&af)[MWB][KH], BFrag (&bq)[NBW]) {
+        // MA: row blocks of the wave that hold rows (a prefix); the others are neither read
+        // nor multiplied
+        auto read_frags = [&](int stage, bf16x8 (&af)[MWB][KH], BFrag (&bq)[NBW], auto ma) {
+            constexpr int MA = decltype(ma)::value;
             const u32x4* la = lds + (size_t)stage * STAGE * 64;
             const u32x4* lb = la + ABLK * 64;
 #pragma unroll
-            for (int mb = 0; mb < MWB; ++mb)
+            for (int mb = 0; mb < MA; ++mb)
 #pragma unroll
                 for (int kh = 0; kh < KH; ++kh)
                     af[mb][kh] = __builtin_bit_cast(bf16x8, la[((wm * MWB + mb) * KH + kh) * 64 + lane]);
 #pragma unroll
             for (int nb = 0; nb < NBW; ++nb) bq[nb] = __builtin_bit_cast(BFrag, lb[(wn * NBW + nb) * 64 + lane]);
         };
-        auto mfma_frags = [&](const bf16x8 (&af)[MWB][KH], const BFrag (&bq)[NBW]) {
+        auto mfma_frags = [&](const bf16x8 (&af)[MWB][KH], const BFrag (&bq)[NBW], auto ma) {
+            constexpr int MA = decltype(ma)::value;
             if constexpr (INT8) {
                 // column block outermost: each widened B fragment serves every row block
 #pragma unroll
@@ -246,12 +250,12 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
                         const bf16x8 bw = __builtin_bit_cast(bf16x8, kh ? i8x8_to_bf16x8(bq[nb].z, bq[nb].w)
                                                                         : i8x8_to_bf16x8(bq[nb].x, bq[nb].y));
 #pragma unroll
-                        for (int mb = 0; mb < MWB; ++mb)
+                        for (int mb = 0; mb < MA; ++mb)
                             acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb][kh], bw, acc[mb][nb], 0, 0, 0);
                     }
             } else {
 #pragma unroll
-                for (int mb = 0; mb < MWB; ++mb)
+                for (int mb = 0; mb < MA; ++mb)
 #pragma unroll
                     for (int nb = 0; nb < NBW; ++nb)
                         acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb][0], bq[nb], acc[mb][nb], 0, 0, 0);
@@ -262,26 +266,26 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
         // the last stage it re-loads the last stage into the free slot, which is never
         // read -- and reads the next step's fragments. Steps run in pairs so the register
         // buffer parity is static; one or two steps remain after the pairs.
-        // A wave whose 64 rows all lie past the expert's last row (the ragged last row
-        // tile) runs the same loop without fragment reads or MFMAs: it still loads its
-        // share of the tiles and meets every barrier.
-        auto run = [&](auto compute, auto nac) {
-            constexpr bool C = decltype(compute)::value;
+        // In the ragged last row tile of an expert a wave reads and multiplies only its
+        // row blocks that hold rows (MA of MWB; none when all its rows lie past the
+        // expert's last row): it still loads its share of the tiles and meets every barrier.
+        auto run = [&](auto ma, auto nac) {
+            constexpr bool C = decltype(ma)::value > 0;
             constexpr int L = decltype(nac)::value + BW;  // LDS-DMA loads per stage of this wave
             auto step = [&](int k, auto& ca, auto& cb, auto& na, auto& nb) {
                 wait_vm_le<(STAGES - 3) * L>();    // stage k+1 has landed
                 lds_barrier();                     // ... for every wave; stage k-1 is free
                 issue(min(k + STAGES - 1, KT - 1), (k + STAGES - 1) % STAGES, nac);
                 if constexpr (C) {
-                    read_frags((k + 1) % STAGES, na, nb);
-                    mfma_frags(ca, cb);
+                    read_frags((k + 1) % STAGES, na, nb, ma);
+                    mfma_frags(ca, cb, ma);
                 }
             };
 #pragma unroll
             for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(min(s0, KT - 1), s0, nac);
             wait_vm_le<(STAGES - 2) * L>();
             lds_barrier();
-            if constexpr (C) read_frags(0, fa[0], fb[0]);
+            if constexpr (C) read_frags(0, fa[0], fb[0], ma);
             int k = 0;
             for (; k + 2 < KT; k += 2) {
                 step(k, fa[0], fb[0], fa[1], fb[1]);
@@ -292,7 +296,7 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
             // not exist and is dropped)
             step(k, fa[0], fb[0], fa[1], fb[1]);
             if constexpr (C) {
-                if (!INT8 || KT - k == 2) mfma_frags(fa[1], fb[1]);
+                if (!INT8 || KT - k == 2) mfma_frags(fa[1], fb[1], ma);
             }
         };
         const bool has_rows = wm * MWB * 16 < tl.rows;
@@ -301,17 +305,33 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
         for (int i = 0; i < AW; ++i)
             if (((wave + kWaves * i) / KH / MWB) * MWB * 16 < tl.rows) nA = i + 1;
         static_assert(AW >= 1 && AW <= 2, "A loads per wave");
+        static_assert(MWB >= 2, "row blocks per wave");
         using I0 = std::integral_constant<int, 0>;
         using I1 = std::integral_constant<int, 1>;
         using I2 = std::integral_constant<int, AW>;  // == 2 when AW == 2
-        if (has_rows) {
-            if (nA == AW) run(std::true_type{}, I2{});
-            else if (nA == 1) run(std::true_type{}, I1{});
-            else run(std::true_type{}, I0{});
+        using MF = std::integral_constant<int, MWB>;
+        if constexpr (INT8) {
+            // row blocks holding rows: 0, 1, 2 or all (3 rounds up to all)
+            const int rw = tl.rows - wm * MWB * 16;
+            auto run_nac = [&](auto ma) {
+                if (nA == AW) run(ma, I2{});
+                else if (nA == 1) run(ma, I1{});
+                else run(ma, I0{});
+            };
+            if (rw > 32) run_nac(MF{});
+            else if (rw > 16) run_nac(std::integral_constant<int, 2>{});
+            else if (rw > 0) run_nac(std::integral_constant<int, 1>{});
+            else run_nac(I0{});
+        } else if (has_rows) {
+            // bf16 tiles are MFMA-bound and full but for each expert's last one, which is
+            // bound by its weight loads: all or none of a wave's row blocks
+            if (nA == AW) run(MF{}, I2{});
+            else if (nA == 1) run(MF{}, I1{});
+            else run(MF{}, I0{});
         } else {
-            if (nA == AW) run(std::false_type{}, I2{});
-            else if (nA == 1) run(std::false_type{}, I1{});
-            else run(std::false_type{}, I0{});
+            if (nA == AW) run(I0{}, I2{});
+            else if (nA == 1) run(I0{}, I1{});
+            else run(I0{}, I0{});
         }
         wait_vm_le<0>();  // no LDS-DMA write may outlive the workgroup
     }
