@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <new>
 
 #include "../../include/moe.h"
@@ -42,6 +43,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 struct moe_layer {
     moe_desc desc{};
     int device = 0;
+    int cus = 256;  // compute units of the device
     int E = 0, V = 0, Et = 0, kt = 0, Ec = 0;
     bool has_bias = false;
     // packed weights
@@ -144,6 +146,7 @@ int create_impl(const moe_desc* desc, const moe_weights* w, moe_layer* L) {
     L->Ec = L->E + (d.shared_d_ff > 0 ? 1 : 0);
     L->has_bias = w->b_router != nullptr;
     HIP_TRY(hipGetDevice(&L->device));
+    HIP_TRY(hipDeviceGetAttribute(&L->cus, hipDeviceAttributeMultiprocessorCount, L->device));
 
     const size_t dm = d.d_model, F = d.d_ff, E = L->E, Et = L->Et;
     const bool f32 = d.expert_dtype == MOE_F32;
@@ -303,10 +306,31 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
         // and outruns 128-row tiles even when most experts leave their last tile half empty);
         // int8: 128-row tiles (see the GEMM launcher)
         bm = i8 ? 128 : 256;
-        // split the down projection's K in two when its tiles alone fill the GPU less than
-        // ~8 workgroups per CU and K is long enough for both halves to stay efficient
-        const int est_tiles = (T * L->kt + bm - 1) / bm + std::min(L->Et, T * L->kt);
-        if (est_tiles * (d.d_model / 256) < 2048 && d.d_ff >= 4096 && d.d_ff % (2 * 64) == 0) ksplit = 2;
+        // split the down projection's K (S = 2 or 4) when that fills the last round of
+        // workgroups better: with W = tiles * column tiles * S workgroups, one per CU at a
+        // time, the busy fraction is W / (rounds * CUs); a split must gain 0.1 of it (the
+        // partial rows cost combine traffic), keep K >= 2048 per split and fit the combine
+        // buffer. The tile count is its expectation under uniform routing: a routed expert
+        // holds n ~ Binomial(T, k/E) rows (normal approximation) and needs
+        // ceil(n / bm) = sum_j [n > j*bm] tiles; a shared slice holds all T rows.
+        const double p_e = (double)k / L->E;
+        const double mu = T * p_e, sd = std::sqrt(std::max(T * p_e * (1.0 - p_e), 1e-12));
+        double tiles_e = 0.0;
+        for (int j = 0; j * bm < T; ++j) tiles_e += 0.5 * std::erfc((j * bm + 0.5 - mu) / (sd * std::sqrt(2.0)));
+        const double est_tiles = L->E * tiles_e + L->V * (double)((T + bm - 1) / bm);
+        const int nt_down = (d.d_model + 255) / 256;
+        auto busy = [&](int S) {
+            const double w = est_tiles * nt_down * S;
+            return w / (std::ceil(w / L->cus) * L->cus);
+        };
+        double best = busy(1);
+        for (int S = 2; S <= 4; S *= 2) {
+            if (d.d_ff / S < 2048 || d.d_ff % (S * 64) != 0 || (size_t)T * L->kt * S > L->ow_rows) break;
+            if (busy(S) > best + 0.1) {
+                best = busy(S);
+                ksplit = S;
+            }
+        }
     }
     if ((size_t)T * L->kt * ksplit > L->ow_rows) ksplit = 1;  // never past the combine buffer
     ScatterOut so{L->counts, L->offsets, L->tile_start, L->sorted_c, r->expert_counts, r->expert_offsets,
