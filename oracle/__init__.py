@@ -11,7 +11,8 @@ www.trdm.cn/news/555962, [pptc] www.pptc.cn/news/100465.
 
 Pinned (see tests/test_oracle.py): router logits, top-k selection and tie rule,
 top-k weights, shared-expert gate, scatter (counts, offsets, permutation),
-SwiGLU expert, combine, int8 dequantisation. No function is parity-unpinned.
+SwiGLU expert, combine, int8 dequantisation, the layer with a caller-given
+routing. No function is parity-unpinned.
 """
 from .moe_oracle import (
     router_logits,
@@ -24,11 +25,12 @@ from .moe_oracle import (
     swiglu_expert,
     valid_selections,
     moe_forward,
+    moe_forward_routed,
     OracleLayer,
 )
 
 __all__ = [
     "router_logits", "select_topk", "topk_weights", "shared_gate",
     "scatter_stable_sort", "scatter_counting", "dequantize", "swiglu_expert",
-    "valid_selections", "moe_forward", "OracleLayer",
+    "valid_selections", "moe_forward", "moe_forward_routed", "OracleLayer",
 ]

@@ -202,31 +202,13 @@ def valid_selections(logits_row, k: int, tol: float) -> list:
     return out
 
 
-def moe_forward(x, layer: OracleLayer, routing=None, tokens: Optional[Sequence[int]] = None):
-    """The whole layer ([hotelren §2.1] six steps; [0539edu §2.2] Gate -> Scatter
-    -> Expert Compute -> Gather).
-
-    x[T, d]. `routing` optionally replaces the top-k choice with an idx[T, k]
-    the caller built from this module's own valid_selections. `tokens`
-    optionally restricts the expert compute and combine to a subset of token
-    rows (the gate and scatter still cover all T tokens), so large batches can
-    be checked on a sample.
-
-    Returns a dict: logits, idx, margin, w, counts, offsets, sorted_assign,
-    g_s (or None), y (fp64, rows in `tokens` order when given).
-    """
-    x = _f64(x)
+def _experts_and_gather(x, layer: OracleLayer, idx, w, g_s, sorted_assign, offsets, tokens):
+    """Expert Compute and Gather for a routing already scattered: every expert's
+    token rows through its SwiGLU FFN, then y[t] = sum_j w[t, j] * o(t, j)
+    (+ g_s[t] * S(x[t])) ([hotelren §2.1] steps 4-6, §2.3 combine_kernel)."""
     T = x.shape[0]
-    k = layer.top_k
+    k = idx.shape[1]
     E = layer.n_experts
-    logits = router_logits(x, layer.w_router, layer.b_router)
-    idx, margin = select_topk(logits, k)
-    if routing is not None:
-        idx = np.asarray(routing, dtype=np.int64)
-    w = topk_weights(logits, idx)
-    counts, offsets, sorted_assign = scatter_stable_sort(idx, E)
-    g_s = shared_gate(x, layer.w_shared_gate) if layer.w_shared_gate is not None else None
-
     rows = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     row_of = {int(t): i for i, t in enumerate(rows)}
     y = np.zeros((rows.size, x.shape[1]))
@@ -245,5 +227,57 @@ def moe_forward(x, layer: OracleLayer, routing=None, tokens: Optional[Sequence[i
     if g_s is not None:
         s = swiglu_expert(x[rows], layer.ws_gate, layer.ws_up, layer.ws_down)
         y += g_s[rows, None] * s
+    return y
+
+
+def moe_forward(x, layer: OracleLayer, routing=None, tokens: Optional[Sequence[int]] = None):
+    """The whole layer ([hotelren §2.1] six steps; [0539edu §2.2] Gate -> Scatter
+    -> Expert Compute -> Gather).
+
+    x[T, d]. `routing` optionally replaces the top-k choice with an idx[T, k]
+    the caller built from this module's own valid_selections. `tokens`
+    optionally restricts the expert compute and combine to a subset of token
+    rows (the gate and scatter still cover all T tokens), so large batches can
+    be checked on a sample.
+
+    Returns a dict: logits, idx, margin, w, counts, offsets, sorted_assign,
+    g_s (or None), y (fp64, rows in `tokens` order when given).
+    """
+    x = _f64(x)
+    k = layer.top_k
+    E = layer.n_experts
+    logits = router_logits(x, layer.w_router, layer.b_router)
+    idx, margin = select_topk(logits, k)
+    if routing is not None:
+        idx = np.asarray(routing, dtype=np.int64)
+    w = topk_weights(logits, idx)
+    counts, offsets, sorted_assign = scatter_stable_sort(idx, E)
+    g_s = shared_gate(x, layer.w_shared_gate) if layer.w_shared_gate is not None else None
+
+    y = _experts_and_gather(x, layer, idx, w, g_s, sorted_assign, offsets, tokens)
     return dict(logits=logits, idx=idx, margin=margin, w=w, counts=counts,
                 offsets=offsets, sorted_assign=sorted_assign, g_s=g_s, y=y)
+
+
+def moe_forward_routed(x, layer: OracleLayer, idx, w, g_s=None, tokens: Optional[Sequence[int]] = None):
+    """The layer with the routing given instead of computed ([pptc §3.4]: the
+    engine consumes routing results made elsewhere, token-major [T][k]).
+
+    idx[T, k] int expert ids, w[T, k] weights used as given, g_s[T] the shared
+    expert's scale (layers with a shared expert). An id outside [0, E) is read
+    as expert 0 with weight 0 (the library's documented reading: it contributes
+    nothing). Returns a dict: idx, w (as read), counts, offsets, sorted_assign,
+    y (fp64, rows in `tokens` order when given).
+    """
+    x = _f64(x)
+    E = layer.n_experts
+    idx = np.asarray(idx, dtype=np.int64).copy()
+    w = _f64(w).copy()
+    bad = (idx < 0) | (idx >= E)
+    idx[bad] = 0
+    w[bad] = 0.0
+    if (layer.w_shared_gate is not None) != (g_s is not None):
+        raise ValueError("g_s is required exactly when the layer has a shared expert")
+    counts, offsets, sorted_assign = scatter_stable_sort(idx, E)
+    y = _experts_and_gather(x, layer, idx, w, None if g_s is None else _f64(g_s), sorted_assign, offsets, tokens)
+    return dict(idx=idx, w=w, counts=counts, offsets=offsets, sorted_assign=sorted_assign, y=y)

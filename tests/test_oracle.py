@@ -349,3 +349,74 @@ def test_skewed_routing_share():
     assert 0.85 <= top4 <= 0.95, top4
     assert (counts == 0).sum() >= 64
     assert counts.max() <= 8192
+
+
+# ---------------------------------------------------------------- routing given by the caller
+def _routed_bruteforce(x, lay, idx, w, g_s=None):
+    """Brute force of the routed layer: token by token, slot by slot, torch's
+    textbook SwiGLU of the slot's expert times the given weight; ids outside
+    [0, E) add nothing."""
+    x = np.asarray(x, dtype=np.float64)
+    E = lay.n_experts
+    y = np.zeros_like(x)
+    for t in range(x.shape[0]):
+        for j in range(idx.shape[1]):
+            e = int(idx[t, j])
+            if 0 <= e < E:
+                y[t] += w[t, j] * _torch_swiglu(x[t:t + 1], *lay.expert(e))[0]
+        if g_s is not None:
+            y[t] += g_s[t] * _torch_swiglu(x[t:t + 1], lay.ws_gate, lay.ws_up, lay.ws_down)[0]
+    return y
+
+
+@pytest.mark.parametrize("shared,int8", [(0, False), (16, False), (0, True)])
+def test_routed_bruteforce(shared, int8):
+    rng = np.random.default_rng(11)
+    d, E, F, k, T = 16, 6, 8, 3, 7
+    lay = _rand_layer(rng, d, E, F, k, shared=shared, int8=int8)
+    x = rng.standard_normal((T, d))
+    idx = rng.integers(-2, E + 2, size=(T, k))  # repeats and out-of-range ids included
+    w = rng.standard_normal((T, k))
+    g_s = rng.random(T) if shared else None
+    ref = oracle.moe_forward_routed(x, lay, idx, w, g_s)
+    np.testing.assert_allclose(ref["y"], _routed_bruteforce(x, lay, idx, w, g_s), rtol=1e-12, atol=1e-12)
+    # the scatter of the ids as read: every slot counted once, ids outside [0, E) under expert 0
+    read = np.where((idx < 0) | (idx >= E), 0, idx)
+    assert np.array_equal(ref["counts"], np.bincount(read.ravel(), minlength=E))
+    assert ref["offsets"][-1] == T * k
+    assert np.array_equal(ref["w"][(idx < 0) | (idx >= E)], np.zeros(int(((idx < 0) | (idx >= E)).sum())))
+
+
+def test_routed_repeated_expert_and_linearity():
+    rng = np.random.default_rng(12)
+    d, E, F, k, T = 16, 5, 8, 2, 4
+    lay = _rand_layer(rng, d, E, F, k)
+    x = rng.standard_normal((T, d))
+    # the same expert twice with weights a, b equals it once with a + b (the other slot at weight 0)
+    idx2 = np.array([[3, 3]] * T)
+    w2 = np.array([[0.25, 0.5]] * T)
+    idx1 = np.array([[3, 1]] * T)
+    w1 = np.array([[0.75, 0.0]] * T)
+    y2 = oracle.moe_forward_routed(x, lay, idx2, w2)["y"]
+    y1 = oracle.moe_forward_routed(x, lay, idx1, w1)["y"]
+    np.testing.assert_allclose(y2, y1, rtol=1e-12, atol=1e-12)
+    # linear in the weights; all-zero weights give y = 0
+    idx = rng.integers(0, E, size=(T, k))
+    w = rng.standard_normal((T, k))
+    ya = oracle.moe_forward_routed(x, lay, idx, w)["y"]
+    yb = oracle.moe_forward_routed(x, lay, idx, -2.5 * w)["y"]
+    np.testing.assert_allclose(yb, -2.5 * ya, rtol=1e-12, atol=1e-12)
+    assert not oracle.moe_forward_routed(x, lay, idx, 0 * w)["y"].any()
+
+
+def test_routed_with_the_gates_routing_is_the_layer():
+    rng = np.random.default_rng(13)
+    d, E, F, k, T = 16, 6, 8, 2, 9
+    lay = _rand_layer(rng, d, E, F, k, bias=True, shared=8)
+    x = rng.standard_normal((T, d))
+    ref = oracle.moe_forward(x, lay)
+    rt = oracle.moe_forward_routed(x, lay, ref["idx"], ref["w"], ref["g_s"])
+    np.testing.assert_allclose(rt["y"], ref["y"], rtol=1e-12, atol=1e-12)
+    assert np.array_equal(rt["sorted_assign"], ref["sorted_assign"])
+    with pytest.raises(ValueError):
+        oracle.moe_forward_routed(x, lay, ref["idx"], ref["w"])  # shared expert needs g_s
