@@ -143,6 +143,31 @@ MOE_API int moe_layer_create(const moe_desc* desc, const moe_weights* weights, m
 MOE_API int moe_forward(moe_layer* layer, const void* x, int32_t T, void* y,
                 const moe_route_out* route, void* stream);
 
+/* The same forward with the routing given by the caller instead of the Gate
+ * ([pptc §3.4]: the engine consumes routing results produced elsewhere, on the
+ * host or by another kernel, token-major [T][k]). Reads
+ *   topk_idx     [T][k] int32, required: the expert of slot j of token t. Ids
+ *                need not be distinct (a repeated expert processes the token
+ *                once per slot); an id outside [0, n_experts) is read as expert
+ *                0 with weight 0, so it adds nothing to y (and is counted under
+ *                expert 0 in expert_counts).
+ *   topk_w       [T][k] fp32, required: the weight of each slot, used as given
+ *                (no normalisation).
+ *   shared_gate  [T] fp32: the shared expert's scale, required exactly when the
+ *                layer has a shared expert, else NULL.
+ * and computes y[t] = sum_j topk_w[t, j] * expert(topk_idx[t, j], x[t])
+ * (+ shared_gate[t] * S(x[t])), with the Scatter, Expert and Gather stages of
+ * moe_forward (bit-identical to it when given moe_forward's own routing).
+ * route may be NULL; of it only expert_counts, expert_offsets and
+ * sorted_assign are written (when not NULL), its other fields are ignored.
+ * x, y: as moe_forward; all routing pointers 4-byte aligned. Allocates nothing.
+ * Statuses: EINVAL (as moe_forward, and NULL topk_idx/topk_w, shared_gate
+ * missing or given against the layer's shape), EHIP. Stage times: the gate
+ * entry times the reading of the given routing. */
+MOE_API int moe_forward_routed(moe_layer* layer, const void* x, int32_t T, const int32_t* topk_idx,
+                               const float* topk_w, const float* shared_gate, void* y,
+                               const moe_route_out* route, void* stream);
+
 /* Turn per-stage HIP event timing on (1) or off (0) for the following
  * moe_forward calls on this layer ([0539edu §3.3]: profiling is a per-call
  * switch of the inference config). The initial state is desc->profile. Events

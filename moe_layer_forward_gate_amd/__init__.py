@@ -2,7 +2,7 @@
 
 Argument marshalling only: every step of the forward runs in libmoe's HIP
 kernels. The raw C entry points keep their C names (moe_layer_create,
-moe_forward, moe_set_profiling, moe_stage_times, moe_destroy, moe_status_str,
+moe_forward, moe_forward_routed, moe_set_profiling, moe_stage_times, moe_destroy, moe_status_str,
 moe_last_error);
 MoeLayer wraps them for torch device tensors. PyTorch supplies device memory and
 streams. If libmoe.so has not been built, loading raises: there is no fallback.
@@ -16,8 +16,8 @@ from typing import Optional
 
 __all__ = [
     "MoeError", "lib", "MOE_F32", "MOE_BF16", "MOE_I8", "MoeDesc", "MoeWeights", "MoeRouteOut",
-    "moe_layer_create", "moe_forward", "moe_set_profiling", "moe_stage_times", "moe_destroy",
-    "moe_status_str", "moe_last_error", "MoeLayer", "LIB_PATH", "EXPORTED",
+    "moe_layer_create", "moe_forward", "moe_forward_routed", "moe_set_profiling", "moe_stage_times",
+    "moe_destroy", "moe_status_str", "moe_last_error", "MoeLayer", "LIB_PATH", "EXPORTED",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
@@ -26,8 +26,8 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOMEM, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_I8 = 0, 1, 2
 
 # every symbol include/moe.h declares
-EXPORTED = ("moe_layer_create", "moe_forward", "moe_set_profiling", "moe_stage_times", "moe_destroy",
-            "moe_status_str", "moe_last_error")
+EXPORTED = ("moe_layer_create", "moe_forward", "moe_forward_routed", "moe_set_profiling", "moe_stage_times",
+            "moe_destroy", "moe_status_str", "moe_last_error")
 
 
 class MoeError(RuntimeError):
@@ -70,6 +70,10 @@ def lib() -> ctypes.CDLL:
         L.moe_forward.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                   ctypes.POINTER(MoeRouteOut), ctypes.c_void_p]
         L.moe_forward.restype = ctypes.c_int
+        L.moe_forward_routed.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.POINTER(MoeRouteOut), ctypes.c_void_p]
+        L.moe_forward_routed.restype = ctypes.c_int
         L.moe_set_profiling.argtypes = [ctypes.c_void_p, ctypes.c_int]
         L.moe_set_profiling.restype = ctypes.c_int
         L.moe_stage_times.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]
@@ -108,6 +112,15 @@ def moe_layer_create(desc: MoeDesc, weights: MoeWeights) -> ctypes.c_void_p:
 def moe_forward(handle, x_ptr: int, T: int, y_ptr: int, route: MoeRouteOut, stream_ptr: int = 0) -> None:
     """Raw forward on device pointers; enqueues on the given HIP stream."""
     _check(lib().moe_forward(handle, x_ptr, T, y_ptr, ctypes.byref(route), stream_ptr), "moe_forward")
+
+
+def moe_forward_routed(handle, x_ptr: int, T: int, idx_ptr: int, w_ptr: int, shared_gate_ptr: int, y_ptr: int,
+                       route: Optional[MoeRouteOut] = None, stream_ptr: int = 0) -> None:
+    """Raw forward with a given routing (topk_idx [T][k] int32, topk_w [T][k] fp32,
+    shared_gate [T] fp32 or 0); route may be None."""
+    _check(lib().moe_forward_routed(handle, x_ptr, T, idx_ptr, w_ptr, shared_gate_ptr or None, y_ptr,
+                                    ctypes.byref(route) if route is not None else None, stream_ptr),
+           "moe_forward_routed")
 
 
 def moe_set_profiling(handle, enable: bool) -> None:
@@ -212,6 +225,35 @@ class MoeLayer:
                             _ptr(out.expert_offsets), _ptr(out.sorted_assign), _ptr(out.shared_gate))
         s = stream if stream is not None else torch.cuda.current_stream()
         moe_forward(self._h, _ptr(x), T, _ptr(out.y), route, int(s.cuda_stream))
+        return out
+
+    def forward_routed(self, x, topk_idx, topk_w, shared_gate=None, out: Optional[RouteResult] = None,
+                       scatter: bool = False, stream=None) -> RouteResult:
+        """Enqueue the layer with the routing given (topk_idx [T, k] int32, topk_w [T, k]
+        float32, shared_gate [T] float32 for a layer with a shared expert) instead of the
+        gate. The returned RouteResult holds y (and the scatter tables if `scatter`); its
+        topk_idx / topk_w are the given tensors."""
+        torch = self.torch
+        if x.dim() != 2 or x.shape[1] != self.d_model or x.dtype != self._act_torch:
+            raise ValueError(f"x must be [T, {self.d_model}] {self._act_torch}")
+        T = x.shape[0]
+        for name, t, dt, shape in (("topk_idx", topk_idx, torch.int32, (T, self.top_k)),
+                                   ("topk_w", topk_w, torch.float32, (T, self.top_k)),
+                                   ("shared_gate", shared_gate, torch.float32, (T,))):
+            if t is None:
+                continue
+            if tuple(t.shape) != shape or t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous GPU {dt} tensor of shape {shape}")
+        for name, t in (("x", x),):
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous GPU tensor")
+        if out is None:
+            out = self.outputs(T, scatter)
+            out.topk_idx, out.topk_w, out.shared_gate = topk_idx, topk_w, shared_gate
+        route = MoeRouteOut(0, 0, _ptr(out.expert_counts), _ptr(out.expert_offsets), _ptr(out.sorted_assign), 0)
+        s = stream if stream is not None else torch.cuda.current_stream()
+        moe_forward_routed(self._h, _ptr(x), T, _ptr(topk_idx), _ptr(topk_w), _ptr(shared_gate), _ptr(out.y),
+                           route, int(s.cuda_stream))
         return out
 
     def set_profiling(self, enable: bool) -> None:

@@ -104,6 +104,10 @@ hipError_t launch_expert_down_bf16(const GemmArgs& a, bool int8, hipStream_t s);
 // first one's rows for them). Reads the scatter's tile list on the device; writes
 // max_tiles*bm rows at most.
 hipError_t launch_pack_a(const GemmArgs& a, hipStream_t s);
+// A caller's routing (ids [N], weights [N]) into the layer's buffers: ids outside
+// [0, E) become expert 0 with weight 0.
+hipError_t launch_route_in(const int32_t* idx, const float* w, int N, int E, int32_t* idx_out, float* w_out,
+                           hipStream_t s);
 // Small-batch variants (a.bm = 16, 32 or 64: an active expert usually fits one row tile;
 // one that does not takes several, each streaming the weights again).
 hipError_t launch_expert_up_stream(const GemmArgs& a, bool int8, hipStream_t s);

@@ -61,6 +61,8 @@ struct moe_layer {
     int32_t* tile_start = nullptr;
     int32_t* sorted_c = nullptr;
     float* gs = nullptr;
+    int32_t* ridx = nullptr;  // a caller's routing, checked (moe_forward_routed)
+    float* rw = nullptr;
     float* gate_part = nullptr;  // partial router dots of the split decode gate
     int32_t* scatter_work = nullptr;  // chunk counts and ranks of the multi-workgroup scatter
     bf16_t* xp = nullptr;  // tiled up operand (bf16/int8 experts)
@@ -78,7 +80,7 @@ namespace {
 void release(moe_layer* L) {
     if (!L) return;
     void* bufs[] = {L->wr_t, L->wr_planes, L->bias, L->wgu, L->wdn, L->s_gate, L->s_up, L->s_down, L->counts, L->offsets,
-                    L->tile_start, L->sorted_c, L->gs, L->gate_part, L->scatter_work, L->xp, L->h, L->ow};
+                    L->tile_start, L->sorted_c, L->gs, L->ridx, L->rw, L->gate_part, L->scatter_work, L->xp, L->h, L->ow};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
     for (hipEvent_t e : L->ev)
@@ -169,6 +171,8 @@ int create_impl(const moe_desc* desc, const moe_weights* w, moe_layer* L) {
     if ((rc = dev_alloc(&L->tile_start, (Et + 1) * 4))) return rc;
     if ((rc = dev_alloc(&L->sorted_c, P * 4))) return rc;
     if ((rc = dev_alloc(&L->gs, T * 4))) return rc;
+    if ((rc = dev_alloc(&L->ridx, T * d.top_k * 4))) return rc;
+    if ((rc = dev_alloc(&L->rw, T * d.top_k * 4))) return rc;
     if ((rc = dev_alloc(&L->gate_part, gate_split_workspace((int)std::min(T, (size_t)64), d.d_model, L->E,
                                                              d.shared_d_ff > 0))))
         return rc;
@@ -221,74 +225,42 @@ int create_impl(const moe_desc* desc, const moe_weights* w, moe_layer* L) {
     return MOE_OK;
 }
 
-}  // namespace
+// ---- the forward, shared by moe_forward and moe_forward_routed
 
-extern "C" {
-
-const char* moe_status_str(int status) {
-    switch (status) {
-        case MOE_OK: return "MOE_OK";
-        case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
-        case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: unsupported configuration";
-        case MOE_ENOMEM: return "MOE_ENOMEM: device allocation failed";
-        case MOE_EHIP: return "MOE_EHIP: HIP runtime error";
-        default: return "unknown moe status";
-    }
-}
-
-const char* moe_last_error(void) { return g_err; }
-
-int moe_layer_create(const moe_desc* desc, const moe_weights* weights, moe_layer** out) {
-    g_err[0] = 0;
-    if (!out) return fail(MOE_EINVAL, "out is NULL");
-    *out = nullptr;
-    if (!desc || !weights) return fail(MOE_EINVAL, "desc and weights are required");
-    int rc = check_desc(desc, weights);
-    if (rc) return rc;
-    moe_layer* L = new (std::nothrow) moe_layer();
-    if (!L) return fail(MOE_ENOMEM, "host allocation failed");
-    rc = create_impl(desc, weights, L);
-    if (rc) {
-        release(L);
-        return rc;
-    }
-    *out = L;
-    return MOE_OK;
-}
-
-int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route_out* r, void* stream) {
-    g_err[0] = 0;
+// Checks common to both forward entry points (before any HIP call).
+int check_call(const moe_layer* L, const void* x, int32_t T, void* y) {
     if (!L) return fail(MOE_EINVAL, "layer is NULL");
     if (T < 0 || T > L->desc.max_tokens) return fail(MOE_EINVAL, "T=%d outside [0, %d]", T, L->desc.max_tokens);
     if (T == 0) return MOE_OK;  // nothing to read or write; buffers may be empty
-    if (!x || !y || !r || !r->topk_idx || !r->topk_w)
-        return fail(MOE_EINVAL, "x, y, route, route->topk_idx and route->topk_w are required");
+    if (!x || !y) return fail(MOE_EINVAL, "x and y are required");
     if (!aligned(x, 16) || !aligned(y, 16)) return fail(MOE_EINVAL, "x and y must be 16-byte aligned");
-    const void* rp[] = {r->topk_idx, r->topk_w, r->expert_counts, r->expert_offsets, r->sorted_assign,
-                        r->shared_gate};
-    for (const void* p : rp)
-        if (p && !aligned(p, 4)) return fail(MOE_EINVAL, "route outputs must be 4-byte aligned");
+    return MOE_OK;
+}
+
+int check_device(const moe_layer* L) {
     int dev = -1;
     HIP_TRY(hipGetDevice(&dev));
     if (dev != L->device) return fail(MOE_EINVAL, "current device %d is not the layer's device %d", dev, L->device);
+    return MOE_OK;
+}
 
-    hipStream_t s = (hipStream_t)stream;
+// Launch plan (host side, from T, k and the layer shape only):
+//  - small batches (T <= 64) stream the weights: row tiles of 16, 32 or 64 rows,
+//    sized so an active expert almost always fits one tile, the down projection's K
+//    split so ~1024 workgroups run;
+//  - larger batches use the LDS-tiled MFMA GEMMs (256-row tiles for bf16 weights,
+//    128 for int8), with the down projection's K split when that fills the CUs better.
+struct Plan {
+    bool streaming;
+    int bm, ksplit, max_tiles;
+    bool merge;  // tiled down projection of a multi-slice shared expert as one K loop
+};
+
+Plan make_plan(const moe_layer* L, int T) {
     const moe_desc& d = L->desc;
     const bool f32 = d.expert_dtype == MOE_F32;
     const bool i8 = d.expert_dtype == MOE_I8;
     const int k = d.top_k;
-    float* gs = r->shared_gate ? r->shared_gate : L->gs;
-    const bool prof = L->profiling;
-    if (prof) HIP_TRY(hipEventRecord(L->ev[0], s));
-
-
-    // Launch plan (host side, from T, k and the layer shape only):
-    //  - small batches (T <= 64) stream the weights: row tiles of 16, 32 or 64 rows,
-    //    sized so an active expert almost always fits one tile, the down projection's K
-    //    split so ~1024 workgroups run;
-    //  - larger batches use the LDS-tiled MFMA GEMMs (256-row tiles for bf16 weights,
-    //    128 for int8), with a 2-way K split of the down projection when its tiles alone
-    //    would leave the GPU short of work.
     const bool streaming = !f32 && T <= kStreamMaxT;
     int bm, ksplit = 1;
     if (f32) {
@@ -333,8 +305,6 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
         }
     }
     if ((size_t)T * L->kt * ksplit > L->ow_rows) ksplit = 1;  // never past the combine buffer
-    ScatterOut so{L->counts, L->offsets, L->tile_start, L->sorted_c, r->expert_counts, r->expert_offsets,
-                  r->sorted_assign};
     // upper bound on sum_e ceil(n_e / bm) over experts with rows: one tile per active
     // expert, plus sum_e floor((n_e - 1) / bm) <= floor((P - 1) / bm) more for experts past
     // one tile (the streaming tile is sized to the expected busiest expert, not a bound)
@@ -343,9 +313,125 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
     // tiled down projection of a shared expert in several slices: the slices of a row tile
     // are summed in one K loop (one partial row per token instead of one per slice)
     const bool merge = !f32 && !streaming && !i8 && L->V > 1 && ksplit == 1;
-    const GemmArgs a{L->tile_start, L->offsets, L->sorted_c, L->Et, L->kt, k, max_tiles, bm, ksplit, merge ? 1 : 0,
-                     (const bf16_t*)x, L->xp, (bf16_t*)L->h, L->wgu, L->wdn, L->s_gate, L->s_up, L->s_down,
-                     r->topk_w, gs, L->ow, d.d_model, d.d_ff};
+    return Plan{streaming, bm, ksplit, max_tiles, merge};
+}
+
+ScatterOut scatter_out(const moe_layer* L, int32_t* counts, int32_t* offsets, int32_t* sorted) {
+    return ScatterOut{L->counts, L->offsets, L->tile_start, L->sorted_c, counts, offsets, sorted};
+}
+
+// Scatter of a routing already in device memory (idx [T][k]).
+int run_scatter(moe_layer* L, const int32_t* idx, int T, const Plan& pl, const ScatterOut& so, hipStream_t s) {
+    const int k = L->desc.top_k;
+#ifndef MOE_SCATTER_WIDE_MIN
+#define MOE_SCATTER_WIDE_MIN 4095
+#endif
+    // many assignments: the scatter over many workgroups (three launches)
+    if (T * k > MOE_SCATTER_WIDE_MIN)
+        HIP_TRY(launch_scatter_wide(idx, T, L->E, k, L->V, pl.bm, so, L->scatter_work, s));
+    else
+        HIP_TRY(launch_scatter(idx, T, L->E, k, L->V, pl.bm, so, s));
+    return MOE_OK;
+}
+
+// Expert compute and Gather once the scatter tables are on the device: the gathering
+// of token rows for the tiled GEMMs, up, down, combine (with the per-stage events).
+int run_experts(moe_layer* L, const void* x, int T, void* y, const float* topk_w, const float* gs, const Plan& pl,
+                hipStream_t s) {
+    const moe_desc& d = L->desc;
+    const bool f32 = d.expert_dtype == MOE_F32;
+    const bool i8 = d.expert_dtype == MOE_I8;
+    const int k = d.top_k;
+    const bool prof = L->profiling;
+    const GemmArgs a{L->tile_start, L->offsets, L->sorted_c, L->Et, L->kt, k, pl.max_tiles, pl.bm, pl.ksplit,
+                     pl.merge ? 1 : 0, (const bf16_t*)x, L->xp, (bf16_t*)L->h, L->wgu, L->wdn, L->s_gate, L->s_up,
+                     L->s_down, topk_w, gs, L->ow, d.d_model, d.d_ff};
+    // the tiled GEMMs take the token rows already gathered into fragment order
+    if (!f32 && !pl.streaming) HIP_TRY(launch_pack_a(a, s));
+    if (prof) HIP_TRY(hipEventRecord(L->ev[2], s));
+    if (f32) {
+        GemmF32Args af{L->tile_start, L->offsets, L->sorted_c, L->Et, L->kt, k, pl.max_tiles,
+                       (const float*)x, (float*)L->h, (const float*)L->wgu,
+                       (const float*)L->wgu + (size_t)L->E * d.d_model * d.d_ff, (const float*)L->wdn,
+                       topk_w, gs, L->ow, d.d_model, d.d_ff};
+        HIP_TRY(launch_expert_up_f32(af, s));
+        if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));
+        HIP_TRY(launch_expert_down_f32(af, s));
+    } else if (pl.streaming) {
+        HIP_TRY(launch_expert_up_stream(a, i8, s));
+        if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));
+        HIP_TRY(launch_expert_down_stream(a, i8, s));
+    } else {
+        HIP_TRY(launch_expert_up_bf16(a, i8, s));
+        if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));
+        HIP_TRY(launch_expert_down_bf16(a, i8, s));
+    }
+    if (prof) HIP_TRY(hipEventRecord(L->ev[4], s));
+    HIP_TRY(launch_combine(L->ow, T, (pl.merge ? k + 1 : L->kt) * pl.ksplit, L->kt * pl.ksplit, d.d_model, y, !f32,
+                           s));
+    if (prof) {
+        HIP_TRY(hipEventRecord(L->ev[5], s));
+        L->ran = true;
+    }
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(int status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+        case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: unsupported configuration";
+        case MOE_ENOMEM: return "MOE_ENOMEM: device allocation failed";
+        case MOE_EHIP: return "MOE_EHIP: HIP runtime error";
+        default: return "unknown moe status";
+    }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int moe_layer_create(const moe_desc* desc, const moe_weights* weights, moe_layer** out) {
+    g_err[0] = 0;
+    if (!out) return fail(MOE_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (!desc || !weights) return fail(MOE_EINVAL, "desc and weights are required");
+    int rc = check_desc(desc, weights);
+    if (rc) return rc;
+    moe_layer* L = new (std::nothrow) moe_layer();
+    if (!L) return fail(MOE_ENOMEM, "host allocation failed");
+    rc = create_impl(desc, weights, L);
+    if (rc) {
+        release(L);
+        return rc;
+    }
+    *out = L;
+    return MOE_OK;
+}
+
+int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route_out* r, void* stream) {
+    g_err[0] = 0;
+    int rc = check_call(L, x, T, y);
+    if (rc || T == 0) return rc;
+    if (!r || !r->topk_idx || !r->topk_w) return fail(MOE_EINVAL, "route, route->topk_idx and route->topk_w are required");
+    const void* rp[] = {r->topk_idx, r->topk_w, r->expert_counts, r->expert_offsets, r->sorted_assign,
+                        r->shared_gate};
+    for (const void* q : rp)
+        if (q && !aligned(q, 4)) return fail(MOE_EINVAL, "route outputs must be 4-byte aligned");
+    if ((rc = check_device(L))) return rc;
+
+    hipStream_t s = (hipStream_t)stream;
+    const moe_desc& d = L->desc;
+    const bool f32 = d.expert_dtype == MOE_F32;
+    const int k = d.top_k;
+    float* gs = r->shared_gate ? r->shared_gate : L->gs;
+    const bool prof = L->profiling;
+    const Plan pl = make_plan(L, T);
+    const ScatterOut so = scatter_out(L, r->expert_counts, r->expert_offsets, r->sorted_assign);
+    if (prof) HIP_TRY(hipEventRecord(L->ev[0], s));
+
     // Routing for decode batches: up to 16 router columns, one workgroup reads the whole
     // router quickly enough (tiny batches fuse gate and scatter; larger ones run one gate
     // workgroup per token, then the scatter); more columns spread the router over many
@@ -354,56 +440,47 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
     if (!wide_router && gate_scatter_small_fits(T, d.d_model, L->E, L->V > 0, !f32)) {
         // tiny batch: both stages in one workgroup (the scatter stage then times as empty)
         HIP_TRY(launch_gate_scatter_small(x, !f32, L->wr_t, L->bias, T, d.d_model, L->E, L->V > 0, k, r->topk_idx,
-                                          r->topk_w, gs, L->V, bm, so, s));
+                                          r->topk_w, gs, L->V, pl.bm, so, s));
         if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
     } else if (wide_router && gate_split_fits(T, k)) {
         // decode batch: router dots on many workgroups, then top-k and scatter in one
         HIP_TRY(launch_gate_split(x, !f32, L->wr_t, L->bias, T, d.d_model, L->E, L->V > 0, k, r->topk_idx,
-                                  r->topk_w, gs, L->V, bm, so, L->gate_part, s));
+                                  r->topk_w, gs, L->V, pl.bm, so, L->gate_part, s));
         if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
     } else {
         HIP_TRY(launch_gate(x, !f32, L->wr_t, L->wr_planes, L->bias, T, d.d_model, L->E, L->V > 0, k, r->topk_idx,
                             r->topk_w, gs, s));
         if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
-#ifndef MOE_SCATTER_WIDE_MIN
-#define MOE_SCATTER_WIDE_MIN 4095
-#endif
-        // many assignments: the scatter over many workgroups (three launches)
-        if (T * k > MOE_SCATTER_WIDE_MIN)
-            HIP_TRY(launch_scatter_wide(r->topk_idx, T, L->E, k, L->V, bm, so, L->scatter_work, s));
-        else
-            HIP_TRY(launch_scatter(r->topk_idx, T, L->E, k, L->V, bm, so, s));
+        if ((rc = run_scatter(L, r->topk_idx, T, pl, so, s))) return rc;
     }
-    // the tiled GEMMs take the token rows already gathered into fragment order
-    if (!f32 && !streaming) HIP_TRY(launch_pack_a(a, s));
-    if (prof) HIP_TRY(hipEventRecord(L->ev[2], s));
+    return run_experts(L, x, T, y, r->topk_w, gs, pl, s);
+}
 
-    if (f32) {
-        GemmF32Args a{L->tile_start, L->offsets, L->sorted_c, L->Et, L->kt, k, max_tiles,
-                      (const float*)x, (float*)L->h, (const float*)L->wgu,
-                      (const float*)L->wgu + (size_t)L->E * d.d_model * d.d_ff, (const float*)L->wdn,
-                      r->topk_w, gs, L->ow, d.d_model, d.d_ff};
-        HIP_TRY(launch_expert_up_f32(a, s));
-        if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));
-        HIP_TRY(launch_expert_down_f32(a, s));
-    } else {
-        if (streaming) {
-            HIP_TRY(launch_expert_up_stream(a, i8, s));
-            if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));
-            HIP_TRY(launch_expert_down_stream(a, i8, s));
-        } else {
-            HIP_TRY(launch_expert_up_bf16(a, i8, s));
-            if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));
-            HIP_TRY(launch_expert_down_bf16(a, i8, s));
-        }
-    }
-    if (prof) HIP_TRY(hipEventRecord(L->ev[4], s));
-    HIP_TRY(launch_combine(L->ow, T, (merge ? k + 1 : L->kt) * ksplit, L->kt * ksplit, d.d_model, y, !f32, s));
-    if (prof) {
-        HIP_TRY(hipEventRecord(L->ev[5], s));
-        L->ran = true;
-    }
-    return MOE_OK;
+int moe_forward_routed(moe_layer* L, const void* x, int32_t T, const int32_t* topk_idx, const float* topk_w,
+                       const float* shared_gate, void* y, const moe_route_out* r, void* stream) {
+    g_err[0] = 0;
+    int rc = check_call(L, x, T, y);
+    if (rc || T == 0) return rc;
+    if (!topk_idx || !topk_w) return fail(MOE_EINVAL, "topk_idx and topk_w are required");
+    if (L->V > 0 && !shared_gate) return fail(MOE_EINVAL, "a layer with a shared expert needs shared_gate");
+    if (L->V == 0 && shared_gate) return fail(MOE_EINVAL, "shared_gate given but the layer has no shared expert");
+    const void* ip[] = {topk_idx, topk_w, shared_gate, r ? r->expert_counts : nullptr,
+                        r ? r->expert_offsets : nullptr, r ? r->sorted_assign : nullptr};
+    for (const void* q : ip)
+        if (q && !aligned(q, 4)) return fail(MOE_EINVAL, "routing inputs and outputs must be 4-byte aligned");
+    if ((rc = check_device(L))) return rc;
+
+    hipStream_t s = (hipStream_t)stream;
+    const bool prof = L->profiling;
+    const Plan pl = make_plan(L, T);
+    const ScatterOut so = scatter_out(L, r ? r->expert_counts : nullptr, r ? r->expert_offsets : nullptr,
+                                      r ? r->sorted_assign : nullptr);
+    if (prof) HIP_TRY(hipEventRecord(L->ev[0], s));
+    // the given routing, with ids outside [0, E) read as expert 0 at weight 0
+    HIP_TRY(launch_route_in(topk_idx, topk_w, T * L->desc.top_k, L->E, L->ridx, L->rw, s));
+    if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
+    if ((rc = run_scatter(L, L->ridx, T, pl, so, s))) return rc;
+    return run_experts(L, x, T, y, L->rw, shared_gate, pl, s);
 }
 
 int moe_set_profiling(moe_layer* L, int enable) {

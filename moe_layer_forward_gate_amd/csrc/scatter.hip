@@ -157,7 +157,29 @@ __global__ __launch_bounds__(256) void scatter_place(const int32_t* __restrict__
     }
 }
 
+// A routing given by the caller ([pptc §3.4]: the engine consumes routing results made
+// elsewhere, token-major [T][k]); an id outside [0, E) would index past the expert
+// tables, so it is read as expert 0 at weight 0 and adds nothing to the output.
+__global__ __launch_bounds__(256) void route_in_kernel(const int32_t* __restrict__ idx, const float* __restrict__ w,
+                                                       int N, int E, int32_t* __restrict__ idx_out,
+                                                       float* __restrict__ w_out) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < N) {
+        const int e = idx[i];
+        const bool ok = e >= 0 && e < E;
+        idx_out[i] = ok ? e : 0;
+        w_out[i] = ok ? w[i] : 0.0f;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_route_in(const int32_t* idx, const float* w, int N, int E, int32_t* idx_out, float* w_out,
+                           hipStream_t s) {
+    if (N <= 0) return hipSuccess;
+    hipLaunchKernelGGL(route_in_kernel, dim3((N + 255) / 256), dim3(256), 0, s, idx, w, N, E, idx_out, w_out);
+    return hipGetLastError();
+}
 
 size_t scatter_wide_workspace(int N, int E) {
     const size_t C = ((size_t)N + kChunk - 1) / kChunk;

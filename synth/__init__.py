@@ -6,7 +6,7 @@ holds none of the layer's forward arithmetic, and it is the one module that both
 the CPU oracle (via the tests) and the GPU binding consume.
 """
 from .configs import CONFIGS, LayerConfig, get_config
-from .generate import make_layer, make_tokens, zipf_bias, quantize_per_out_channel, SynthLayer
+from .generate import make_layer, make_tokens, make_routing, zipf_bias, quantize_per_out_channel, SynthLayer
 
-__all__ = ["CONFIGS", "LayerConfig", "get_config", "make_layer", "make_tokens", "zipf_bias",
+__all__ = ["CONFIGS", "LayerConfig", "get_config", "make_layer", "make_tokens", "make_routing", "zipf_bias",
            "quantize_per_out_channel", "SynthLayer"]

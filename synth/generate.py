@@ -140,3 +140,23 @@ def make_tokens(cfg: LayerConfig, T: int, device="cpu", instance: int = 0) -> to
     """x[T, d_model] ~ N(0, 1) in the activation dtype."""
     x = _normal(cfg, device, (T, cfg.d_model), 1.0, instance, "x", T)
     return x.to(_TORCH_DT[cfg.act_dtype])
+
+
+def make_routing(cfg: LayerConfig, T: int, invalid: float = 0.0, device="cpu", instance: int = 0):
+    """A routing drawn without a router, for layers fed a given routing: ids
+    [T, top_k] int32 uniform over the experts (repeats within a token allowed), a
+    fraction `invalid` of them replaced by ids outside [0, E) (-1 or E); weights
+    [T, top_k] fp32 ~ U(0, 1) divided by their sum over the token's slots (the
+    router's weights also sum to 1); the shared expert's scale [T] fp32 ~ U(0, 1)
+    when the layer has one (else None)."""
+    g = _gen(cfg, device, instance, "route", T)
+    E = cfg.n_experts
+    idx = torch.randint(0, E, (T, cfg.top_k), generator=g, device=device, dtype=torch.int64)
+    if invalid > 0:
+        bad = torch.rand((T, cfg.top_k), generator=g, device=device) < invalid
+        alt = torch.where(torch.rand((T, cfg.top_k), generator=g, device=device) < 0.5, -1, E)
+        idx = torch.where(bad, alt, idx)
+    w = torch.rand((T, cfg.top_k), generator=g, device=device, dtype=torch.float32)
+    w = w / w.sum(dim=1, keepdim=True)
+    gs = torch.rand((T,), generator=g, device=device, dtype=torch.float32) if cfg.shared_d_ff else None
+    return idx.to(torch.int32), w, gs

@@ -108,3 +108,10 @@ def test_stage_times_profiling_and_destroy_null():
     assert L.moe_stage_times(None, ms) == moe.MOE_EINVAL
     assert L.moe_set_profiling(None, 1) == moe.MOE_EINVAL
     L.moe_destroy(None)  # NULL-safe
+
+
+def test_forward_routed_rejects_before_gpu():
+    L = moe.lib()
+    fake = 0x10000
+    assert L.moe_forward_routed(None, fake, 4, fake, fake, None, fake, None, None) == moe.MOE_EINVAL
+    assert "layer" in moe.moe_last_error()
