@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--instances", type=int, default=4)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
+    ap.add_argument("--routed", action="store_true",
+                    help="time moe_forward_routed on a drawn routing (no gate) instead of moe_forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens of the batch the oracle runs on (0: the whole batch)")
@@ -110,7 +112,9 @@ def kernel_work(cfg, counts, T):
     return up, dn, dict(bytes=layer_bytes, flops=layer_flops, active=active)
 
 
-def build_instances(cfg, n, T, torch, synth, moe_tensors):
+def build_instances(cfg, n, T, torch, synth, moe_tensors, routed=False):
+    """n layer instances with their token batch and output buffers; with `routed`, each
+    instance's forward is moe_forward_routed on a routing drawn by synth.make_routing."""
     from harness import gpu_layer
     insts = []
     for i in range(n):
@@ -118,6 +122,10 @@ def build_instances(cfg, n, T, torch, synth, moe_tensors):
         lay = gpu_layer(L, T, profile=False)
         x = synth.make_tokens(cfg, T, device="cuda", instance=i)
         out = lay.outputs(T, scatter=True)
+        if routed:
+            idx, w, gs = synth.make_routing(cfg, T, device="cuda", instance=i)
+            out.topk_idx, out.topk_w, out.shared_gate = idx, w, gs
+            lay = _Routed(lay)
         insts.append((lay, x, out))
         if i == 0 and moe_tensors is not None:
             moe_tensors["layer0"] = L.to("cpu")
@@ -126,12 +134,25 @@ def build_instances(cfg, n, T, torch, synth, moe_tensors):
     return insts
 
 
-def run_workload(cfg, T, steps, warmup, n_inst, torch, synth, keep_layer0=False, graph=False):
+class _Routed:
+    """A layer whose forward(x, out=out) runs moe_forward_routed on out's routing."""
+
+    def __init__(self, lay):
+        self.lay = lay
+
+    def forward(self, x, out):
+        return self.lay.forward_routed(x, out.topk_idx, out.topk_w, out.shared_gate, out=out)
+
+    def __getattr__(self, name):
+        return getattr(self.lay, name)
+
+
+def run_workload(cfg, T, steps, warmup, n_inst, torch, synth, keep_layer0=False, graph=False, routed=False):
     """Time `steps` forwards (rotating over n_inst layers) with per-stage events off, then run
     the same steps again with libmoe's per-stage HIP events on and average the stage times."""
     import numpy as np
     keep = {} if keep_layer0 else None
-    insts = build_instances(cfg, n_inst, T, torch, synth, keep)
+    insts = build_instances(cfg, n_inst, T, torch, synth, keep, routed=routed)
     for i in range(warmup):
         lay, x, out = insts[i % n_inst]
         lay.forward(x, out=out)
@@ -170,11 +191,16 @@ def run_workload(cfg, T, steps, warmup, n_inst, torch, synth, keep_layer0=False,
     counts = insts[(steps - 1) % n_inst][2].expert_counts.cpu().numpy()
     res = dict(T=T, ms_per_step=1e3 * wall / steps, stage_ms=st, counts=counts)
     x0 = insts[0][1].cpu() if keep_layer0 else None
+    if keep_layer0 and routed:
+        o = insts[0][2]
+        keep["routing0"] = (o.topk_idx.cpu(), o.topk_w.cpu(), None if o.shared_gate is None else o.shared_gate.cpu())
     del graphs
     for lay, _, _ in insts:
         lay.close()
     del insts
     torch.cuda.empty_cache()
+    if keep_layer0:
+        res["routing0"] = keep.get("routing0")
     return res, (keep["layer0"] if keep_layer0 else None), x0
 
 
@@ -207,9 +233,10 @@ def summarize(cfg, res):
         active_experts=layer["active"], roofline=rf)
 
 
-def cpu_baseline(cfg, layer_cpu, x_cpu, n_tok, min_s):
+def cpu_baseline(cfg, layer_cpu, x_cpu, n_tok, min_s, routing=None):
     """The oracle as it stands, on the first n_tok tokens of the same batch, repeated (at most
-    4 passes) until min_s seconds have passed."""
+    4 passes) until min_s seconds have passed (with `routing` (idx, w, g_s): the oracle of
+    the layer fed that routing)."""
     import numpy as np
     import oracle
     from harness import oracle_layer
@@ -218,8 +245,13 @@ def cpu_baseline(cfg, layer_cpu, x_cpu, n_tok, min_s):
     xs = x_cpu[:n_tok].float().numpy()
     passes = 0
     t0 = time.perf_counter()
+    if routing is not None:
+        ridx, rw, rgs = (None if t is None else t[:n_tok].numpy() for t in routing)
     while True:
-        oracle.moe_forward(xs, olay)
+        if routing is None:
+            oracle.moe_forward(xs, olay)
+        else:
+            oracle.moe_forward_routed(xs, olay, ridx, rw, rgs)
         passes += 1
         dt = time.perf_counter() - t0
         if dt >= min_s or passes == 4:
@@ -227,7 +259,8 @@ def cpu_baseline(cfg, layer_cpu, x_cpu, n_tok, min_s):
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     return dict(value=passes * n_tok / dt, unit="tokens/s", cores=int(threads), kind="oracle",
                 sample=f"{passes} pass(es) over {n_tok} tokens of the T={x_cpu.shape[0]} batch, whole layer "
-                       f"forward in fp64 (gate, scatter, {cfg.n_experts} experts, combine), {dt:.1f} s")
+                       f"forward in fp64 ({'given routing' if routing is not None else 'gate'}, scatter, "
+                       f"{cfg.n_experts} experts, combine), {dt:.1f} s")
 
 
 def measure_peaks(torch):
@@ -288,7 +321,7 @@ def main():
     print(f"[bench] {cfg.name} T={T} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
     want_cpu = not args.no_cpu_baseline
     res, layer0, x0 = run_workload(cfg, T, args.steps, args.warmup, args.instances, torch, synth,
-                                   keep_layer0=want_cpu, graph=args.graph)
+                                   keep_layer0=want_cpu, graph=args.graph, routed=args.routed)
     main_s = summarize(cfg, res)
     print(f"[bench] main {json.dumps(main_s)}", file=sys.stderr, flush=True)
     sweep = []
@@ -297,14 +330,14 @@ def main():
             if Ts == T:
                 continue
             r, _, _ = run_workload(cfg, Ts, max(args.steps, 20), args.warmup, args.instances, torch, synth,
-                                   graph=args.graph)
+                                   graph=args.graph, routed=args.routed)
             s = summarize(cfg, r)
             sweep.append(s)
             print(f"[bench] sweep {json.dumps(s)}", file=sys.stderr, flush=True)
     cpu = None
     if want_cpu:
         n_tok = T if args.cpu_sample_tokens <= 0 else min(args.cpu_sample_tokens, T)
-        cpu = cpu_baseline(cfg, layer0, x0, n_tok, args.cpu_min_seconds)
+        cpu = cpu_baseline(cfg, layer0, x0, n_tok, args.cpu_min_seconds, routing=res.get("routing0"))
         print(f"[bench] cpu {json.dumps(cpu)}", file=sys.stderr, flush=True)
     line = {
         "metric": "MoE-layer tokens/s; decode HBM TB/s and prefill MFMA TFLOP/s vs roofline",
@@ -322,7 +355,8 @@ def main():
         "config": {"workload": f"{cfg.name}: MoE layer d_model={cfg.d_model} E={cfg.n_experts} "
                                f"d_ff={cfg.d_ff} top-{cfg.top_k}"
                                + (f" + shared d_ff={cfg.shared_d_ff}" if cfg.shared_d_ff else ""),
-                   "tokens": T, "instances": args.instances, "hip_graph": bool(args.graph)},
+                   "tokens": T, "instances": args.instances, "hip_graph": bool(args.graph),
+                   "routing": "given" if args.routed else "gate"},
         "roofline": {k: main_s["roofline"][k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
         "roofline_kernel": main_s["roofline"]["kernel"],
         "stage_ms": main_s["stage_ms"],
