@@ -11,7 +11,7 @@ www.trdm.cn/news/555962, [pptc] www.pptc.cn/news/100465.
 
 Pinned (see tests/test_oracle.py): router logits, top-k selection and tie rule,
 top-k weights, shared-expert gate, scatter (counts, offsets, permutation),
-SwiGLU expert, combine, int8 dequantisation, the layer with a caller-given
+SwiGLU expert, combine, int8 and int4 group-wise dequantisation, the layer with a caller-given
 routing. No function is parity-unpinned.
 """
 from .moe_oracle import (
@@ -22,6 +22,7 @@ from .moe_oracle import (
     scatter_stable_sort,
     scatter_counting,
     dequantize,
+    dequantize_groupwise,
     swiglu_expert,
     valid_selections,
     moe_forward,
@@ -31,6 +32,6 @@ from .moe_oracle import (
 
 __all__ = [
     "router_logits", "select_topk", "topk_weights", "shared_gate",
-    "scatter_stable_sort", "scatter_counting", "dequantize", "swiglu_expert",
+    "scatter_stable_sort", "scatter_counting", "dequantize", "dequantize_groupwise", "swiglu_expert",
     "valid_selections", "moe_forward", "moe_forward_routed", "OracleLayer",
 ]

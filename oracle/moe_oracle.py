@@ -1,7 +1,8 @@
 """fp64 reference of the MoE layer forward: Gate -> Scatter -> Expert Compute -> Gather.
 
 Test infrastructure only (see the package docstring). Everything is evaluated in
-float64 on the exact stored input values (bf16 / fp32 upcast, int8 as q * scale),
+float64 on the exact stored input values (bf16 / fp32 upcast, int8 and int4 as
+q * scale),
 one expert at a time, with no blocking, fusion or reordering beyond the
 definitions below.
 
@@ -137,6 +138,17 @@ def dequantize(q, scale) -> np.ndarray:
     return _f64(q) * _f64(scale)[..., None, :]
 
 
+def dequantize_groupwise(q, scale, group: int) -> np.ndarray:
+    """w[..., i, o] = q[..., i, o] * scale[..., i // group, o]: int4 weights with one
+    scale per `group` consecutive input rows of each output column ([mhpq §4.2]:
+    group-wise int4 quantisation with group size 128; [trdm §6.1]: int4 halves the
+    int8 footprint, two values per byte). Exact in fp64."""
+    q = _f64(q)
+    s = np.repeat(_f64(scale), group, axis=-2)
+    assert s.shape == q.shape, "scale rows times the group size must equal the input rows"
+    return q * s
+
+
 def _silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
@@ -167,6 +179,7 @@ class OracleLayer:
     ws_gate: Optional[np.ndarray] = None
     ws_up: Optional[np.ndarray] = None
     ws_down: Optional[np.ndarray] = None
+    group: Optional[int] = None  # int4: input rows per scale (scales [E, in/group, out])
 
     @property
     def n_experts(self) -> int:
@@ -174,6 +187,11 @@ class OracleLayer:
 
     def expert(self, e: int):
         """fp64 (W_gate, W_up, W_down) of expert e."""
+        if self.group is not None:
+            g = self.group
+            return (dequantize_groupwise(self.w_gate[e], self.s_gate[e], g),
+                    dequantize_groupwise(self.w_up[e], self.s_up[e], g),
+                    dequantize_groupwise(self.w_down[e], self.s_down[e], g))
         if self.s_gate is not None:
             return (dequantize(self.w_gate[e], self.s_gate[e]),
                     dequantize(self.w_up[e], self.s_up[e]),

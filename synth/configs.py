@@ -1,10 +1,10 @@
-"""Layer shapes of the five synthetic workloads.
+"""Layer shapes of the synthetic workloads.
 
 The shapes follow the MoE layers the Colibri pages deploy or benchmark on:
 Mixtral-8x7B (d_model 4096, 8 experts, d_ff 14336, top-2), a shared-expert
 augmented fine-grained layer, a many-expert layer with skewed routing, and an
-int8-weight Mixtral-8x22B-shaped decode layer, plus a tiny fp32 layer that the
-oracle evaluates in full.
+int8-weight Mixtral-8x22B-shaped decode layer (and its int4 group-wise twin),
+plus a tiny fp32 layer that the oracle evaluates in full.
 """
 from dataclasses import dataclass, field
 from typing import Tuple
@@ -18,7 +18,7 @@ class LayerConfig:
     d_ff: int
     top_k: int
     act_dtype: str            # "f32" | "bf16"
-    expert_dtype: str         # "f32" | "bf16" | "i8"
+    expert_dtype: str         # "f32" | "bf16" | "i8" | "i4"
     tokens: Tuple[int, ...]   # the token counts the workload is run at
     shared_d_ff: int = 0      # 0: no shared expert
     zipf_s: float = 0.0       # >0: router bias drawn from a Zipf law over experts
@@ -39,6 +39,9 @@ CONFIGS = {
     "skewed_bf16": LayerConfig("skewed_bf16", 2048, 128, 768, 4, "bf16", "bf16",
                                (8192,), zipf_s=1.2, zipf_beta=3.0),
     "int8_mixtral22b": LayerConfig("int8_mixtral22b", 6144, 8, 16384, 2, "bf16", "i8",
+                                   (1, 16, 256)),
+    # the same layer with int4 group-wise weights (group 128), the next step below int8
+    "int4_mixtral22b": LayerConfig("int4_mixtral22b", 6144, 8, 16384, 2, "bf16", "i4",
                                    (1, 16, 256)),
 }
 

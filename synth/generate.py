@@ -11,9 +11,12 @@ Distributions (one per tensor, independent streams):
   ws_down        ~ N(0, 1/Fs)       [Fs, d_model]     bf16
 
 Draws are made in fp32 and then stored in the target dtype: bf16 by
-round-to-nearest-even (torch's conversion), or int8 by symmetric
+round-to-nearest-even (torch's conversion), int8 by symmetric
 per-output-channel quantisation (scale = max|w| / 127 over the input axis,
 q = round-half-even(w / scale) clipped to [-127, 127]; an all-zero channel gets
+scale 0 and q 0), or int4 by symmetric group-wise quantisation (one scale per
+128 consecutive input rows of each output column, scale = max|w| / 7 over the
+group, q = round-half-even(w / scale) clipped to [-7, 7]; an all-zero group gets
 scale 0 and q 0). The stored values are the ground truth for every consumer.
 
 Each tensor (and each expert's slice of it) has its own torch.Generator seeded
@@ -65,6 +68,34 @@ def quantize_per_out_channel(w: torch.Tensor):
     return q.to(torch.int8), scale.to(torch.float32)
 
 
+INT4_GROUP = 128  # input rows per int4 scale
+
+
+def quantize_int4_groupwise(w: torch.Tensor, group: int = INT4_GROUP):
+    """Symmetric int4 quantisation of w[..., in, out] in groups of `group` input rows.
+
+    Returns (q int8 of w's shape holding values in [-7, 7], scale fp32 of shape
+    w.shape[:-2] + (in / group, out)).
+    """
+    *lead, n_in, n_out = w.shape
+    assert n_in % group == 0, "input axis must be a multiple of the group size"
+    wg = w.reshape(*lead, n_in // group, group, n_out)
+    scale = wg.abs().amax(dim=-2) / 7.0               # [..., in/group, out]
+    safe = torch.where(scale > 0, scale, torch.ones_like(scale))
+    q = torch.round(wg / safe.unsqueeze(-2)).clamp_(-7, 7)
+    q = torch.where(scale.unsqueeze(-2) > 0, q, torch.zeros_like(q))
+    return q.reshape(w.shape).to(torch.int8), scale.to(torch.float32)
+
+
+def pack_int4_pairs(q: torch.Tensor) -> torch.Tensor:
+    """Storage of int4 values q[..., in, out] (int8 tensor, values in [-8, 7]) two per
+    byte along the input axis: byte [..., i, o] holds q[..., 2i, o] in its low nibble
+    and q[..., 2i+1, o] in its high nibble, each as a 4-bit two's complement code."""
+    *lead, n_in, n_out = q.shape
+    u = (q.to(torch.int16) & 0xF).reshape(*lead, n_in // 2, 2, n_out)
+    return (u[..., 0, :] | (u[..., 1, :] << 4)).to(torch.uint8)
+
+
 @dataclass
 class SynthLayer:
     cfg: LayerConfig
@@ -73,9 +104,9 @@ class SynthLayer:
     w_gate: torch.Tensor                   # [E, d, F]
     w_up: torch.Tensor                     # [E, d, F]
     w_down: torch.Tensor                   # [E, F, d]
-    s_gate: Optional[torch.Tensor] = None  # [E, F] fp32 (int8 only)
-    s_up: Optional[torch.Tensor] = None    # [E, F]
-    s_down: Optional[torch.Tensor] = None  # [E, d]
+    s_gate: Optional[torch.Tensor] = None  # [E, F] fp32 (int8); [E, d/128, F] (int4)
+    s_up: Optional[torch.Tensor] = None    # [E, F]; [E, d/128, F]
+    s_down: Optional[torch.Tensor] = None  # [E, d]; [E, F/128, d]
     w_shared_gate: Optional[torch.Tensor] = None  # [d] fp32
     ws_gate: Optional[torch.Tensor] = None        # [d, Fs]
     ws_up: Optional[torch.Tensor] = None          # [d, Fs]
@@ -90,8 +121,17 @@ class SynthLayer:
 
 
 def _expert_stack(cfg, device, name, rows, cols, std, instance):
-    """[E, rows, cols] stored in the expert dtype (+ per-column scales for int8)."""
+    """[E, rows, cols] stored in the expert dtype (+ per-column scales for int8, per
+    (group, column) scales for int4, whose values are kept one per int8 element)."""
     E = cfg.n_experts
+    if cfg.expert_dtype == "i4":
+        q = torch.empty((E, rows, cols), dtype=torch.int8, device=device)
+        s = torch.empty((E, rows // INT4_GROUP, cols), dtype=torch.float32, device=device)
+        for e in range(E):
+            w = _normal(cfg, device, (rows, cols), std, instance, name, e)
+            q[e], s[e] = quantize_int4_groupwise(w)
+            del w
+        return q, s
     if cfg.expert_dtype == "i8":
         q = torch.empty((E, rows, cols), dtype=torch.int8, device=device)
         s = torch.empty((E, cols), dtype=torch.float32, device=device)

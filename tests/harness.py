@@ -51,7 +51,8 @@ def oracle_layer(L: "synth.SynthLayer") -> oracle.OracleLayer:
         w_router=_np(L.w_router), w_gate=_np(L.w_gate), w_up=_np(L.w_up), w_down=_np(L.w_down),
         top_k=L.cfg.top_k, b_router=_np(L.b_router), s_gate=_np(L.s_gate), s_up=_np(L.s_up),
         s_down=_np(L.s_down), w_shared_gate=_np(L.w_shared_gate), ws_gate=_np(L.ws_gate),
-        ws_up=_np(L.ws_up), ws_down=_np(L.ws_down))
+        ws_up=_np(L.ws_up), ws_down=_np(L.ws_down),
+        group=synth.INT4_GROUP if L.cfg.expert_dtype == "i4" else None)
 
 
 def compare(cfg, x, olay: oracle.OracleLayer, out, sample=None, label=""):

@@ -420,3 +420,55 @@ def test_routed_with_the_gates_routing_is_the_layer():
     assert np.array_equal(rt["sorted_assign"], ref["sorted_assign"])
     with pytest.raises(ValueError):
         oracle.moe_forward_routed(x, lay, ref["idx"], ref["w"])  # shared expert needs g_s
+
+
+# ---------------------------------------------------------------- int4 group-wise weights
+def test_dequantize_groupwise_hand_fixture():
+    # 4 input rows, 2 output columns, groups of 2 rows: rows 0-1 take scale row 0, rows 2-3 row 1
+    q = np.array([[1, -2], [3, 4], [-5, 6], [7, -7]], dtype=np.int8)
+    s = np.array([[0.5, 2.0], [0.25, 1.0]], dtype=np.float32)
+    want = np.array([[0.5, -4.0], [1.5, 8.0], [-1.25, 6.0], [1.75, -7.0]])
+    assert np.array_equal(oracle.dequantize_groupwise(q, s, 2), want)
+
+
+def test_int4_quantiser_roundtrip_groups_and_axis():
+    # scales that differ by 1000x across columns and by 10x between the two K groups:
+    # a scale taken from the wrong group or the wrong axis breaks the half-step bound
+    rng = np.random.default_rng(21)
+    w = rng.standard_normal((2, 256, 16)) * np.logspace(-3, 0, 16)[None, None, :]
+    w[:, 128:, :] *= 10.0
+    w[1, :128, 3] = 0.0  # an all-zero group
+    q, s = synth.quantize_int4_groupwise(torch.from_numpy(w).float())
+    q, s = q.numpy(), s.numpy()
+    assert q.dtype == np.int8 and s.shape == (2, 2, 16)
+    assert q.min() >= -7 and q.max() <= 7
+    assert s[1, 0, 3] == 0 and not q[1, :128, 3].any()
+    nz = s > 0
+    amax = np.abs(q.reshape(2, 2, 128, 16)).max(axis=2)
+    assert (amax[nz] == 7).all()  # every nonzero group reaches the end of the range
+    deq = oracle.dequantize_groupwise(q, s, 128)
+    w32 = torch.from_numpy(w).float().double().numpy()
+    bound = np.repeat(s, 128, axis=1) * 0.5 * (1 + 1e-6)
+    assert (np.abs(deq - w32) <= bound).all()
+
+
+def test_int4_storage_encoding():
+    # two values per byte along the input axis, low nibble first, 4-bit two's complement
+    q = torch.tensor([[[1, -8], [-1, 7], [0, -3], [5, 2]]], dtype=torch.int8)  # [1, in=4, out=2]
+    p = synth.pack_int4_pairs(q)
+    assert p.dtype == torch.uint8 and tuple(p.shape) == (1, 2, 2)
+    assert p.tolist() == [[[0xF1, 0x78], [0x50, 0x2D]]]
+
+
+def test_dense_masked_bruteforce_int4():
+    rng = np.random.default_rng(22)
+    d, E, F, k = 256, 5, 128, 2
+    ws = [rng.standard_normal((E, a, b)) / np.sqrt(a) for a, b in ((d, F), (d, F), (F, d))]
+    qs = [synth.quantize_int4_groupwise(torch.from_numpy(w).float()) for w in ws]
+    (wg, sg), (wu, su), (wd, sd) = [(q.numpy(), s.numpy()) for q, s in qs]
+    lay = oracle.OracleLayer(w_router=rng.standard_normal((d, E)) * 0.1, w_gate=wg, w_up=wu, w_down=wd,
+                             top_k=k, s_gate=sg, s_up=su, s_down=sd, group=128)
+    x = rng.standard_normal((5, d))
+    out = oracle.moe_forward(x, lay)
+    ref = _dense_masked(x, lay)
+    assert np.abs(out["y"] - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
