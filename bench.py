@@ -93,17 +93,23 @@ def kernel_work(cfg, counts, T):
     slices take all T tokens. Bytes: weights (+ scales) of experts with rows,
     the activations read and the GEMM output written."""
     d, F, k = cfg.d_model, cfg.d_ff, cfg.top_k
-    welt = 1 if cfg.expert_dtype == "i8" else (4 if cfg.expert_dtype == "f32" else 2)
+    # bytes per weight: int4 packs two in a byte
+    welt = {"i8": 1.0, "i4": 0.5, "f32": 4.0}.get(cfg.expert_dtype, 2.0)
     aelt = 4 if cfg.act_dtype == "f32" else 2
     helt = 4 if cfg.expert_dtype == "f32" else 2
     active = int((counts > 0).sum())
     P = T * k
     V = cfg.shared_d_ff // F if cfg.shared_d_ff else 0
     rows = P + V * T
-    scale_up = active * 2 * F * 4 if welt == 1 else 0
-    scale_dn = active * d * 4 if welt == 1 else 0
-    up_w = (active + V) * 2 * d * F * welt + scale_up
-    dn_w = (active + V) * F * d * welt + scale_dn
+    # fp32 scales: one per output channel (int8), one per 128 input rows of each (int4)
+    if cfg.expert_dtype == "i8":
+        scale_up, scale_dn = active * 2 * F * 4, active * d * 4
+    elif cfg.expert_dtype == "i4":
+        scale_up, scale_dn = active * (d // 128) * 2 * F * 4, active * (F // 128) * d * 4
+    else:
+        scale_up = scale_dn = 0
+    up_w = int((active + V) * 2 * d * F * welt) + scale_up
+    dn_w = int((active + V) * F * d * welt) + scale_dn
     up = dict(flops=2.0 * rows * d * 2 * F, bytes=up_w + T * d * aelt + rows * F * helt)
     dn = dict(flops=2.0 * rows * F * d, bytes=dn_w + rows * F * helt + rows * d * 4)
     layer_bytes = up_w + dn_w + d * cfg.n_experts * 4 + 2 * T * d * aelt + T * k * 8
@@ -350,7 +356,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "f32": "f32"}[cfg.act_dtype] + ("+i8w" if cfg.expert_dtype == "i8" else ""),
+        "dtype": {"bf16": "bf16", "f32": "f32"}[cfg.act_dtype] + {"i8": "+i8w", "i4": "+i4w"}.get(cfg.expert_dtype, ""),
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: MoE layer d_model={cfg.d_model} E={cfg.n_experts} "
                                f"d_ff={cfg.d_ff} top-{cfg.top_k}"

@@ -59,14 +59,21 @@ typedef enum moe_status {
 typedef enum moe_dtype {
     MOE_F32 = 0,   /* IEEE binary32 */
     MOE_BF16 = 1,  /* bfloat16, stored as 16-bit patterns */
-    MOE_I8 = 2     /* int8 with one fp32 scale per output channel */
+    MOE_I8 = 2,    /* int8 with one fp32 scale per output channel */
+    MOE_I4 = 3     /* int4 with one fp32 scale per 128 input rows of each output
+                      channel ([mhpq §4.2] group-wise int4, group size 128); two
+                      values per byte along the input axis ([trdm §6.1]), low
+                      nibble = even row, 4-bit two's complement */
 } moe_dtype;
 
 /* Layer shape. Supported (act_dtype, expert_dtype) pairs: (F32, F32),
- * (BF16, BF16), (BF16, I8). Limits: 1 <= top_k <= n_experts <= 128;
- * for BF16/I8 experts d_model % 128 == 0 and d_ff % 64 == 0; for F32 experts
- * d_model % 64 == 0 and d_ff % 64 == 0. shared_d_ff > 0 adds a shared expert
- * (BF16 experts only) and must be a multiple of d_ff. */
+ * (BF16, BF16), (BF16, I8), (BF16, I4). Limits: 1 <= top_k <= n_experts <= 128;
+ * for BF16/I8 experts d_model % 128 == 0 and d_ff % 64 == 0; for I4 experts
+ * d_model % 128 == 0 and d_ff % 128 == 0; for F32 experts d_model % 64 == 0
+ * and d_ff % 64 == 0. shared_d_ff > 0 adds a shared expert (BF16 experts only)
+ * and must be a multiple of d_ff. I4 layers run every batch on the weight-
+ * streaming kernels (built for decode; batches over 64 tokens re-stream the
+ * weights once per 64 rows of an expert). */
 typedef struct moe_desc {
     int32_t d_model;
     int32_t n_experts;
@@ -82,9 +89,13 @@ typedef struct moe_desc {
 /* Layer weights (device pointers, read only during moe_layer_create).
  * Expert matrices are stacked over experts and multiply from the right:
  *   w_gate, w_up  [E][d_model][d_ff]     element type = expert_dtype
- *   w_down        [E][d_ff][d_model]
+ *   w_down        [E][d_ff][d_model]     (I4: [E][d_model/2][d_ff] and
+ *                                        [E][d_ff/2][d_model] bytes, two rows a byte)
  *   s_gate, s_up  [E][d_ff]   fp32, I8 only: scale of each output column
  *   s_down        [E][d_model] fp32, I8 only
+ *   (I4: s_gate, s_up [E][d_model/128][d_ff] and s_down [E][d_ff/128][d_model]
+ *   fp32, the scale of each group of 128 input rows of each output column;
+ *   weight = q * scale)
  *   w_router      [d_model][E] fp32 (required)
  *   b_router      [E] fp32 or NULL (no bias)
  *   w_shared_gate [d_model] fp32; ws_gate, ws_up [d_model][shared_d_ff] and

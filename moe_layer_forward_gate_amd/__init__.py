@@ -15,7 +15,7 @@ from dataclasses import dataclass
 from typing import Optional
 
 __all__ = [
-    "MoeError", "lib", "MOE_F32", "MOE_BF16", "MOE_I8", "MoeDesc", "MoeWeights", "MoeRouteOut",
+    "MoeError", "lib", "MOE_F32", "MOE_BF16", "MOE_I8", "MOE_I4", "MoeDesc", "MoeWeights", "MoeRouteOut",
     "moe_layer_create", "moe_forward", "moe_forward_routed", "moe_set_profiling", "moe_stage_times",
     "moe_destroy", "moe_status_str", "moe_last_error", "MoeLayer", "LIB_PATH", "EXPORTED",
 ]
@@ -23,7 +23,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOMEM, MOE_EHIP = 0, -1, -2, -3, -4
-MOE_F32, MOE_BF16, MOE_I8 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_I8, MOE_I4 = 0, 1, 2, 3
 
 # every symbol include/moe.h declares
 EXPORTED = ("moe_layer_create", "moe_forward", "moe_forward_routed", "moe_set_profiling", "moe_stage_times",
@@ -161,7 +161,7 @@ class MoeLayer:
     copied into libmoe's packed layout, so they may be freed afterwards.
     """
 
-    _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "i8": MOE_I8}
+    _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "i8": MOE_I8, "i4": MOE_I4}
 
     def __init__(self, *, d_model: int, n_experts: int, d_ff: int, top_k: int, max_tokens: int,
                  act_dtype: str, expert_dtype: str, w_router, w_gate, w_up, w_down, b_router=None,

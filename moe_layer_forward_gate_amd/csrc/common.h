@@ -110,8 +110,12 @@ hipError_t launch_route_in(const int32_t* idx, const float* w, int N, int E, int
                            hipStream_t s);
 // Small-batch variants (a.bm = 16, 32 or 64: an active expert usually fits one row tile;
 // one that does not takes several, each streaming the weights again).
-hipError_t launch_expert_up_stream(const GemmArgs& a, bool int8, hipStream_t s);
-hipError_t launch_expert_down_stream(const GemmArgs& a, bool int8, hipStream_t s);
+// wq: the weight kind, kWBf16, kWI8 (per-channel scales s_gate/s_up/s_down) or kWI4
+// (group scales: s_gate = the up projection's [E][d/128][2F] in packed column order,
+// s_down = [E][F/128][d]).
+constexpr int kWBf16 = 0, kWI8 = 1, kWI4 = 2;
+hipError_t launch_expert_up_stream(const GemmArgs& a, int wq, hipStream_t s);
+hipError_t launch_expert_down_stream(const GemmArgs& a, int wq, hipStream_t s);
 constexpr int kStreamMaxT = 64;     // largest T served by the streaming kernels
 constexpr int kStreamMaxSplit = 16; // largest K split of their down projection
 
@@ -150,6 +154,13 @@ hipError_t pack_gu_bf16(const bf16_t* wg, const bf16_t* wu, int E, int d, int F,
 hipError_t pack_dn_bf16(const bf16_t* wd, int E, int F, int d, bf16_t* dst, hipStream_t s);
 hipError_t pack_gu_i8(const int8_t* wg, const int8_t* wu, int E, int d, int F, int8_t* dst, hipStream_t s);
 hipError_t pack_dn_i8(const int8_t* wd, int E, int F, int d, int8_t* dst, hipStream_t s);
+// int4 (two per byte along K, low nibble first, two's complement) into 1 KB blocks of
+// 16 columns x 128 K (one scale group): lane l's four words hold column l%16, K rows
+// 32*s + 8*(l/16) + 0..7 of word s as codes q + 8, rows 2i in nibble i and 2i+1 in
+// nibble i+4; and the group scales [E][K/128][N] into the packed column order.
+hipError_t pack_gu_i4(const uint8_t* wg, const uint8_t* wu, int E, int d, int F, uint8_t* dst, hipStream_t s);
+hipError_t pack_dn_i4(const uint8_t* wd, int E, int F, int d, uint8_t* dst, hipStream_t s);
+hipError_t pack_scales_gu_i4(const float* sg, const float* su, int E, int d, int F, float* dst, hipStream_t s);
 
 // Row tile height of the fp32 GEMMs (the bf16/int8 GEMMs take 256 or 128, chosen per call).
 constexpr int kBMf32 = 64;

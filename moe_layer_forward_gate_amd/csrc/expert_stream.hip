@@ -5,8 +5,9 @@
 // is built to stream each active expert's packed weights from HBM exactly once
 // at full width, with every weight byte fetched by exactly one wave:
 //   - every wave owns NBW 16-column weight blocks and a K range; it reads them
-//     as contiguous 1 KB fragment blocks (16 B per lane) straight into MFMA
-//     operand registers, U K-steps at a time so many loads are in flight;
+//     as contiguous 1 KB fragment blocks (16 B per lane: 32 bf16, 64 int8 or 128
+//     int4 K rows of one column) straight into MFMA operand registers, U K-steps
+//     at a time so many loads are in flight;
 //   - the few token rows (<= 16*MB) come in as MFMA A fragments from L2;
 //   - the down projection splits K over S workgroups when the active experts
 //     alone would leave the GPU idle; each split writes its own partial row of
@@ -28,9 +29,23 @@ __device__ __forceinline__ uint32_t i8x2_bf16(uint32_t w, int sh) {
     return (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
 }
 
-template <int MB, int NBW, bool INT8, bool UP, int U>
+// int4 codes (q + 8, 4 bits) to bf16 pairs: a code u placed in the low mantissa bits of
+// 0x4300 (bf16 128.0, whose unit in the last place is 1) reads as 128 + u = q + 136, so
+// one mask-and-or turns two codes into two exact bf16 values; the products' excess
+// 136 * sum(a) over the group is taken off after the MFMAs. A lane's 32-bit word holds
+// K rows 2i in nibble i and 2i+1 in nibble i+4 (i < 4), so word >> 4i yields the pair
+// (2i, 2i+1) in the two bf16 halves.
+__device__ __forceinline__ u32x4 i4x8_bf16(uint32_t w) {
+    return u32x4{(w & 0x000F000Fu) | 0x43004300u, ((w >> 4) & 0x000F000Fu) | 0x43004300u,
+                 ((w >> 8) & 0x000F000Fu) | 0x43004300u, ((w >> 12) & 0x000F000Fu) | 0x43004300u};
+}
+
+template <int MB, int NBW, int WQ, bool UP, int U>  // WQ: weight kind (kWBf16, kWI8, kWI4)
 __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
-    constexpr int KSTEP = INT8 ? 64 : 32;  // K covered by one 16-byte weight chunk per lane
+    constexpr bool INT8 = WQ == kWI8;
+    constexpr bool INT4 = WQ == kWI4;
+    // K covered by one 16-byte weight chunk per lane (an int4 chunk is one scale group)
+    constexpr int KSTEP = INT4 ? 128 : INT8 ? 64 : 32;
     constexpr int KH = KSTEP / 32;
     const int K = UP ? a.d : a.F;
     const int N = UP ? 2 * a.F : a.d;
@@ -60,14 +75,16 @@ __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
 
     // weight stream of each owned column block: contiguous 1 KB chunks along K
     const u32x4* bptr[NBW];
+    const float* sptr[NBW];  // int4: the group scales of the lane's column, one per K step
     {
         const int KB = K / KSTEP;
-        const u32x4* wb = reinterpret_cast<const u32x4*>(INT8 ? (const void*)((const int8_t*)(UP ? a.wgu : a.wdn) +
-                                                                                (size_t)e * N * K)
-                                                              : (const void*)((const bf16_t*)(UP ? a.wgu : a.wdn) +
-                                                                              (size_t)e * N * K));
+        // one expert: N * K / KSTEP blocks of 1 KB (64 chunks of 16 bytes)
+        const u32x4* wb = reinterpret_cast<const u32x4*>(UP ? a.wgu : a.wdn) + (size_t)e * N * KB * 4;
 #pragma unroll
         for (int j = 0; j < NBW; ++j) bptr[j] = wb + ((size_t)(nb0 + j) * KB + kbase / KSTEP) * 64 + lane;
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+            sptr[j] = (UP ? a.s_gate : a.s_down) + ((size_t)e * KB + kbase / KSTEP) * N + (nb0 + j) * 16 + lane % 16;
     }
     // token rows as A fragments: lane holds row 16*mb + lane%16, K 8*(lane/16)..+7
     const bf16_t* aptr[MB];
@@ -85,7 +102,39 @@ __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
 #pragma unroll
         for (int j = 0; j < NBW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto step = [&](const u32x4 (&bb)[NBW], const u32x4 (&aa)[MB][KH]) {
+    auto step = [&](const u32x4 (&bb)[NBW], const u32x4 (&aa)[MB][KH], const float (&sc)[NBW]) {
+        if constexpr (INT4) {
+            // one scale group: its partial products (codes read as q + 136) and 136 * the
+            // rows' sums over the group, then acc += scale * (partial - 136 * sum)
+            const bf16x8 k136 = __builtin_bit_cast(bf16x8, u32x4{0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u});
+            f32x4 zr[MB], g[NBW][MB];
+#pragma unroll
+            for (int kh = 0; kh < KH; ++kh) {
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    if (mb < mb_act)
+                        zr[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aa[mb][kh]), k136,
+                                                                         kh ? zr[mb] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < NBW; ++j) {
+                    const bf16x8 bw = __builtin_bit_cast(bf16x8, i4x8_bf16(bb[j][kh]));
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        if (mb < mb_act)
+                            g[j][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8, aa[mb][kh]), bw, kh ? g[j][mb] : f32x4{0.f, 0.f, 0.f, 0.f},
+                                0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NBW; ++j)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    if (mb < mb_act)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[mb][j][i] = fmaf(sc[j], g[j][mb][i] - zr[mb][i], acc[mb][j][i]);
+            return;
+        }
 #pragma unroll
         for (int kh = 0; kh < KH; ++kh)
 #pragma unroll
@@ -111,12 +160,19 @@ __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
     struct Round {
         u32x4 bb[U][NBW];
         u32x4 aa[U][MB][KH];
+        float sc[U][NBW];  // int4 only
     };
     auto load_round = [&](Round& R, int s0) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int j = 0; j < NBW; ++j) R.bb[u][j] = bptr[j][(size_t)(s0 + u) * 64];
+        if constexpr (INT4) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int j = 0; j < NBW; ++j) R.sc[u][j] = sptr[j][(size_t)(s0 + u) * N];
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -129,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
     };
     auto compute_round = [&](const Round& R) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) step(R.bb[u], R.aa[u]);
+        for (int u = 0; u < U; ++u) step(R.bb[u], R.aa[u], R.sc[u]);
     };
     const int nround = nsteps / U;
     Round r0, r1;
@@ -146,15 +202,20 @@ __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
     for (; s < nsteps; ++s) {
         u32x4 bb[NBW];
         u32x4 aa[MB][KH];
+        float sc[NBW] = {};
 #pragma unroll
         for (int j = 0; j < NBW; ++j) bb[j] = bptr[j][(size_t)s * 64];
+        if constexpr (INT4) {
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) sc[j] = sptr[j][(size_t)s * N];
+        }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int kh = 0; kh < KH; ++kh)
                 aa[mb][kh] = mb < mb_act ? *reinterpret_cast<const u32x4*>(aptr[mb] + s * KSTEP + kh * 32)
                                          : u32x4{0u, 0u, 0u, 0u};
-        step(bb, aa);
+        step(bb, aa, sc);
     }
 
     // ---- epilogue (same fragment layout as the prefill kernels)
@@ -202,37 +263,48 @@ __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
     }
 }
 
-template <int MB, bool INT8, bool UP>
+template <int MB, int WQ, bool UP>
 hipError_t launch_mb(const GemmArgs& a, int S, hipStream_t s) {
     constexpr int NBW = 2;
-    // K-steps per round (two rounds are in flight per wave)
-    constexpr int U = INT8 ? 2 : (MB <= 2 ? 4 : 2);
+    // K-steps per round (two rounds are in flight per wave); an int4 step holds four
+    // 32-K token fragments per row block, so wide row tiles take one step per round
+    constexpr int U = WQ == kWI4 ? (MB <= 1 ? 2 : 1) : WQ == kWI8 ? 2 : (MB <= 2 ? 4 : 2);
+    constexpr int KSTEP = WQ == kWI4 ? 128 : WQ == kWI8 ? 64 : 32;
     const int N = UP ? 2 * a.F : a.d;
+    if (((UP ? a.d : a.F) / S) % KSTEP != 0) return hipErrorInvalidValue;  // whole K steps per split
     const int NG = N / (16 * NBW * 4);
     dim3 grid((unsigned)((size_t)a.max_tiles * NG * S));
-    hipLaunchKernelGGL((expert_stream<MB, NBW, INT8, UP, U>), grid, dim3(kThreads), 0, s, a, S);
+    hipLaunchKernelGGL((expert_stream<MB, NBW, WQ, UP, U>), grid, dim3(kThreads), 0, s, a, S);
     return hipGetLastError();
 }
 
-template <bool INT8, bool UP>
+template <int WQ, bool UP>
 hipError_t launch_t(const GemmArgs& a, int S, hipStream_t s) {
     switch ((a.bm + 15) / 16) {
-        case 1: return launch_mb<1, INT8, UP>(a, S, s);
-        case 2: return launch_mb<2, INT8, UP>(a, S, s);
+        case 1: return launch_mb<1, WQ, UP>(a, S, s);
+        case 2: return launch_mb<2, WQ, UP>(a, S, s);
         case 3:
-        case 4: return launch_mb<4, INT8, UP>(a, S, s);
+        case 4: return launch_mb<4, WQ, UP>(a, S, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <bool UP>
+hipError_t launch_kind(const GemmArgs& a, int wq, int S, hipStream_t s) {
+    switch (wq) {
+        case kWBf16: return launch_t<kWBf16, UP>(a, S, s);
+        case kWI8: return launch_t<kWI8, UP>(a, S, s);
+        case kWI4: return launch_t<kWI4, UP>(a, S, s);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-hipError_t launch_expert_up_stream(const GemmArgs& a, bool int8, hipStream_t s) {
-    return int8 ? launch_t<true, true>(a, 1, s) : launch_t<false, true>(a, 1, s);
-}
+hipError_t launch_expert_up_stream(const GemmArgs& a, int wq, hipStream_t s) { return launch_kind<true>(a, wq, 1, s); }
 
-hipError_t launch_expert_down_stream(const GemmArgs& a, bool int8, hipStream_t s) {
-    return int8 ? launch_t<true, false>(a, a.ksplit, s) : launch_t<false, false>(a, a.ksplit, s);
+hipError_t launch_expert_down_stream(const GemmArgs& a, int wq, hipStream_t s) {
+    return launch_kind<false>(a, wq, a.ksplit, s);
 }
 
 }  // namespace moe

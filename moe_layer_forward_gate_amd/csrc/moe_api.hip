@@ -112,11 +112,12 @@ int check_desc(const moe_desc* d, const moe_weights* w) {
     const bool f32 = d->act_dtype == MOE_F32 && d->expert_dtype == MOE_F32;
     const bool bf = d->act_dtype == MOE_BF16 && d->expert_dtype == MOE_BF16;
     const bool i8 = d->act_dtype == MOE_BF16 && d->expert_dtype == MOE_I8;
-    if (!(f32 || bf || i8))
+    const bool i4 = d->act_dtype == MOE_BF16 && d->expert_dtype == MOE_I4;
+    if (!(f32 || bf || i8 || i4))
         return fail(MOE_EUNSUPPORTED, "dtype pair (act=%d, expert=%d) not supported", d->act_dtype,
                     d->expert_dtype);
-    if (i8 && (!w->s_gate || !w->s_up || !w->s_down))
-        return fail(MOE_EINVAL, "int8 experts need s_gate, s_up and s_down");
+    if ((i8 || i4) && (!w->s_gate || !w->s_up || !w->s_down))
+        return fail(MOE_EINVAL, "int8 and int4 experts need s_gate, s_up and s_down");
     if (d->shared_d_ff > 0 && (!w->w_shared_gate || !w->ws_gate || !w->ws_up || !w->ws_down))
         return fail(MOE_EINVAL, "shared expert needs w_shared_gate, ws_gate, ws_up and ws_down");
     if (d->n_experts > kMaxExperts) return fail(MOE_EUNSUPPORTED, "n_experts=%d > %d", d->n_experts, kMaxExperts);
@@ -125,6 +126,8 @@ int check_desc(const moe_desc* d, const moe_weights* w) {
     if (d->d_model % dm || d->d_ff % 64)
         return fail(MOE_EUNSUPPORTED, "need d_model %% %d == 0 and d_ff %% 64 == 0 (d_model=%d d_ff=%d)", dm,
                     d->d_model, d->d_ff);
+    if (i4 && d->d_ff % 128)
+        return fail(MOE_EUNSUPPORTED, "int4 experts need d_ff %% 128 == 0 (d_ff=%d)", d->d_ff);
     if (d->shared_d_ff > 0) {
         if (!bf) return fail(MOE_EUNSUPPORTED, "a shared expert needs bf16 experts");
         if (d->shared_d_ff % d->d_ff)
@@ -153,13 +156,20 @@ int create_impl(const moe_desc* desc, const moe_weights* w, moe_layer* L) {
     const size_t dm = d.d_model, F = d.d_ff, E = L->E, Et = L->Et;
     const bool f32 = d.expert_dtype == MOE_F32;
     const bool i8 = d.expert_dtype == MOE_I8;
-    const size_t esz = f32 ? 4 : (i8 ? 1 : 2);
+    const bool i4 = d.expert_dtype == MOE_I4;
+    // bytes per 2 weights (int4 packs two in a byte)
+    const size_t esz2 = f32 ? 8 : (i8 ? 2 : (i4 ? 1 : 4));
     int rc;
     if ((rc = dev_alloc(&L->wr_t, (size_t)L->Ec * dm * 4))) return rc;
     if (!f32 && (rc = dev_alloc(&L->wr_planes, (size_t)3 * ((L->Ec + 15) / 16) * 16 * dm * 2))) return rc;
     if (L->has_bias && (rc = dev_alloc(&L->bias, E * 4))) return rc;
-    if ((rc = dev_alloc(&L->wgu, Et * 2 * F * dm * esz))) return rc;
-    if ((rc = dev_alloc(&L->wdn, Et * F * dm * esz))) return rc;
+    if ((rc = dev_alloc(&L->wgu, Et * F * dm * esz2))) return rc;
+    if ((rc = dev_alloc(&L->wdn, Et * F * dm * esz2 / 2))) return rc;
+    if (i4) {
+        // group scales: the up projection's in packed column order, the down projection's as given
+        if ((rc = dev_alloc(&L->s_gate, E * (dm / 128) * 2 * F * 4))) return rc;
+        if ((rc = dev_alloc(&L->s_down, E * (F / 128) * dm * 4))) return rc;
+    }
     if (i8) {
         if ((rc = dev_alloc(&L->s_gate, E * F * 4))) return rc;
         if ((rc = dev_alloc(&L->s_up, E * F * 4))) return rc;
@@ -201,6 +211,12 @@ int create_impl(const moe_desc* desc, const moe_weights* w, moe_layer* L) {
         HIP_TRY(hipMemcpyAsync(L->wgu, w->w_gate, E * dm * F * 4, hipMemcpyDeviceToDevice, s));
         HIP_TRY(hipMemcpyAsync((char*)L->wgu + E * dm * F * 4, w->w_up, E * dm * F * 4, hipMemcpyDeviceToDevice, s));
         HIP_TRY(hipMemcpyAsync(L->wdn, w->w_down, E * F * dm * 4, hipMemcpyDeviceToDevice, s));
+    } else if (i4) {
+        HIP_TRY(pack_gu_i4((const uint8_t*)w->w_gate, (const uint8_t*)w->w_up, L->E, d.d_model, d.d_ff,
+                           (uint8_t*)L->wgu, s));
+        HIP_TRY(pack_dn_i4((const uint8_t*)w->w_down, L->E, d.d_ff, d.d_model, (uint8_t*)L->wdn, s));
+        HIP_TRY(pack_scales_gu_i4(w->s_gate, w->s_up, L->E, d.d_model, d.d_ff, L->s_gate, s));
+        HIP_TRY(hipMemcpyAsync(L->s_down, w->s_down, E * (F / 128) * dm * 4, hipMemcpyDeviceToDevice, s));
     } else if (i8) {
         HIP_TRY(pack_gu_i8((const int8_t*)w->w_gate, (const int8_t*)w->w_up, L->E, d.d_model, d.d_ff,
                            (int8_t*)L->wgu, s));
@@ -245,9 +261,10 @@ int check_device(const moe_layer* L) {
 }
 
 // Launch plan (host side, from T, k and the layer shape only):
-//  - small batches (T <= 64) stream the weights: row tiles of 16, 32 or 64 rows,
-//    sized so an active expert almost always fits one tile, the down projection's K
-//    split so ~1024 workgroups run;
+//  - small batches (T <= 64), and every batch of an int4 layer, stream the weights: row
+//    tiles of 16, 32 or 64 rows, sized so an active expert almost always fits one tile
+//    (an int4 layer's larger batches take several 64-row tiles per expert, each
+//    streaming the weights again), the down projection's K split so ~1024 workgroups run;
 //  - larger batches use the LDS-tiled MFMA GEMMs (256-row tiles for bf16 weights,
 //    128 for int8), with the down projection's K split when that fills the CUs better.
 struct Plan {
@@ -260,8 +277,9 @@ Plan make_plan(const moe_layer* L, int T) {
     const moe_desc& d = L->desc;
     const bool f32 = d.expert_dtype == MOE_F32;
     const bool i8 = d.expert_dtype == MOE_I8;
+    const bool i4 = d.expert_dtype == MOE_I4;
     const int k = d.top_k;
-    const bool streaming = !f32 && T <= kStreamMaxT;
+    const bool streaming = !f32 && (T <= kStreamMaxT || i4);
     int bm, ksplit = 1;
     if (f32) {
         bm = kBMf32;
@@ -272,7 +290,10 @@ Plan make_plan(const moe_layer* L, int T) {
         bm = need <= 16 ? 16 : (need <= 32 ? 32 : 64);
         const int active = std::min(L->E, T * k) + L->V;
         const int groups = active * (d.d_model / 128);
-        while (ksplit < kStreamMaxSplit && groups * ksplit < 1024 && d.d_ff % (ksplit * 2 * 64) == 0) ksplit *= 2;
+        const int kstep = i4 ? 128 : 64;  // every split a whole number of weight steps
+        while (ksplit < kStreamMaxSplit && groups * ksplit < 1024 && d.d_ff % (ksplit * 2 * kstep) == 0 &&
+               (size_t)T * L->kt * ksplit * 2 <= L->ow_rows)
+            ksplit *= 2;
     } else {
         // bf16: 256-row tiles (the 256 x 256 workgroup tile reads the least LDS and L2 per MFMA
         // and outruns 128-row tiles even when most experts leave their last tile half empty);
@@ -341,6 +362,7 @@ int run_experts(moe_layer* L, const void* x, int T, void* y, const float* topk_w
     const moe_desc& d = L->desc;
     const bool f32 = d.expert_dtype == MOE_F32;
     const bool i8 = d.expert_dtype == MOE_I8;
+    const int wq = d.expert_dtype == MOE_I4 ? kWI4 : (i8 ? kWI8 : kWBf16);
     const int k = d.top_k;
     const bool prof = L->profiling;
     const GemmArgs a{L->tile_start, L->offsets, L->sorted_c, L->Et, L->kt, k, pl.max_tiles, pl.bm, pl.ksplit,
@@ -358,9 +380,9 @@ int run_experts(moe_layer* L, const void* x, int T, void* y, const float* topk_w
         if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));
         HIP_TRY(launch_expert_down_f32(af, s));
     } else if (pl.streaming) {
-        HIP_TRY(launch_expert_up_stream(a, i8, s));
+        HIP_TRY(launch_expert_up_stream(a, wq, s));
         if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));
-        HIP_TRY(launch_expert_down_stream(a, i8, s));
+        HIP_TRY(launch_expert_down_stream(a, wq, s));
     } else {
         HIP_TRY(launch_expert_up_bf16(a, i8, s));
         if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));

@@ -10,6 +10,8 @@
 //   bf16 down:    [Et][d/16][F/32][64][8], column nb*16 + l%16 of W_down
 //   int8:         the same with 64 K rows per block and 16 bytes per lane,
 //                 bytes 0-7 from the block's first 32 rows, bytes 8-15 the next 32
+//   int4:         the same with 128 K rows (one scale group) per block, four
+//                 words per lane, one per 32 rows (see pack_i4_kernel)
 // and the router weight transposed to [Ec][d] (row E = the shared-expert gate).
 // One thread writes one 16-byte lane chunk; runs once per layer.
 #include "common.h"
@@ -90,7 +92,80 @@ hipError_t launch_pack(const T* s0, const T* s1, int E, int K, int N, int64_t ld
     return hipGetLastError();
 }
 
+// int4: one thread per 16-byte lane chunk of a 1 KB block (16 columns x 128 K rows,
+// one scale group). Source: two values per byte along K, low nibble = even row, 4-bit
+// two's complement; packed: word s of lane l holds column l%16, K rows
+// 128*kb + 32*s + 8*(l/16) + r for r = 0, 2, 4, 6 in nibbles 0-3 and r = 1, 3, 5, 7 in
+// nibbles 4-7, as codes q + 8.
+__global__ void pack_i4_kernel(const uint8_t* src0, const uint8_t* src1, int E, int K, int N, bool gu, uint32_t* dst) {
+    const int NB = gu ? 2 * N / 16 : N / 16;
+    const int KB = K / 128;
+    const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t total = (size_t)E * NB * KB * 64;
+    if (q >= total) return;
+    const int ln = (int)(q % 64);
+    size_t rest = q / 64;
+    const int kb = (int)(rest % KB);
+    rest /= KB;
+    const int nb = (int)(rest % NB);
+    const int e = (int)(rest / NB);
+    const uint8_t* src = ((gu && (nb & 1)) ? src1 : src0) + (size_t)e * (K / 2) * N;
+    const int n = (gu ? (nb / 2) : nb) * 16 + ln % 16;
+    uint32_t out[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int k0 = kb * 128 + 32 * w + 8 * (ln / 16);
+        uint32_t word = 0;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int k = k0 + r;
+            const uint32_t code = ((src[(size_t)(k / 2) * N + n] >> (4 * (k & 1))) + 8u) & 15u;  // (q + 8) mod 16
+            const int nib = (r & 1) ? 4 + r / 2 : r / 2;
+            word |= code << (4 * nib);
+        }
+        out[w] = word;
+    }
+    reinterpret_cast<uint4*>(dst)[q] = uint4{out[0], out[1], out[2], out[3]};
+}
+
+// Up-projection group scales [E][d/128][F] (gate, up) into [E][d/128][2F] in packed
+// column order (block nb: gate columns 16*(nb/2).. when even, up when odd).
+__global__ void pack_scales_gu_kernel(const float* sg, const float* su, int E, int G, int F, float* dst) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (size_t)E * G * 2 * F) return;
+    const int p = (int)(i % (2 * F));
+    const size_t eg = i / (2 * F);
+    const int nb = p / 16;
+    const int n = (nb / 2) * 16 + p % 16;
+    dst[i] = ((nb & 1) ? su : sg)[eg * F + n];
+}
+
+hipError_t launch_pack_i4(const uint8_t* s0, const uint8_t* s1, int E, int K, int N, bool gu, uint8_t* dst,
+                          hipStream_t s) {
+    if (K % 128) return hipErrorInvalidValue;
+    const int NB = gu ? 2 * N / 16 : N / 16;
+    const size_t total = (size_t)E * NB * (K / 128) * 64;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(pack_i4_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, s0, s1, E, K, N, gu,
+                       reinterpret_cast<uint32_t*>(dst));
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t pack_gu_i4(const uint8_t* wg, const uint8_t* wu, int E, int d, int F, uint8_t* dst, hipStream_t s) {
+    return launch_pack_i4(wg, wu, E, d, F, true, dst, s);
+}
+hipError_t pack_dn_i4(const uint8_t* wd, int E, int F, int d, uint8_t* dst, hipStream_t s) {
+    return launch_pack_i4(wd, wd, E, F, d, false, dst, s);
+}
+hipError_t pack_scales_gu_i4(const float* sg, const float* su, int E, int d, int F, float* dst, hipStream_t s) {
+    const size_t n = (size_t)E * (d / 128) * 2 * F;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(pack_scales_gu_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, sg, su, E, d / 128,
+                       F, dst);
+    return hipGetLastError();
+}
 
 hipError_t pack_router(const float* wr, const float* wsg, int d, int E, float* wr_t, hipStream_t s) {
     const int Ec = E + (wsg ? 1 : 0);

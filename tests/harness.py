@@ -29,6 +29,9 @@ def gpu_layer(L: "synth.SynthLayer", max_tokens: int, profile: bool = False):
     c = L.cfg
     dev = torch.device("cuda", torch.cuda.current_device())
     t = {k: (v.to(dev).contiguous() if v is not None else None) for k, v in L.tensors().items()}
+    if c.expert_dtype == "i4":  # the library takes int4 weights two to a byte
+        for k in ("w_gate", "w_up", "w_down"):
+            t[k] = synth.pack_int4_pairs(t[k]).contiguous()
     return moe.MoeLayer(
         d_model=c.d_model, n_experts=c.n_experts, d_ff=c.d_ff, top_k=c.top_k, max_tokens=max_tokens,
         act_dtype=c.act_dtype, expert_dtype=c.expert_dtype, w_router=t["w_router"], b_router=t.get("b_router"),

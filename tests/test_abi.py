@@ -82,6 +82,13 @@ def _create(desc, weights):
      _weights(s_gate=1 << 16, s_up=1 << 16, s_down=1 << 16, w_shared_gate=1 << 16, ws_gate=1 << 16,
               ws_up=1 << 16, ws_down=1 << 16), moe.MOE_EUNSUPPORTED),
     (_desc(max_tokens=1 << 29, top_k=2), _weights(), moe.MOE_EUNSUPPORTED),
+    (_desc(expert_dtype=moe.MOE_I4), _weights(), moe.MOE_EINVAL),            # group scales missing
+    (_desc(expert_dtype=moe.MOE_I4, d_ff=192), _weights(s_gate=1 << 16, s_up=1 << 16, s_down=1 << 16),
+     moe.MOE_EUNSUPPORTED),                                                   # int4 needs d_ff % 128
+    (_desc(act_dtype=moe.MOE_F32, expert_dtype=moe.MOE_I4), _weights(), moe.MOE_EUNSUPPORTED),
+    (_desc(expert_dtype=moe.MOE_I4, shared_d_ff=512),
+     _weights(s_gate=1 << 16, s_up=1 << 16, s_down=1 << 16, w_shared_gate=1 << 16, ws_gate=1 << 16,
+              ws_up=1 << 16, ws_down=1 << 16), moe.MOE_EUNSUPPORTED),    # shared expert needs bf16
 ])
 def test_create_rejects(desc, weights, status):
     rc, h = _create(desc, weights)

@@ -4,8 +4,8 @@ Covers: k = 1 and k = E, expert counts that are not multiples of 8 or 16 (up to 
 128-expert limit), the smallest supported widths, T at the max_tokens bound and on
 both sides of the streaming / tiled switch, every token routed to one expert, an
 expert holding more rows than the streaming row tile (more tiles than active experts), a
-shared expert of one and of sixteen d_ff slices, int8 output channels whose
-scale is zero, and the decode routing paths for routers wider than 16 columns.
+shared expert of one and of sixteen d_ff slices, int8 output channels and int4
+groups whose scale is zero, the smallest int4 widths, and the decode routing paths for routers wider than 16 columns.
 """
 import pytest
 import torch
@@ -92,6 +92,18 @@ def test_int8_zero_scale_channels():
         L.w_down[1, :, 7] = 0
         L.s_down[1, 7] = 0
     _run(synth.get_config("int8_mixtral22b", d_model=256, d_ff=128), [1, 300], mutate=zero)
+
+
+def test_int4_zero_groups_and_smallest_width():
+    # groups quantised from all-zero weights have s = 0 and q = 0; d_model = d_ff = 128
+    # is one scale group along each input axis
+    def zero(L):
+        L.w_gate[2, 128:256, 5] = 0
+        L.s_gate[2, 1, 5] = 0
+        L.w_down[1, 0:128, 7] = 0
+        L.s_down[1, 0, 7] = 0
+    _run(synth.get_config("int4_mixtral22b", d_model=256, d_ff=256), [1, 300], mutate=zero)
+    _run(synth.get_config("int4_mixtral22b", d_model=128, d_ff=128), [1, 70])
 
 
 def test_wide_router_decode_paths():

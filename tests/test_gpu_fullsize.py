@@ -60,3 +60,7 @@ def test_skewed_bf16_full():
 
 def test_int8_mixtral22b_full():
     _run("int8_mixtral22b", [1, 16, 256])
+
+
+def test_int4_mixtral22b_full():
+    _run("int4_mixtral22b", [1, 16, 256])

@@ -1,6 +1,6 @@
 """GPU parity of libmoe against the CPU oracle, through the C ABI.
 
-Reduced-width layers keep every kernel path (fp32 VALU, bf16 MFMA, int8 MFMA,
+Reduced-width layers keep every kernel path (fp32 VALU, bf16 MFMA, int8 and int4 MFMA,
 shared expert, skewed routing with empty and overfull experts, ragged row tiles)
 at sizes the oracle evaluates in full within seconds. Full-size layers live in
 test_gpu_fullsize.py.
@@ -63,6 +63,13 @@ def test_skewed_many_experts_reduced_bf16():
 def test_int8_reduced():
     cfg = synth.get_config("int8_mixtral22b", d_model=512, d_ff=1024)
     _run(cfg, [1, 16, 256, 1024, 3072])
+
+
+def test_int4_reduced():
+    # int4 group-wise weights run on the streaming kernels at every T: row tiles of 16, 32
+    # and 64 rows (one to four 16-row blocks), and several 64-row tiles per expert past 64
+    cfg = synth.get_config("int4_mixtral22b", d_model=512, d_ff=1024)
+    _run(cfg, [1, 2, 16, 40, 64, 65, 256, 1000])
 
 
 def test_tiny_batches_single_workgroup_route():

@@ -1,7 +1,7 @@
 """GPU parity of moe_forward_routed: the layer fed a routing drawn without the router
 ([pptc §3.4]: the engine consumes routing results produced elsewhere, token-major).
 
-Covers: fp32, bf16, int8 and shared-expert layers; T on both sides of the
+Covers: fp32, bf16, int8, int4 and shared-expert layers; T on both sides of the
 streaming / tiled switch and of the single / multi-workgroup scatter; repeated
 experts within a token and ids outside [0, E) (read as expert 0 at weight 0); the
 scatter tables bit for bit; and bit-identity with moe_forward when it is given
@@ -61,6 +61,10 @@ def test_routed_bf16():
 
 def test_routed_int8():
     _run(synth.get_config("int8_mixtral22b", d_model=256, d_ff=128), [1, 16, 300])
+
+
+def test_routed_int4():
+    _run(synth.get_config("int4_mixtral22b", d_model=256, d_ff=256), [1, 16, 300])
 
 
 def test_routed_shared_expert_and_many_experts():
