@@ -35,9 +35,12 @@ __device__ __forceinline__ uint32_t i8x2_bf16(uint32_t w, int sh) {
 // 136 * sum(a) over the group is taken off after the MFMAs. A lane's 32-bit word holds
 // K rows 2i in nibble i and 2i+1 in nibble i+4 (i < 4), so word >> 4i yields the pair
 // (2i, 2i+1) in the two bf16 halves.
-__device__ __forceinline__ u32x4 i4x8_bf16(uint32_t w) {
-    return u32x4{(w & 0x000F000Fu) | 0x43004300u, ((w >> 4) & 0x000F000Fu) | 0x43004300u,
-                 ((w >> 8) & 0x000F000Fu) | 0x43004300u, ((w >> 12) & 0x000F000Fu) | 0x43004300u};
+// The caller passes the nibble mask in a register (opaque to the compiler), so that each
+// pair is one v_and_or_b32 with the bf16 pattern as its literal (a VOP3 instruction
+// reads at most one literal or scalar).
+__device__ __forceinline__ u32x4 i4x8_bf16(uint32_t w, uint32_t m) {
+    return u32x4{(w & m) | 0x43004300u, ((w >> 4) & m) | 0x43004300u, ((w >> 8) & m) | 0x43004300u,
+                 ((w >> 12) & m) | 0x43004300u};
 }
 
 template <int MB, int NBW, int WQ, bool UP, int U>  // WQ: weight kind (kWBf16, kWI8, kWI4)
@@ -96,6 +99,9 @@ __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
         aptr[mb] = base + kbase + 8 * (lane / 16);
     }
 
+    uint32_t nib_mask = 0x000F000Fu;  // int4 unpacking (see i4x8_bf16)
+    if constexpr (INT4) asm volatile("" : "+v"(nib_mask));
+
     f32x4 acc[MB][NBW];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -117,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
                                                                          kh ? zr[mb] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
                 for (int j = 0; j < NBW; ++j) {
-                    const bf16x8 bw = __builtin_bit_cast(bf16x8, i4x8_bf16(bb[j][kh]));
+                    const bf16x8 bw = __builtin_bit_cast(bf16x8, i4x8_bf16(bb[j][kh], nib_mask));
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb)
                         if (mb < mb_act)
@@ -263,19 +269,31 @@ __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
     }
 }
 
-template <int MB, int WQ, bool UP>
-hipError_t launch_mb(const GemmArgs& a, int S, hipStream_t s) {
-    constexpr int NBW = 2;
+template <int MB, int NBW, int WQ, bool UP>
+hipError_t launch_nbw(const GemmArgs& a, int S, hipStream_t s) {
     // K-steps per round (two rounds are in flight per wave); an int4 step holds four
     // 32-K token fragments per row block, so wide row tiles take one step per round
     constexpr int U = WQ == kWI4 ? (MB <= 1 ? 2 : 1) : WQ == kWI8 ? 2 : (MB <= 2 ? 4 : 2);
     constexpr int KSTEP = WQ == kWI4 ? 128 : WQ == kWI8 ? 64 : 32;
     const int N = UP ? 2 * a.F : a.d;
     if (((UP ? a.d : a.F) / S) % KSTEP != 0) return hipErrorInvalidValue;  // whole K steps per split
+    if (N % (16 * NBW * 4) != 0) return hipErrorInvalidValue;             // whole column groups
     const int NG = N / (16 * NBW * 4);
     dim3 grid((unsigned)((size_t)a.max_tiles * NG * S));
     hipLaunchKernelGGL((expert_stream<MB, NBW, WQ, UP, U>), grid, dim3(kThreads), 0, s, a, S);
     return hipGetLastError();
+}
+
+template <int MB, int WQ, bool UP>
+hipError_t launch_mb(const GemmArgs& a, int S, hipStream_t s) {
+    // int4: four column blocks per wave (the token fragments and the group sums serve
+    // twice the weights) when that still leaves ~4 workgroups per CU and the row tile is
+    // narrow enough for the registers
+    if constexpr (WQ == kWI4 && MB <= 2) {
+        const int N = UP ? 2 * a.F : a.d;
+        if (N % 256 == 0 && (size_t)a.max_tiles * (N / 256) * S >= 1024) return launch_nbw<MB, 4, WQ, UP>(a, S, s);
+    }
+    return launch_nbw<MB, 2, WQ, UP>(a, S, s);
 }
 
 template <int WQ, bool UP>
