@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--instances", type=int, default=4)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
+    ap.add_argument("--streams", type=int, default=1,
+                    help="S > 1: S layer instances forwarded concurrently on S streams (decode throughput)")
     ap.add_argument("--routed", action="store_true",
                     help="time moe_forward_routed on a drawn routing (no gate) instead of moe_forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -239,6 +241,37 @@ def summarize(cfg, res):
         active_experts=layer["active"], roofline=rf)
 
 
+def run_streams(cfg, T, steps, warmup, S, torch, synth):
+    """S independent layer instances, each on its own HIP stream (default priority), all
+    enqueued every step: the decode throughput of concurrent layers (one layer per stream,
+    as the library requires). Returns the wall time per step and the algorithmic bytes of
+    one step (every instance's expert weights with rows, router, tokens)."""
+    insts = build_instances(cfg, S, T, torch, synth, None)
+    streams = [torch.cuda.Stream() for _ in range(S)]
+    cur = torch.cuda.current_stream()
+    for st in streams:
+        st.wait_stream(cur)  # the inputs were written on the current stream
+
+    def step():
+        for (lay, x, out), st in zip(insts, streams):
+            lay.forward(x, out=out, stream=st)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_bytes = sum(kernel_work(cfg, out.expert_counts.cpu().numpy(), T)[2]["bytes"] for _, _, out in insts)
+    for lay, _, _ in insts:
+        lay.close()
+    del insts
+    torch.cuda.empty_cache()
+    return dict(ms_per_step=1e3 * wall / steps, step_bytes=step_bytes)
+
+
 def cpu_baseline(cfg, layer_cpu, x_cpu, n_tok, min_s, routing=None):
     """The oracle as it stands, on the first n_tok tokens of the same batch, repeated (at most
     4 passes) until min_s seconds have passed (with `routing` (idx, w, g_s): the oracle of
@@ -325,6 +358,21 @@ def main():
     cfg = synth.get_config(args.config)
     T = args.tokens or max(cfg.tokens)
     print(f"[bench] {cfg.name} T={T} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
+    if args.streams > 1:
+        r = run_streams(cfg, T, args.steps, args.warmup, args.streams, torch, synth)
+        ach = r["step_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
+        print(json.dumps({
+            "metric": "MoE-layer tokens/s; decode HBM TB/s and prefill MFMA TFLOP/s vs roofline",
+            "value": args.streams * T / (r["ms_per_step"] * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": {"bf16": "bf16", "f32": "f32"}[cfg.act_dtype] + {"i8": "+i8w", "i4": "+i4w"}.get(cfg.expert_dtype, ""),
+            "data": "synthetic",
+            "config": {"workload": f"{cfg.name}: {args.streams} independent layers, one per stream, "
+                                   f"{T} tokens each", "tokens": T, "streams": args.streams},
+            "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": "whole layers, all streams"}}))
+        return
     want_cpu = not args.no_cpu_baseline
     res, layer0, x0 = run_workload(cfg, T, args.steps, args.warmup, args.instances, torch, synth,
                                    keep_layer0=want_cpu, graph=args.graph, routed=args.routed)
