@@ -180,6 +180,7 @@ class OracleLayer:
     ws_up: Optional[np.ndarray] = None
     ws_down: Optional[np.ndarray] = None
     group: Optional[int] = None  # int4: input rows per scale (scales [E, in/group, out])
+    gate_clamp: bool = False     # clamp the routed logits to [-50, 50] before top-k and softmax
 
     @property
     def n_experts(self) -> int:
@@ -265,6 +266,10 @@ def moe_forward(x, layer: OracleLayer, routing=None, tokens: Optional[Sequence[i
     k = layer.top_k
     E = layer.n_experts
     logits = router_logits(x, layer.w_router, layer.b_router)
+    if layer.gate_clamp:
+        # [0539edu §5.2]: the gate's clip option bounds the logits to [-50, 50] before the
+        # softmax; the selection and the weights both use the bounded values
+        logits = np.clip(logits, -50.0, 50.0)
     idx, margin = select_topk(logits, k)
     if routing is not None:
         idx = np.asarray(routing, dtype=np.int64)

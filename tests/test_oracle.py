@@ -472,3 +472,35 @@ def test_dense_masked_bruteforce_int4():
     out = oracle.moe_forward(x, lay)
     ref = _dense_masked(x, lay)
     assert np.abs(out["y"] - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
+# ---------------------------------------------------------------- the gate's clamp option
+def test_gate_clamp_hand_fixture():
+    # zero router, bias [60, 55, 0, -70, 52]: clamped to [50, 50, 0, -50, 50] the three
+    # largest tie, so the lower ids win and the weights are equal
+    E, d = 5, 4
+    w_r = np.zeros((d, E))
+    b = np.array([60.0, 55.0, 0.0, -70.0, 52.0])
+    wg = np.zeros((E, d, 2)); wd = np.zeros((E, 2, d))
+    x = np.ones((1, d))
+    for k, clamped, raw in ((2, [0, 1], [0, 1]), (3, [0, 1, 4], [0, 1, 4])):
+        lay = oracle.OracleLayer(w_router=w_r, w_gate=wg, w_up=wg, w_down=wd, top_k=k, b_router=b)
+        ref = oracle.moe_forward(x, lay)
+        assert ref["idx"][0].tolist() == raw
+        np.testing.assert_allclose(ref["w"][0], softmax(b[raw]), rtol=1e-15)
+        lay.gate_clamp = True
+        out = oracle.moe_forward(x, lay)
+        assert out["idx"][0].tolist() == clamped
+        np.testing.assert_allclose(out["w"][0], np.full(k, 1.0 / k), rtol=1e-15)
+        assert out["margin"][0] == 0.0 if k == 2 else out["margin"][0] == 50.0  # tie at 50 / 50 vs 0
+
+
+def test_gate_clamp_inactive_inside_bounds():
+    rng = np.random.default_rng(31)
+    lay = _rand_layer(rng, d=16, E=6, F=8, k=2, bias=True)
+    x = rng.standard_normal((9, 16))
+    a = oracle.moe_forward(x, lay)
+    assert np.abs(a["logits"]).max() < 50
+    lay.gate_clamp = True
+    b = oracle.moe_forward(x, lay)
+    assert np.array_equal(a["idx"], b["idx"]) and np.array_equal(a["y"], b["y"])
