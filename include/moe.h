@@ -84,6 +84,9 @@ typedef struct moe_desc {
     int32_t expert_dtype;   /* moe_dtype of the expert weights */
     int32_t shared_d_ff;    /* 0: no shared expert */
     int32_t profile;        /* 1: start with per-stage HIP events on (moe_set_profiling) */
+    int32_t gate_clamp;     /* 1: clamp the routed logits to [-50, 50] before the top-k and
+                               the softmax ([0539edu §5.2], the gate's clip option against
+                               overflow); 0: use them as computed */
 } moe_desc;
 
 /* Layer weights (device pointers, read only during moe_layer_create).

@@ -39,7 +39,7 @@ class MoeError(RuntimeError):
 class MoeDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "d_model", "n_experts", "d_ff", "top_k", "max_tokens", "act_dtype", "expert_dtype",
-        "shared_d_ff", "profile")]
+        "shared_d_ff", "profile", "gate_clamp")]
 
 
 class MoeWeights(ctypes.Structure):
@@ -166,7 +166,7 @@ class MoeLayer:
     def __init__(self, *, d_model: int, n_experts: int, d_ff: int, top_k: int, max_tokens: int,
                  act_dtype: str, expert_dtype: str, w_router, w_gate, w_up, w_down, b_router=None,
                  s_gate=None, s_up=None, s_down=None, shared_d_ff: int = 0, w_shared_gate=None,
-                 ws_gate=None, ws_up=None, ws_down=None, profile: bool = False):
+                 ws_gate=None, ws_up=None, ws_down=None, profile: bool = False, gate_clamp: bool = False):
         import torch
         self.torch = torch
         self.d_model, self.n_experts, self.d_ff, self.top_k = d_model, n_experts, d_ff, top_k
@@ -180,7 +180,7 @@ class MoeLayer:
             if t is not None and (not t.is_cuda or not t.is_contiguous()):
                 raise ValueError(f"{name} must be a contiguous GPU tensor")
         desc = MoeDesc(d_model, n_experts, d_ff, top_k, max_tokens, self._DT[act_dtype],
-                       self._DT[expert_dtype], shared_d_ff, 1 if profile else 0)
+                       self._DT[expert_dtype], shared_d_ff, 1 if profile else 0, 1 if gate_clamp else 0)
         w = MoeWeights(*[_ptr(tensors[f]) for f, _ in MoeWeights._fields_])
         self._h = moe_layer_create(desc, w)
 

@@ -29,12 +29,17 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // ------------------------------------------------------------------ launchers
+// Gate flags: kGateShared -- router column E is the shared expert's gate (its sigmoid
+// goes to gs); kGateClamp -- the routed logits are clamped to [-kGateClampAbs,
+// kGateClampAbs] before the top-k and the softmax.
+constexpr int kGateShared = 1, kGateClamp = 2;
+constexpr float kGateClampAbs = 50.0f;
 // Gate: router logits, top-k with (logit desc, id asc) order, softmax weights over
-// the chosen logits, and (when has_shared) the shared-expert sigmoid gate read
+// the chosen logits, and (with kGateShared) the shared-expert sigmoid gate read
 // from router column E. wr_t is the router weight transposed to [Ec][d].
 // planes: the router weight split into three bf16 planes in fragment order (bf16 tokens only).
 hipError_t launch_gate(const void* x, bool x_bf16, const float* wr_t, const void* planes, const float* bias, int T,
-                       int d, int E, bool has_shared, int k, int32_t* idx, float* w, float* gs, hipStream_t s);
+                       int d, int E, int gflags, int k, int32_t* idx, float* w, float* gs, hipStream_t s);
 
 // Scatter: counts, offsets and the stable by-expert permutation of the T*k routed
 // assignments, V shared virtual experts appended (each takes every token), and the
@@ -61,13 +66,13 @@ hipError_t launch_scatter_wide(const int32_t* idx, int T, int E, int k, int V, i
 bool gate_split_fits(int T, int k);
 size_t gate_split_workspace(int T, int d, int E, bool has_shared);
 hipError_t launch_gate_split(const void* x, bool x_bf16, const float* wr_t, const float* bias, int T, int d, int E,
-                             bool has_shared, int k, int32_t* idx, float* w, float* gs, int V, int bm,
+                             int gflags, int k, int32_t* idx, float* w, float* gs, int V, int bm,
                              const ScatterOut& o, float* part, hipStream_t s);
 // Gate then Scatter in a single workgroup, for tiny batches: up to 4 tokens,
 // d_model <= 8192, at most 16 router columns (experts + shared gate).
 bool gate_scatter_small_fits(int T, int d, int E, bool has_shared, bool x_bf16);
 hipError_t launch_gate_scatter_small(const void* x, bool x_bf16, const float* wr_t, const float* bias, int T, int d,
-                                     int E, bool has_shared, int k, int32_t* idx, float* w, float* gs, int V,
+                                     int E, int gflags, int k, int32_t* idx, float* w, float* gs, int V,
                                      int bm, const ScatterOut& o, hipStream_t s);
 
 // Grouped expert GEMMs on bf16 MFMA (expert weights bf16 or int8 in fragment order).

@@ -79,12 +79,20 @@ __device__ __forceinline__ float wave_sum_many(float (&v)[N]) {
 }
 
 // One wave: top-k of logits[0..E) (bias already added), weights, shared gate.
-// `logits` may live in LDS; E <= 128, k <= 64.
-__device__ void wave_topk_write(const float* logits, int E, int k, bool has_shared, int t, int32_t* idx,
+// `logits` may live in LDS; E <= 128, k <= 64. With kGateClamp the routed logits are
+// first clamped to [-50, 50] ([0539edu §5.2]: the gate's clip option bounds the logits
+// before the softmax), so the top-k and the weights both see the clamped values.
+__device__ void wave_topk_write(const float* logits, int E, int k, int gflags, int t, int32_t* idx,
                                 float* w, float* gs, int32_t* ids_copy = nullptr) {
+    const bool has_shared = (gflags & kGateShared) != 0;
+    const bool clamp = (gflags & kGateClamp) != 0;
+    auto logit = [&](int e) {
+        const float v = logits[e];
+        return clamp ? fminf(fmaxf(v, -kGateClampAbs), kGateClampAbs) : v;
+    };
     const int lane = threadIdx.x % kWave;
-    uint64_t k0 = lane < E ? topk_key(logits[lane], lane) : 0ull;
-    uint64_t k1 = lane + kWave < E ? topk_key(logits[lane + kWave], lane + kWave) : 0ull;
+    uint64_t k0 = lane < E ? topk_key(logit(lane), lane) : 0ull;
+    uint64_t k1 = lane + kWave < E ? topk_key(logit(lane + kWave), lane + kWave) : 0ull;
     int my_e = -1;     // lane j < k keeps slot j's expert
     for (int j = 0; j < k; ++j) {
         uint64_t m = wave_max_u64(k0 > k1 ? k0 : k1);
@@ -94,8 +102,8 @@ __device__ void wave_topk_write(const float* logits, int E, int k, bool has_shar
         if (lane == j) my_e = e;
     }
     // softmax over the chosen logits, relative to slot 0 (the maximum)
-    float l0 = __shfl(my_e >= 0 ? logits[my_e] : 0.0f, 0, kWave);
-    float ex = lane < k ? expf(logits[my_e] - l0) : 0.0f;
+    float l0 = __shfl(my_e >= 0 ? logit(my_e) : 0.0f, 0, kWave);
+    float ex = lane < k ? expf(logit(my_e) - l0) : 0.0f;
     float sum = wave_sum(ex);
     if (lane < k) {
         idx[(size_t)t * k + lane] = my_e;
@@ -136,7 +144,7 @@ constexpr int kRowXC = 4;
 template <typename XT>
 __global__ __launch_bounds__(256) void gate_rowdot(const XT* __restrict__ x, const float* __restrict__ wr_t,
                                                    const float* __restrict__ bias, int d, int E, int Ec, int k,
-                                                   bool has_shared, int32_t* __restrict__ idx,
+                                                   int gflags, int32_t* __restrict__ idx,
                                                    float* __restrict__ w, float* __restrict__ gs) {
     __shared__ float part[4][kMaxExperts + 8];
     __shared__ float logits[kMaxExperts + 8];
@@ -199,7 +207,7 @@ __global__ __launch_bounds__(256) void gate_rowdot(const XT* __restrict__ x, con
         logits[tid] = (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]) + b;
     }
     __syncthreads();
-    if (wave == 0) wave_topk_write(logits, E, k, has_shared, t, idx, w, gs);
+    if (wave == 0) wave_topk_write(logits, E, k, gflags, t, idx, w, gs);
 }
 
 // ---------------------------------------------------------------- prefill path, bf16 tokens
@@ -212,8 +220,9 @@ __global__ __launch_bounds__(256) void gate_rowdot(const XT* __restrict__ x, con
 template <int NB, int TB>
 __global__ __launch_bounds__(256) void gate_mfma(const bf16_t* __restrict__ x, const u32x4* __restrict__ planes,
                                                  const float* __restrict__ bias, int T, int d, int E, int k,
-                                                 bool has_shared, int32_t* __restrict__ idx, float* __restrict__ w,
+                                                 int gflags, int32_t* __restrict__ idx, float* __restrict__ w,
                                                  float* __restrict__ gs) {
+    const bool has_shared = (gflags & kGateShared) != 0;
     constexpr int LP = NB * 16 + 1;
     __shared__ float part[4][16 * LP];
     __shared__ float logits[16 * TB * LP];
@@ -281,7 +290,7 @@ __global__ __launch_bounds__(256) void gate_mfma(const bf16_t* __restrict__ x, c
         __syncthreads();
     }
     for (int r = wave; r < 16 * TB; r += 4)
-        if (t0 + r < T) wave_topk_write(logits + r * LP, E, k, has_shared, t0 + r, idx, w, gs);
+        if (t0 + r < T) wave_topk_write(logits + r * LP, E, k, gflags, t0 + r, idx, w, gs);
 }
 
 // ---------------------------------------------------------------- prefill path, fp32 tokens
@@ -294,7 +303,7 @@ constexpr int kKC = 32;
 template <typename XT, int EJ>
 __global__ __launch_bounds__(256) void gate_tiled(const XT* __restrict__ x, const float* __restrict__ wr_t,
                                                   const float* __restrict__ bias, int T, int d, int E, int Ec,
-                                                  int k, bool has_shared, int32_t* __restrict__ idx,
+                                                  int k, int gflags, int32_t* __restrict__ idx,
                                                   float* __restrict__ w, float* __restrict__ gs) {
     constexpr int ECP = 16 * EJ;
     constexpr int XP = kTB + 4;                       // padded token stride of the x tile
@@ -398,7 +407,7 @@ __global__ __launch_bounds__(256) void gate_tiled(const XT* __restrict__ x, cons
     __syncthreads();
     const int wave = tid / kWave;
     for (int r = wave; r < kTB; r += 4) {
-        if (t0 + r < T) wave_topk_write(lt + r * LP, E, k, has_shared, t0 + r, idx, w, gs);
+        if (t0 + r < T) wave_topk_write(lt + r * LP, E, k, gflags, t0 + r, idx, w, gs);
     }
 }
 
@@ -420,7 +429,7 @@ struct SmallGate {
 template <typename XT>
 __global__ __launch_bounds__(1024) void gate_scatter_small(const XT* __restrict__ x, const float* __restrict__ wr_t,
                                                            const float* __restrict__ bias, int T, int d, int E,
-                                                           int Ec, int k, bool has_shared, int32_t* __restrict__ idx,
+                                                           int Ec, int k, int gflags, int32_t* __restrict__ idx,
                                                            float* __restrict__ w, float* __restrict__ gs, int V,
                                                            int bm, ScatterOut o) {
     constexpr int MT = SmallGate<XT>::T, EC = SmallGate<XT>::EC, EG = SmallGate<XT>::EG;
@@ -490,7 +499,7 @@ __global__ __launch_bounds__(1024) void gate_scatter_small(const XT* __restrict_
         }
     }
     __syncthreads();
-    if (wave < T) wave_topk_write(logits[wave], E, k, has_shared, wave, idx, w, gs, ids);
+    if (wave < T) wave_topk_write(logits[wave], E, k, gflags, wave, idx, w, gs, ids);
     __syncthreads();
     scatter_block<NW>(ids, T, E, k, V, bm, o, sm);
 }
@@ -565,7 +574,7 @@ __global__ __launch_bounds__(1024) void gate_partial(const XT* __restrict__ x, c
 constexpr int kFinishT = 64;  // tokens per gate_finish (the decode bound)
 
 __global__ __launch_bounds__(1024) void gate_finish(const float* __restrict__ part, int KS, int NC, int T, int E,
-                                                    int Ec, const float* __restrict__ bias, int k, bool has_shared,
+                                                    int Ec, const float* __restrict__ bias, int k, int gflags,
                                                     int32_t* __restrict__ idx, float* __restrict__ w,
                                                     float* __restrict__ gs, int V, int bm, ScatterOut o) {
     constexpr int NW = 16;
@@ -587,19 +596,19 @@ __global__ __launch_bounds__(1024) void gate_finish(const float* __restrict__ pa
         logits[t][e] = v + ((bias && e < E) ? bias[e] : 0.0f);
     }
     __syncthreads();
-    for (int t = wave; t < T; t += NW) wave_topk_write(logits[t], E, k, has_shared, t, idx, w, gs, ids);
+    for (int t = wave; t < T; t += NW) wave_topk_write(logits[t], E, k, gflags, t, idx, w, gs, ids);
     __syncthreads();
     scatter_block<NW>(ids, T, E, k, V, bm, o, sm);
 }
 
 template <int TB>
 hipError_t launch_gate_mfma_tb(int NB, const bf16_t* x, const u32x4* planes, const float* bias, int T, int d, int E,
-                               int k, bool has_shared, int32_t* idx, float* w, float* gs, hipStream_t s) {
+                               int k, int gflags, int32_t* idx, float* w, float* gs, hipStream_t s) {
     dim3 grid((T + 16 * TB - 1) / (16 * TB));
     switch (NB) {
 #define GATE_MFMA_CASE(J)                                                                                          \
     case J:                                                                                                        \
-        hipLaunchKernelGGL((gate_mfma<J, TB>), grid, dim3(256), 0, s, x, planes, bias, T, d, E, k, has_shared, idx, \
+        hipLaunchKernelGGL((gate_mfma<J, TB>), grid, dim3(256), 0, s, x, planes, bias, T, d, E, k, gflags, idx, \
                            w, gs);                                                                                 \
         break;
         GATE_MFMA_CASE(1) GATE_MFMA_CASE(2) GATE_MFMA_CASE(3) GATE_MFMA_CASE(4) GATE_MFMA_CASE(5)
@@ -612,18 +621,19 @@ hipError_t launch_gate_mfma_tb(int NB, const bf16_t* x, const u32x4* planes, con
 }
 
 hipError_t launch_gate_mfma_nb(int TB, int NB, const bf16_t* x, const u32x4* planes, const float* bias, int T, int d,
-                               int E, int k, bool has_shared, int32_t* idx, float* w, float* gs, hipStream_t s) {
-    if (TB == 4) return launch_gate_mfma_tb<4>(NB, x, planes, bias, T, d, E, k, has_shared, idx, w, gs, s);
-    if (TB == 2) return launch_gate_mfma_tb<2>(NB, x, planes, bias, T, d, E, k, has_shared, idx, w, gs, s);
-    return launch_gate_mfma_tb<1>(NB, x, planes, bias, T, d, E, k, has_shared, idx, w, gs, s);
+                               int E, int k, int gflags, int32_t* idx, float* w, float* gs, hipStream_t s) {
+    if (TB == 4) return launch_gate_mfma_tb<4>(NB, x, planes, bias, T, d, E, k, gflags, idx, w, gs, s);
+    if (TB == 2) return launch_gate_mfma_tb<2>(NB, x, planes, bias, T, d, E, k, gflags, idx, w, gs, s);
+    return launch_gate_mfma_tb<1>(NB, x, planes, bias, T, d, E, k, gflags, idx, w, gs, s);
 }
 
 template <typename XT>
 hipError_t launch_gate_t(const XT* x, const float* wr_t, const u32x4* planes, const float* bias, int T, int d, int E,
-                         bool has_shared, int k, int32_t* idx, float* w, float* gs, hipStream_t s) {
+                         int gflags, int k, int32_t* idx, float* w, float* gs, hipStream_t s) {
+    const bool has_shared = (gflags & kGateShared) != 0;
     const int Ec = E + (has_shared ? 1 : 0);
     if (T <= 64 && d <= 2048 * kRowXC) {
-        hipLaunchKernelGGL((gate_rowdot<XT>), dim3(T), dim3(256), 0, s, x, wr_t, bias, d, E, Ec, k, has_shared, idx, w,
+        hipLaunchKernelGGL((gate_rowdot<XT>), dim3(T), dim3(256), 0, s, x, wr_t, bias, d, E, Ec, k, gflags, idx, w,
                            gs);
     } else if (planes != nullptr && (d / 32) >= 4) {
         // token blocks per workgroup: as many as keep >= 256 workgroups (up to 4)
@@ -632,7 +642,7 @@ hipError_t launch_gate_t(const XT* x, const float* wr_t, const u32x4* planes, co
 #else
         const int TB = T >= 16 * 4 * 256 ? 4 : (T >= 16 * 2 * 256 ? 2 : 1);
 #endif
-        return launch_gate_mfma_nb(TB, (Ec + 15) / 16, (const bf16_t*)x, planes, bias, T, d, E, k, has_shared, idx, w,
+        return launch_gate_mfma_nb(TB, (Ec + 15) / 16, (const bf16_t*)x, planes, bias, T, d, E, k, gflags, idx, w,
                                    gs, s);
     } else {
         const int EJ = (Ec + 15) / 16;
@@ -641,7 +651,7 @@ hipError_t launch_gate_t(const XT* x, const float* wr_t, const u32x4* planes, co
 #define GATE_CASE(J)                                                                                          \
     case J:                                                                                                   \
         hipLaunchKernelGGL((gate_tiled<XT, J>), grid, dim3(256), 0, s, x, wr_t, bias, T, d, E, Ec, k,         \
-                           has_shared, idx, w, gs);                                                           \
+                           gflags, idx, w, gs);                                                               \
         break;
             GATE_CASE(1) GATE_CASE(2) GATE_CASE(3) GATE_CASE(4) GATE_CASE(5)
             GATE_CASE(6) GATE_CASE(7) GATE_CASE(8) GATE_CASE(9)
@@ -663,8 +673,9 @@ size_t gate_split_workspace(int T, int d, int E, bool has_shared) {
 }
 
 hipError_t launch_gate_split(const void* x, bool x_bf16, const float* wr_t, const float* bias, int T, int d, int E,
-                             bool has_shared, int k, int32_t* idx, float* w, float* gs, int V, int bm,
+                             int gflags, int k, int32_t* idx, float* w, float* gs, int V, int bm,
                              const ScatterOut& o, float* part, hipStream_t s) {
+    const bool has_shared = (gflags & kGateShared) != 0;
     if (!gate_split_fits(T, k) || d % 32 || E > kMaxExperts || E + V > kMaxEt) return hipErrorInvalidValue;
     const int Ec = E + (has_shared ? 1 : 0);
     const int NB = (Ec + 15) / 16, KS = (d + kPartK - 1) / kPartK;
@@ -677,7 +688,7 @@ hipError_t launch_gate_split(const void* x, bool x_bf16, const float* wr_t, cons
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(gate_finish, dim3(1), dim3(1024), 0, s, (const float*)part, KS, NB * 16, T, E, Ec, bias, k,
-                       has_shared, idx, w, gs, V, bm, o);
+                       gflags, idx, w, gs, V, bm, o);
     return hipGetLastError();
 }
 
@@ -687,25 +698,26 @@ bool gate_scatter_small_fits(int T, int d, int E, bool has_shared, bool x_bf16) 
 }
 
 hipError_t launch_gate_scatter_small(const void* x, bool x_bf16, const float* wr_t, const float* bias, int T, int d,
-                                     int E, bool has_shared, int k, int32_t* idx, float* w, float* gs, int V,
+                                     int E, int gflags, int k, int32_t* idx, float* w, float* gs, int V,
                                      int bm, const ScatterOut& o, hipStream_t s) {
+    const bool has_shared = (gflags & kGateShared) != 0;
     if (!gate_scatter_small_fits(T, d, E, has_shared, x_bf16) || E + V > kMaxEt) return hipErrorInvalidValue;
     const int Ec = E + (has_shared ? 1 : 0);
     if (x_bf16)
         hipLaunchKernelGGL(gate_scatter_small<bf16_t>, dim3(1), dim3(1024), 0, s, (const bf16_t*)x, wr_t, bias, T, d,
-                           E, Ec, k, has_shared, idx, w, gs, V, bm, o);
+                           E, Ec, k, gflags, idx, w, gs, V, bm, o);
     else
         hipLaunchKernelGGL(gate_scatter_small<float>, dim3(1), dim3(1024), 0, s, (const float*)x, wr_t, bias, T, d,
-                           E, Ec, k, has_shared, idx, w, gs, V, bm, o);
+                           E, Ec, k, gflags, idx, w, gs, V, bm, o);
     return hipGetLastError();
 }
 
 hipError_t launch_gate(const void* x, bool x_bf16, const float* wr_t, const void* planes, const float* bias, int T,
-                       int d, int E, bool has_shared, int k, int32_t* idx, float* w, float* gs, hipStream_t s) {
+                       int d, int E, int gflags, int k, int32_t* idx, float* w, float* gs, hipStream_t s) {
     if (x_bf16)
-        return launch_gate_t<bf16_t>((const bf16_t*)x, wr_t, (const u32x4*)planes, bias, T, d, E, has_shared, k, idx,
-                                     w, gs, s);
-    return launch_gate_t<float>((const float*)x, wr_t, nullptr, bias, T, d, E, has_shared, k, idx, w, gs, s);
+        return launch_gate_t<bf16_t>((const bf16_t*)x, wr_t, (const u32x4*)planes, bias, T, d, E, gflags, k, idx, w,
+                                     gs, s);
+    return launch_gate_t<float>((const float*)x, wr_t, nullptr, bias, T, d, E, gflags, k, idx, w, gs, s);
 }
 
 }  // namespace moe

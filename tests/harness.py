@@ -24,7 +24,7 @@ W_TOL = 1e-5
 Y_TOL = {"bf16": (1e-2, 3e-2), "f32": (1e-4, 3e-4)}
 
 
-def gpu_layer(L: "synth.SynthLayer", max_tokens: int, profile: bool = False):
+def gpu_layer(L: "synth.SynthLayer", max_tokens: int, profile: bool = False, gate_clamp: bool = False):
     import moe_layer_forward_gate_amd as moe
     c = L.cfg
     dev = torch.device("cuda", torch.cuda.current_device())
@@ -37,7 +37,8 @@ def gpu_layer(L: "synth.SynthLayer", max_tokens: int, profile: bool = False):
         act_dtype=c.act_dtype, expert_dtype=c.expert_dtype, w_router=t["w_router"], b_router=t.get("b_router"),
         w_gate=t["w_gate"], w_up=t["w_up"], w_down=t["w_down"], s_gate=t.get("s_gate"), s_up=t.get("s_up"),
         s_down=t.get("s_down"), shared_d_ff=c.shared_d_ff, w_shared_gate=t.get("w_shared_gate"),
-        ws_gate=t.get("ws_gate"), ws_up=t.get("ws_up"), ws_down=t.get("ws_down"), profile=profile)
+        ws_gate=t.get("ws_gate"), ws_up=t.get("ws_up"), ws_down=t.get("ws_down"), profile=profile,
+        gate_clamp=gate_clamp)
 
 
 def _np(t):
@@ -49,13 +50,13 @@ def _np(t):
     return t.numpy()
 
 
-def oracle_layer(L: "synth.SynthLayer") -> oracle.OracleLayer:
+def oracle_layer(L: "synth.SynthLayer", gate_clamp: bool = False) -> oracle.OracleLayer:
     return oracle.OracleLayer(
         w_router=_np(L.w_router), w_gate=_np(L.w_gate), w_up=_np(L.w_up), w_down=_np(L.w_down),
         top_k=L.cfg.top_k, b_router=_np(L.b_router), s_gate=_np(L.s_gate), s_up=_np(L.s_up),
         s_down=_np(L.s_down), w_shared_gate=_np(L.w_shared_gate), ws_gate=_np(L.ws_gate),
         ws_up=_np(L.ws_up), ws_down=_np(L.ws_down),
-        group=synth.INT4_GROUP if L.cfg.expert_dtype == "i4" else None)
+        group=synth.INT4_GROUP if L.cfg.expert_dtype == "i4" else None, gate_clamp=gate_clamp)
 
 
 def compare(cfg, x, olay: oracle.OracleLayer, out, sample=None, label=""):

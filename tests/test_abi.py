@@ -37,7 +37,7 @@ def test_status_strings():
 
 def _desc(**kw):
     base = dict(d_model=256, n_experts=8, d_ff=512, top_k=2, max_tokens=64, act_dtype=moe.MOE_BF16,
-                expert_dtype=moe.MOE_BF16, shared_d_ff=0, profile=0)
+                expert_dtype=moe.MOE_BF16, shared_d_ff=0, profile=0, gate_clamp=0)
     base.update(kw)
     return moe.MoeDesc(**base)
 
@@ -65,6 +65,7 @@ def _create(desc, weights):
     (_desc(top_k=9), _weights(), moe.MOE_EINVAL),
     (_desc(top_k=0), _weights(), moe.MOE_EINVAL),
     (_desc(profile=2), _weights(), moe.MOE_EINVAL),
+    (_desc(gate_clamp=2), _weights(), moe.MOE_EINVAL),
     (_desc(), _weights(w_gate=0), moe.MOE_EINVAL),
     (_desc(), _weights(w_router=0), moe.MOE_EINVAL),
     (_desc(expert_dtype=moe.MOE_I8), _weights(), moe.MOE_EINVAL),            # scales missing

@@ -111,3 +111,30 @@ def test_wide_router_decode_paths():
     # and the per-token gate kernel when k > 8
     _run(synth.get_config("tiny_f32", d_model=64, d_ff=64, n_experts=32, top_k=4), [1, 8, 64])
     _run(synth.get_config("mixtral_bf16", d_model=128, d_ff=64, n_experts=32, top_k=10), [1, 8, 64])
+
+
+@pytest.mark.parametrize("name,kw,Ts", [
+    ("mixtral_bf16", dict(d_model=256, d_ff=128), [1, 5, 300]),       # fused tiny, per-token, MFMA gates
+    ("tiny_f32", dict(d_model=64, d_ff=64), [1, 100]),                 # fp32 tokens: fused tiny, tiled gate
+    ("mixtral_bf16", dict(d_model=128, d_ff=64, n_experts=32, top_k=4), [32]),  # split decode gate
+])
+def test_gate_clamp(name, kw, Ts):
+    # a bias of 49.9 on three experts puts their logits on both sides of the bound: the
+    # clamped ones tie at 50 (lower id first, equal weights)
+    cfg = synth.get_config(name, **kw)
+    L = synth.make_layer(cfg)
+    b = torch.zeros(cfg.n_experts, dtype=torch.float32)
+    b[[1, 2, 4]] = 49.9
+    L.b_router = b
+    olay = oracle_layer(L, gate_clamp=True)
+    lay = gpu_layer(L, max(Ts), gate_clamp=True)
+    for T in Ts:
+        print(f"[edge] gate clamp {cfg.name} E={cfg.n_experts} k={cfg.top_k} T={T}", flush=True)
+        x = synth.make_tokens(cfg, T).cuda()
+        out = lay.forward(x, scatter=True)
+        torch.cuda.synchronize()
+        compare(cfg, x, olay, out, label=f"clamp {cfg.name} T={T}")
+        # the clamp is active: some token holds two tied experts at equal weights
+        w = out.topk_w.cpu()
+        assert ((w[:, 0] - w[:, 1]).abs() < 1e-7).any() or T < 32
+    lay.close()
