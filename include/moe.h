@@ -72,8 +72,8 @@ typedef enum moe_dtype {
  * d_model % 128 == 0 and d_ff % 128 == 0; for F32 experts d_model % 64 == 0
  * and d_ff % 64 == 0. shared_d_ff > 0 adds a shared expert (BF16 experts only)
  * and must be a multiple of d_ff. I4 layers run every batch on the weight-
- * streaming kernels (built for decode; batches over 64 tokens re-stream the
- * weights once per 64 rows of an expert). */
+ * streaming kernels (built for decode; larger batches re-stream the weights
+ * once per 32 rows of an expert). */
 typedef struct moe_desc {
     int32_t d_model;
     int32_t n_experts;

@@ -302,7 +302,9 @@ hipError_t launch_t(const GemmArgs& a, int S, hipStream_t s) {
         case 1: return launch_mb<1, WQ, UP>(a, S, s);
         case 2: return launch_mb<2, WQ, UP>(a, S, s);
         case 3:
-        case 4: return launch_mb<4, WQ, UP>(a, S, s);
+        case 4:
+            if constexpr (WQ == kWI4) return hipErrorInvalidValue;  // int4 row tiles are at most 32 rows
+            else return launch_mb<4, WQ, UP>(a, S, s);
         default: return hipErrorInvalidValue;
     }
 }

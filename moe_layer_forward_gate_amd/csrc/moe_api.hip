@@ -263,8 +263,8 @@ int check_device(const moe_layer* L) {
 
 // Launch plan (host side, from T, k and the layer shape only):
 //  - small batches (T <= 64), and every batch of an int4 layer, stream the weights: row
-//    tiles of 16, 32 or 64 rows, sized so an active expert almost always fits one tile
-//    (an int4 layer's larger batches take several 64-row tiles per expert, each
+//    tiles of 16, 32 or 64 rows (int4: 16 or 32), sized so an active expert almost always
+//    fits one tile (an int4 layer's larger batches take several tiles per expert, each
 //    streaming the weights again), the down projection's K split so ~1024 workgroups run;
 //  - larger batches use the LDS-tiled MFMA GEMMs (256-row tiles for bf16 weights,
 //    128 for int8), with the down projection's K split when that fills the CUs better.
@@ -288,7 +288,9 @@ Plan make_plan(const moe_layer* L, int T) {
         // row tile: expected rows of the busiest expert (shared slices hold all T rows; routed
         // experts about twice their average), so an expert rarely needs a second tile
         const int need = L->V > 0 ? T : std::min(T, 2 * ((T * k + L->E - 1) / L->E));
-        bm = need <= 16 ? 16 : (need <= 32 ? 32 : 64);
+        // int4 takes at most 32 rows a tile: its 64-row kernel holds too many registers
+        // to hide memory latency, and re-streaming the (small) weights per tile costs less
+        bm = need <= 16 ? 16 : (need <= 32 || i4 ? 32 : 64);
         const int active = std::min(L->E, T * k) + L->V;
         const int groups = active * (d.d_model / 128);
         const int kstep = i4 ? 128 : 64;  // every split a whole number of weight steps
