@@ -140,8 +140,10 @@ __device__ __forceinline__ void load8<float>(const float* p, float* v) {
 // grid = T workgroups of 256 threads. Thread tid owns K chunks tid*8 + 2048*c
 // (c < XC, d <= 2048*XC); router rows are taken 8 at a time, each thread forms 8
 // partial dots, a wave butterfly folds them and the 4 wave partials meet in LDS.
-constexpr int kRowXC = 4;
-template <typename XT>
+// The token's chunks stay packed until the multiply-adds, so the router loads are
+// issued without waiting for them (a decode step is a chain of memory latencies).
+constexpr int kRowXC = 4;  // d <= 8192
+template <typename XT, int XC>
 __global__ __launch_bounds__(256) void gate_rowdot(const XT* __restrict__ x, const float* __restrict__ wr_t,
                                                    const float* __restrict__ bias, int d, int E, int Ec, int k,
                                                    int gflags, int32_t* __restrict__ idx,
@@ -151,49 +153,50 @@ __global__ __launch_bounds__(256) void gate_rowdot(const XT* __restrict__ x, con
     const int t = blockIdx.x;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const XT* xr = x + (size_t)t * d;
-    // every load is unconditional (out-of-range chunks and rows read a valid address and are
-    // zeroed or dropped), so the compiler can keep all of them in flight at once
-    constexpr int XQ = sizeof(XT) / 2;  // 16-byte chunks per 8 elements
-    u32x4 xq[kRowXC][XQ];
+    // every load is unconditional (a chunk past d reads a valid address and is dropped)
+    float wv[XC][8][8];
+    auto load_group = [&](int e0) {
 #pragma unroll
-    for (int c = 0; c < kRowXC; ++c) {
-        const int kk = tid * 8 + 2048 * c;
-        const u32x4* p = reinterpret_cast<const u32x4*>(xr + (kk < d ? kk : 0));
-#pragma unroll
-        for (int q = 0; q < XQ; ++q) xq[c][q] = p[q];
-    }
-    float xv[kRowXC][8];
-#pragma unroll
-    for (int c = 0; c < kRowXC; ++c) {
-        const bool ok = tid * 8 + 2048 * c < d;
-#pragma unroll
-        for (int v = 0; v < 8; ++v) {
-            float f;
-            if constexpr (XQ == 1) {
-                const uint32_t wv = xq[c][0][v / 2];
-                f = __uint_as_float((v & 1) ? (wv & 0xFFFF0000u) : (wv << 16));
-            } else {
-                f = __uint_as_float(xq[c][v / 4][v % 4]);
-            }
-            xv[c][v] = ok ? f : 0.0f;
-        }
-    }
-    for (int e0 = 0; e0 < Ec; e0 += 8) {
-        float acc[8];
-#pragma unroll
-        for (int g = 0; g < 8; ++g) acc[g] = 0.0f;
-#pragma unroll
-        for (int c = 0; c < kRowXC; ++c) {
+        for (int c = 0; c < XC; ++c) {
             const int kk = tid * 8 + 2048 * c;
             const int kc = kk < d ? kk : 0;
 #pragma unroll
             for (int g = 0; g < 8; ++g) {
                 const int e = e0 + g < Ec ? e0 + g : 0;
-                float wv[8];
-                load8<float>(wr_t + (size_t)e * d + kc, wv);
-#pragma unroll
-                for (int v = 0; v < 8; ++v) acc[g] = fmaf(xv[c][v], wv[v], acc[g]);
+                load8<float>(wr_t + (size_t)e * d + kc, wv[c][g]);
             }
+        }
+    };
+    load_group(0);  // requested before the token's chunks, so both are in flight together
+    constexpr int XQ = sizeof(XT) / 2;  // 16-byte chunks per 8 elements
+    u32x4 xq[XC][XQ];
+#pragma unroll
+    for (int c = 0; c < XC; ++c) {
+        const int kk = tid * 8 + 2048 * c;
+        const u32x4* p = reinterpret_cast<const u32x4*>(xr + (kk < d ? kk : 0));
+#pragma unroll
+        for (int q = 0; q < XQ; ++q) xq[c][q] = p[q];
+    }
+    auto xval = [&](int c, int v) {
+        if constexpr (XQ == 1) {
+            const uint32_t u = xq[c][0][v / 2];
+            return __uint_as_float((v & 1) ? (u & 0xFFFF0000u) : (u << 16));
+        } else {
+            return __uint_as_float(xq[c][v / 4][v % 4]);
+        }
+    };
+    for (int e0 = 0; e0 < Ec; e0 += 8) {
+        if (e0 > 0) load_group(e0);
+        float acc[8];
+#pragma unroll
+        for (int g = 0; g < 8; ++g) acc[g] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < XC; ++c) {
+            const bool ok = tid * 8 + 2048 * c < d;
+#pragma unroll
+            for (int g = 0; g < 8; ++g)
+#pragma unroll
+                for (int v = 0; v < 8; ++v) acc[g] = fmaf(ok ? xval(c, v) : 0.0f, wv[c][g][v], acc[g]);
         }
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
@@ -442,6 +445,18 @@ __global__ __launch_bounds__(1024) void gate_scatter_small(const XT* __restrict_
     const bool has = tid * 8 < d;
     const int kc = has ? tid * 8 : 0;
     constexpr int XQ = sizeof(XT) / 2;  // 16-byte chunks per 8 elements
+    // the first column group's router chunks are requested before the token rows, so both
+    // are in flight together (the token rows' unpacking is hoisted above the column loop)
+    u32x4 wq[EG][2];
+    auto load_w = [&](int e0) {
+#pragma unroll
+        for (int g = 0; g < EG; ++g) {
+            const u32x4* p = reinterpret_cast<const u32x4*>(wr_t + (size_t)(e0 + g < Ec ? e0 + g : 0) * d + kc);
+            wq[g][0] = p[0];
+            wq[g][1] = p[1];
+        }
+    };
+    load_w(0);
     u32x4 xq[MT][XQ];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
@@ -450,13 +465,7 @@ __global__ __launch_bounds__(1024) void gate_scatter_small(const XT* __restrict_
         for (int q = 0; q < XQ; ++q) xq[t][q] = p[q];
     }
     for (int e0 = 0; e0 < Ec; e0 += EG) {
-        u32x4 wq[EG][2];
-#pragma unroll
-        for (int g = 0; g < EG; ++g) {
-            const u32x4* p = reinterpret_cast<const u32x4*>(wr_t + (size_t)(e0 + g < Ec ? e0 + g : 0) * d + kc);
-            wq[g][0] = p[0];
-            wq[g][1] = p[1];
-        }
+        if (e0 > 0) load_w(e0);
         // per token, RG dots at a time, each group folded with one transposed butterfly
         constexpr int RG = 4;  // register budget at 1024 threads
 #pragma unroll
@@ -633,8 +642,17 @@ hipError_t launch_gate_t(const XT* x, const float* wr_t, const u32x4* planes, co
     const bool has_shared = (gflags & kGateShared) != 0;
     const int Ec = E + (has_shared ? 1 : 0);
     if (T <= 64 && d <= 2048 * kRowXC) {
-        hipLaunchKernelGGL((gate_rowdot<XT>), dim3(T), dim3(256), 0, s, x, wr_t, bias, d, E, Ec, k, gflags, idx, w,
-                           gs);
+        switch ((d + 2047) / 2048) {
+#define ROWDOT_CASE(C)                                                                                            \
+    case C:                                                                                                       \
+        hipLaunchKernelGGL((gate_rowdot<XT, C>), dim3(T), dim3(256), 0, s, x, wr_t, bias, d, E, Ec, k, gflags, idx, \
+                           w, gs);                                                                                \
+        break;
+            ROWDOT_CASE(1) ROWDOT_CASE(2) ROWDOT_CASE(3) ROWDOT_CASE(4)
+#undef ROWDOT_CASE
+            default:
+                return hipErrorInvalidValue;
+        }
     } else if (planes != nullptr && (d / 32) >= 4) {
         // token blocks per workgroup: as many as keep >= 256 workgroups (up to 4)
 #ifdef MOE_GATE_TB
