@@ -439,7 +439,7 @@ __global__ __launch_bounds__(1024) void gate_scatter_small(const XT* __restrict_
     constexpr int NW = 16;
     __shared__ float part[NW][MT * EC];
     __shared__ float logits[MT][EC + 1];
-    __shared__ ScatterSmem<NW> sm;
+    __shared__ ScatterWaveSmem sm;
     __shared__ int32_t ids[MT * kMaxTopK];  // the top-k ids again, for the scatter to read from LDS
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const bool has = tid * 8 < d;
@@ -510,7 +510,7 @@ __global__ __launch_bounds__(1024) void gate_scatter_small(const XT* __restrict_
     __syncthreads();
     if (wave < T) wave_topk_write(logits[wave], E, k, gflags, wave, idx, w, gs, ids);
     __syncthreads();
-    scatter_block<NW>(ids, T, E, k, V, bm, o, sm);
+    if (wave == 0) scatter_wave(ids, T, E, k, V, bm, o, sm);  // at most 4 x 16 assignments
 }
 
 // ---------------------------------------------------------------- decode batches, split
@@ -589,7 +589,8 @@ __global__ __launch_bounds__(1024) void gate_finish(const float* __restrict__ pa
     constexpr int NW = 16;
     __shared__ float logits[kFinishT][kMaxExperts + 2];
     __shared__ int32_t ids[kFinishT * 8];  // top-k ids (k <= 8 here) for the scatter to read from LDS
-    __shared__ ScatterSmem<NW> sm;
+    __shared__ ScatterWaveSmem sm;
+    __shared__ ScatterSmem<NW> smb;
     const int tid = threadIdx.x, wave = tid / kWave;
     for (int i = tid; i < T * Ec; i += NW * kWave) {
         const int t = i / Ec, e = i - (i / Ec) * Ec;
@@ -607,7 +608,11 @@ __global__ __launch_bounds__(1024) void gate_finish(const float* __restrict__ pa
     __syncthreads();
     for (int t = wave; t < T; t += NW) wave_topk_write(logits[t], E, k, gflags, t, idx, w, gs, ids);
     __syncthreads();
-    scatter_block<NW>(ids, T, E, k, V, bm, o, sm);
+    if (T * k <= kScatterWaveMaxN) {
+        if (wave == 0) scatter_wave(ids, T, E, k, V, bm, o, sm);
+    } else {
+        scatter_block<NW>(ids, T, E, k, V, bm, o, smb);
+    }
 }
 
 template <int TB>

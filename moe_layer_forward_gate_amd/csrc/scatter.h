@@ -1,5 +1,6 @@
-// Scatter as a workgroup-level routine, shared by the standalone scatter kernel and the
-// small-batch gate kernel (which runs it in the last workgroup to finish).
+// Scatter as a workgroup-level routine (scatter_block) and as a one-wavefront routine for
+// small batches (scatter_wave), shared by the standalone scatter kernel and the decode
+// gate kernels that end with the scatter.
 //
 // [0539edu §2.2] Scatter stage; [hotelren §2.3] dispatch_kernel sends each token
 // to its k experts' input buffers; [mhpq §2.1] tokens of one expert form one
@@ -138,6 +139,77 @@ __device__ void scatter_block(const int32_t* __restrict__ idx, int T, int E, int
         o.sorted_c[N + i] = t * kt + k + v;
     }
     for (int e = tid; e <= Et; e += nthr) {
+        if (e < Et) o.counts[e] = sm.cnt[e];
+        o.offsets[e] = sm.offs[e];
+        o.tile_start[e] = sm.tstart[e];
+        if (e < E && o.user_counts) o.user_counts[e] = sm.cnt[e];
+        if (e <= E && o.user_offsets) o.user_offsets[e] = sm.offs[e];
+    }
+}
+
+// ---- the same scatter run by one wavefront, for small batches (a few hundred
+// assignments): no workgroup barriers, one expert cursor array. A wave's LDS operations
+// execute in order; lds_order() keeps the compiler from moving LDS accesses across the
+// phase boundaries and waits for the phase's LDS writes.
+constexpr int kScatterWaveMaxN = 256;  // assignments up to which one wavefront is faster
+
+struct ScatterWaveSmem {
+    int cnt[kMaxEt];
+    int offs[kMaxEt + 1];
+    int cur[kMaxEt];  // tiles per expert, then the running cursor of each expert
+    int tstart[kMaxEt + 1];
+};
+
+__device__ __forceinline__ void lds_order() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ inline void scatter_wave(const int32_t* __restrict__ idx, int T, int E, int k, int V, int bm,
+                                    const ScatterOut& o, ScatterWaveSmem& sm) {
+    const int lane = threadIdx.x % kWave;
+    const int N = T * k;
+    const int kt = k + V;
+    const int Et = E + V;
+    for (int e = lane; e < Et; e += kWave) sm.cnt[e] = e < E ? 0 : T;  // shared slices: every token
+    lds_order();
+    for (int a = lane; a < N; a += kWave) atomicAdd(&sm.cnt[idx[a]], 1);
+    lds_order();
+    wave_exclusive_scan(sm.cnt, Et, sm.offs);
+    for (int e = lane; e < Et; e += kWave) sm.cur[e] = (sm.cnt[e] + bm - 1) / bm;
+    lds_order();
+    wave_exclusive_scan(sm.cur, Et, sm.tstart);
+    lds_order();
+    for (int e = lane; e < E; e += kWave) sm.cur[e] = sm.offs[e];
+    lds_order();
+    // stable ranks, 64 assignments a round: lanes holding the same expert are found with
+    // 7 ballots over the expert-id bits; the group's lowest lane advances the cursor
+    const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (kWave - lane));
+    for (int base = 0; base < N; base += kWave) {
+        const int a = base + lane;
+        const bool valid = a < N;
+        const int e = valid ? idx[a] : 0;
+        uint64_t same = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < 7; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t bb = __ballot(valid && bit);
+            same &= bit ? bb : ~bb;
+        }
+        const int rank = __popcll(same & lt_mask);
+        if (valid) {
+            const int pos = sm.cur[e] + rank;
+            const int t = a / k, j = a - t * k;
+            o.sorted_c[pos] = t * kt + j;
+            if (o.user_sorted) o.user_sorted[pos] = a;
+        }
+        lds_order();
+        if (valid && rank == 0) sm.cur[e] += __popcll(same);
+        lds_order();
+    }
+    // shared virtual experts: every token, in order
+    for (int i = lane; i < V * T; i += kWave) {
+        const int v = i / T, t = i - v * T;
+        o.sorted_c[N + i] = t * kt + k + v;
+    }
+    for (int e = lane; e <= Et; e += kWave) {
         if (e < Et) o.counts[e] = sm.cnt[e];
         o.offsets[e] = sm.offs[e];
         o.tile_start[e] = sm.tstart[e];

@@ -1,5 +1,6 @@
-// Scatter kernel: one workgroup of 16 waves runs scatter_block (scatter.h); and the
-// physical scatter of token rows into the tiled up-projection operand.
+// Scatter kernels: one workgroup of 16 waves runs scatter_block (scatter.h), or one
+// wavefront runs scatter_wave for small batches; and the physical scatter of token rows
+// into the tiled up-projection operand.
 #include "scatter.h"
 
 namespace moe {
@@ -11,6 +12,13 @@ __global__ __launch_bounds__(1024) void scatter_kernel(const int32_t* __restrict
                                                       int V, int bm, ScatterOut o) {
     __shared__ ScatterSmem<kScatterWaves> sm;
     scatter_block<kScatterWaves>(idx, T, E, k, V, bm, o, sm);
+}
+
+// Small batches: one wavefront does it all (no workgroup barriers).
+__global__ __launch_bounds__(64) void scatter_wave_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
+                                                          int V, int bm, ScatterOut o) {
+    __shared__ ScatterWaveSmem sm;
+    scatter_wave(idx, T, E, k, V, bm, o, sm);
 }
 
 // Token rows into the tiled up operand ([0539edu §2.2] Scatter: the tokens of one
@@ -214,7 +222,10 @@ hipError_t launch_pack_a(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_scatter(const int32_t* idx, int T, int E, int k, int V, int bm, const ScatterOut& o,
                           hipStream_t s) {
     if (E > kMaxExperts || E + V > kMaxEt) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(scatter_kernel, dim3(1), dim3(kScatterWaves * kWave), 0, s, idx, T, E, k, V, bm, o);
+    if (T * k <= kScatterWaveMaxN)
+        hipLaunchKernelGGL(scatter_wave_kernel, dim3(1), dim3(kWave), 0, s, idx, T, E, k, V, bm, o);
+    else
+        hipLaunchKernelGGL(scatter_kernel, dim3(1), dim3(kScatterWaves * kWave), 0, s, idx, T, E, k, V, bm, o);
     return hipGetLastError();
 }
 

@@ -111,6 +111,8 @@ def test_wide_router_decode_paths():
     # and the per-token gate kernel when k > 8
     _run(synth.get_config("tiny_f32", d_model=64, d_ff=64, n_experts=32, top_k=4), [1, 8, 64])
     _run(synth.get_config("mixtral_bf16", d_model=128, d_ff=64, n_experts=32, top_k=10), [1, 8, 64])
+    # split gate with more than 256 assignments: its scatter runs on the whole workgroup
+    _run(synth.get_config("mixtral_bf16", d_model=128, d_ff=64, n_experts=32, top_k=8), [33, 64])
 
 
 @pytest.mark.parametrize("name,kw,Ts", [
