@@ -64,3 +64,34 @@ def test_int8_mixtral22b_full():
 
 def test_int4_mixtral22b_full():
     _run("int4_mixtral22b", [1, 16, 256])
+
+
+def test_mixtral_bf16_routed_full():
+    # the given-routing entry at full size: scatter tables bit for bit, outputs on all rows
+    # at decode sizes and on a sample of rows at T = 4096
+    from harness import Y_TOL, _np
+    import oracle
+    cfg = synth.get_config("mixtral_bf16")
+    L = synth.make_layer(cfg, device="cuda")
+    olay = oracle_layer(L)
+    lay = gpu_layer(L, 4096)
+    for T in (1, 64, 4096):
+        print(f"[fullsize] routed mixtral_bf16 T={T}", flush=True)
+        x = synth.make_tokens(cfg, T, device="cuda")
+        idx, w, _ = synth.make_routing(cfg, T, device="cuda")
+        out = lay.forward_routed(x, idx, w, scatter=True)
+        torch.cuda.synchronize()
+        rows = _sample(T)
+        ref = oracle.moe_forward_routed(_np(x), olay, idx.cpu().numpy(), w.cpu().numpy(), tokens=rows)
+        assert np.array_equal(out.expert_counts.cpu().numpy(), ref["counts"])
+        assert np.array_equal(out.expert_offsets.cpu().numpy(), ref["offsets"])
+        assert np.array_equal(out.sorted_assign.cpu().numpy(), ref["sorted_assign"])
+        y = _np(out.y).astype(np.float64)
+        y = y if rows is None else y[rows]
+        yr = ref["y"]
+        rel, mabs = Y_TOL[cfg.act_dtype]
+        den = np.linalg.norm(yr)
+        rms = den / np.sqrt(yr.size)
+        assert np.linalg.norm(y - yr) / den <= rel
+        assert np.abs(y - yr).max() <= mabs * rms
+    lay.close()
