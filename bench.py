@@ -312,7 +312,10 @@ def measure_peaks(torch):
     P.moe_peak_read_gbps.argtypes = [ctypes.c_size_t, ctypes.c_int, ctypes.c_int]
     P.moe_peak_mfma_tflops.restype = ctypes.c_double
     P.moe_peak_mfma_tflops.argtypes = [ctypes.c_int, ctypes.c_int]
+    P.moe_peak_read_nt_gbps.restype = ctypes.c_double
+    P.moe_peak_read_nt_gbps.argtypes = [ctypes.c_size_t, ctypes.c_int, ctypes.c_int]
     out["read_stream_GBps"] = {w: P.moe_peak_read_gbps(4 << 30, w, 5) for w in (2048, 4096, 8192)}
+    out["read_stream_nontemporal_GBps"] = {w: P.moe_peak_read_nt_gbps(4 << 30, w, 5) for w in (2048, 4096, 8192)}
     out["mfma_bf16_TFLOPs"] = {w: P.moe_peak_mfma_tflops(w, 20000) for w in (256, 512)}
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     n = 10

@@ -85,6 +85,8 @@ struct GemmArgs {
     int bm;                     // row tile height: 256 (bf16) or 128 (int8); must match the scatter's tile list
     int ksplit;                 // down projection: K split into ksplit partial sums (ow rows c*ksplit + s)
     int merge_shared;           // tiled down projection: shared slices summed as one K = V*F tile (ksplit 1)
+    int weights_once;           // streaming kernels: an expert's weights are read by one row tile only
+                                // (non-temporal loads), else by several (cached loads: re-reads hit)
     // Streaming kernels: A = x rows gathered by token (up), H rows [P][F] (down).
     // Tiled kernels: A in fragment order over padded rows (tile g owns padded rows
     // [g*bm, (g+1)*bm)): xp = the gathered tokens [R/16][d/32][64][8] written by

@@ -7,7 +7,9 @@
 //   - every wave owns NBW 16-column weight blocks and a K range; it reads them
 //     as contiguous 1 KB fragment blocks (16 B per lane: 32 bf16, 64 int8 or 128
 //     int4 K rows of one column) straight into MFMA operand registers, U K-steps
-//     at a time so many loads are in flight;
+//     at a time so many loads are in flight, as non-temporal loads when each
+//     weight byte is read once per forward (keeping it out of the caches'
+//     working set streams ~10% faster);
 //   - the few token rows (<= 16*MB) come in as MFMA A fragments from L2;
 //   - the down projection splits K over S workgroups when the active experts
 //     alone would leave the GPU idle; each split writes its own partial row of
@@ -43,7 +45,14 @@ __device__ __forceinline__ u32x4 i4x8_bf16(uint32_t w, uint32_t m) {
                  ((w >> 12) & m) | 0x43004300u};
 }
 
-template <int MB, int NBW, int WQ, bool UP, int U>  // WQ: weight kind (kWBf16, kWI8, kWI4)
+template <bool NT>
+__device__ __forceinline__ u32x4 load_w(const u32x4* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+// WQ: weight kind (kWBf16, kWI8, kWI4); NT: the weights are loaded non-temporally
+template <int MB, int NBW, int WQ, bool UP, int U, bool NT>
 __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
     constexpr bool INT8 = WQ == kWI8;
     constexpr bool INT4 = WQ == kWI4;
@@ -172,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int j = 0; j < NBW; ++j) R.bb[u][j] = bptr[j][(size_t)(s0 + u) * 64];
+            for (int j = 0; j < NBW; ++j) R.bb[u][j] = load_w<NT>(&bptr[j][(size_t)(s0 + u) * 64]);
         if constexpr (INT4) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -210,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
         u32x4 aa[MB][KH];
         float sc[NBW] = {};
 #pragma unroll
-        for (int j = 0; j < NBW; ++j) bb[j] = bptr[j][(size_t)s * 64];
+        for (int j = 0; j < NBW; ++j) bb[j] = load_w<NT>(&bptr[j][(size_t)s * 64]);
         if constexpr (INT4) {
 #pragma unroll
             for (int j = 0; j < NBW; ++j) sc[j] = sptr[j][(size_t)s * N];
@@ -280,7 +289,12 @@ hipError_t launch_nbw(const GemmArgs& a, int S, hipStream_t s) {
     if (N % (16 * NBW * 4) != 0) return hipErrorInvalidValue;             // whole column groups
     const int NG = N / (16 * NBW * 4);
     dim3 grid((unsigned)((size_t)a.max_tiles * NG * S));
-    hipLaunchKernelGGL((expert_stream<MB, NBW, WQ, UP, U>), grid, dim3(kThreads), 0, s, a, S);
+    // non-temporal weight loads when each expert's weights are read by one row tile; int4
+    // layers past ~64 tokens stream them once per 32-row tile and keep them cached
+    if (WQ != kWI4 || a.weights_once)
+        hipLaunchKernelGGL((expert_stream<MB, NBW, WQ, UP, U, true>), grid, dim3(kThreads), 0, s, a, S);
+    else if constexpr (WQ == kWI4)
+        hipLaunchKernelGGL((expert_stream<MB, NBW, WQ, UP, U, false>), grid, dim3(kThreads), 0, s, a, S);
     return hipGetLastError();
 }
 

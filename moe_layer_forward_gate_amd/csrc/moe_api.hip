@@ -271,7 +271,8 @@ int check_device(const moe_layer* L) {
 struct Plan {
     bool streaming;
     int bm, ksplit, max_tiles;
-    bool merge;  // tiled down projection of a multi-slice shared expert as one K loop
+    bool merge;         // tiled down projection of a multi-slice shared expert as one K loop
+    bool weights_once;  // streaming: the busiest expert is expected to fit one row tile
 };
 
 Plan make_plan(const moe_layer* L, int T) {
@@ -282,6 +283,7 @@ Plan make_plan(const moe_layer* L, int T) {
     const int k = d.top_k;
     const bool streaming = !f32 && (T <= kStreamMaxT || i4);
     int bm, ksplit = 1;
+    bool weights_once = true;
     if (f32) {
         bm = kBMf32;
     } else if (streaming) {
@@ -291,6 +293,7 @@ Plan make_plan(const moe_layer* L, int T) {
         // int4 takes at most 32 rows a tile: its 64-row kernel holds too many registers
         // to hide memory latency, and re-streaming the (small) weights per tile costs less
         bm = need <= 16 ? 16 : (need <= 32 || i4 ? 32 : 64);
+        weights_once = need <= bm;
         const int active = std::min(L->E, T * k) + L->V;
         const int groups = active * (d.d_model / 128);
         const int kstep = i4 ? 128 : 64;  // every split a whole number of weight steps
@@ -337,7 +340,7 @@ Plan make_plan(const moe_layer* L, int T) {
     // tiled down projection of a shared expert in several slices: the slices of a row tile
     // are summed in one K loop (one partial row per token instead of one per slice)
     const bool merge = !f32 && !streaming && !i8 && L->V > 1 && ksplit == 1;
-    return Plan{streaming, bm, ksplit, max_tiles, merge};
+    return Plan{streaming, bm, ksplit, max_tiles, merge, weights_once};
 }
 
 ScatterOut scatter_out(const moe_layer* L, int32_t* counts, int32_t* offsets, int32_t* sorted) {
@@ -369,7 +372,7 @@ int run_experts(moe_layer* L, const void* x, int T, void* y, const float* topk_w
     const int k = d.top_k;
     const bool prof = L->profiling;
     const GemmArgs a{L->tile_start, L->offsets, L->sorted_c, L->Et, L->kt, k, pl.max_tiles, pl.bm, pl.ksplit,
-                     pl.merge ? 1 : 0, (const bf16_t*)x, L->xp, (bf16_t*)L->h, L->wgu, L->wdn, L->s_gate, L->s_up,
+                     pl.merge ? 1 : 0, pl.weights_once ? 1 : 0, (const bf16_t*)x, L->xp, (bf16_t*)L->h, L->wgu, L->wdn, L->s_gate, L->s_up,
                      L->s_down, topk_w, gs, L->ow, d.d_model, d.d_ff};
     // the tiled GEMMs take the token rows already gathered into fragment order
     if (!f32 && !pl.streaming) HIP_TRY(launch_pack_a(a, s));

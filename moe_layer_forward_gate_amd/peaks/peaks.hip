@@ -14,6 +14,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kU = 16;  // loads in flight per lane
 
+template <bool NT>  // NT: non-temporal loads (the data is read once)
 __global__ __launch_bounds__(256) void read_stream(const u32x4* __restrict__ p, size_t chunks_per_wave,
                                                    uint32_t* __restrict__ out) {
     const int lane = threadIdx.x % 64;
@@ -23,7 +24,7 @@ __global__ __launch_bounds__(256) void read_stream(const u32x4* __restrict__ p, 
     for (size_t c = 0; c < chunks_per_wave; c += kU) {
         u32x4 v[kU];
 #pragma unroll
-        for (int u = 0; u < kU; ++u) v[u] = q[(c + u) * 64];
+        for (int u = 0; u < kU; ++u) v[u] = NT ? __builtin_nontemporal_load(&q[(c + u) * 64]) : q[(c + u) * 64];
 #pragma unroll
         for (int u = 0; u < kU; ++u) acc ^= v[u];
     }
@@ -60,11 +61,9 @@ float time_ms(hipEvent_t a, hipEvent_t b) {
 
 }  // namespace
 
-extern "C" {
-
-// Streaming read rate in GB/s over `bytes` (rounded down to whole 16-KB rounds per wave)
-// read by `waves` waves; returns a negative value on a HIP error.
-__attribute__((visibility("default"))) double moe_peak_read_gbps(size_t bytes, int waves, int reps) {
+namespace {
+template <bool NT>
+double read_gbps(size_t bytes, int waves, int reps) {
     if (waves <= 0 || waves % 4 || reps <= 0) return -1.0;
     const size_t cpw = bytes / 1024 / (size_t)waves / kU * kU;
     if (cpw == 0) return -1.0;
@@ -76,9 +75,10 @@ __attribute__((visibility("default"))) double moe_peak_read_gbps(size_t bytes, i
     hipEvent_t a, b;
     if (hipMemset(d, 1, cpw * 1024 * waves) == hipSuccess && hipEventCreate(&a) == hipSuccess &&
         hipEventCreate(&b) == hipSuccess) {
-        hipLaunchKernelGGL(read_stream, dim3(waves / 4), dim3(256), 0, 0, d, cpw, o);
+        hipLaunchKernelGGL(read_stream<NT>, dim3(waves / 4), dim3(256), 0, 0, d, cpw, o);
         hipEventRecord(a, 0);
-        for (int i = 0; i < reps; ++i) hipLaunchKernelGGL(read_stream, dim3(waves / 4), dim3(256), 0, 0, d, cpw, o);
+        for (int i = 0; i < reps; ++i)
+            hipLaunchKernelGGL(read_stream<NT>, dim3(waves / 4), dim3(256), 0, 0, d, cpw, o);
         hipEventRecord(b, 0);
         if (hipEventSynchronize(b) == hipSuccess)
             r = (double)cpw * 1024 * waves * reps / (time_ms(a, b) * 1e-3) / 1e9;
@@ -88,6 +88,19 @@ __attribute__((visibility("default"))) double moe_peak_read_gbps(size_t bytes, i
     hipFree(o);
     hipFree(d);
     return r;
+}
+}  // namespace
+
+extern "C" {
+
+// Streaming read rate in GB/s over `bytes` (rounded down to whole 16-KB rounds per wave)
+// read by `waves` waves; returns a negative value on a HIP error.
+__attribute__((visibility("default"))) double moe_peak_read_gbps(size_t bytes, int waves, int reps) {
+    return read_gbps<false>(bytes, waves, reps);
+}
+// The same with non-temporal loads.
+__attribute__((visibility("default"))) double moe_peak_read_nt_gbps(size_t bytes, int waves, int reps) {
+    return read_gbps<true>(bytes, waves, reps);
 }
 
 // bf16 MFMA rate in TFLOP/s with `wgs` workgroups of 8 waves; negative on a HIP error.
