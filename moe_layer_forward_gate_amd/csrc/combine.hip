@@ -14,6 +14,12 @@
 namespace moe {
 namespace {
 
+// the partial rows are read once: non-temporal loads keep them out of the caches
+__device__ __forceinline__ float4 load_once(const float4* p) {
+    const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    return make_float4(t[0], t[1], t[2], t[3]);
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ow, int T, int kt, int stride,
                                                       int d, void* __restrict__ y) {
@@ -28,14 +34,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     for (; j + 8 <= kt; j += 8) {
         float4 v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(j + u) * d4];
+        for (int u = 0; u < 8; ++u) v[u] = load_once(&src[(size_t)(j + u) * d4]);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
         }
     }
     for (; j < kt; ++j) {
-        const float4 v = src[(size_t)j * d4];
+        const float4 v = load_once(&src[(size_t)j * d4]);
         s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
     }
     if (BF16) {
