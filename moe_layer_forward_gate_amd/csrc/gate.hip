@@ -214,25 +214,30 @@ __global__ __launch_bounds__(256) void gate_rowdot(const XT* __restrict__ x, con
 }
 
 // ---------------------------------------------------------------- prefill path, bf16 tokens
-// 16*TB tokens per workgroup; wave v takes the K quarter [v*d/4, (v+1)*d/4) and all
-// 16-column router blocks (NB = ceil(Ec/16) <= 9) for all TB token blocks, so every
-// router fragment it loads serves TB MFMAs (the router is re-read once per workgroup:
-// TB sets how many tokens share that read). A fragments come straight from the token
-// rows, B fragments from the three packed planes ([plane][NB][d/32][64] lanes x 16 B,
-// fragment order). The four wave partials are added in LDS one token block at a time.
-template <int NB, int TB>
-__global__ __launch_bounds__(256) void gate_mfma(const bf16_t* __restrict__ x, const u32x4* __restrict__ planes,
-                                                 const float* __restrict__ bias, int T, int d, int E, int k,
-                                                 int gflags, int32_t* __restrict__ idx, float* __restrict__ w,
-                                                 float* __restrict__ gs) {
+// 16*TB tokens per workgroup; NW waves split K (wave v takes the K steps
+// [v*(KS/NW), (v+1)*(KS/NW)), the last wave the rest) and each takes all 16-column
+// router blocks (NB = ceil(Ec/16) <= 9) for all TB token blocks, so every router
+// fragment it loads serves TB MFMAs (the router is re-read once per workgroup: TB sets
+// how many tokens share that read). Four waves suffice when the batch gives >= 512
+// workgroups; smaller batches take 16 waves so that each wave has fewer K steps of
+// dependent loads to wait through. A fragments come straight from the token rows, B
+// fragments from the three packed planes ([plane][NB][d/32][64] lanes x 16 B, fragment
+// order). The wave partials are added in LDS one token block at a time, in a fixed order.
+template <int NB, int TB, int NW>
+__global__ __launch_bounds__(NW * 64) void gate_mfma(const bf16_t* __restrict__ x, const u32x4* __restrict__ planes,
+                                                     const float* __restrict__ bias, int T, int d, int E, int k,
+                                                     int gflags, int32_t* __restrict__ idx, float* __restrict__ w,
+                                                     float* __restrict__ gs) {
+    static_assert(NW == 4 || NW == 16, "wave count");
     const bool has_shared = (gflags & kGateShared) != 0;
     constexpr int LP = NB * 16 + 1;
-    __shared__ float part[4][16 * LP];
+    constexpr int NP = NW == 4 ? 4 : 8;  // partial slots: 16 waves fold pairwise into 8 first
+    __shared__ float part[NP][16 * LP];
     __shared__ float logits[16 * TB * LP];
     const int t0 = blockIdx.x * 16 * TB;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int KS = d / 32;
-    const int ks0 = wave * (KS / 4), ks1 = (wave == 3) ? KS : ks0 + KS / 4;
+    const int ks0 = wave * (KS / NW), ks1 = (wave == NW - 1) ? KS : ks0 + KS / NW;
     const bf16_t* xr[TB];
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
@@ -246,7 +251,10 @@ __global__ __launch_bounds__(256) void gate_mfma(const bf16_t* __restrict__ x, c
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[tb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     // U K-steps per round, every load of the round issued before the first MFMA
-    constexpr int U = NB * TB <= 2 ? 8 : (NB * TB <= 4 ? 4 : (NB * TB <= 12 ? 2 : 1));
+    // (16 waves: at most 64 registers of loads in flight, the budget of four waves per SIMD)
+    constexpr int LR = TB + 3 * NB;  // 16-byte loads per K step
+    constexpr int U = NW == 4 ? (NB * TB <= 2 ? 8 : (NB * TB <= 4 ? 4 : (NB * TB <= 12 ? 2 : 1)))
+                              : (LR <= 4 ? 4 : (LR <= 8 ? 2 : 1));
     auto round = [&](int ks, auto uconst) {
         constexpr int UU = decltype(uconst)::value;
         u32x4 av[UU][TB], bv[UU][NB][3];
@@ -279,20 +287,43 @@ __global__ __launch_bounds__(256) void gate_mfma(const bf16_t* __restrict__ x, c
     const int Ec = E + (has_shared ? 1 : 0);
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
+        if constexpr (NW == 16) {
+            // waves 8..15 hand their partials to waves 0..7, which add them to their own
+            if (wave >= 8) {
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
+                for (int j = 0; j < NB; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) part[wave][(4 * (lane / 16) + i) * LP + 16 * j + lane % 16] = acc[tb][j][i];
+                    for (int i = 0; i < 4; ++i)
+                        part[wave - 8][(4 * (lane / 16) + i) * LP + 16 * j + lane % 16] = acc[tb][j][i];
+            }
+            __syncthreads();
+            if (wave < 8) {
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[tb][j][i] += part[wave][(4 * (lane / 16) + i) * LP + 16 * j + lane % 16];
+            }
+            __syncthreads();
+        }
+        if (wave < NP) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) part[wave][(4 * (lane / 16) + i) * LP + 16 * j + lane % 16] = acc[tb][j][i];
+        }
         __syncthreads();
-        for (int q = tid; q < 16 * Ec; q += 256) {
+        for (int q = tid; q < 16 * Ec; q += NW * 64) {
             const int r = q / Ec, col = q - r * Ec;
             const float b = (bias && col < E) ? bias[col] : 0.0f;
             const int o = r * LP + col;
-            logits[tb * 16 * LP + o] = (part[0][o] + part[1][o]) + (part[2][o] + part[3][o]) + b;
+            float sum = (part[0][o] + part[1][o]) + (part[2][o] + part[3][o]);
+            if constexpr (NP == 8) sum += (part[4][o] + part[5][o]) + (part[6][o] + part[7][o]);
+            logits[tb * 16 * LP + o] = sum + b;
         }
         __syncthreads();
     }
-    for (int r = wave; r < 16 * TB; r += 4)
+    for (int r = wave; r < 16 * TB; r += NW)
         if (t0 + r < T) wave_topk_write(logits + r * LP, E, k, gflags, t0 + r, idx, w, gs);
 }
 
@@ -615,16 +646,24 @@ __global__ __launch_bounds__(1024) void gate_finish(const float* __restrict__ pa
     }
 }
 
-template <int TB>
+// largest router width (16-column blocks) the 16-wave gate takes: its LDS partials
+// (8 x 16 tokens x (16 NB + 1) floats) stay within the 64 KB of static LDS
+constexpr int kGate16MaxNB = 6;
+
+template <int TB, int NW>
 hipError_t launch_gate_mfma_tb(int NB, const bf16_t* x, const u32x4* planes, const float* bias, int T, int d, int E,
                                int k, int gflags, int32_t* idx, float* w, float* gs, hipStream_t s) {
     dim3 grid((T + 16 * TB - 1) / (16 * TB));
     switch (NB) {
-#define GATE_MFMA_CASE(J)                                                                                          \
-    case J:                                                                                                        \
-        hipLaunchKernelGGL((gate_mfma<J, TB>), grid, dim3(256), 0, s, x, planes, bias, T, d, E, k, gflags, idx, \
-                           w, gs);                                                                                 \
-        break;
+#define GATE_MFMA_CASE(J)                                                                                       \
+    case J:                                                                                                     \
+        if constexpr (NW == 4 || J <= kGate16MaxNB) {                                                           \
+            hipLaunchKernelGGL((gate_mfma<J, TB, NW>), grid, dim3(NW * 64), 0, s, x, planes, bias, T, d, E, k,   \
+                               gflags, idx, w, gs);                                                             \
+            break;                                                                                              \
+        } else {                                                                                                \
+            return hipErrorInvalidValue;                                                                        \
+        }
         GATE_MFMA_CASE(1) GATE_MFMA_CASE(2) GATE_MFMA_CASE(3) GATE_MFMA_CASE(4) GATE_MFMA_CASE(5)
         GATE_MFMA_CASE(6) GATE_MFMA_CASE(7) GATE_MFMA_CASE(8) GATE_MFMA_CASE(9)
 #undef GATE_MFMA_CASE
@@ -636,9 +675,13 @@ hipError_t launch_gate_mfma_tb(int NB, const bf16_t* x, const u32x4* planes, con
 
 hipError_t launch_gate_mfma_nb(int TB, int NB, const bf16_t* x, const u32x4* planes, const float* bias, int T, int d,
                                int E, int k, int gflags, int32_t* idx, float* w, float* gs, hipStream_t s) {
-    if (TB == 4) return launch_gate_mfma_tb<4>(NB, x, planes, bias, T, d, E, k, gflags, idx, w, gs, s);
-    if (TB == 2) return launch_gate_mfma_tb<2>(NB, x, planes, bias, T, d, E, k, gflags, idx, w, gs, s);
-    return launch_gate_mfma_tb<1>(NB, x, planes, bias, T, d, E, k, gflags, idx, w, gs, s);
+    if (TB == 4) return launch_gate_mfma_tb<4, 4>(NB, x, planes, bias, T, d, E, k, gflags, idx, w, gs, s);
+    if (TB == 2) return launch_gate_mfma_tb<2, 4>(NB, x, planes, bias, T, d, E, k, gflags, idx, w, gs, s);
+    // one token block per workgroup: fewer than 512 workgroups take 16 waves each (every
+    // wave keeps at least one K step)
+    if (T < 16 * 512 && NB <= kGate16MaxNB && d / 32 >= 16)
+        return launch_gate_mfma_tb<1, 16>(NB, x, planes, bias, T, d, E, k, gflags, idx, w, gs, s);
+    return launch_gate_mfma_tb<1, 4>(NB, x, planes, bias, T, d, E, k, gflags, idx, w, gs, s);
 }
 
 template <typename XT>
