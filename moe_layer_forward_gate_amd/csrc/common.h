@@ -104,8 +104,9 @@ struct GemmArgs {
     float* ow;                  // [T*kt*ksplit][d] weighted expert outputs (partial sums)
     int d, F;
 };
-hipError_t launch_expert_up_bf16(const GemmArgs& a, bool int8, hipStream_t s);
-hipError_t launch_expert_down_bf16(const GemmArgs& a, bool int8, hipStream_t s);
+// LDS-tiled MFMA GEMMs; wq: the weight kind (kWBf16, kWI8, kWI4), with a.bm 256, 128, 64
+hipError_t launch_expert_up_tiled(const GemmArgs& a, int wq, hipStream_t s);
+hipError_t launch_expert_down_tiled(const GemmArgs& a, int wq, hipStream_t s);
 // Token rows into the tiled up operand a.xp (padded rows past an expert's last row are
 // zero; shared virtual experts after the first are not written, the up kernel reads the
 // first one's rows for them). Reads the scatter's tile list on the device; writes

@@ -31,6 +31,13 @@
 // in LDS as int8 by the same LDS-DMA (half the bytes of bf16) and widened to bf16 in
 // registers right before their MFMAs (exact: |q| <= 127 fits bf16's significand);
 // their per-column scale multiplies the fp32 accumulator in the epilogue.
+// int4 weights ([E][N/16][K/128][64][16 B], one 1 KB block per 16 columns and 128-row
+// scale group) take one K step per group: a stage holds the group's A blocks, the int4
+// blocks and the group's 256 column scales (one more 1 KB block, its eighths loaded by
+// the eight waves). Each code u = q + 8 is placed in the low mantissa bits of bf16 128.0
+// (one mask-and-or per pair of values), so the MFMAs form sum(a * (q + 136)); one more
+// MFMA of the token fragments against the constant 136 gives 136 * sum(a), and the
+// group's partial, less that, times the column's group scale is added in fp32.
 // Up-projection columns are packed gate/up interleaved per 16 columns, so each
 // lane holds the gate and up accumulators of the same (row, f) and SiLU * up
 // runs in registers.
@@ -78,28 +85,32 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 // Pipeline shape: both operands stream through LDS-DMA, four stages (three K steps of
 // loads in flight). bf16: K step 32. int8: K step 64 (one 1 KB int8 block holds 16
 // columns x 64 K), widened to bf16 when the wave reads its B fragments from LDS.
-template <bool INT8> struct Pipe;
-template <> struct Pipe<false> { static constexpr int BK = 32, STAGES = 4; };
-template <> struct Pipe<true> { static constexpr int BK = 64, STAGES = 4; };
+// int4: K step 128 (one scale group).
+template <int WQ> struct Pipe;
+template <> struct Pipe<kWBf16> { static constexpr int BK = 32, STAGES = 4; };
+template <> struct Pipe<kWI8> { static constexpr int BK = 64, STAGES = 4; };
+template <> struct Pipe<kWI4> { static constexpr int BK = 128, STAGES = 4; };
 
 // Wave layout: NW waves with 64-row wave tiles: 16 waves tile a 256-row block 4 x 4
 // (64 x 64 wave tiles, four waves per SIMD, 128 registers each); 8 waves tile a 128-row
 // block 2 x 4 (64 x 64) or a 256-row block 4 x 2 (64 x 128); 4 waves would tile it 2 x 2
-// with (BM/2)-row x 128-column wave tiles.
+// with (BM/2)-row x 128-column wave tiles; 8 waves tile a 64-row block 2 x 4 (32 x 64).
 template <int BM, int NW>
 struct WaveShape {
-    static constexpr int WM = NW >= 8 ? BM / 64 : 2;  // waves along M
+    static constexpr int WM = NW >= 8 ? (BM >= 128 ? BM / 64 : 2) : 2;  // waves along M
     static constexpr int WN = NW / WM;                // waves along N
     static constexpr int MWB = BM / 16 / WM;          // 16-row blocks per wave
     static constexpr int NBW = (BN / 16) / WN;        // 16-column blocks per wave
 };
 
-template <int BM, int NW, bool INT8, bool UP>
+template <int BM, int NW, int WQ, bool UP>
 __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
+    constexpr bool INT8 = WQ == kWI8;
+    constexpr bool INT4 = WQ == kWI4;
     constexpr int kThreads = NW * 64;
     constexpr int kWaves = NW;
-    constexpr int BK = Pipe<INT8>::BK;
-    constexpr int STAGES = Pipe<INT8>::STAGES;
+    constexpr int BK = Pipe<WQ>::BK;
+    constexpr int STAGES = Pipe<WQ>::STAGES;
     constexpr int KH = BK / 32;               // 32-K halves per K step
     constexpr int MBLK = BM / 16;             // 16-row blocks per tile
     constexpr int WM = WaveShape<BM, NW>::WM;
@@ -107,11 +118,13 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
     constexpr int MWB = WaveShape<BM, NW>::MWB;
     constexpr int NBW = WaveShape<BM, NW>::NBW;
     constexpr int ABLK = MBLK * KH;           // A blocks per stage
-    constexpr int BBLK = INT8 ? BN / 16 : (BN / 16) * KH;  // B blocks per stage (an int8 block spans 64 K)
-    constexpr int STAGE = ABLK + BBLK;        // 1 KB blocks per stage
+    constexpr int BBLK = INT8 || INT4 ? BN / 16 : (BN / 16) * KH;  // B blocks per stage (int8/int4: one spans BK)
+    constexpr int SBLK = INT4 ? 1 : 0;        // int4: the group's column scales
+    constexpr int STAGE = ABLK + BBLK + SBLK; // 1 KB blocks per stage
+    static_assert(!INT4 || kWaves == 8, "int4 scales: one eighth of the block per wave");
     constexpr int AW = ABLK / kWaves;         // A block loads per wave per stage
     constexpr int BW = BBLK / kWaves;         // B block loads per wave per stage
-    constexpr int LPS = AW + BW;              // LDS-DMA loads per wave per stage
+    constexpr int LPS = AW + BW + SBLK;       // LDS-DMA loads per wave per stage
 
     const int K = UP ? a.d : a.F;
     const int N = UP ? 2 * a.F : a.d;
@@ -159,9 +172,17 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
     // ---- B
     const int KS = K / 32;
     const u32x4* b_src;
-    if constexpr (INT8) {
-        const int8_t* wb = (const int8_t*)(UP ? a.wgu : a.wdn) + (size_t)tl.e * N * K;
-        b_src = reinterpret_cast<const u32x4*>(wb) + kbase / 64 * 64;
+    const u32x4* s_src = nullptr;  // int4: this lane's 16 bytes of the first group's column scales
+    if constexpr (INT8 || INT4) {
+        const uint8_t* wb = (const uint8_t*)(UP ? a.wgu : a.wdn) + (size_t)tl.e * N * K / (INT4 ? 2 : 1);
+        b_src = reinterpret_cast<const u32x4*>(wb) + kbase / BK * 64;
+        if constexpr (INT4) {
+            // scales [E][K/128][N] (up: packed column order); a partial last column tile
+            // holds N % 256 = 128 columns, read by lanes 0-31 (the other lanes repeat lane 31)
+            const int ls = min(lane, (min(BN, N - tl.n * BN) / 4) - 1);
+            s_src = reinterpret_cast<const u32x4*>((UP ? a.s_gate : a.s_down) +
+                                                   ((size_t)tl.e * (K / BK) + kbase / BK) * N + (size_t)tl.n * BN) + ls;
+        }
     } else {
         const bf16_t* wb = (const bf16_t*)(UP ? a.wgu : a.wdn) + (size_t)tl.e * N * K;
         b_src = reinterpret_cast<const u32x4*>(wb) + kbase / 32 * 64;
@@ -181,7 +202,7 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
     // (wave + NW*i) / KH, read only by the waves of row group (that block) / MWB; a block
     // whose readers hold no rows (past the expert's last row) is not loaded. Blocks grow
     // with i, so the loads made are always a prefix.
-    auto issue = [&](int kt, int stage, auto na) {
+    auto issue = [&](int kt, int stage, auto na) __attribute__((always_inline)) {
         constexpr int NA = decltype(na)::value;
         u32x4* st = lds + (size_t)stage * STAGE * 64;
         size_t oa = 0, ob = 0;
@@ -196,14 +217,19 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < BW; ++j) {
             const int blk = wave * BW + j;  // bf16: n-block blk / KH, K half blk % KH; int8: n-block blk
-            if constexpr (INT8) {
+            if constexpr (INT8 || INT4) {
                 const int nbg = min(tl.n * (BN / 16) + blk, NB16 - 1);
-                dma16(b_src + ob + ((size_t)nbg * (K / 64) + kt) * 64 + lane, st + (ABLK + blk) * 64);
+                dma16(b_src + ob + ((size_t)nbg * (K / BK) + kt) * 64 + lane, st + (ABLK + blk) * 64);
             } else {
                 const int nb = blk / KH, kh = blk % KH;
                 const int nbg = min(tl.n * (BN / 16) + nb, NB16 - 1);
                 dma16(b_src + ob + ((size_t)nbg * KS + kt * KH + kh) * 64 + lane, st + (ABLK + blk) * 64);
             }
+        }
+        // int4: the group's 256 column scales, lanes 8w..8w+7 of wave w (every wave makes
+        // one load instruction per stage, so the vmcnt bookkeeping is the same for all)
+        if constexpr (INT4) {
+            if ((lane >> 3) == wave) dma16(s_src + (size_t)kt * (N / 4), st + (ABLK + BBLK) * 64);
         }
     };
 
@@ -261,6 +287,53 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
                         acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb][0], bq[nb], acc[mb][nb], 0, 0, 0);
             }
         };
+        // int4: one K step is one scale group; its fragments are read from the stage as they
+        // are needed (stage k is complete from iteration k-1's barrier on and is refilled
+        // only after iteration k+1's barrier).
+        uint32_t nib_mask = 0x000F000Fu;  // held in a register: one v_and_or_b32 per pair
+        if constexpr (INT4) asm volatile("" : "+v"(nib_mask));
+        auto mfma_i4 = [&](int stage, auto ma) __attribute__((always_inline)) {
+            constexpr int MA = decltype(ma)::value;
+            const u32x4* la = lds + (size_t)stage * STAGE * 64;
+            const u32x4* lb = la + ABLK * 64;
+            const float* ls = reinterpret_cast<const float*>(lb + BBLK * 64);
+            const bf16x8 k136 = __builtin_bit_cast(bf16x8, u32x4{0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u});
+            u32x4 bq[NBW];
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) bq[nb] = lb[(wn * NBW + nb) * 64 + lane];
+            f32x4 g[MA][NBW], zr[MA];
+#pragma unroll
+            for (int kh = 0; kh < KH; ++kh) {
+                bf16x8 af[MA];
+#pragma unroll
+                for (int mb = 0; mb < MA; ++mb)
+                    af[mb] = __builtin_bit_cast(bf16x8, la[((wm * MWB + mb) * KH + kh) * 64 + lane]);
+#pragma unroll
+                for (int mb = 0; mb < MA; ++mb)
+                    zr[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], k136, kh ? zr[mb] : f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                     0, 0, 0);
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb) {
+                    // word kh of the lane's chunk: K rows 32 kh + 8 (lane / 16) + 0..7 of its column
+                    const uint32_t w = bq[nb][kh];
+                    const bf16x8 bw = __builtin_bit_cast(
+                        bf16x8, u32x4{(w & nib_mask) | 0x43004300u, ((w >> 4) & nib_mask) | 0x43004300u,
+                                      ((w >> 8) & nib_mask) | 0x43004300u, ((w >> 12) & nib_mask) | 0x43004300u});
+#pragma unroll
+                    for (int mb = 0; mb < MA; ++mb)
+                        g[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            af[mb], bw, kh ? g[mb][nb] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) {
+                const float sc = ls[(wn * NBW + nb) * 16 + lane % 16];
+#pragma unroll
+                for (int mb = 0; mb < MA; ++mb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[mb][nb][i] = fmaf(sc, g[mb][nb][i] - zr[mb][i], acc[mb][nb][i]);
+            }
+        };
         // Branch-free steady state (a join in the loop would make the compiler drain every
         // LDS read before the MFMAs): every step issues one stage of LDS-DMA loads -- past
         // the last stage it re-loads the last stage into the free slot, which is never
@@ -269,14 +342,16 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
         // In the ragged last row tile of an expert a wave reads and multiplies only its
         // row blocks that hold rows (MA of MWB; none when all its rows lie past the
         // expert's last row): it still loads its share of the tiles and meets every barrier.
-        auto run = [&](auto ma, auto nac) {
+        auto run = [&](auto ma, auto nac) __attribute__((always_inline)) {
             constexpr bool C = decltype(ma)::value > 0;
-            constexpr int L = decltype(nac)::value + BW;  // LDS-DMA loads per stage of this wave
-            auto step = [&](int k, auto& ca, auto& cb, auto& na, auto& nb) {
+            constexpr int L = decltype(nac)::value + BW + SBLK;  // LDS-DMA loads per stage of this wave
+            auto step = [&](int k, auto& ca, auto& cb, auto& na, auto& nb) __attribute__((always_inline)) {
                 wait_vm_le<(STAGES - 3) * L>();    // stage k+1 has landed
                 lds_barrier();                     // ... for every wave; stage k-1 is free
                 issue(min(k + STAGES - 1, KT - 1), (k + STAGES - 1) % STAGES, nac);
-                if constexpr (C) {
+                if constexpr (C && INT4) {
+                    mfma_i4(k % STAGES, ma);
+                } else if constexpr (C) {
                     read_frags((k + 1) % STAGES, na, nb, ma);
                     mfma_frags(ca, cb, ma);
                 }
@@ -285,7 +360,7 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
             for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(min(s0, KT - 1), s0, nac);
             wait_vm_le<(STAGES - 2) * L>();
             lds_barrier();
-            if constexpr (C) read_frags(0, fa[0], fb[0], ma);
+            if constexpr (C && !INT4) read_frags(0, fa[0], fb[0], ma);
             int k = 0;
             for (; k + 2 < KT; k += 2) {
                 step(k, fa[0], fb[0], fa[1], fb[1]);
@@ -295,7 +370,9 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
             // in either case (with one step left its fragment read is of a stage that does
             // not exist and is dropped)
             step(k, fa[0], fb[0], fa[1], fb[1]);
-            if constexpr (C) {
+            if constexpr (C && INT4) {
+                if (KT - k == 2) mfma_i4((k + 1) % STAGES, ma);  // stage k+1 landed before step k's barrier
+            } else if constexpr (C) {
                 if (!INT8 || KT - k == 2) mfma_frags(fa[1], fb[1], ma);
             }
         };
@@ -310,18 +387,24 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
         using I1 = std::integral_constant<int, 1>;
         using I2 = std::integral_constant<int, AW>;  // == 2 when AW == 2
         using MF = std::integral_constant<int, MWB>;
-        if constexpr (INT8) {
-            // row blocks holding rows: 0, 1, 2 or all (3 rounds up to all)
+        if constexpr (INT8 || INT4) {
+            // row blocks holding rows: 0, 1, 2 or all (3 rounds up to all; int4 waves hold two)
             const int rw = tl.rows - wm * MWB * 16;
-            auto run_nac = [&](auto ma) {
+            auto run_nac = [&](auto ma) __attribute__((always_inline)) {
                 if (nA == AW) run(ma, I2{});
                 else if (nA == 1) run(ma, I1{});
                 else run(ma, I0{});
             };
-            if (rw > 32) run_nac(MF{});
-            else if (rw > 16) run_nac(std::integral_constant<int, 2>{});
-            else if (rw > 0) run_nac(std::integral_constant<int, 1>{});
-            else run_nac(I0{});
+            if constexpr (MWB == 2) {
+                if (rw > 16) run_nac(MF{});
+                else if (rw > 0) run_nac(std::integral_constant<int, 1>{});
+                else run_nac(I0{});
+            } else {
+                if (rw > 32) run_nac(MF{});
+                else if (rw > 16) run_nac(std::integral_constant<int, 2>{});
+                else if (rw > 0) run_nac(std::integral_constant<int, 1>{});
+                else run_nac(I0{});
+            }
         } else if (has_rows) {
             // bf16 tiles are MFMA-bound and full but for each expert's last one, which is
             // bound by its weight loads: all or none of a wave's row blocks
@@ -413,13 +496,14 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
     }
 }
 
-template <int BM, int NW, bool INT8, bool UP>
+template <int BM, int NW, int WQ, bool UP>
 hipError_t launch(const GemmArgs& a, hipStream_t s) {
-    constexpr int KH = Pipe<INT8>::BK / 32;
-    constexpr int STAGE = (BM / 16) * KH + (INT8 ? BN / 16 : (BN / 16) * KH);  // as in the kernel
-    static_assert(Pipe<INT8>::STAGES * STAGE * 1024 <= 160 * 1024, "LDS");
-    const size_t lds_bytes = (size_t)Pipe<INT8>::STAGES * STAGE * 64 * 16;
-    auto kern = expert_gemm<BM, NW, INT8, UP>;
+    constexpr int BK = Pipe<WQ>::BK;
+    constexpr int KH = BK / 32;
+    constexpr int STAGE = (BM / 16) * KH + (WQ != kWBf16 ? BN / 16 : (BN / 16) * KH) + (WQ == kWI4 ? 1 : 0);  // as in the kernel
+    static_assert(Pipe<WQ>::STAGES * STAGE * 1024 <= 160 * 1024, "LDS");
+    const size_t lds_bytes = (size_t)Pipe<WQ>::STAGES * STAGE * 64 * 16;
+    auto kern = expert_gemm<BM, NW, WQ, UP>;
     static bool attr_set = false;  // one-time opt-in above the default dynamic LDS limit
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -430,7 +514,9 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
     const int N = UP ? 2 * a.F : a.d;
     const int S = UP ? 1 : a.ksplit;
     const int Kpart = (UP ? a.d : a.F) / S;
-    if (Kpart % 64 != 0 || Kpart < 64) return hipErrorInvalidValue;  // whole K steps of 64 (int8) or 2 x 32
+    // whole K steps (an even count of 32-K steps for bf16)
+    if (Kpart % std::max(BK, 64) != 0 || Kpart < std::max(BK, 64)) return hipErrorInvalidValue;
+    if (WQ == kWI4 && (N % 128 != 0 || a.merge_shared)) return hipErrorInvalidValue;
     const int NTp = ((N + BN - 1) / BN + GN - 1) / GN * GN;
     // a multiple of 8 workgroups, so every XCD gets ceil(tiles / 8) slots (a merged shared
     // down projection starts its routed tiles at the next multiple of 8 after its own)
@@ -441,25 +527,27 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
 }
 
 template <bool UP>
-hipError_t launch_dispatch(const GemmArgs& a, bool int8, hipStream_t s) {
+hipError_t launch_dispatch(const GemmArgs& a, int wq, hipStream_t s) {
     // bf16 weights: 256-row tiles on 16 waves (four per SIMD hide more latency than two
     // waves with 64 x 128 tiles, though they read a third more LDS per MFMA); int8: 128-row
     // tiles on 8 waves (two K halves of int8 fragments need the registers of two waves per
     // SIMD). Measured slower: 4 waves with 128 x 128 wave tiles (one wave per SIMD hides
-    // nothing), 128-row bf16 tiles (more operand traffic per MFMA).
-    if (!int8 && a.bm == 256) return launch<256, kBf16Waves, false, UP>(a, s);
-    if (int8 && a.bm == 128) return launch<128, 8, true, UP>(a, s);
+    // nothing), 128-row bf16 tiles (more operand traffic per MFMA). int4: 64-row tiles on
+    // 8 waves (32 x 64 wave tiles), the batches it serves holding ~64 rows per expert.
+    if (wq == kWBf16 && a.bm == 256) return launch<256, kBf16Waves, kWBf16, UP>(a, s);
+    if (wq == kWI8 && a.bm == 128) return launch<128, 8, kWI8, UP>(a, s);
+    if (wq == kWI4 && a.bm == 64) return launch<64, 8, kWI4, UP>(a, s);
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_expert_up_bf16(const GemmArgs& a, bool int8, hipStream_t s) {
-    return launch_dispatch<true>(a, int8, s);
+hipError_t launch_expert_up_tiled(const GemmArgs& a, int wq, hipStream_t s) {
+    return launch_dispatch<true>(a, wq, s);
 }
 
-hipError_t launch_expert_down_bf16(const GemmArgs& a, bool int8, hipStream_t s) {
-    return launch_dispatch<false>(a, int8, s);
+hipError_t launch_expert_down_tiled(const GemmArgs& a, int wq, hipStream_t s) {
+    return launch_dispatch<false>(a, wq, s);
 }
 
 }  // namespace moe

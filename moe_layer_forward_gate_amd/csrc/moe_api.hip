@@ -262,12 +262,11 @@ int check_device(const moe_layer* L) {
 }
 
 // Launch plan (host side, from T, k and the layer shape only):
-//  - small batches (T <= 64), and every batch of an int4 layer, stream the weights: row
-//    tiles of 16, 32 or 64 rows (int4: 16 or 32), sized so an active expert almost always
-//    fits one tile (an int4 layer's larger batches take several tiles per expert, each
-//    streaming the weights again), the down projection's K split so ~1024 workgroups run;
-//  - larger batches use the LDS-tiled MFMA GEMMs (256-row tiles for bf16 weights,
-//    128 for int8), with the down projection's K split when that fills the CUs better.
+//  - small batches (T <= 64) stream the weights: row tiles of 16, 32 or 64 rows (int4: 16
+//    or 32), sized so an active expert almost always fits one tile, the down projection's
+//    K split so ~1024 workgroups run;
+//  - larger batches use the LDS-tiled MFMA GEMMs (256-row tiles for bf16 weights, 128 for
+//    int8, 64 for int4), with the down projection's K split when that fills the CUs better.
 struct Plan {
     bool streaming;
     int bm, ksplit, max_tiles;
@@ -281,7 +280,7 @@ Plan make_plan(const moe_layer* L, int T) {
     const bool i8 = d.expert_dtype == MOE_I8;
     const bool i4 = d.expert_dtype == MOE_I4;
     const int k = d.top_k;
-    const bool streaming = !f32 && (T <= kStreamMaxT || i4);
+    const bool streaming = !f32 && T <= kStreamMaxT;
     int bm, ksplit = 1;
     bool weights_once = true;
     if (f32) {
@@ -303,8 +302,9 @@ Plan make_plan(const moe_layer* L, int T) {
     } else {
         // bf16: 256-row tiles (the 256 x 256 workgroup tile reads the least LDS and L2 per MFMA
         // and outruns 128-row tiles even when most experts leave their last tile half empty);
-        // int8: 128-row tiles (see the GEMM launcher)
-        bm = i8 ? 128 : 256;
+        // int8: 128-row tiles; int4: 64-row tiles (see the GEMM launcher)
+        bm = i4 ? 64 : (i8 ? 128 : 256);
+        const int kq = i4 ? 128 : 64;  // every split a whole number of K steps
         // split the down projection's K (S = 2 or 4) when that fills the last round of
         // workgroups better: with W = tiles * column tiles * S workgroups, one per CU at a
         // time, the busy fraction is W / (rounds * CUs); a split must gain 0.1 of it (the
@@ -324,7 +324,7 @@ Plan make_plan(const moe_layer* L, int T) {
         };
         double best = busy(1);
         for (int S = 2; S <= 4; S *= 2) {
-            if (d.d_ff / S < 2048 || d.d_ff % (S * 64) != 0 || (size_t)T * L->kt * S > L->ow_rows) break;
+            if (d.d_ff / S < 2048 || d.d_ff % (S * kq) != 0 || (size_t)T * L->kt * S > L->ow_rows) break;
             if (busy(S) > best + 0.1) {
                 best = busy(S);
                 ksplit = S;
@@ -339,7 +339,7 @@ Plan make_plan(const moe_layer* L, int T) {
     const int max_tiles = std::min(L->Et, P) + (P - 1) / bm;
     // tiled down projection of a shared expert in several slices: the slices of a row tile
     // are summed in one K loop (one partial row per token instead of one per slice)
-    const bool merge = !f32 && !streaming && !i8 && L->V > 1 && ksplit == 1;
+    const bool merge = !f32 && !streaming && !i8 && !i4 && L->V > 1 && ksplit == 1;
     return Plan{streaming, bm, ksplit, max_tiles, merge, weights_once};
 }
 
@@ -390,9 +390,9 @@ int run_experts(moe_layer* L, const void* x, int T, void* y, const float* topk_w
         if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));
         HIP_TRY(launch_expert_down_stream(a, wq, s));
     } else {
-        HIP_TRY(launch_expert_up_bf16(a, i8, s));
+        HIP_TRY(launch_expert_up_tiled(a, wq, s));
         if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));
-        HIP_TRY(launch_expert_down_bf16(a, i8, s));
+        HIP_TRY(launch_expert_down_tiled(a, wq, s));
     }
     if (prof) HIP_TRY(hipEventRecord(L->ev[4], s));
     HIP_TRY(launch_combine(L->ow, T, (pl.merge ? k + 1 : L->kt) * pl.ksplit, L->kt * pl.ksplit, d.d_model, y, !f32,
