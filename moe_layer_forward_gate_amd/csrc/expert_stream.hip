@@ -289,8 +289,9 @@ hipError_t launch_nbw(const GemmArgs& a, int S, hipStream_t s) {
     if (N % (16 * NBW * 4) != 0) return hipErrorInvalidValue;             // whole column groups
     const int NG = N / (16 * NBW * 4);
     dim3 grid((unsigned)((size_t)a.max_tiles * NG * S));
-    // non-temporal weight loads when each expert's weights are read by one row tile; int4
-    // layers past ~64 tokens stream them once per 32-row tile and keep them cached
+    // non-temporal weight loads when each expert's weights are read by one row tile; an int4
+    // layer whose busiest expert needs several 32-row tiles streams them once per tile and
+    // keeps them cached
     if (WQ != kWI4 || a.weights_once)
         hipLaunchKernelGGL((expert_stream<MB, NBW, WQ, UP, U, true>), grid, dim3(kThreads), 0, s, a, S);
     else if constexpr (WQ == kWI4)
