@@ -58,7 +58,9 @@ __device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w, int sh) {
     // bytes sh/8 and sh/8+1 of w as two bf16 (exact widening of small integers)
     const float f0 = (float)(int)(int8_t)(w >> sh);
     const float f1 = (float)(int)(int8_t)(w >> (sh + 8));
-    return (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+    // the high halves of the two fp32 patterns (exact: |q| <= 128 has at most 8 significant
+    // bits), picked by one byte permute: bytes 2-3 of f0, then bytes 2-3 of f1
+    return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
 }
 
 __device__ __forceinline__ u32x4 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {

@@ -28,7 +28,9 @@ constexpr int kThreads = 256;
 __device__ __forceinline__ uint32_t i8x2_bf16(uint32_t w, int sh) {
     const float f0 = (float)(int)(int8_t)(w >> sh);
     const float f1 = (float)(int)(int8_t)(w >> (sh + 8));
-    return (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+    // the high halves of the two fp32 patterns (exact: |q| <= 128 has at most 8 significant
+    // bits), picked by one byte permute: bytes 2-3 of f0, then bytes 2-3 of f1
+    return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
 }
 
 // int4 codes (q + 8, 4 bits) to bf16 pairs: a code u placed in the low mantissa bits of
