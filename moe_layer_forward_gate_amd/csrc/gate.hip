@@ -219,8 +219,9 @@ __global__ __launch_bounds__(256) void gate_rowdot(const XT* __restrict__ x, con
 // router blocks (NB = ceil(Ec/16) <= 9) for all TB token blocks, so every router
 // fragment it loads serves TB MFMAs (the router is re-read once per workgroup: TB sets
 // how many tokens share that read). Four waves suffice when the batch gives >= 512
-// workgroups; smaller batches take 16 waves so that each wave has fewer K steps of
-// dependent loads to wait through. A fragments come straight from the token rows, B
+// workgroups with one token block each; smaller batches take 16 waves and batches of
+// two token blocks per workgroup take 8, so that each wave has fewer K steps of dependent
+// loads to wait through. A fragments come straight from the token rows, B
 // fragments from the three packed planes ([plane][NB][d/32][64] lanes x 16 B, fragment
 // order). The wave partials are added in LDS one token block at a time, in a fixed order.
 template <int NB, int TB, int NW>
@@ -228,10 +229,10 @@ __global__ __launch_bounds__(NW * 64) void gate_mfma(const bf16_t* __restrict__ 
                                                      const float* __restrict__ bias, int T, int d, int E, int k,
                                                      int gflags, int32_t* __restrict__ idx, float* __restrict__ w,
                                                      float* __restrict__ gs) {
-    static_assert(NW == 4 || NW == 16, "wave count");
+    static_assert(NW == 4 || NW == 8 || NW == 16, "wave count");
     const bool has_shared = (gflags & kGateShared) != 0;
     constexpr int LP = NB * 16 + 1;
-    constexpr int NP = NW == 4 ? 4 : 8;  // partial slots: 16 waves fold pairwise into 8 first
+    constexpr int NP = NW == 16 ? 8 : 4;  // partial slots: 8 or 16 waves fold pairwise first
     __shared__ float part[NP][16 * LP];
     __shared__ float logits[16 * TB * LP];
     const int t0 = blockIdx.x * 16 * TB;
@@ -251,10 +252,12 @@ __global__ __launch_bounds__(NW * 64) void gate_mfma(const bf16_t* __restrict__ 
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[tb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     // U K-steps per round, every load of the round issued before the first MFMA
-    // (16 waves: at most 64 registers of loads in flight, the budget of four waves per SIMD)
+    // (16 waves: at most 64 registers of loads in flight, the budget of four waves per SIMD;
+    // 8 waves: at most ~110, two waves per SIMD)
     constexpr int LR = TB + 3 * NB;  // 16-byte loads per K step
     constexpr int U = NW == 4 ? (NB * TB <= 2 ? 8 : (NB * TB <= 4 ? 4 : (NB * TB <= 12 ? 2 : 1)))
-                              : (LR <= 4 ? 4 : (LR <= 8 ? 2 : 1));
+                              : NW == 8 ? (LR <= 6 ? 4 : (LR <= 13 ? 2 : 1))
+                                        : (LR <= 4 ? 4 : (LR <= 8 ? 2 : 1));
     auto round = [&](int ks, auto uconst) {
         constexpr int UU = decltype(uconst)::value;
         u32x4 av[UU][TB], bv[UU][NB][3];
@@ -287,17 +290,17 @@ __global__ __launch_bounds__(NW * 64) void gate_mfma(const bf16_t* __restrict__ 
     const int Ec = E + (has_shared ? 1 : 0);
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
-        if constexpr (NW == 16) {
-            // waves 8..15 hand their partials to waves 0..7, which add them to their own
-            if (wave >= 8) {
+        if constexpr (NW > NP) {
+            // waves NP..2NP-1 hand their partials to waves 0..NP-1, which add them to their own
+            if (wave >= NP) {
 #pragma unroll
                 for (int j = 0; j < NB; ++j)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        part[wave - 8][(4 * (lane / 16) + i) * LP + 16 * j + lane % 16] = acc[tb][j][i];
+                        part[wave - NP][(4 * (lane / 16) + i) * LP + 16 * j + lane % 16] = acc[tb][j][i];
             }
             __syncthreads();
-            if (wave < 8) {
+            if (wave < NP) {
 #pragma unroll
                 for (int j = 0; j < NB; ++j)
 #pragma unroll
@@ -646,9 +649,11 @@ __global__ __launch_bounds__(1024) void gate_finish(const float* __restrict__ pa
     }
 }
 
-// largest router width (16-column blocks) the 16-wave gate takes: its LDS partials
-// (8 x 16 tokens x (16 NB + 1) floats) stay within the 64 KB of static LDS
-constexpr int kGate16MaxNB = 6;
+// largest router widths (16-column blocks) the 16-wave gate (one token block) and the
+// 8-wave gate (two token blocks) take: past them their loads and accumulators no longer
+// fit the registers of four and two waves per SIMD without spills
+constexpr int kGate16MaxNB = 5;
+constexpr int kGate8MaxNB = 8;
 
 template <int TB, int NW>
 hipError_t launch_gate_mfma_tb(int NB, const bf16_t* x, const u32x4* planes, const float* bias, int T, int d, int E,
@@ -657,7 +662,7 @@ hipError_t launch_gate_mfma_tb(int NB, const bf16_t* x, const u32x4* planes, con
     switch (NB) {
 #define GATE_MFMA_CASE(J)                                                                                       \
     case J:                                                                                                     \
-        if constexpr (NW == 4 || J <= kGate16MaxNB) {                                                           \
+        if constexpr ((NW != 16 || J <= kGate16MaxNB) && (NW != 8 || J <= kGate8MaxNB)) {                      \
             hipLaunchKernelGGL((gate_mfma<J, TB, NW>), grid, dim3(NW * 64), 0, s, x, planes, bias, T, d, E, k,   \
                                gflags, idx, w, gs);                                                             \
             break;                                                                                              \
@@ -676,6 +681,7 @@ hipError_t launch_gate_mfma_tb(int NB, const bf16_t* x, const u32x4* planes, con
 hipError_t launch_gate_mfma_nb(int TB, int NB, const bf16_t* x, const u32x4* planes, const float* bias, int T, int d,
                                int E, int k, int gflags, int32_t* idx, float* w, float* gs, hipStream_t s) {
     if (TB == 4) return launch_gate_mfma_tb<4, 4>(NB, x, planes, bias, T, d, E, k, gflags, idx, w, gs, s);
+    if (TB == 2 && NB <= kGate8MaxNB) return launch_gate_mfma_tb<2, 8>(NB, x, planes, bias, T, d, E, k, gflags, idx, w, gs, s);
     if (TB == 2) return launch_gate_mfma_tb<2, 4>(NB, x, planes, bias, T, d, E, k, gflags, idx, w, gs, s);
     // one token block per workgroup: fewer than 512 workgroups take 16 waves each (every
     // wave keeps at least one K step)

@@ -161,3 +161,14 @@ def test_hip_graph_replays_match_eager():
             torch.cuda.synchronize()
         del g
     lay.close()
+
+
+def test_gate_token_block_shapes():
+    # the MFMA gate's workgroup shapes: 16 waves over one 16-token block (T < 8192, up to 80
+    # router columns), 8 waves over two blocks (8192 <= T < 16384, up to 128 columns), 4 waves
+    # over two (wider routers) or four blocks (T >= 16384); ragged last token blocks
+    _run(synth.get_config("mixtral_bf16", d_model=256, d_ff=128), [8200, 16400])
+    _run(synth.get_config("shared_fine_bf16", d_model=256, d_ff=128, n_experts=100, top_k=4, shared_d_ff=256),
+         [8195])
+    _run(synth.get_config("shared_fine_bf16", d_model=256, d_ff=128, n_experts=128, top_k=2, shared_d_ff=256),
+         [8200])
