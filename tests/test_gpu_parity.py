@@ -133,11 +133,17 @@ def test_forward_argument_errors():
     lay.close()
 
 
-def test_hip_graph_replays_match_eager():
+@pytest.mark.parametrize("name,kw", [
+    ("shared_fine_bf16", dict(d_model=256, d_ff=128, shared_d_ff=512)),
+    ("int8_mixtral22b", dict(d_model=256, d_ff=128)),
+    ("int4_mixtral22b", dict(d_model=256, d_ff=256)),
+])
+def test_hip_graph_replays_match_eager(name, kw):
     # moe_forward only enqueues kernels (no allocation, no host sync, no memset nodes), so it
     # can be captured in a HIP graph; every replay, with eager work and synchronisations in
-    # between, must reproduce the eager result bit for bit (prefill and decode plans)
-    cfg = synth.get_config("shared_fine_bf16", d_model=256, d_ff=128, shared_d_ff=512)
+    # between, must reproduce the eager result bit for bit (prefill and decode plans of the
+    # bf16, int8 and int4 kernels)
+    cfg = synth.get_config(name, **kw)
     L = synth.make_layer(cfg)
     lay = gpu_layer(L, 300)
     for T in (300, 3, 16):
@@ -150,12 +156,14 @@ def test_hip_graph_replays_match_eager():
         with torch.cuda.graph(g, stream=s):
             lay.forward(x, out=out, stream=s)
         torch.cuda.synchronize()
+        fields = [f for f in ("y", "topk_idx", "topk_w", "expert_counts", "expert_offsets", "sorted_assign",
+                              "shared_gate") if getattr(out, f, None) is not None]
         for rep in range(3):
-            for f in ("y", "topk_idx", "topk_w", "expert_counts", "expert_offsets", "sorted_assign", "shared_gate"):
+            for f in fields:
                 getattr(out, f).fill_(-1) if getattr(out, f).dtype != torch.bfloat16 else getattr(out, f).fill_(7)
             g.replay()
             torch.cuda.synchronize()
-            for f in ("y", "topk_idx", "topk_w", "expert_counts", "expert_offsets", "sorted_assign", "shared_gate"):
+            for f in fields:
                 assert torch.equal(getattr(out, f), getattr(ref, f)), (T, rep, f)
             lay.forward(x[: max(1, T // 2)], scatter=True)  # eager work between replays
             torch.cuda.synchronize()
