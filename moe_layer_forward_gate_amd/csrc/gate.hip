@@ -218,10 +218,10 @@ __global__ __launch_bounds__(256) void gate_rowdot(const XT* __restrict__ x, con
 // [v*(KS/NW), (v+1)*(KS/NW)), the last wave the rest) and each takes all 16-column
 // router blocks (NB = ceil(Ec/16) <= 9) for all TB token blocks, so every router
 // fragment it loads serves TB MFMAs (the router is re-read once per workgroup: TB sets
-// how many tokens share that read). Four waves suffice when the batch gives >= 512
-// workgroups with one token block each; smaller batches take 16 waves and batches of
-// two token blocks per workgroup take 8, so that each wave has fewer K steps of dependent
-// loads to wait through. A fragments come straight from the token rows, B
+// how many tokens share that read). One token block takes 16 waves (routers of up to 80
+// columns), two take 8 (up to 128 columns), four and wider routers take 4: the more waves
+// split K, the fewer K steps of dependent loads each waits through, as far as registers
+// and LDS allow. A fragments come straight from the token rows, B
 // fragments from the three packed planes ([plane][NB][d/32][64] lanes x 16 B, fragment
 // order). The wave partials are added in LDS one token block at a time, in a fixed order.
 template <int NB, int TB, int NW>
