@@ -73,6 +73,14 @@ def test_int4_reduced():
     _run(cfg, [1, 2, 16, 40, 64, 65, 256, 1000])
 
 
+def test_quantised_partial_column_tiles():
+    # d_model = 384: the down projections' last 256-column tile holds 128 columns (int4: its
+    # group scales are read by lanes 0-31 only); d_ff = 192 (int8): the up projection's last
+    # tile of gate/up columns holds 128
+    _run(synth.get_config("int4_mixtral22b", d_model=384, d_ff=384), [70, 200])
+    _run(synth.get_config("int8_mixtral22b", d_model=384, d_ff=192), [70, 200])
+
+
 def test_tiny_batches_single_workgroup_route():
     # T <= 4 with at most 16 router columns: gate and scatter run in one workgroup
     _run(synth.get_config("mixtral_bf16", d_model=512, d_ff=1024), [1, 2, 3, 4, 5])
