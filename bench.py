@@ -70,6 +70,8 @@ def parse():
     ap.add_argument("--tokens", type=int, default=None, help="main workload T (default: largest of the config)")
     ap.add_argument("--instances", type=int, default=4)
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-measured-peaks", action="store_true",
+                    help="leave out the measured HBM-read and MFMA rates (two microbenchmarks, ~0.3 s)")
     ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
     ap.add_argument("--streams", type=int, default=1,
                     help="S > 1: S layer instances forwarded concurrently on S streams (decode throughput)")
@@ -302,21 +304,48 @@ def cpu_baseline(cfg, layer_cpu, x_cpu, n_tok, min_s, routing=None):
                        f"{cfg.n_experts} experts, combine), {dt:.1f} s")
 
 
+def peaks_lib():
+    import ctypes
+    P = ctypes.CDLL(os.path.join(ROOT, "moe_layer_forward_gate_amd", "libmoe_peaks.so"))
+    for f in ("moe_peak_read_gbps", "moe_peak_read_nt_gbps"):
+        getattr(P, f).restype = ctypes.c_double
+        getattr(P, f).argtypes = [ctypes.c_size_t, ctypes.c_int, ctypes.c_int]
+    for f in ("moe_peak_mfma_tflops", "moe_peak_mfma_random_tflops"):
+        getattr(P, f).restype = ctypes.c_double
+        getattr(P, f).argtypes = [ctypes.c_int, ctypes.c_int]
+    return P
+
+
+def measured_peaks(rf):
+    """The two rates measured on this GPU that the kernels can reach, and the dominant kernel's
+    achieved rate against the one of its bound: a 4 GiB non-temporal streaming read, and bf16
+    MFMA issue on random register operands that change every instruction (about 60 ms, long
+    enough for the clock to settle at the power the multipliers draw on real data)."""
+    try:
+        P = peaks_lib()
+    except OSError:
+        return None
+    hbm = max(P.moe_peak_read_nt_gbps(4 << 30, w, 5) for w in (4096, 8192))
+    P.moe_peak_mfma_random_tflops(256, 20000)  # clock settles
+    mfma = P.moe_peak_mfma_random_tflops(256, 100000)
+    peak = hbm if rf["bound"] == "hbm" else mfma
+    return {"hbm_read_GBps": hbm, "mfma_bf16_TFLOPs": mfma,
+            "bound_peak": peak, "frac_of_measured": rf["achieved"] / peak if peak > 0 else None,
+            "how": "non-temporal streaming read of 4 GiB; v_mfma_f32_16x16x32_bf16 issue on random "
+                   "register operands changing every instruction"}
+
+
 def measure_peaks(torch):
     """Achievable rates on this GPU: libmoe_peaks microbenchmarks (streaming HBM read, bf16
-    MFMA issue from registers) and, for comparison, hipBLASLt bf16 GEMMs of the expert shapes."""
-    import ctypes
+    MFMA issue from registers on constant and on random operands) and, for comparison,
+    hipBLASLt bf16 GEMMs of the expert shapes."""
     out = {}
-    P = ctypes.CDLL(os.path.join(ROOT, "moe_layer_forward_gate_amd", "libmoe_peaks.so"))
-    P.moe_peak_read_gbps.restype = ctypes.c_double
-    P.moe_peak_read_gbps.argtypes = [ctypes.c_size_t, ctypes.c_int, ctypes.c_int]
-    P.moe_peak_mfma_tflops.restype = ctypes.c_double
-    P.moe_peak_mfma_tflops.argtypes = [ctypes.c_int, ctypes.c_int]
-    P.moe_peak_read_nt_gbps.restype = ctypes.c_double
-    P.moe_peak_read_nt_gbps.argtypes = [ctypes.c_size_t, ctypes.c_int, ctypes.c_int]
+    P = peaks_lib()
     out["read_stream_GBps"] = {w: P.moe_peak_read_gbps(4 << 30, w, 5) for w in (2048, 4096, 8192)}
     out["read_stream_nontemporal_GBps"] = {w: P.moe_peak_read_nt_gbps(4 << 30, w, 5) for w in (2048, 4096, 8192)}
     out["mfma_bf16_TFLOPs"] = {w: P.moe_peak_mfma_tflops(w, 20000) for w in (256, 512)}
+    P.moe_peak_mfma_random_tflops(256, 20000)
+    out["mfma_bf16_random_operands_TFLOPs"] = {w: P.moe_peak_mfma_random_tflops(w, 50000) for w in (256, 512)}
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     n = 10
     for M, K, N in ((8192, 8192, 8192), (1024, 4096, 28672), (1024, 14336, 4096)):
@@ -422,6 +451,7 @@ def main():
         "sweep": [{k: s[k] for k in ("T", "tokens_per_s", "ms_per_step", "stage_ms", "layer_GBps",
                                      "layer_hbm_frac", "layer_mfma_frac", "roofline")} for s in sweep],
         "cpu_baseline": cpu,
+        "measured_peaks": None if args.no_measured_peaks else measured_peaks(main_s["roofline"]),
     }
     print(json.dumps(line), flush=True)
 

@@ -1,8 +1,11 @@
 // Microbenchmarks of the two rates the MoE kernels are held against on this GPU: a
 // streaming HBM read (each wave reads its own contiguous region 16 bytes per lane,
 // several loads in flight) and bf16 MFMA issue (v_mfma_f32_16x16x32_bf16 on a 4 x 8 grid
-// of independent accumulators per wave, operands in registers, no memory traffic).
-// Built into libmoe_peaks.so, separate from libmoe; used by bench.py --peaks.
+// of independent accumulators per wave, operands in registers, no memory traffic), once
+// with constant operands and once with random operands that change every MFMA: the
+// multipliers' switching activity sets the power draw, and with it the clock the chip
+// holds, so only the second rate is reachable by a GEMM on real data.
+// Built into libmoe_peaks.so, separate from libmoe; used by bench.py.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -51,6 +54,55 @@ __global__ __launch_bounds__(512) void mfma_issue(int iters, float* __restrict__
     for (int m = 0; m < 4; ++m)
         for (int n = 0; n < 8; ++n) s += acc[m][n][0] + acc[m][n][3];
     out[blockIdx.x * 512 + threadIdx.x] = s;
+}
+
+// 32-bit integer mix (the finaliser of the MurmurHash3 family) for operand bits
+__device__ __forceinline__ uint32_t mix32(uint32_t h) {
+    h ^= h >> 16;
+    h *= 0x85ebca6bu;
+    h ^= h >> 13;
+    h *= 0xc2b2ae35u;
+    h ^= h >> 16;
+    return h;
+}
+
+// bf16 values +-[1, 2) with random mantissas: sign bit 15, exponent of 1.0, mantissa bits 0-6
+__device__ __forceinline__ bf16x8 random_bf16x8(uint32_t seed) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t h = mix32(seed * 4u + (uint32_t)i);
+        w[i] = (0x3F803F80u | (h & 0x007F007Fu)) | (h & 0x80008000u);
+    }
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+// The same MFMA grid as mfma_issue, with two sets of random operands used in turn, so
+// consecutive MFMAs of a wave never see the same inputs.
+__global__ __launch_bounds__(512) void mfma_issue_random(int iters, float* __restrict__ out) {
+    const uint32_t t = blockIdx.x * 512u + threadIdx.x;
+    bf16x8 a[2][4], b[2][8];
+    for (int s = 0; s < 2; ++s) {
+        for (int j = 0; j < 4; ++j) a[s][j] = random_bf16x8(t * 64u + s * 32u + j);
+        for (int j = 0; j < 8; ++j) b[s][j] = random_bf16x8(t * 64u + s * 32u + 8u + j);
+    }
+    f32x4 acc[4][8];
+    for (int m = 0; m < 4; ++m)
+        for (int n = 0; n < 8; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int n = 0; n < 8; ++n)
+                    acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s][m], b[s ^ (n & 1)][n], acc[m][n], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    float sum = 0.f;
+    for (int m = 0; m < 4; ++m)
+        for (int n = 0; n < 8; ++n) sum += acc[m][n][0] + acc[m][n][3];
+    out[blockIdx.x * 512 + threadIdx.x] = sum;
 }
 
 float time_ms(hipEvent_t a, hipEvent_t b) {
@@ -117,6 +169,27 @@ __attribute__((visibility("default"))) double moe_peak_mfma_tflops(int wgs, int 
         hipEventRecord(b, 0);
         if (hipEventSynchronize(b) == hipSuccess)
             r = (double)wgs * 8 * iters * 32 * 16384.0 / (time_ms(a, b) * 1e-3) / 1e12;
+        hipEventDestroy(a);
+        hipEventDestroy(b);
+    }
+    hipFree(o);
+    return r;
+}
+
+// The same with random operands that change every MFMA (64 MFMAs per wave per iteration).
+__attribute__((visibility("default"))) double moe_peak_mfma_random_tflops(int wgs, int iters) {
+    if (wgs <= 0 || iters <= 0) return -1.0;
+    float* o = nullptr;
+    if (hipMalloc(&o, (size_t)wgs * 512 * 4) != hipSuccess) return -2.0;
+    double r = -3.0;
+    hipEvent_t a, b;
+    if (hipEventCreate(&a) == hipSuccess && hipEventCreate(&b) == hipSuccess) {
+        hipLaunchKernelGGL(mfma_issue_random, dim3(wgs), dim3(512), 0, 0, 10, o);
+        hipEventRecord(a, 0);
+        hipLaunchKernelGGL(mfma_issue_random, dim3(wgs), dim3(512), 0, 0, iters, o);
+        hipEventRecord(b, 0);
+        if (hipEventSynchronize(b) == hipSuccess)
+            r = (double)wgs * 8 * iters * 64 * 16384.0 / (time_ms(a, b) * 1e-3) / 1e12;
         hipEventDestroy(a);
         hipEventDestroy(b);
     }
