@@ -82,7 +82,8 @@ struct GemmArgs {
     const int32_t* sorted_c;    // [P]
     int Et, kt, k;              // experts incl. virtual, slots per token incl. virtual, routed k
     int max_tiles;              // bound on sum_e ceil(n_e / bm)
-    int bm;                     // row tile height: 256 (bf16) or 128 (int8); must match the scatter's tile list
+    int bm;                     // row tile height: tiled 256 (bf16), 128 (int8), 64 (int4); streaming 16-64;
+                                // must match the scatter's tile list
     int ksplit;                 // down projection: K split into ksplit partial sums (ow rows c*ksplit + s)
     int merge_shared;           // tiled down projection: shared slices summed as one K = V*F tile (ksplit 1)
     int weights_once;           // streaming kernels: an expert's weights are read by one row tile only
@@ -96,9 +97,9 @@ struct GemmArgs {
     bf16_t* h;                  // [P][F] or packed [R/16][F/32][64][8]
     const void* wgu;            // packed gate/up
     const void* wdn;            // packed down
-    const float* s_gate;        // [E][F] (int8)
-    const float* s_up;          // [E][F]
-    const float* s_down;        // [E][d]
+    const float* s_gate;        // int8: [E][F]; int4: the up projection's [E][d/128][2F] (packed column order)
+    const float* s_up;          // int8: [E][F]
+    const float* s_down;        // int8: [E][d]; int4: [E][F/128][d]
     const float* topk_w;        // [T][k]
     const float* gs;            // [T] shared gate or null
     float* ow;                  // [T*kt*ksplit][d] weighted expert outputs (partial sums)

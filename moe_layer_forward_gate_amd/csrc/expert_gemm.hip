@@ -13,9 +13,10 @@
 //       aggregation).
 //
 // Workgroup tile BM x 256 (BM = 256 on 16 waves for bf16 weights, 128 on 8 waves
-// for int8); each wave owns a 64 x 64 block of v_mfma_f32_16x16x32_bf16
-// accumulators. K step 32 (bf16 weights) or 64 (int8), four LDS stages, three K
-// steps of loads in flight, one barrier per step. Operands are
+// for int8, 64 on 8 waves for int4); each wave owns a 64 x 64 block of
+// v_mfma_f32_16x16x32_bf16 accumulators (int4: 32 x 64). K step 32 (bf16 weights), 64
+// (int8) or 128 (int4), four LDS stages, three K steps of loads in flight, one barrier
+// per step. Operands are
 // staged in LDS in MFMA fragment order: one 1 KB block = 16 rows x 32 K, lane l
 // holding row l%16, K 8*(l/16)..+7, so every fragment read is a conflict-free
 // 16-byte-per-lane ds_read. Global -> LDS traffic uses the gfx950 LDS-DMA load
