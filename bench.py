@@ -199,7 +199,10 @@ def run_workload(cfg, T, steps, warmup, n_inst, torch, synth, keep_layer0=False,
         stages.append(lay.stage_times())
     st = np.mean(np.array(stages), axis=0).tolist()
     counts = insts[(steps - 1) % n_inst][2].expert_counts.cpu().numpy()
-    res = dict(T=T, ms_per_step=1e3 * wall / steps, stage_ms=st, counts=counts)
+    # per-step spread from the event pass (gate start to combine end; each stage event adds a few us)
+    per_step = np.sum(np.array(stages), axis=1)
+    pct = {f"p{q}": float(np.percentile(per_step, q)) for q in (10, 50, 90)}
+    res = dict(T=T, ms_per_step=1e3 * wall / steps, stage_ms=st, counts=counts, step_ms_pct=pct)
     x0 = insts[0][1].cpu() if keep_layer0 else None
     if keep_layer0 and routed:
         o = insts[0][2]
@@ -240,7 +243,7 @@ def summarize(cfg, res):
         layer_mfma_frac=layer["flops"] / layer_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         down_frac=(dn["bytes"] / (dn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS) if decode else
         (dn["flops"] / (dn_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS),
-        active_experts=layer["active"], roofline=rf)
+        active_experts=layer["active"], roofline=rf, step_ms_pct=res["step_ms_pct"])
 
 
 def run_streams(cfg, T, steps, warmup, S, torch, synth):
@@ -446,6 +449,7 @@ def main():
         "roofline": {k: main_s["roofline"][k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
         "roofline_kernel": main_s["roofline"]["kernel"],
         "stage_ms": main_s["stage_ms"],
+        "stage_pass_step_ms": main_s["step_ms_pct"],
         "layer": {k: main_s[k] for k in ("layer_GBps", "layer_TFLOPs", "layer_hbm_frac", "layer_mfma_frac",
                                          "down_frac", "active_experts")},
         "sweep": [{k: s[k] for k in ("T", "tokens_per_s", "ms_per_step", "stage_ms", "layer_GBps",
