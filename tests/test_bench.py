@@ -54,3 +54,31 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=60)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_int4_bytes_count_group_scales():
+    # two codes per byte, and one fp32 scale per 128 input rows of every output column
+    cfg = synth.get_config("int4_mixtral22b")
+    counts = np.array([0, 0, 1, 0, 0, 0, 1, 0])
+    up, dn, _ = bench.kernel_work(cfg, counts, 1)
+    d, F = 6144, 16384
+    assert up["bytes"] == 2 * (2 * d * F // 2 + (d // 128) * 2 * F * 4) + d * 2 + 2 * F * 2
+    assert dn["bytes"] == 2 * (F * d // 2 + (F // 128) * d * 4) + 2 * F * 2 + 2 * d * 4
+
+
+def test_summary_roofline_picks_the_bound_of_the_up_kernel():
+    # one token: below the ridge point, priced on HBM bytes; 4096 tokens: on MFMA flops
+    cfg = synth.get_config("mixtral_bf16")
+    for T, bound in ((1, "hbm"), (4096, "mfma")):
+        counts = np.zeros(8, dtype=np.int64)
+        counts[:2 if T == 1 else 8] = 1
+        res = dict(T=T, ms_per_step=1.0, stage_ms=[0.01, 0.01, 0.5, 0.3, 0.01], counts=counts,
+                   step_ms_pct={"p10": 0.9, "p50": 1.0, "p90": 1.1})
+        s = bench.summarize(cfg, res)
+        rf = s["roofline"]
+        up, _, _ = bench.kernel_work(cfg, counts, T)
+        want = up["bytes"] / 0.5e-3 / 1e9 if bound == "hbm" else up["flops"] / 0.5e-3 / 1e12
+        assert rf["bound"] == bound
+        assert abs(rf["achieved"] - want) < 1e-6 * want
+        assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-12
+        assert s["tokens_per_s"] == T / 1e-3
