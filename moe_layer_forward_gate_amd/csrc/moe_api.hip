@@ -262,9 +262,9 @@ int check_device(const moe_layer* L) {
 }
 
 // Launch plan (host side, from T, k and the layer shape only):
-//  - small batches (T <= 64; int4: T <= 32) stream the weights: row tiles of 16, 32 or 64
-//    rows (int4: 16 or 32), sized so an active expert almost always fits one tile, the down
-//    projection's K split so ~1024 workgroups run;
+//  - small batches (T <= 64; int8 and int4 weights: T <= 32) stream the weights: row tiles
+//    of 16, 32 or 64 rows (int4: 16 or 32), sized so an active expert almost always fits one
+//    tile, the down projection's K split so ~1024 workgroups run;
 //  - larger batches use the LDS-tiled MFMA GEMMs (256-row tiles for bf16 weights, 128 for
 //    int8, 64 for int4), with the down projection's K split when that fills the CUs better.
 struct Plan {
@@ -280,9 +280,11 @@ Plan make_plan(const moe_layer* L, int T) {
     const bool i8 = d.expert_dtype == MOE_I8;
     const bool i4 = d.expert_dtype == MOE_I4;
     const int k = d.top_k;
-    // int4 at 33-64 tokens: the tiled kernel is faster (8-expert 6144 x 16384 layer, T = 64:
-    // 0.37 against 0.41 ms; T = 32: 0.31 against 0.29 ms streaming)
-    const bool streaming = !f32 && T <= (i4 ? kStreamMaxT / 2 : kStreamMaxT);
+    // quantised weights at 33-64 tokens: the tiled kernels are faster (8-expert 6144 x 16384
+    // layer, T = 64: int4 0.37 against 0.41 ms, int8 0.51 against 0.54 ms; T = 32: int4 0.31
+    // against 0.29 ms streaming, int8 equal); bf16 weights stream up to 64 (T = 64: 0.50
+    // against 0.58 ms tiled)
+    const bool streaming = !f32 && T <= ((i4 || i8) ? kStreamMaxT / 2 : kStreamMaxT);
     int bm, ksplit = 1;
     bool weights_once = true;
     if (f32) {

@@ -61,8 +61,9 @@ def test_skewed_many_experts_reduced_bf16():
 
 
 def test_int8_reduced():
+    # streaming kernels up to T = 32, tiled past it
     cfg = synth.get_config("int8_mixtral22b", d_model=512, d_ff=1024)
-    _run(cfg, [1, 16, 256, 1024, 3072])
+    _run(cfg, [1, 16, 32, 33, 64, 256, 1024, 3072])
 
 
 def test_int4_reduced():
