@@ -59,11 +59,12 @@ def test_skewed_bf16_full():
 
 
 def test_int8_mixtral22b_full():
-    _run("int8_mixtral22b", [1, 16, 256])
+    # T = 1, 16 on the streaming kernels; 64 (every row compared) and 256 on the tiled ones
+    _run("int8_mixtral22b", [1, 16, 64, 256])
 
 
 def test_int4_mixtral22b_full():
-    _run("int4_mixtral22b", [1, 16, 256])
+    _run("int4_mixtral22b", [1, 16, 64, 256])
 
 
 def test_mixtral_bf16_routed_full():
