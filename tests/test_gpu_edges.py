@@ -65,11 +65,12 @@ def test_every_token_on_one_expert():
     _run(synth.get_config("mixtral_bf16", d_model=256, d_ff=128), [1, 64, 1000], mutate=bias)
 
 
-@pytest.mark.parametrize("name", ["mixtral_bf16", "int8_mixtral22b"])
+@pytest.mark.parametrize("name", ["mixtral_bf16", "int8_mixtral22b", "int4_mixtral22b"])
 def test_streaming_expert_past_one_tile(name):
     # a bias of 2 on expert 3 puts it in slot 0 of (nearly) every token while the slot-1
-    # weights stay near 0.2: at T = 32 and 64 expert 3 holds T rows, twice the streaming
-    # row tile, so the tiles outnumber the active experts (9 against 8 for this draw)
+    # weights stay near 0.2: at T = 32 (and 64 for bf16 weights) expert 3 holds T rows, twice
+    # the streaming row tile, so the tiles outnumber the active experts (9 against 8 for this
+    # draw); quantised weights take the tiled kernels at T = 64, with one expert over its tile
     def bias(L):
         b = torch.zeros(L.cfg.n_experts, dtype=torch.float32)
         b[3] = 2.0
@@ -92,6 +93,12 @@ def test_int8_zero_scale_channels():
         L.w_down[1, :, 7] = 0
         L.s_down[1, 7] = 0
     _run(synth.get_config("int8_mixtral22b", d_model=256, d_ff=128), [1, 300], mutate=zero)
+
+
+@pytest.mark.parametrize("name", ["int8_mixtral22b", "int4_mixtral22b"])
+def test_quantised_every_expert_chosen(name):
+    # k = E = 3: every token on every expert, both kernel families
+    _run(synth.get_config(name, d_model=256, d_ff=256, n_experts=3, top_k=3), [5, 40, 100])
 
 
 def test_int4_zero_groups_and_smallest_width():
