@@ -535,10 +535,11 @@ hipError_t launch_dispatch(const GemmArgs& a, int wq, hipStream_t s) {
     // waves with 64 x 128 tiles, though they read a third more LDS per MFMA); int8: 128-row
     // tiles on 8 waves (two K halves of int8 fragments need the registers of two waves per
     // SIMD). Measured slower: 4 waves with 128 x 128 wave tiles (one wave per SIMD hides
-    // nothing), 128-row bf16 tiles (more operand traffic per MFMA). int4: 64-row tiles on
-    // 8 waves (32 x 64 wave tiles), the batches it serves holding ~64 rows per expert.
+    // nothing), 128-row bf16 tiles (more operand traffic per MFMA). int4, and int8 batches
+    // of at most ~24 rows per expert: 64-row tiles on 8 waves (32 x 64 wave tiles).
     if (wq == kWBf16 && a.bm == 256) return launch<256, kBf16Waves, kWBf16, UP>(a, s);
     if (wq == kWI8 && a.bm == 128) return launch<128, 8, kWI8, UP>(a, s);
+    if (wq == kWI8 && a.bm == 64) return launch<64, 8, kWI8, UP>(a, s);
     if (wq == kWI4 && a.bm == 64) return launch<64, 8, kWI4, UP>(a, s);
     return hipErrorInvalidValue;
 }
