@@ -64,6 +64,11 @@ hipError_t launch_scatter_wide(const int32_t* idx, int T, int E, int k, int V, i
 // dots over (16-column block, 128-wide K slice) workgroups into `part`
 // (gate_split_workspace bytes), then one workgroup for the sums, top-k and scatter.
 bool gate_split_fits(int T, int k);
+// Routers wider than 16 columns with bf16 tokens take the split gate (or the per-token
+// one) up to this batch and the MFMA gate past it: the split gate's one-workgroup finish
+// grows with T (64-expert + shared layer, T = 64: 50 us split, 30 us MFMA; T = 16: 24 us
+// split, 30 us MFMA).
+constexpr int kGateSplitMaxT = 24;
 size_t gate_split_workspace(int T, int d, int E, bool has_shared);
 hipError_t launch_gate_split(const void* x, bool x_bf16, const float* wr_t, const float* bias, int T, int d, int E,
                              int gflags, int k, int32_t* idx, float* w, float* gs, int V, int bm,

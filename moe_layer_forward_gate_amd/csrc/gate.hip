@@ -695,7 +695,9 @@ hipError_t launch_gate_t(const XT* x, const float* wr_t, const u32x4* planes, co
                          int gflags, int k, int32_t* idx, float* w, float* gs, hipStream_t s) {
     const bool has_shared = (gflags & kGateShared) != 0;
     const int Ec = E + (has_shared ? 1 : 0);
-    if (T <= 64 && d <= 2048 * kRowXC) {
+    // per-token dots for decode batches, but routers wider than 16 columns with bf16 tokens
+    // past kGateSplitMaxT tokens, which the MFMA path below serves faster
+    if (T <= 64 && d <= 2048 * kRowXC && (Ec <= 16 || planes == nullptr || T <= kGateSplitMaxT)) {
         switch ((d + 2047) / 2048) {
 #define ROWDOT_CASE(C)                                                                                            \
     case C:                                                                                                       \

@@ -477,7 +477,7 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
         HIP_TRY(launch_gate_scatter_small(x, !f32, L->wr_t, L->bias, T, d.d_model, L->E, gflags, k, r->topk_idx,
                                           r->topk_w, gs, L->V, pl.bm, so, s));
         if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
-    } else if (wide_router && gate_split_fits(T, k)) {
+    } else if (wide_router && gate_split_fits(T, k) && (f32 || T <= kGateSplitMaxT)) {
         // decode batch: router dots on many workgroups, then top-k and scatter in one
         HIP_TRY(launch_gate_split(x, !f32, L->wr_t, L->bias, T, d.d_model, L->E, gflags, k, r->topk_idx,
                                   r->topk_w, gs, L->V, pl.bm, so, L->gate_part, s));
