@@ -51,7 +51,15 @@ namespace {
 
 constexpr int BN = 256;
 constexpr int kBf16Waves = 16;
-constexpr int GN = 4;       // column tiles per group (see decode_tile)
+constexpr int GN = 4;       // column tiles per group (see decode_tile), or all of them when at most kGNAll
+
+// Column tiles per group: 4, or every column tile of the projection when there are at most
+// 6 (one group spans the expert's width, so each row tile's A operand is read by all its
+// column tiles together: the skewed 128-expert layer's up projection, 6 column tiles,
+// 235 -> 200 us; its down projection, 8 column tiles, ran 167 us in groups of 4 against
+// 171 in one group of 8).
+constexpr int kGNAll = 6;
+__host__ __device__ __forceinline__ int col_group(int nt) { return nt <= kGNAll ? nt : GN; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -142,11 +150,12 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
     int split = 0;
     int kv = 1;  // shared slices this tile sums as one K (merged shared down projection)
     if (!UP && a.merge_shared) {
-        if (!decode_tile_down_merged(a.tile_start, a.offsets, a.Et - (a.kt - a.k), a.kt - a.k, NT, GN, BM, tl, kv))
+        if (!decode_tile_down_merged(a.tile_start, a.offsets, a.Et - (a.kt - a.k), a.kt - a.k, NT, col_group(NT), BM,
+                                     tl, kv))
             return;
     } else {
         // split-K: logical tile index = tile * S + split
-        if (!decode_tile_split(a.tile_start, a.offsets, a.Et, NT, GN, BM, S, tl, split)) return;
+        if (!decode_tile_split(a.tile_start, a.offsets, a.Et, NT, col_group(NT), BM, S, tl, split)) return;
     }
     const int Kpart = K / S;
     const int kbase = split * Kpart;
@@ -520,7 +529,8 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
     // whole K steps (an even count of 32-K steps for bf16)
     if (Kpart % std::max(BK, 64) != 0 || Kpart < std::max(BK, 64)) return hipErrorInvalidValue;
     if (WQ == kWI4 && (N % 128 != 0 || a.merge_shared)) return hipErrorInvalidValue;
-    const int NTp = ((N + BN - 1) / BN + GN - 1) / GN * GN;
+    const int gn = col_group((N + BN - 1) / BN);
+    const int NTp = ((N + BN - 1) / BN + gn - 1) / gn * gn;
     // a multiple of 8 workgroups, so every XCD gets ceil(tiles / 8) slots (a merged shared
     // down projection starts its routed tiles at the next multiple of 8 after its own)
     const size_t blocks = (size_t)a.max_tiles * NTp * S + (!UP && a.merge_shared ? 2 * kXcds : 0);
