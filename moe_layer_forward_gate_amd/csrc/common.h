@@ -188,25 +188,36 @@ struct Tile {
 };
 
 // Map this workgroup to a tile. Tiles are ordered expert by expert; inside an
-// expert, column tiles come in groups of GN, and within a group the row tiles
-// run fastest, so workgroups that share a weight tile (same n) or an activation
-// tile (same row0) run close together. Workgroup i is dealt to XCD i % 8 by the
-// hardware; the logical index is remapped so each XCD works on one contiguous
-// stretch of tiles and keeps its weight/activation tiles in its own L2.
+// expert, column tiles come in groups of GN, and within a group the GN column tiles
+// of a row tile run together, row tile after row tile, so workgroups that share a
+// weight tile (same n) or an activation tile (same row0) run close together.
+// Workgroup i is dealt to XCD i % 8 by the hardware; the logical index is remapped
+// so each XCD works on contiguous tiles and keeps their weight/activation tiles in
+// its own L2: one stretch of total/8 tiles per XCD (chunk = 0), or chunks of `chunk`
+// consecutive tiles dealt to the XCDs in turn, which spreads the cheap ragged tiles
+// of the experts' last rows, and any run of costlier tiles, over all XCDs.
 // tile_start[e] = sum of ceil(n_e' / bm) over e' < e; it and offsets are read
 // from device memory (the scatter just wrote them), so the grid is launched for
 // an upper bound and idle workgroups return at once.
 __device__ __forceinline__ bool decode_tile_at(const int32_t* __restrict__ ts, const int32_t* __restrict__ offs,
                                                int Ecount, int NT, int GN, int bm, int S, int i, Tile& tl,
-                                               int& split) {
+                                               int& split, int chunk = 0) {
     // i: the workgroup's index in the launch, dealt to XCD i % 8; S K-splits of every tile
     // (logical index = tile * S + split), the XCD remap applied to the combined index
     const int NTp = (NT + GN - 1) / GN * GN;
     const int total = ts[Ecount] * NTp * S;
-    const int per = (total + kXcds - 1) / kXcds;
     const int slot = i / kXcds, xcd = i % kXcds;
-    if (slot >= per) return false;
-    const int L = xcd * per + slot;
+    int L;
+    if (chunk > 0) {
+        // the launch holds at least total + kXcds * chunk workgroups
+        const int per = (total + kXcds * chunk - 1) / (kXcds * chunk) * chunk;
+        if (slot >= per) return false;
+        L = ((slot / chunk) * kXcds + xcd) * chunk + slot % chunk;
+    } else {
+        const int per = (total + kXcds - 1) / kXcds;
+        if (slot >= per) return false;
+        L = xcd * per + slot;
+    }
     if (L >= total) return false;
     const int Lt = L / S;
     split = L - Lt * S;
@@ -242,8 +253,9 @@ __device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ ts, cons
 
 // decode_tile over S K-splits of every tile.
 __device__ __forceinline__ bool decode_tile_split(const int32_t* __restrict__ ts, const int32_t* __restrict__ offs,
-                                                  int Et, int NT, int GN, int bm, int S, Tile& tl, int& split) {
-    return decode_tile_at(ts, offs, Et, NT, GN, bm, S, blockIdx.x, tl, split);
+                                                  int Et, int NT, int GN, int bm, int S, Tile& tl, int& split,
+                                                  int chunk = 0) {
+    return decode_tile_at(ts, offs, Et, NT, GN, bm, S, blockIdx.x, tl, split, chunk);
 }
 
 // Down projection with the shared expert's V slices merged into one K = V*F sum per

@@ -59,6 +59,11 @@ constexpr int GN = 4;       // column tiles per group (see decode_tile), or all 
 // 235 -> 200 us; its down projection, 8 column tiles, ran 167 us in groups of 4 against
 // 171 in one group of 8).
 constexpr int kGNAll = 6;
+// Tiles dealt to the XCDs in chunks of 32 (decode_tile_at): against one contiguous stretch
+// per XCD, 8-expert layer T = 4096 2.76 -> 2.68 ms, int8 T = 256 0.69 -> 0.67 ms, int4
+// T = 256 0.79 -> 0.75 ms, the shared + fine and skewed layers within 1%; chunks of 64
+// were slower than one stretch, chunks of 16 about as fast as 32.
+constexpr int kXcdChunk = 32;
 __host__ __device__ __forceinline__ int col_group(int nt) { return nt <= kGNAll ? nt : GN; }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -155,7 +160,8 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
             return;
     } else {
         // split-K: logical tile index = tile * S + split
-        if (!decode_tile_split(a.tile_start, a.offsets, a.Et, NT, col_group(NT), BM, S, tl, split)) return;
+        if (!decode_tile_split(a.tile_start, a.offsets, a.Et, NT, col_group(NT), BM, S, tl, split, kXcdChunk))
+            return;
     }
     const int Kpart = K / S;
     const int kbase = split * Kpart;
@@ -533,7 +539,9 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
     const int NTp = ((N + BN - 1) / BN + gn - 1) / gn * gn;
     // a multiple of 8 workgroups, so every XCD gets ceil(tiles / 8) slots (a merged shared
     // down projection starts its routed tiles at the next multiple of 8 after its own)
-    const size_t blocks = (size_t)a.max_tiles * NTp * S + (!UP && a.merge_shared ? 2 * kXcds : 0);
+    // (+ kXcds * kXcdChunk: the chunked deal needs the tile count rounded up to whole chunks)
+    const size_t blocks =
+        (size_t)a.max_tiles * NTp * S + (!UP && a.merge_shared ? 2 * kXcds : 0) + kXcds * kXcdChunk;
     dim3 grid((unsigned)((blocks + kXcds - 1) / kXcds * kXcds));
     hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds_bytes, s, a);
     return hipGetLastError();
