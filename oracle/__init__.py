@@ -10,14 +10,16 @@ www.mhpq.cn/news/563172, [hotelren] www.hotelren.com/news/4731937, [trdm]
 www.trdm.cn/news/555962, [pptc] www.pptc.cn/news/100465.
 
 Pinned (see tests/test_oracle.py): router logits, top-k selection and tie rule,
-top-k weights, shared-expert gate, scatter (counts, offsets, permutation),
-SwiGLU expert, combine, int8 and int4 group-wise dequantisation, the layer with a caller-given
+top-k weights (softmax over the chosen logits, or the chosen raw logits),
+shared-expert gate, scatter (counts, offsets, permutation), SwiGLU expert,
+combine, int8 and int4 group-wise dequantisation, the layer with a caller-given
 routing. No function is parity-unpinned.
 """
 from .moe_oracle import (
     router_logits,
     select_topk,
     topk_weights,
+    topk_raw_weights,
     shared_gate,
     scatter_stable_sort,
     scatter_counting,
@@ -31,7 +33,7 @@ from .moe_oracle import (
 )
 
 __all__ = [
-    "router_logits", "select_topk", "topk_weights", "shared_gate",
+    "router_logits", "select_topk", "topk_weights", "topk_raw_weights", "shared_gate",
     "scatter_stable_sort", "scatter_counting", "dequantize", "dequantize_groupwise", "swiglu_expert",
     "valid_selections", "moe_forward", "moe_forward_routed", "OracleLayer",
 ]

@@ -12,7 +12,8 @@ Readings of the pages taken here where they are silent or disagree:
   * the k experts are chosen on raw logits ordered by (logit desc, id asc),
     slot 0 holding the largest; -0.0 and +0.0 compare equal;
   * the routing weights are the softmax over the k chosen logits (identical to
-    the full softmax renormalised over the chosen set);
+    the full softmax renormalised over the chosen set); as an option, the
+    chosen raw logits themselves (top-k on raw logits with no softmax);
   * the scatter orders assignments a = t*k + j stably by expert, and
     expert_offsets has E + 1 token-row entries;
   * the shared expert is one SwiGLU FFN applied to every token, scaled by
@@ -81,6 +82,19 @@ def topk_weights(logits, idx) -> np.ndarray:
     chosen = np.take_along_axis(L, np.asarray(idx), axis=-1)
     e = np.exp(chosen - chosen[:, :1])
     return e / e.sum(axis=-1, keepdims=True)
+
+
+def topk_raw_weights(logits, idx) -> np.ndarray:
+    """w[t, j] = l[t, idx[t, j]]: the chosen logits themselves, unnormalised.
+
+    [hotelren §3.2] the router's two steps are the linear projection and the
+    top-k taken directly on the raw logits, with no softmax; [hotelren §2.3]
+    combine_kernel weights the k expert outputs by the router's gating score.
+    Read together: with no softmax, a chosen expert's gating score is its raw
+    logit (bias included, after the clamp when that option is on).
+    """
+    L = _f64(logits)
+    return np.take_along_axis(L, np.asarray(idx), axis=-1).copy()
 
 
 def shared_gate(x, w_shared_gate) -> np.ndarray:
@@ -181,6 +195,7 @@ class OracleLayer:
     ws_down: Optional[np.ndarray] = None
     group: Optional[int] = None  # int4: input rows per scale (scales [E, in/group, out])
     gate_clamp: bool = False     # clamp the routed logits to [-50, 50] before top-k and softmax
+    gate_weighting: str = "softmax"  # "softmax": over the chosen logits; "raw": the chosen logits
 
     @property
     def n_experts(self) -> int:
@@ -273,7 +288,12 @@ def moe_forward(x, layer: OracleLayer, routing=None, tokens: Optional[Sequence[i
     idx, margin = select_topk(logits, k)
     if routing is not None:
         idx = np.asarray(routing, dtype=np.int64)
-    w = topk_weights(logits, idx)
+    if layer.gate_weighting == "softmax":
+        w = topk_weights(logits, idx)
+    elif layer.gate_weighting == "raw":
+        w = topk_raw_weights(logits, idx)
+    else:
+        raise ValueError("gate_weighting must be 'softmax' or 'raw'")
     counts, offsets, sorted_assign = scatter_stable_sort(idx, E)
     g_s = shared_gate(x, layer.w_shared_gate) if layer.w_shared_gate is not None else None
 

@@ -504,3 +504,92 @@ def test_gate_clamp_inactive_inside_bounds():
     lay.gate_clamp = True
     b = oracle.moe_forward(x, lay)
     assert np.array_equal(a["idx"], b["idx"]) and np.array_equal(a["y"], b["y"])
+
+
+# ---------------------------------------------------------------- raw-logit weighting
+def _one_token_layer(logits, k, clamp=False):
+    """A layer whose router gives `logits` for the token x = ones(1, 1): W_r = 0 and the
+    logits as the bias (no experts' work matters here)."""
+    E = len(logits)
+    z = np.zeros((E, 1, 2))
+    return oracle.OracleLayer(w_router=np.zeros((1, E)), w_gate=z, w_up=z, w_down=np.zeros((E, 2, 1)),
+                              top_k=k, b_router=np.asarray(logits, dtype=np.float64), gate_clamp=clamp,
+                              gate_weighting="raw")
+
+
+def test_topk_raw_hand_fixture():
+    g = _load("topk_raw_hand.json")
+    for case in g["cases"]:
+        lay = _one_token_layer(case["logits"], case["top_k"], case.get("clamp", False))
+        out = oracle.moe_forward(np.ones((1, 1)), lay)
+        assert out["idx"][0].tolist() == case["idx"], case
+        assert out["w"][0].tolist() == case["w"], case
+
+
+def _dense_masked_raw(x, lay):
+    """Brute force with raw-logit weights: y_t = sum over ALL experts of 1[e chosen] *
+    l_te * FFN_e(x_t), the choice from a full stable sort of the logits."""
+    x = np.asarray(x, dtype=np.float64)
+    T, E, k = x.shape[0], lay.n_experts, lay.top_k
+    logits = x @ np.asarray(lay.w_router, dtype=np.float64)
+    if lay.b_router is not None:
+        logits = logits + lay.b_router
+    y = np.zeros_like(x)
+    for t in range(T):
+        chosen = set(np.argsort(-logits[t], kind="stable")[:k].tolist())
+        for e in range(E):
+            wg, wu, wd = lay.expert(e)
+            y[t] += (logits[t, e] if e in chosen else 0.0) * _torch_swiglu(x[t:t + 1], wg, wu, wd)[0]
+    if lay.w_shared_gate is not None:
+        y += expit(x @ lay.w_shared_gate)[:, None] * _torch_swiglu(x, lay.ws_gate, lay.ws_up, lay.ws_down)
+    return y
+
+
+@pytest.mark.parametrize("bias,shared,k", [(False, 0, 2), (True, 0, 3), (True, 24, 2)])
+def test_raw_weighting_dense_masked_bruteforce(bias, shared, k):
+    rng = np.random.default_rng(41 + k)
+    lay = _rand_layer(rng, d=18, E=7, F=20, k=k, bias=bias, shared=shared)
+    lay.gate_weighting = "raw"
+    x = rng.standard_normal((9, 18))
+    out = oracle.moe_forward(x, lay)
+    ref = _dense_masked_raw(x, lay)
+    assert np.abs(out["y"] - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
+def test_raw_weighting_closed_forms():
+    rng = np.random.default_rng(43)
+    d, E, F = 14, 6, 10
+    wg, wu, wd = rng.standard_normal((d, F)), rng.standard_normal((d, F)), rng.standard_normal((F, d))
+    W_r = rng.standard_normal((d, E))
+    x = rng.standard_normal((11, d))
+    ffn = _torch_swiglu(x, wg, wu, wd)
+    # identical experts: y_t = (sum of the k largest logits of token t) * FFN(x_t)
+    lay = oracle.OracleLayer(W_r, np.stack([wg] * E), np.stack([wu] * E), np.stack([wd] * E), top_k=3,
+                             gate_weighting="raw")
+    top3 = -np.sort(-(x @ W_r), axis=1)[:, :3].sum(1)
+    np.testing.assert_allclose(oracle.moe_forward(x, lay)["y"], top3[:, None] * ffn, rtol=1e-11, atol=1e-11)
+    # k = 1: raw weighting is the softmax layer (weight 1) scaled by the chosen logit
+    lay1 = _rand_layer(rng, d=d, E=E, F=F, k=1)
+    soft = oracle.moe_forward(x, lay1)
+    lay1.gate_weighting = "raw"
+    raw = oracle.moe_forward(x, lay1)
+    assert np.array_equal(soft["idx"], raw["idx"])
+    lmax = (x @ lay1.w_router).max(1)
+    np.testing.assert_allclose(raw["y"], lmax[:, None] * soft["y"], rtol=1e-12, atol=1e-12)
+    # a positive scale c of router weight and bias keeps the choice and scales y by c
+    # (softmax weights would not scale)
+    lay2 = _rand_layer(rng, d=d, E=E, F=F, k=2, bias=True)
+    lay2.gate_weighting = "raw"
+    a = oracle.moe_forward(x, lay2)
+    lay2.w_router = lay2.w_router * 2.5
+    lay2.b_router = lay2.b_router * 2.5
+    b = oracle.moe_forward(x, lay2)
+    assert np.array_equal(a["idx"], b["idx"])
+    np.testing.assert_allclose(b["y"], 2.5 * a["y"], rtol=1e-12, atol=1e-12)
+
+
+def test_raw_weighting_rejects_unknown_mode():
+    lay = _one_token_layer([1.0, 0.0], 1)
+    lay.gate_weighting = "sparsemax"
+    with pytest.raises(ValueError):
+        oracle.moe_forward(np.ones((1, 1)), lay)
