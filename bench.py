@@ -8,11 +8,11 @@ steps never reuse weights from the 256 MB last-level cache.
 Prints one JSON line: tokens/s of the main workload (timed with libmoe's stage
 events off), the roofline of its dominant kernel (the expert up-projection GEMM;
 its average duration comes from libmoe's per-stage HIP events, recorded on the
-stream the kernels run on over a second pass of the same steps), a sweep of the
-other token counts of the same layer, and the CPU oracle timed on a bounded
-sample.
+stream the kernels run on over a second pass of the same steps), the same
+figures for every other workload (each layer shape at each of its token counts,
+under "workloads"), and the CPU oracle timed on a bounded sample.
 
-  python bench.py [--steps K] [--warmup W] [--config NAME] [--tokens T]
+  python bench.py [--steps K] [--warmup W] [--config NAME] [--tokens T] [--only-main]
 """
 from __future__ import annotations
 
@@ -69,7 +69,8 @@ def parse():
     ap.add_argument("--config", default="mixtral_bf16")
     ap.add_argument("--tokens", type=int, default=None, help="main workload T (default: largest of the config)")
     ap.add_argument("--instances", type=int, default=4)
-    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--only-main", "--no-sweep", dest="only_main", action="store_true",
+                    help="time the main workload only (default: every layer shape at each of its token counts)")
     ap.add_argument("--no-measured-peaks", action="store_true",
                     help="leave out the measured HBM-read and MFMA rates (two microbenchmarks, ~0.3 s)")
     ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
@@ -122,14 +123,26 @@ def kernel_work(cfg, counts, T):
     return up, dn, dict(bytes=layer_bytes, flops=layer_flops, active=active)
 
 
-def build_instances(cfg, n, T, torch, synth, moe_tensors, routed=False):
-    """n layer instances with their token batch and output buffers; with `routed`, each
-    instance's forward is moe_forward_routed on a routing drawn by synth.make_routing."""
-    from harness import gpu_layer
-    insts = []
+def build_layers(cfg, n, max_tokens, torch, synth, moe, keep_layer0=False):
+    """n independently drawn layer instances held by libmoe (and, with keep_layer0, a host
+    copy of instance 0's tensors for the CPU baseline)."""
+    layers, layer0 = [], None
+    dev = torch.device("cuda", torch.cuda.current_device())
     for i in range(n):
         L = synth.make_layer(cfg, device="cuda", instance=i)
-        lay = gpu_layer(L, T, profile=False)
+        layers.append(moe.MoeLayer(max_tokens=max_tokens, **synth.layer_kwargs(L, dev)))
+        if i == 0 and keep_layer0:
+            layer0 = L.to("cpu")
+        del L
+        torch.cuda.empty_cache()
+    return layers, layer0
+
+
+def batch_instances(cfg, layers, T, synth, routed=False):
+    """(layer, x, outputs) per layer instance for a batch of T tokens; with `routed`, each
+    instance's forward is moe_forward_routed on a routing drawn by synth.make_routing."""
+    insts = []
+    for i, lay in enumerate(layers):
         x = synth.make_tokens(cfg, T, device="cuda", instance=i)
         out = lay.outputs(T, scatter=True)
         if routed:
@@ -137,10 +150,6 @@ def build_instances(cfg, n, T, torch, synth, moe_tensors, routed=False):
             out.topk_idx, out.topk_w, out.shared_gate = idx, w, gs
             lay = _Routed(lay)
         insts.append((lay, x, out))
-        if i == 0 and moe_tensors is not None:
-            moe_tensors["layer0"] = L.to("cpu")
-        del L
-        torch.cuda.empty_cache()
     return insts
 
 
@@ -157,12 +166,13 @@ class _Routed:
         return getattr(self.lay, name)
 
 
-def run_workload(cfg, T, steps, warmup, n_inst, torch, synth, keep_layer0=False, graph=False, routed=False):
-    """Time `steps` forwards (rotating over n_inst layers) with per-stage events off, then run
-    the same steps again with libmoe's per-stage HIP events on and average the stage times."""
+def run_workload(cfg, T, steps, warmup, layers, torch, synth, graph=False, routed=False):
+    """Time `steps` forwards (rotating over the layer instances) with per-stage events off,
+    then run the same steps again with libmoe's per-stage HIP events on and average the
+    stage times."""
     import numpy as np
-    keep = {} if keep_layer0 else None
-    insts = build_instances(cfg, n_inst, T, torch, synth, keep, routed=routed)
+    insts = batch_instances(cfg, layers, T, synth, routed=routed)
+    n_inst = len(insts)
     for i in range(warmup):
         lay, x, out = insts[i % n_inst]
         lay.forward(x, out=out)
@@ -203,18 +213,15 @@ def run_workload(cfg, T, steps, warmup, n_inst, torch, synth, keep_layer0=False,
     per_step = np.sum(np.array(stages), axis=1)
     pct = {f"p{q}": float(np.percentile(per_step, q)) for q in (10, 50, 90)}
     res = dict(T=T, ms_per_step=1e3 * wall / steps, stage_ms=st, counts=counts, step_ms_pct=pct)
-    x0 = insts[0][1].cpu() if keep_layer0 else None
-    if keep_layer0 and routed:
-        o = insts[0][2]
-        keep["routing0"] = (o.topk_idx.cpu(), o.topk_w.cpu(), None if o.shared_gate is None else o.shared_gate.cpu())
-    del graphs
     for lay, _, _ in insts:
-        lay.close()
-    del insts
+        lay.set_profiling(False)
+    res["x0"] = insts[0][1].cpu()
+    if routed:
+        o = insts[0][2]
+        res["routing0"] = (o.topk_idx.cpu(), o.topk_w.cpu(), None if o.shared_gate is None else o.shared_gate.cpu())
+    del graphs, insts
     torch.cuda.empty_cache()
-    if keep_layer0:
-        res["routing0"] = keep.get("routing0")
-    return res, (keep["layer0"] if keep_layer0 else None), x0
+    return res
 
 
 def summarize(cfg, res):
@@ -230,11 +237,22 @@ def summarize(cfg, res):
         rf = dict(bound="mfma", achieved=up["flops"] / (up_ms * 1e-3) / 1e12, peak=MFMA_BF16_PEAK_TFLOPS,
                   unit="TFLOP/s")
     rf["frac"] = rf["achieved"] / rf["peak"]
-    kern = "expert_stream" if (T <= 64 and cfg.expert_dtype != "f32") else "expert_gemm"
+    stream_max = 32 if cfg.expert_dtype in ("i8", "i4") else 64  # the library's launch plan
+    kern = ("expert_stream" if T <= stream_max else "expert_gemm") if cfg.expert_dtype != "f32" else "expert_f32"
     rf["kernel"] = f"{kern}<up>"
-    rf["traffic"] = lookup_traffic(kern, f"up|{cfg.name}|T={T}")
+    rf["traffic"] = lookup_traffic(kern, f"up|{cfg.name}|T={T}") if kern in KERNEL_SOURCES else None
     rf["avg_ms"] = up_ms
     layer_s = res["ms_per_step"] * 1e-3
+    # the layer against its target: bytes of the active experts against HBM for batches below
+    # the ridge point, the grouped GEMM's flops (up + down kernels) against bf16 MFMA above it
+    if cfg.act_dtype == "f32":
+        target = dict(bound="none", note="fp32 layer: parity only")
+    elif decode:
+        f = layer["bytes"] / layer_s / 1e9 / HBM_PEAK_GBS
+        target = dict(bound="hbm", what="layer, active-expert bytes", frac=f, want=0.70, met=f >= 0.70)
+    else:
+        f = (up["flops"] + dn["flops"]) / ((up_ms + dn_ms) * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
+        target = dict(bound="mfma", what="grouped GEMM (up + down kernels)", frac=f, want=0.60, met=f >= 0.60)
     return dict(
         T=T, ms_per_step=res["ms_per_step"], tokens_per_s=T / layer_s,
         stage_ms=dict(gate=gate_ms, scatter=scat_ms, up=up_ms, down=dn_ms, combine=comb_ms),
@@ -243,7 +261,7 @@ def summarize(cfg, res):
         layer_mfma_frac=layer["flops"] / layer_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         down_frac=(dn["bytes"] / (dn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS) if decode else
         (dn["flops"] / (dn_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS),
-        active_experts=layer["active"], roofline=rf, step_ms_pct=res["step_ms_pct"])
+        active_experts=layer["active"], roofline=rf, step_ms_pct=res["step_ms_pct"], target=target)
 
 
 def run_streams(cfg, T, steps, warmup, S, torch, synth):
@@ -251,7 +269,9 @@ def run_streams(cfg, T, steps, warmup, S, torch, synth):
     enqueued every step: the decode throughput of concurrent layers (one layer per stream,
     as the library requires). Returns the wall time per step and the algorithmic bytes of
     one step (every instance's expert weights with rows, router, tokens)."""
-    insts = build_instances(cfg, S, T, torch, synth, None)
+    import moe_layer_forward_gate_amd as moe
+    layers, _ = build_layers(cfg, S, T, torch, synth, moe)
+    insts = batch_instances(cfg, layers, T, synth)
     streams = [torch.cuda.Stream() for _ in range(S)]
     cur = torch.cuda.current_stream()
     for st in streams:
@@ -277,15 +297,30 @@ def run_streams(cfg, T, steps, warmup, S, torch, synth):
     return dict(ms_per_step=1e3 * wall / steps, step_bytes=step_bytes)
 
 
+def _oracle_layer(L):
+    """The oracle's layer from a host copy of a synthetic layer (exact stored values)."""
+    import oracle
+    import synth
+
+    def np_(t):
+        return None if t is None else t.float().numpy() if t.is_floating_point() else t.numpy()
+    return oracle.OracleLayer(
+        w_router=np_(L.w_router), w_gate=np_(L.w_gate), w_up=np_(L.w_up), w_down=np_(L.w_down),
+        top_k=L.cfg.top_k, b_router=np_(L.b_router), s_gate=np_(L.s_gate), s_up=np_(L.s_up),
+        s_down=np_(L.s_down), w_shared_gate=np_(L.w_shared_gate), ws_gate=np_(L.ws_gate),
+        ws_up=np_(L.ws_up), ws_down=np_(L.ws_down),
+        group=synth.INT4_GROUP if L.cfg.expert_dtype == "i4" else None)
+
+
 def cpu_baseline(cfg, layer_cpu, x_cpu, n_tok, min_s, routing=None):
     """The oracle as it stands, on the first n_tok tokens of the same batch, repeated (at most
     4 passes) until min_s seconds have passed (with `routing` (idx, w, g_s): the oracle of
-    the layer fed that routing)."""
-    import numpy as np
+    the layer fed that routing). Then the tiny fp32 layer's whole 64-token batch on one BLAS
+    thread, for a single-core figure."""
     import oracle
-    from harness import oracle_layer
-    from threadpoolctl import threadpool_info
-    olay = oracle_layer(layer_cpu)
+    import synth
+    from threadpoolctl import threadpool_info, threadpool_limits
+    olay = _oracle_layer(layer_cpu)
     xs = x_cpu[:n_tok].float().numpy()
     passes = 0
     t0 = time.perf_counter()
@@ -301,10 +336,25 @@ def cpu_baseline(cfg, layer_cpu, x_cpu, n_tok, min_s, routing=None):
         if dt >= min_s or passes == 4:
             break
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    # one thread, the tiny fp32 layer (d_model 256, 8 experts, d_ff 512, top-2), T = 64
+    tcfg = synth.get_config("tiny_f32")
+    tl = _oracle_layer(synth.make_layer(tcfg))
+    tx = synth.make_tokens(tcfg, 64).numpy()
+    with threadpool_limits(limits=1):
+        n1, t1 = 0, time.perf_counter()
+        while True:
+            oracle.moe_forward(tx, tl)
+            n1 += 1
+            d1 = time.perf_counter() - t1
+            if d1 >= 1.0:
+                break
     return dict(value=passes * n_tok / dt, unit="tokens/s", cores=int(threads), kind="oracle",
+                host_cpus=os.cpu_count(),
                 sample=f"{passes} pass(es) over {n_tok} tokens of the T={x_cpu.shape[0]} batch, whole layer "
                        f"forward in fp64 ({'given routing' if routing is not None else 'gate'}, scatter, "
-                       f"{cfg.n_experts} experts, combine), {dt:.1f} s")
+                       f"{cfg.n_experts} experts, combine), {dt:.1f} s on {threads} BLAS threads",
+                single_thread={"config": "tiny_f32", "tokens": 64, "passes": n1,
+                               "value": n1 * 64 / d1, "unit": "tokens/s", "cores": 1})
 
 
 def peaks_lib():
@@ -385,7 +435,6 @@ def main():
     if args.peaks:
         print(json.dumps(measure_peaks(torch)), flush=True)
         return
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
     import synth
     import moe_layer_forward_gate_amd as moe
     moe.lib()
@@ -409,24 +458,43 @@ def main():
                          "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": "whole layers, all streams"}}))
         return
     want_cpu = not args.no_cpu_baseline
-    res, layer0, x0 = run_workload(cfg, T, args.steps, args.warmup, args.instances, torch, synth,
-                                   keep_layer0=want_cpu, graph=args.graph, routed=args.routed)
+    layers, layer0 = build_layers(cfg, args.instances, max(T, max(cfg.tokens)), torch, synth, moe,
+                                  keep_layer0=want_cpu)
+    res = run_workload(cfg, T, args.steps, args.warmup, layers, torch, synth, graph=args.graph, routed=args.routed)
     main_s = summarize(cfg, res)
-    print(f"[bench] main {json.dumps(main_s)}", file=sys.stderr, flush=True)
-    sweep = []
-    if not args.no_sweep:
-        for Ts in cfg.tokens:
-            if Ts == T:
-                continue
-            r, _, _ = run_workload(cfg, Ts, max(args.steps, 20), args.warmup, args.instances, torch, synth,
-                                   graph=args.graph, routed=args.routed)
-            s = summarize(cfg, r)
-            sweep.append(s)
-            print(f"[bench] sweep {json.dumps(s)}", file=sys.stderr, flush=True)
+    print(f"[bench] main {cfg.name} T={T} {json.dumps(main_s)}", file=sys.stderr, flush=True)
+    # every workload: each layer shape at each of its token counts (the main one included,
+    # timed again in its turn), layers built once per shape
+    workloads = []
+    if not args.only_main:
+        names = [cfg.name] + [n for n in synth.CONFIGS if n != cfg.name]
+        for name in names:
+            c = synth.get_config(name)
+            if c.name == cfg.name:
+                lays = layers
+            else:
+                print(f"[bench] building {c.name}", file=sys.stderr, flush=True)
+                lays, _ = build_layers(c, args.instances, max(c.tokens), torch, synth, moe)
+            for Ts in c.tokens:
+                r = run_workload(c, Ts, max(args.steps, 20), args.warmup, lays, torch, synth,
+                                 graph=args.graph, routed=args.routed)
+                s = summarize(c, r)
+                s["config"] = c.name
+                workloads.append(s)
+                print(f"[bench] workload {c.name} T={Ts} {json.dumps(s)}", file=sys.stderr, flush=True)
+            if lays is not layers:
+                for lay in lays:
+                    lay.close()
+                del lays
+                torch.cuda.empty_cache()
+    for lay in layers:
+        lay.close()
+    del layers
+    torch.cuda.empty_cache()
     cpu = None
     if want_cpu:
         n_tok = T if args.cpu_sample_tokens <= 0 else min(args.cpu_sample_tokens, T)
-        cpu = cpu_baseline(cfg, layer0, x0, n_tok, args.cpu_min_seconds, routing=res.get("routing0"))
+        cpu = cpu_baseline(cfg, layer0, res["x0"], n_tok, args.cpu_min_seconds, routing=res.get("routing0"))
         print(f"[bench] cpu {json.dumps(cpu)}", file=sys.stderr, flush=True)
     line = {
         "metric": "MoE-layer tokens/s; decode HBM TB/s and prefill MFMA TFLOP/s vs roofline",
@@ -452,8 +520,10 @@ def main():
         "stage_pass_step_ms": main_s["step_ms_pct"],
         "layer": {k: main_s[k] for k in ("layer_GBps", "layer_TFLOPs", "layer_hbm_frac", "layer_mfma_frac",
                                          "down_frac", "active_experts")},
-        "sweep": [{k: s[k] for k in ("T", "tokens_per_s", "ms_per_step", "stage_ms", "layer_GBps",
-                                     "layer_hbm_frac", "layer_mfma_frac", "roofline")} for s in sweep],
+        "target": main_s["target"],
+        "workloads": [{k: s[k] for k in ("config", "T", "tokens_per_s", "ms_per_step", "stage_ms", "layer_GBps",
+                                         "layer_TFLOPs", "layer_hbm_frac", "layer_mfma_frac", "roofline",
+                                         "target", "active_experts")} for s in workloads],
         "cpu_baseline": cpu,
         "measured_peaks": None if args.no_measured_peaks else measured_peaks(main_s["roofline"]),
     }

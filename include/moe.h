@@ -12,6 +12,8 @@
  *            largest; equal logits go to the lower expert id ([mhpq §3.2],
  *            the routing kernel's strict greater-than test);
  *            w[t, j] = softmax of the k chosen logits    [0539edu §2.1]
+ *            or, as an option, the chosen logits themselves ([hotelren §3.2]
+ *            top-k on raw logits without a softmax)
  *   Scatter  assignments a = t*k + j grouped by expert, stable in a, with an
  *            (E+1)-entry row-offset table                [0539edu §2.2],
  *            [hotelren §2.3] dispatch_kernel, [pptc §3.3] expert_offsets
@@ -66,14 +68,26 @@ typedef enum moe_dtype {
                       nibble = even row, 4-bit two's complement */
 } moe_dtype;
 
-/* Layer shape. Supported (act_dtype, expert_dtype) pairs: (F32, F32),
- * (BF16, BF16), (BF16, I8), (BF16, I4). Limits: 1 <= top_k <= n_experts <= 128;
- * for BF16/I8 experts d_model % 128 == 0 and d_ff % 64 == 0; for I4 experts
- * d_model % 128 == 0 and d_ff % 128 == 0; for F32 experts d_model % 64 == 0
- * and d_ff % 64 == 0. shared_d_ff > 0 adds a shared expert (BF16 experts only)
- * and must be a multiple of d_ff. I4 layers run every batch on the weight-
- * streaming kernels (built for decode; larger batches re-stream the weights
- * once per 32 rows of an expert). */
+/* Routing weights of the Gate ([0539edu §2.1] softmax over the gate logits;
+ * [hotelren §3.2] the router variant that takes the top-k of the raw logits and
+ * skips the softmax, its combine weighting each expert by that gating score). */
+typedef enum moe_gate_weighting {
+    MOE_WEIGHT_SOFTMAX = 0,  /* w[t, j] = softmax over the k chosen logits (sums to 1) */
+    MOE_WEIGHT_RAW = 1       /* w[t, j] = the chosen logit itself (bias included, after
+                                the clamp when gate_clamp is on), not normalised */
+} moe_gate_weighting;
+
+/* Layer shape ([0539edu §2.2]: an MoE layer of E experts with top-k routing, the
+ * shared-expert variant, and the weights stored expert-major). Supported
+ * (act_dtype, expert_dtype) pairs: (F32, F32), (BF16, BF16), (BF16, I8),
+ * (BF16, I4). Limits: 1 <= top_k <= n_experts <= 128, top_k <= 64; for BF16/I8
+ * experts d_model % 128 == 0 and d_ff % 64 == 0; for I4 experts d_model % 128
+ * == 0 and d_ff % 128 == 0; for F32 experts d_model % 64 == 0 and d_ff % 64 ==
+ * 0. shared_d_ff > 0 adds a shared expert (BF16 experts only) and must be a
+ * multiple of d_ff. Which kernels run is chosen per call from T: BF16 weights
+ * stream from HBM for T <= 64 and run on the LDS-tiled MFMA GEMMs above; I8 and
+ * I4 weights stream for T <= 32 and run tiled above (F32 experts always run on
+ * the fp32 kernels). */
 typedef struct moe_desc {
     int32_t d_model;
     int32_t n_experts;
@@ -87,6 +101,7 @@ typedef struct moe_desc {
     int32_t gate_clamp;     /* 1: clamp the routed logits to [-50, 50] before the top-k and
                                the softmax ([0539edu §5.2], the gate's clip option against
                                overflow); 0: use them as computed */
+    int32_t gate_weighting; /* moe_gate_weighting: MOE_WEIGHT_SOFTMAX (0) or MOE_WEIGHT_RAW (1) */
 } moe_desc;
 
 /* Layer weights (device pointers, read only during moe_layer_create).
@@ -120,7 +135,7 @@ typedef struct moe_weights {
 
 /* Routing results written by moe_forward (device pointers, 4-byte aligned).
  *   topk_idx        [T][k] int32, required: expert of slot j, slot 0 largest
- *   topk_w          [T][k] fp32, required: softmax over the chosen logits
+ *   topk_w          [T][k] fp32, required: the routing weights (moe_desc.gate_weighting)
  *   expert_counts   [E] int32 or NULL: assignments per expert
  *   expert_offsets  [E+1] int32 or NULL: exclusive prefix sum, [E] = T*k
  *   sorted_assign   [T*k] int32 or NULL: assignment ids a = t*k + j grouped
@@ -140,6 +155,10 @@ typedef struct moe_layer moe_layer; /* opaque */
 /* Create a layer on the current HIP device: checks desc and weights, allocates
  * the packed weights and a workspace sized for desc->max_tokens, repacks the
  * caller's weights into the kernels' tile order, and waits for that to finish.
+ * ([0539edu §3.1] and [hotelren §3.1]: weights are converted once, before
+ * inference, into the layout the kernels read -- reordered, transposed and
+ * expert-major -- so the forward never touches the original layout; [mhpq §4.3]:
+ * a failed initialisation hands back NULL and leaves a message to query.)
  * On success *out holds the layer; on failure *out is set to NULL (when out is
  * not NULL) and nothing is leaked. Statuses: EINVAL (NULL desc/weights/out or a
  * required weight pointer, non-positive sizes, top_k > n_experts), EUNSUPPORTED
@@ -147,7 +166,11 @@ typedef struct moe_layer moe_layer; /* opaque */
 MOE_API int moe_layer_create(const moe_desc* desc, const moe_weights* weights, moe_layer** out);
 
 /* Enqueue one forward pass of T tokens on `stream` (a hipStream_t; NULL is the
- * default stream) and return without waiting. x [T][d_model] and y
+ * default stream) and return without waiting. ([hotelren §2.1]: the six steps
+ * Gate, top-k, Scatter, expert GEMMs and the weighted combine; [hotelren §2.2]:
+ * the host works out the launch shapes from the batch and top-k and hands them
+ * to the kernels; [pptc §3.4]: routing results are token-major [T][k]; [0539edu
+ * §2.2]: the four stages Gate -> Scatter -> Expert Compute -> Gather.) x [T][d_model] and y
  * [T][d_model] are in act_dtype and 16-byte aligned; y is fully overwritten.
  * Allocates nothing. T == 0 enqueues nothing and returns MOE_OK (x, y and
  * route may then be NULL). Statuses: EINVAL (NULL layer, T < 0,
@@ -191,23 +214,28 @@ MOE_API int moe_forward_routed(moe_layer* layer, const void* x, int32_t T, const
 MOE_API int moe_set_profiling(moe_layer* layer, int enable);
 
 /* Per-stage times in milliseconds of the last moe_forward that ran with
- * profiling on: ms[0] gate, ms[1] scatter (with the gathering of token rows
+ * profiling on ([0539edu §3.3]: the profiling trace reports Gate, Scatter,
+ * ExpertCompute and Gather times of each call): ms[0] gate, ms[1] scatter (with the gathering of token rows
  * for the large-batch GEMMs), ms[2] expert up (gate/up GEMM and SiLU), ms[3]
  * expert down, ms[4] gather/combine. Where the gate's launches also run the
- * scatter (batches of up to four tokens; batches of up to 64 tokens with more
- * than 16 router columns), its time is booked on the gate and the scatter
- * reads as the event overhead alone. Waits for that call's
+ * scatter (batches of up to four tokens with at most 16 router columns; with
+ * more than 16 router columns -- experts plus the shared gate -- batches of up
+ * to 24 bf16 tokens or 64 fp32 tokens with top_k <= 8), its time is booked on
+ * the gate and the scatter reads as the event overhead alone. Waits for that call's
  * last event. EINVAL if no forward has run with profiling on. */
 MOE_API int moe_stage_times(moe_layer* layer, float ms[5]);
 
-/* Release a layer and everything it allocated. NULL-safe. Waits for the
- * device work of the layer to finish. */
+/* Release a layer and everything it allocated ([mhpq §4.3]: the engine's
+ * context is freed by one call that owns every buffer it made). NULL-safe.
+ * Waits for the device work of the layer to finish. */
 MOE_API void moe_destroy(moe_layer* layer);
 
-/* Static text of a status code. */
+/* Static text of a status code ([0539edu §3.3]: the inference call returns an
+ * int status; [hotelren §5.2]: a failed call returns -1 instead of crashing). */
 MOE_API const char* moe_status_str(int status);
 
-/* Message of the last failed call on this thread ("" if none). */
+/* Message of the last failed call on this thread ("" if none) ([mhpq §4.3]: a
+ * failed call is explained by an error-string query rather than an exception). */
 MOE_API const char* moe_last_error(void);
 
 #ifdef __cplusplus

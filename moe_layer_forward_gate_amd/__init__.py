@@ -15,15 +15,16 @@ from dataclasses import dataclass
 from typing import Optional
 
 __all__ = [
-    "MoeError", "lib", "MOE_F32", "MOE_BF16", "MOE_I8", "MOE_I4", "MoeDesc", "MoeWeights", "MoeRouteOut",
+    "MoeError", "lib", "MOE_F32", "MOE_BF16", "MOE_I8", "MOE_I4", "MOE_WEIGHT_SOFTMAX", "MOE_WEIGHT_RAW", "MoeDesc", "MoeWeights", "MoeRouteOut",
     "moe_layer_create", "moe_forward", "moe_forward_routed", "moe_set_profiling", "moe_stage_times",
-    "moe_destroy", "moe_status_str", "moe_last_error", "MoeLayer", "LIB_PATH", "EXPORTED",
+    "moe_destroy", "moe_status_str", "moe_last_error", "MoeLayer", "check_weight_tensors", "LIB_PATH", "EXPORTED",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOMEM, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_I8, MOE_I4 = 0, 1, 2, 3
+MOE_WEIGHT_SOFTMAX, MOE_WEIGHT_RAW = 0, 1
 
 # every symbol include/moe.h declares
 EXPORTED = ("moe_layer_create", "moe_forward", "moe_forward_routed", "moe_set_profiling", "moe_stage_times",
@@ -39,7 +40,7 @@ class MoeError(RuntimeError):
 class MoeDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "d_model", "n_experts", "d_ff", "top_k", "max_tokens", "act_dtype", "expert_dtype",
-        "shared_d_ff", "profile", "gate_clamp")]
+        "shared_d_ff", "profile", "gate_clamp", "gate_weighting")]
 
 
 class MoeWeights(ctypes.Structure):
@@ -153,6 +154,26 @@ def _ptr(t) -> int:
     return 0 if t is None else int(t.data_ptr())
 
 
+def check_weight_tensors(tensors: dict, expected: dict, device) -> None:
+    """Raise ValueError unless every tensor matches `expected` (MoeLayer.expected_weights):
+    present exactly when expected, contiguous, on `device`, of an accepted dtype and the
+    exact shape."""
+    for name, want in expected.items():
+        t = tensors.get(name)
+        if want is None:
+            if t is not None:
+                raise ValueError(f"{name} given but this layer shape does not take it")
+            continue
+        if t is None:
+            raise ValueError(f"{name} is required for this layer shape")
+        dts, shape = want
+        if t.device != device or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor on {device}")
+        if t.dtype not in dts or tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {' or '.join(str(x) for x in dts)} of shape {shape}, "
+                             f"got {t.dtype} {tuple(t.shape)}")
+
+
 class MoeLayer:
     """One MoE layer held by libmoe on the current GPU.
 
@@ -162,11 +183,42 @@ class MoeLayer:
     """
 
     _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "i8": MOE_I8, "i4": MOE_I4}
+    _WEIGHTING = {"softmax": MOE_WEIGHT_SOFTMAX, "raw": MOE_WEIGHT_RAW}
+
+    @staticmethod
+    def expected_weights(d_model, n_experts, d_ff, act_dtype, expert_dtype, shared_d_ff=0, has_bias=False):
+        """{name: (torch dtypes accepted, shape)} of every weight tensor the layer reads
+        (the layouts include/moe.h states); None marks a tensor that must be absent."""
+        import torch
+        d, E, F = d_model, n_experts, d_ff
+        wdt = {"f32": (torch.float32,), "bf16": (torch.bfloat16,), "i8": (torch.int8,),
+               "i4": (torch.uint8, torch.int8)}[expert_dtype]
+        f32 = (torch.float32,)
+        if expert_dtype == "i4":  # two values a byte along the input axis, group scales
+            exp = dict(w_gate=(wdt, (E, d // 2, F)), w_up=(wdt, (E, d // 2, F)), w_down=(wdt, (E, F // 2, d)),
+                       s_gate=(f32, (E, d // 128, F)), s_up=(f32, (E, d // 128, F)),
+                       s_down=(f32, (E, F // 128, d)))
+        else:
+            exp = dict(w_gate=(wdt, (E, d, F)), w_up=(wdt, (E, d, F)), w_down=(wdt, (E, F, d)))
+            if expert_dtype == "i8":
+                exp.update(s_gate=(f32, (E, F)), s_up=(f32, (E, F)), s_down=(f32, (E, d)))
+            else:
+                exp.update(s_gate=None, s_up=None, s_down=None)
+        exp["w_router"] = (f32, (d, E))
+        exp["b_router"] = (f32, (E,)) if has_bias else None
+        if shared_d_ff:
+            bf = (torch.bfloat16,)
+            exp.update(w_shared_gate=(f32, (d,)), ws_gate=(bf, (d, shared_d_ff)), ws_up=(bf, (d, shared_d_ff)),
+                       ws_down=(bf, (shared_d_ff, d)))
+        else:
+            exp.update(w_shared_gate=None, ws_gate=None, ws_up=None, ws_down=None)
+        return exp
 
     def __init__(self, *, d_model: int, n_experts: int, d_ff: int, top_k: int, max_tokens: int,
                  act_dtype: str, expert_dtype: str, w_router, w_gate, w_up, w_down, b_router=None,
                  s_gate=None, s_up=None, s_down=None, shared_d_ff: int = 0, w_shared_gate=None,
-                 ws_gate=None, ws_up=None, ws_down=None, profile: bool = False, gate_clamp: bool = False):
+                 ws_gate=None, ws_up=None, ws_down=None, profile: bool = False, gate_clamp: bool = False,
+                 gate_weighting: str = "softmax"):
         import torch
         self.torch = torch
         self.d_model, self.n_experts, self.d_ff, self.top_k = d_model, n_experts, d_ff, top_k
@@ -176,11 +228,18 @@ class MoeLayer:
         tensors = dict(w_router=w_router, b_router=b_router, w_gate=w_gate, w_up=w_up, w_down=w_down,
                        s_gate=s_gate, s_up=s_up, s_down=s_down, w_shared_gate=w_shared_gate,
                        ws_gate=ws_gate, ws_up=ws_up, ws_down=ws_down)
-        for name, t in tensors.items():
-            if t is not None and (not t.is_cuda or not t.is_contiguous()):
-                raise ValueError(f"{name} must be a contiguous GPU tensor")
+        if act_dtype not in ("f32", "bf16") or expert_dtype not in self._DT:
+            raise ValueError(f"unknown dtypes act={act_dtype!r} expert={expert_dtype!r}")
+        if gate_weighting not in self._WEIGHTING:
+            raise ValueError(f"gate_weighting must be one of {sorted(self._WEIGHTING)}")
+        # every tensor's dtype, shape and device is checked here, before the library reads
+        # the bytes that the layout implies from its pointer
+        exp = self.expected_weights(d_model, n_experts, d_ff, act_dtype, expert_dtype, shared_d_ff,
+                                    has_bias=b_router is not None)
+        check_weight_tensors(tensors, exp, torch.device("cuda", torch.cuda.current_device()))
         desc = MoeDesc(d_model, n_experts, d_ff, top_k, max_tokens, self._DT[act_dtype],
-                       self._DT[expert_dtype], shared_d_ff, 1 if profile else 0, 1 if gate_clamp else 0)
+                       self._DT[expert_dtype], shared_d_ff, 1 if profile else 0, 1 if gate_clamp else 0,
+                       self._WEIGHTING[gate_weighting])
         w = MoeWeights(*[_ptr(tensors[f]) for f, _ in MoeWeights._fields_])
         self._h = moe_layer_create(desc, w)
 

@@ -31,8 +31,9 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z));
 // ------------------------------------------------------------------ launchers
 // Gate flags: kGateShared -- router column E is the shared expert's gate (its sigmoid
 // goes to gs); kGateClamp -- the routed logits are clamped to [-kGateClampAbs,
-// kGateClampAbs] before the top-k and the softmax.
-constexpr int kGateShared = 1, kGateClamp = 2;
+// kGateClampAbs] before the top-k and the softmax; kGateRaw -- the routing weights are
+// the chosen (clamped, when kGateClamp) logits themselves instead of their softmax.
+constexpr int kGateShared = 1, kGateClamp = 2, kGateRaw = 4;
 constexpr float kGateClampAbs = 50.0f;
 // Gate: router logits, top-k with (logit desc, id asc) order, softmax weights over
 // the chosen logits, and (with kGateShared) the shared-expert sigmoid gate read

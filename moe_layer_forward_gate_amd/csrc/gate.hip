@@ -81,11 +81,15 @@ __device__ __forceinline__ float wave_sum_many(float (&v)[N]) {
 // One wave: top-k of logits[0..E) (bias already added), weights, shared gate.
 // `logits` may live in LDS; E <= 128, k <= 64. With kGateClamp the routed logits are
 // first clamped to [-50, 50] ([0539edu §5.2]: the gate's clip option bounds the logits
-// before the softmax), so the top-k and the weights both see the clamped values.
+// before the softmax), so the top-k and the weights both see the clamped values. With
+// kGateRaw the weights are the chosen logits themselves ([hotelren §3.2]: the top-k is
+// taken on the raw logits with no softmax; [hotelren §2.3]: the combine weights each
+// expert by that gating score).
 __device__ void wave_topk_write(const float* logits, int E, int k, int gflags, int t, int32_t* idx,
                                 float* w, float* gs, int32_t* ids_copy = nullptr) {
     const bool has_shared = (gflags & kGateShared) != 0;
     const bool clamp = (gflags & kGateClamp) != 0;
+    const bool raw = (gflags & kGateRaw) != 0;
     auto logit = [&](int e) {
         const float v = logits[e];
         return clamp ? fminf(fmaxf(v, -kGateClampAbs), kGateClampAbs) : v;
@@ -107,7 +111,7 @@ __device__ void wave_topk_write(const float* logits, int E, int k, int gflags, i
     float sum = wave_sum(ex);
     if (lane < k) {
         idx[(size_t)t * k + lane] = my_e;
-        w[(size_t)t * k + lane] = ex / sum;
+        w[(size_t)t * k + lane] = raw ? logit(my_e) : ex / sum;
         if (ids_copy) ids_copy[t * k + lane] = my_e;
     }
     if (has_shared && lane == 0) {

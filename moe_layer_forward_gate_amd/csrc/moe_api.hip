@@ -108,6 +108,8 @@ int check_desc(const moe_desc* d, const moe_weights* w) {
     if (d->shared_d_ff < 0) return fail(MOE_EINVAL, "shared_d_ff < 0");
     if (d->profile != 0 && d->profile != 1) return fail(MOE_EINVAL, "profile must be 0 or 1");
     if (d->gate_clamp != 0 && d->gate_clamp != 1) return fail(MOE_EINVAL, "gate_clamp must be 0 or 1");
+    if (d->gate_weighting != MOE_WEIGHT_SOFTMAX && d->gate_weighting != MOE_WEIGHT_RAW)
+        return fail(MOE_EINVAL, "gate_weighting must be MOE_WEIGHT_SOFTMAX (0) or MOE_WEIGHT_RAW (1)");
     if (!w->w_router || !w->w_gate || !w->w_up || !w->w_down)
         return fail(MOE_EINVAL, "w_router, w_gate, w_up and w_down are required");
     const bool f32 = d->act_dtype == MOE_F32 && d->expert_dtype == MOE_F32;
@@ -471,7 +473,8 @@ int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route
     // workgroup per token, then the scatter); more columns spread the router over many
     // workgroups (split gate, whose last launch also runs the scatter).
     const bool wide_router = L->E + (L->V > 0 ? 1 : 0) > 16;
-    const int gflags = (L->V > 0 ? kGateShared : 0) | (d.gate_clamp ? kGateClamp : 0);
+    const int gflags = (L->V > 0 ? kGateShared : 0) | (d.gate_clamp ? kGateClamp : 0) |
+                       (d.gate_weighting == MOE_WEIGHT_RAW ? kGateRaw : 0);
     if (!wide_router && gate_scatter_small_fits(T, d.d_model, L->E, L->V > 0, !f32)) {
         // tiny batch: both stages in one workgroup (the scatter stage then times as empty)
         HIP_TRY(launch_gate_scatter_small(x, !f32, L->wr_t, L->bias, T, d.d_model, L->E, gflags, k, r->topk_idx,

@@ -8,7 +8,7 @@ the CPU oracle (via the tests) and the GPU binding consume.
 """
 from .configs import CONFIGS, LayerConfig, get_config
 from .generate import (make_layer, make_tokens, make_routing, zipf_bias, quantize_per_out_channel,
-                       quantize_int4_groupwise, pack_int4_pairs, INT4_GROUP, SynthLayer)
+                       quantize_int4_groupwise, pack_int4_pairs, INT4_GROUP, SynthLayer, layer_kwargs)
 
 __all__ = ["CONFIGS", "LayerConfig", "get_config", "make_layer", "make_tokens", "make_routing", "zipf_bias",
-           "quantize_per_out_channel", "quantize_int4_groupwise", "pack_int4_pairs", "INT4_GROUP", "SynthLayer"]
+           "quantize_per_out_channel", "quantize_int4_groupwise", "pack_int4_pairs", "INT4_GROUP", "SynthLayer", "layer_kwargs"]

@@ -200,3 +200,20 @@ def make_routing(cfg: LayerConfig, T: int, invalid: float = 0.0, device="cpu", i
     w = w / w.sum(dim=1, keepdim=True)
     gs = torch.rand((T,), generator=g, device=device, dtype=torch.float32) if cfg.shared_d_ff else None
     return idx.to(torch.int32), w, gs
+
+
+def layer_kwargs(L: SynthLayer, device) -> dict:
+    """The keyword arguments of the binding's MoeLayer for this layer, its tensors
+    moved to `device` (int4 weights stored two to a byte, as the library takes
+    them). Marshalling only: no arithmetic of the layer."""
+    c = L.cfg
+    t = {k: v.to(device).contiguous() for k, v in L.tensors().items()}
+    if c.expert_dtype == "i4":
+        for k in ("w_gate", "w_up", "w_down"):
+            t[k] = pack_int4_pairs(t[k]).contiguous()
+    kw = dict(d_model=c.d_model, n_experts=c.n_experts, d_ff=c.d_ff, top_k=c.top_k,
+              act_dtype=c.act_dtype, expert_dtype=c.expert_dtype, shared_d_ff=c.shared_d_ff)
+    for k in ("w_router", "b_router", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
+              "w_shared_gate", "ws_gate", "ws_up", "ws_down"):
+        kw[k] = t.get(k)
+    return kw

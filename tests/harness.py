@@ -24,21 +24,12 @@ W_TOL = 1e-5
 Y_TOL = {"bf16": (1e-2, 3e-2), "f32": (1e-4, 3e-4)}
 
 
-def gpu_layer(L: "synth.SynthLayer", max_tokens: int, profile: bool = False, gate_clamp: bool = False):
+def gpu_layer(L: "synth.SynthLayer", max_tokens: int, profile: bool = False, gate_clamp: bool = False,
+              gate_weighting: str = "softmax"):
     import moe_layer_forward_gate_amd as moe
-    c = L.cfg
     dev = torch.device("cuda", torch.cuda.current_device())
-    t = {k: (v.to(dev).contiguous() if v is not None else None) for k, v in L.tensors().items()}
-    if c.expert_dtype == "i4":  # the library takes int4 weights two to a byte
-        for k in ("w_gate", "w_up", "w_down"):
-            t[k] = synth.pack_int4_pairs(t[k]).contiguous()
-    return moe.MoeLayer(
-        d_model=c.d_model, n_experts=c.n_experts, d_ff=c.d_ff, top_k=c.top_k, max_tokens=max_tokens,
-        act_dtype=c.act_dtype, expert_dtype=c.expert_dtype, w_router=t["w_router"], b_router=t.get("b_router"),
-        w_gate=t["w_gate"], w_up=t["w_up"], w_down=t["w_down"], s_gate=t.get("s_gate"), s_up=t.get("s_up"),
-        s_down=t.get("s_down"), shared_d_ff=c.shared_d_ff, w_shared_gate=t.get("w_shared_gate"),
-        ws_gate=t.get("ws_gate"), ws_up=t.get("ws_up"), ws_down=t.get("ws_down"), profile=profile,
-        gate_clamp=gate_clamp)
+    return moe.MoeLayer(max_tokens=max_tokens, profile=profile, gate_clamp=gate_clamp,
+                        gate_weighting=gate_weighting, **synth.layer_kwargs(L, dev))
 
 
 def _np(t):

@@ -16,6 +16,26 @@ def _declared():
     return sorted(set(re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", txt)))
 
 
+def _decl_comments():
+    """{symbol: the block comment right above its MOE_API declaration}."""
+    txt = open(HEADER).read()
+    out = {}
+    for m in re.finditer(r"/\*((?:(?!\*/).)*)\*/\s*MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", txt, re.S):
+        out[m.group(2)] = m.group(1)
+    return out
+
+
+# the page keys every citation in the header uses
+PAGE_CITE = re.compile(r"\[(0539edu|mhpq|hotelren|trdm|pptc) §\d+(\.\d+)*\]")
+
+
+def test_every_declaration_cites_a_page_passage():
+    com = _decl_comments()
+    assert sorted(com) == _declared(), "every MOE_API declaration has a block comment right above it"
+    for name, c in com.items():
+        assert PAGE_CITE.search(c), f"{name}: its comment cites no page passage"
+
+
 def test_header_declares_binding_names():
     assert _declared() == sorted(moe.EXPORTED)
 
@@ -37,7 +57,7 @@ def test_status_strings():
 
 def _desc(**kw):
     base = dict(d_model=256, n_experts=8, d_ff=512, top_k=2, max_tokens=64, act_dtype=moe.MOE_BF16,
-                expert_dtype=moe.MOE_BF16, shared_d_ff=0, profile=0, gate_clamp=0)
+                expert_dtype=moe.MOE_BF16, shared_d_ff=0, profile=0, gate_clamp=0, gate_weighting=0)
     base.update(kw)
     return moe.MoeDesc(**base)
 
@@ -66,6 +86,8 @@ def _create(desc, weights):
     (_desc(top_k=0), _weights(), moe.MOE_EINVAL),
     (_desc(profile=2), _weights(), moe.MOE_EINVAL),
     (_desc(gate_clamp=2), _weights(), moe.MOE_EINVAL),
+    (_desc(gate_weighting=2), _weights(), moe.MOE_EINVAL),
+    (_desc(gate_weighting=-1), _weights(), moe.MOE_EINVAL),
     (_desc(), _weights(w_gate=0), moe.MOE_EINVAL),
     (_desc(), _weights(w_router=0), moe.MOE_EINVAL),
     (_desc(expert_dtype=moe.MOE_I8), _weights(), moe.MOE_EINVAL),            # scales missing
@@ -123,3 +145,44 @@ def test_forward_routed_rejects_before_gpu():
     fake = 0x10000
     assert L.moe_forward_routed(None, fake, 4, fake, fake, None, fake, None, None) == moe.MOE_EINVAL
     assert "layer" in moe.moe_last_error()
+
+
+def test_binding_checks_weight_tensors_before_create():
+    # the binding checks dtype, shape, device and layout of every weight before the
+    # library reads the bytes its layout implies from the pointers
+    import torch
+    import synth
+    cpu = torch.device("cpu")
+    for name in ("mixtral_bf16", "int8_mixtral22b", "int4_mixtral22b", "shared_fine_bf16", "skewed_bf16"):
+        cfg = synth.get_config(name, d_model=256, d_ff=256, n_experts=8, top_k=2,
+                               shared_d_ff=512 if name == "shared_fine_bf16" else 0)
+        L = synth.make_layer(cfg)
+        kw = synth.layer_kwargs(L, cpu)
+        t = {k: kw[k] for k in ("w_router", "b_router", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
+                                "w_shared_gate", "ws_gate", "ws_up", "ws_down")}
+        exp = moe.MoeLayer.expected_weights(cfg.d_model, cfg.n_experts, cfg.d_ff, cfg.act_dtype, cfg.expert_dtype,
+                                            cfg.shared_d_ff, has_bias=t["b_router"] is not None)
+        moe.check_weight_tensors(t, exp, cpu)  # the generator's layers pass
+        bad = dict(t, w_router=t["w_router"].to(torch.bfloat16))
+        with pytest.raises(ValueError, match="w_router"):
+            moe.check_weight_tensors(bad, exp, cpu)
+        bad = dict(t, w_down=t["w_down"][:, :-2])
+        with pytest.raises(ValueError, match="w_down"):
+            moe.check_weight_tensors(bad, exp, cpu)
+        bad = dict(t, w_gate=t["w_gate"].transpose(1, 2))
+        with pytest.raises(ValueError, match="w_gate"):
+            moe.check_weight_tensors(bad, exp, cpu)
+        with pytest.raises(ValueError, match="on meta"):
+            moe.check_weight_tensors(t, exp, torch.device("meta"))
+        if cfg.expert_dtype in ("i8", "i4"):
+            bad = dict(t, s_down=None)
+            with pytest.raises(ValueError, match="s_down"):
+                moe.check_weight_tensors(bad, exp, cpu)
+        else:
+            bad = dict(t, s_gate=torch.ones(8))
+            with pytest.raises(ValueError, match="s_gate"):
+                moe.check_weight_tensors(bad, exp, cpu)
+        if cfg.expert_dtype == "i4":  # unpacked int4 (one value a byte) is refused
+            bad = dict(t, w_up=L.w_up)
+            with pytest.raises(ValueError, match="w_up"):
+                moe.check_weight_tensors(bad, exp, cpu)

@@ -82,3 +82,24 @@ def test_summary_roofline_picks_the_bound_of_the_up_kernel():
         assert abs(rf["achieved"] - want) < 1e-6 * want
         assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-12
         assert s["tokens_per_s"] == T / 1e-3
+
+
+def test_only_the_cpu_baseline_leg_imports_the_oracle():
+    # the GPU path of the benchmark builds its layers through the binding alone; the
+    # oracle (directly or through the test harness) is imported only by the CPU-baseline leg
+    import ast
+    tree = ast.parse(open(os.path.join(ROOT, "bench.py")).read())
+    allowed = {"_oracle_layer", "cpu_baseline"}
+    for fn in [n for n in ast.walk(tree) if isinstance(n, (ast.FunctionDef, ast.Module))]:
+        body_nodes = ast.walk(fn) if isinstance(fn, ast.FunctionDef) else fn.body
+        for node in body_nodes:
+            names = []
+            if isinstance(node, ast.Import):
+                names = [a.name for a in node.names]
+            elif isinstance(node, ast.ImportFrom):
+                names = [node.module or ""]
+            for m in names:
+                assert m.split(".")[0] != "harness", f"bench.py imports the test harness in {getattr(fn, 'name', '<module>')}"
+                if m.split(".")[0] == "oracle":
+                    assert isinstance(fn, ast.FunctionDef) and fn.name in allowed, \
+                        f"bench.py imports the oracle in {getattr(fn, 'name', '<module>')}"

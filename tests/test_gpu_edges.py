@@ -147,3 +147,38 @@ def test_gate_clamp(name, kw, Ts):
         w = out.topk_w.cpu()
         assert ((w[:, 0] - w[:, 1]).abs() < 1e-7).any() or T < 32
     lay.close()
+
+
+@pytest.mark.parametrize("name,kw,Ts,clamp", [
+    ("mixtral_bf16", dict(d_model=256, d_ff=128), [1, 5, 300], False),       # fused tiny, per-token, MFMA gates
+    ("tiny_f32", dict(d_model=64, d_ff=64), [1, 100], False),                 # fp32 tokens: fused tiny, tiled gate
+    ("mixtral_bf16", dict(d_model=128, d_ff=64, n_experts=32, top_k=4), [16], False),  # split decode gate
+    ("mixtral_bf16", dict(d_model=128, d_ff=64, n_experts=32, top_k=10), [8], False),  # per-token gate, k > 8
+    ("shared_fine_bf16", dict(d_model=256, d_ff=128, shared_d_ff=512), [3, 16, 200], False),  # shared column
+    ("int8_mixtral22b", dict(d_model=256, d_ff=128), [2, 70], False),        # int8 streaming and tiled experts
+    ("mixtral_bf16", dict(d_model=256, d_ff=128), [1, 300], True),           # raw weights of clamped logits
+])
+def test_gate_raw_weighting(name, kw, Ts, clamp):
+    # the routing weights are the chosen logits themselves, on every gate path; the expert
+    # kernels and the combine take them as they take softmax weights
+    cfg = synth.get_config(name, **kw)
+    L = synth.make_layer(cfg)
+    if clamp:
+        b = torch.zeros(cfg.n_experts, dtype=torch.float32)
+        b[[1, 2, 4]] = 49.9
+        L.b_router = b
+    olay = oracle_layer(L, gate_clamp=clamp)
+    olay.gate_weighting = "raw"
+    lay = gpu_layer(L, max(Ts), gate_clamp=clamp, gate_weighting="raw")
+    for T in Ts:
+        print(f"[edge] raw weighting {cfg.name} E={cfg.n_experts} k={cfg.top_k} T={T} clamp={clamp}", flush=True)
+        x = synth.make_tokens(cfg, T).cuda()
+        out = lay.forward(x, scatter=True)
+        torch.cuda.synchronize()
+        r = compare(cfg, x, olay, out, label=f"raw {cfg.name} T={T}")
+        # raw weights do not sum to one (softmax weights would)
+        w = out.topk_w.cpu().double()
+        assert (w.sum(1) - 1).abs().max() > 1e-3, r
+        if clamp:
+            assert (w == 50.0).any()
+    lay.close()

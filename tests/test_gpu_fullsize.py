@@ -1,11 +1,12 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
 benchmark times (one layer, one moe_forward per batch).
 
-Routing (indices, weights, counts, offsets, permutation) is compared for every
-token; outputs for all tokens at decode sizes and for a sample of token rows at
-prefill sizes (the oracle evaluates the sampled rows one expert at a time).
-Layers are drawn on the GPU with torch's seeded generator to keep set-up short;
-the oracle gets host copies of the same tensors.
+Routing (indices, weights, counts, offsets, permutation) and outputs are
+compared for every token at every size, prefill batches included (the oracle
+evaluates the whole batch one expert at a time, a few seconds each), so every
+row tile and column tile the GEMMs deal out is checked. Layers are drawn on the
+GPU with torch's seeded generator to keep set-up short; the oracle gets host
+copies of the same tensors.
 """
 import numpy as np
 import pytest
@@ -15,14 +16,6 @@ import synth
 from harness import compare, gpu_layer, oracle_layer
 
 pytestmark = pytest.mark.gpu
-
-
-def _sample(T, n=16, seed=0):
-    if T <= n:
-        return None
-    rng = np.random.default_rng(seed)
-    s = set([0, T - 1]) | set(rng.choice(T, n - 2, replace=False).tolist())
-    return sorted(s)
 
 
 def _run(name, Ts):
@@ -37,7 +30,7 @@ def _run(name, Ts):
         x = synth.make_tokens(cfg, T, device="cuda")
         r = lay.forward(x, scatter=True)
         torch.cuda.synchronize()
-        out[T] = compare(cfg, x, olay, r, sample=_sample(T) if T > 64 else None, label=f"{name} T={T}")
+        out[T] = compare(cfg, x, olay, r, label=f"{name} T={T}")
         print(f"[fullsize] {name} T={T} {out[T]}", flush=True)
     lay.close()
     del L, olay
@@ -68,8 +61,7 @@ def test_int4_mixtral22b_full():
 
 
 def test_mixtral_bf16_routed_full():
-    # the given-routing entry at full size: scatter tables bit for bit, outputs on all rows
-    # at decode sizes and on a sample of rows at T = 4096
+    # the given-routing entry at full size: scatter tables bit for bit, outputs on every row
     from harness import Y_TOL, _np
     import oracle
     cfg = synth.get_config("mixtral_bf16")
@@ -82,13 +74,11 @@ def test_mixtral_bf16_routed_full():
         idx, w, _ = synth.make_routing(cfg, T, device="cuda")
         out = lay.forward_routed(x, idx, w, scatter=True)
         torch.cuda.synchronize()
-        rows = _sample(T)
-        ref = oracle.moe_forward_routed(_np(x), olay, idx.cpu().numpy(), w.cpu().numpy(), tokens=rows)
+        ref = oracle.moe_forward_routed(_np(x), olay, idx.cpu().numpy(), w.cpu().numpy())
         assert np.array_equal(out.expert_counts.cpu().numpy(), ref["counts"])
         assert np.array_equal(out.expert_offsets.cpu().numpy(), ref["offsets"])
         assert np.array_equal(out.sorted_assign.cpu().numpy(), ref["sorted_assign"])
         y = _np(out.y).astype(np.float64)
-        y = y if rows is None else y[rows]
         yr = ref["y"]
         rel, mabs = Y_TOL[cfg.act_dtype]
         den = np.linalg.norm(yr)
