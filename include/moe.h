@@ -205,6 +205,28 @@ MOE_API int moe_forward_routed(moe_layer* layer, const void* x, int32_t T, const
                                const float* topk_w, const float* shared_gate, void* y,
                                const moe_route_out* route, void* stream);
 
+/* Size of the static device scratch that moe_forward_noalloc works in: 64 MiB on every
+ * device the library runs on, held from the library's first use of that device until
+ * the process ends. */
+#define MOE_STATIC_SCRATCH_BYTES (64u << 20)
+
+/* moe_forward for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same computation,
+ * launch plan and results as moe_forward (bit for bit), but the per-call workspace (the
+ * routing tables, the gathered GEMM operand, H and the combine rows) lives in one static
+ * device array of MOE_STATIC_SCRATCH_BYTES instead of the layer's own workspace; the call
+ * allocates nothing and launches kernels only (no memset, copy or host wait). Arguments,
+ * statuses and ownership as moe_forward, plus: EINVAL when the batch needs more scratch
+ * than the array holds (decode batches fit: T <= 64 for BF16 experts, T <= 32 for I8/I4,
+ * on layers up to d_model 8192 and d_ff 16384; large prefill batches do not -- use
+ * moe_forward), with the needed size in moe_last_error(). Every layer and every call on
+ * one device shares that device's array, whatever the stream: calls that overlap in time
+ * on one device race and give wrong results, so serialise them (one stream, or events).
+ * The array keeps the last call's contents; every byte a call reads from it is written
+ * earlier in the same call, so nothing is cleared between calls. */
+MOE_API int moe_forward_noalloc(moe_layer* layer, const void* x, int32_t T, void* y,
+                                const moe_route_out* route, void* stream);
+
 /* Turn per-stage HIP event timing on (1) or off (0) for the following
  * moe_forward calls on this layer ([0539edu §3.3]: profiling is a per-call
  * switch of the inference config). The initial state is desc->profile. Events

@@ -16,7 +16,7 @@ from typing import Optional
 
 __all__ = [
     "MoeError", "lib", "MOE_F32", "MOE_BF16", "MOE_I8", "MOE_I4", "MOE_WEIGHT_SOFTMAX", "MOE_WEIGHT_RAW", "MoeDesc", "MoeWeights", "MoeRouteOut",
-    "moe_layer_create", "moe_forward", "moe_forward_routed", "moe_set_profiling", "moe_stage_times",
+    "moe_layer_create", "moe_forward", "moe_forward_routed", "moe_forward_noalloc", "MOE_STATIC_SCRATCH_BYTES", "moe_set_profiling", "moe_stage_times",
     "moe_destroy", "moe_status_str", "moe_last_error", "MoeLayer", "check_weight_tensors", "LIB_PATH", "EXPORTED",
 ]
 
@@ -27,8 +27,9 @@ MOE_F32, MOE_BF16, MOE_I8, MOE_I4 = 0, 1, 2, 3
 MOE_WEIGHT_SOFTMAX, MOE_WEIGHT_RAW = 0, 1
 
 # every symbol include/moe.h declares
-EXPORTED = ("moe_layer_create", "moe_forward", "moe_forward_routed", "moe_set_profiling", "moe_stage_times",
-            "moe_destroy", "moe_status_str", "moe_last_error")
+EXPORTED = ("moe_layer_create", "moe_forward", "moe_forward_routed", "moe_forward_noalloc", "moe_set_profiling",
+            "moe_stage_times", "moe_destroy", "moe_status_str", "moe_last_error")
+MOE_STATIC_SCRATCH_BYTES = 64 << 20  # the static scratch of moe_forward_noalloc, per device
 
 
 class MoeError(RuntimeError):
@@ -75,6 +76,8 @@ def lib() -> ctypes.CDLL:
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.POINTER(MoeRouteOut), ctypes.c_void_p]
         L.moe_forward_routed.restype = ctypes.c_int
+        L.moe_forward_noalloc.argtypes = L.moe_forward.argtypes
+        L.moe_forward_noalloc.restype = ctypes.c_int
         L.moe_set_profiling.argtypes = [ctypes.c_void_p, ctypes.c_int]
         L.moe_set_profiling.restype = ctypes.c_int
         L.moe_stage_times.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]
@@ -113,6 +116,12 @@ def moe_layer_create(desc: MoeDesc, weights: MoeWeights) -> ctypes.c_void_p:
 def moe_forward(handle, x_ptr: int, T: int, y_ptr: int, route: MoeRouteOut, stream_ptr: int = 0) -> None:
     """Raw forward on device pointers; enqueues on the given HIP stream."""
     _check(lib().moe_forward(handle, x_ptr, T, y_ptr, ctypes.byref(route), stream_ptr), "moe_forward")
+
+
+def moe_forward_noalloc(handle, x_ptr: int, T: int, y_ptr: int, route: MoeRouteOut, stream_ptr: int = 0) -> None:
+    """Raw forward in the library's static scratch (allocates nothing); as moe_forward."""
+    _check(lib().moe_forward_noalloc(handle, x_ptr, T, y_ptr, ctypes.byref(route), stream_ptr),
+           "moe_forward_noalloc")
 
 
 def moe_forward_routed(handle, x_ptr: int, T: int, idx_ptr: int, w_ptr: int, shared_gate_ptr: int, y_ptr: int,
@@ -270,8 +279,11 @@ class MoeLayer:
                 r.shared_gate = torch.empty(T, dtype=torch.float32, device=dev)
         return r
 
-    def forward(self, x, out: Optional[RouteResult] = None, scatter: bool = False, stream=None) -> RouteResult:
-        """Enqueue the layer on `stream` (default: torch's current stream) and return the outputs."""
+    def forward(self, x, out: Optional[RouteResult] = None, scatter: bool = False, stream=None,
+                noalloc: bool = False) -> RouteResult:
+        """Enqueue the layer on `stream` (default: torch's current stream) and return the outputs.
+        noalloc: run moe_forward_noalloc (the library's static scratch instead of the layer's
+        workspace; pass `out` to allocate nothing here either)."""
         torch = self.torch
         if x.dim() != 2 or x.shape[1] != self.d_model or x.dtype != self._act_torch:
             raise ValueError(f"x must be [T, {self.d_model}] {self._act_torch}")
@@ -283,7 +295,8 @@ class MoeLayer:
         route = MoeRouteOut(_ptr(out.topk_idx), _ptr(out.topk_w), _ptr(out.expert_counts),
                             _ptr(out.expert_offsets), _ptr(out.sorted_assign), _ptr(out.shared_gate))
         s = stream if stream is not None else torch.cuda.current_stream()
-        moe_forward(self._h, _ptr(x), T, _ptr(out.y), route, int(s.cuda_stream))
+        (moe_forward_noalloc if noalloc else moe_forward)(self._h, _ptr(x), T, _ptr(out.y), route,
+                                                           int(s.cuda_stream))
         return out
 
     def forward_routed(self, x, topk_idx, topk_w, shared_gate=None, out: Optional[RouteResult] = None,

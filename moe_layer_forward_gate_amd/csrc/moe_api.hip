@@ -10,6 +10,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <new>
 
 #include "../../include/moe.h"
@@ -40,6 +41,24 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 }  // namespace
 
+// Per-call workspace of a forward: routing tables, the gathered GEMM operand, H and the
+// combine rows. A layer owns one sized for desc.max_tokens; the allocation-free forward
+// carves one out of the device's static scratch for the call's own T.
+struct Work {
+    int32_t* counts = nullptr;
+    int32_t* offsets = nullptr;
+    int32_t* tile_start = nullptr;
+    int32_t* sorted_c = nullptr;
+    float* gs = nullptr;
+    int32_t* ridx = nullptr;  // a caller's routing, checked (moe_forward_routed)
+    float* rw = nullptr;
+    float* gate_part = nullptr;  // partial router dots of the split decode gate
+    int32_t* scatter_work = nullptr;  // chunk counts and ranks of the multi-workgroup scatter
+    bf16_t* xp = nullptr;  // tiled up operand (bf16/int8 experts)
+    void* h = nullptr;
+    float* ow = nullptr;
+};
+
 struct moe_layer {
     moe_desc desc{};
     int device = 0;
@@ -55,20 +74,9 @@ struct moe_layer {
     float* s_gate = nullptr;
     float* s_up = nullptr;
     float* s_down = nullptr;
-    // workspace
-    int32_t* counts = nullptr;
-    int32_t* offsets = nullptr;
-    int32_t* tile_start = nullptr;
-    int32_t* sorted_c = nullptr;
-    float* gs = nullptr;
-    int32_t* ridx = nullptr;  // a caller's routing, checked (moe_forward_routed)
-    float* rw = nullptr;
-    float* gate_part = nullptr;  // partial router dots of the split decode gate
-    int32_t* scatter_work = nullptr;  // chunk counts and ranks of the multi-workgroup scatter
-    bf16_t* xp = nullptr;  // tiled up operand (bf16/int8 experts)
-    void* h = nullptr;
-    float* ow = nullptr;
-    size_t ow_rows = 0;
+    // workspace for max_tokens
+    Work w;
+    size_t ow_rows = 0;  // combine rows of that workspace (bounds the plans' K splits)
     // profiling
     bool profiling = false;
     hipEvent_t ev[6] = {};
@@ -79,8 +87,9 @@ namespace {
 
 void release(moe_layer* L) {
     if (!L) return;
-    void* bufs[] = {L->wr_t, L->wr_planes, L->bias, L->wgu, L->wdn, L->s_gate, L->s_up, L->s_down, L->counts, L->offsets,
-                    L->tile_start, L->sorted_c, L->gs, L->ridx, L->rw, L->gate_part, L->scatter_work, L->xp, L->h, L->ow};
+    const Work& w = L->w;
+    void* bufs[] = {L->wr_t, L->wr_planes, L->bias, L->wgu, L->wdn, L->s_gate, L->s_up, L->s_down, w.counts, w.offsets,
+                    w.tile_start, w.sorted_c, w.gs, w.ridx, w.rw, w.gate_part, w.scatter_work, w.xp, w.h, w.ow};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
     for (hipEvent_t e : L->ev)
@@ -144,6 +153,8 @@ int check_desc(const moe_desc* d, const moe_weights* w) {
     return MOE_OK;
 }
 
+int scratch_on_device(int dev, char** out);
+
 int create_impl(const moe_desc* desc, const moe_weights* w, moe_layer* L) {
     const moe_desc& d = *desc;
     L->desc = d;
@@ -155,6 +166,12 @@ int create_impl(const moe_desc* desc, const moe_weights* w, moe_layer* L) {
     L->has_bias = w->b_router != nullptr;
     HIP_TRY(hipGetDevice(&L->device));
     HIP_TRY(hipDeviceGetAttribute(&L->cus, hipDeviceAttributeMultiprocessorCount, L->device));
+    {
+        // the device address of the static scratch on this device, for moe_forward_noalloc
+        char* sp;
+        int rc0 = scratch_on_device(L->device, &sp);
+        if (rc0) return rc0;
+    }
 
     const size_t dm = d.d_model, F = d.d_ff, E = L->E, Et = L->Et;
     const bool f32 = d.expert_dtype == MOE_F32;
@@ -179,25 +196,26 @@ int create_impl(const moe_desc* desc, const moe_weights* w, moe_layer* L) {
         if ((rc = dev_alloc(&L->s_down, E * dm * 4))) return rc;
     }
     const size_t T = d.max_tokens, P = T * L->kt;
-    if ((rc = dev_alloc(&L->counts, (Et + 1) * 4))) return rc;
-    if ((rc = dev_alloc(&L->offsets, (Et + 1) * 4))) return rc;
-    if ((rc = dev_alloc(&L->tile_start, (Et + 1) * 4))) return rc;
-    if ((rc = dev_alloc(&L->sorted_c, P * 4))) return rc;
-    if ((rc = dev_alloc(&L->gs, T * 4))) return rc;
-    if ((rc = dev_alloc(&L->ridx, T * d.top_k * 4))) return rc;
-    if ((rc = dev_alloc(&L->rw, T * d.top_k * 4))) return rc;
-    if ((rc = dev_alloc(&L->gate_part, gate_split_workspace((int)std::min(T, (size_t)64), d.d_model, L->E,
+    Work& ws = L->w;
+    if ((rc = dev_alloc(&ws.counts, (Et + 1) * 4))) return rc;
+    if ((rc = dev_alloc(&ws.offsets, (Et + 1) * 4))) return rc;
+    if ((rc = dev_alloc(&ws.tile_start, (Et + 1) * 4))) return rc;
+    if ((rc = dev_alloc(&ws.sorted_c, P * 4))) return rc;
+    if ((rc = dev_alloc(&ws.gs, T * 4))) return rc;
+    if ((rc = dev_alloc(&ws.ridx, T * d.top_k * 4))) return rc;
+    if ((rc = dev_alloc(&ws.rw, T * d.top_k * 4))) return rc;
+    if ((rc = dev_alloc(&ws.gate_part, gate_split_workspace((int)std::min(T, (size_t)64), d.d_model, L->E,
                                                              d.shared_d_ff > 0))))
         return rc;
-    if ((rc = dev_alloc(&L->scatter_work, scatter_wide_workspace((int)(T * d.top_k), L->E)))) return rc;
+    if ((rc = dev_alloc(&ws.scatter_work, scatter_wide_workspace((int)(T * d.top_k), L->E)))) return rc;
     // the tiled GEMMs work on padded rows: at most P + (bm - 1) + Et*bm of them for bm <= 256
     const size_t R = P + (size_t)256 * (Et + 1);
-    if (!f32 && (rc = dev_alloc(&L->xp, R * dm * 2))) return rc;
-    if ((rc = dev_alloc(&L->h, (f32 ? P : R) * F * (f32 ? 4 : 2)))) return rc;
+    if (!f32 && (rc = dev_alloc(&ws.xp, R * dm * 2))) return rc;
+    if ((rc = dev_alloc(&ws.h, (f32 ? P : R) * F * (f32 ? 4 : 2)))) return rc;
     // combine buffer: one row per (token, slot, K split): 2 splits for large batches,
     // up to kStreamMaxSplit for batches the streaming kernels serve
     L->ow_rows = std::max(P * 2, std::min(T, (size_t)kStreamMaxT) * L->kt * kStreamMaxSplit);
-    if ((rc = dev_alloc(&L->ow, L->ow_rows * dm * 4))) return rc;
+    if ((rc = dev_alloc(&ws.ow, L->ow_rows * dm * 4))) return rc;
     if (d.profile) {
         for (hipEvent_t& e : L->ev) HIP_TRY(hipEventCreate(&e));
         L->profiling = true;
@@ -269,6 +287,9 @@ int check_device(const moe_layer* L) {
 //    tile, the down projection's K split so ~1024 workgroups run;
 //  - larger batches use the LDS-tiled MFMA GEMMs (256-row tiles for bf16 weights, 128 for
 //    int8, 64 for int4), with the down projection's K split when that fills the CUs better.
+// Past this many routed assignments the scatter runs over many workgroups.
+constexpr int kScatterWideMin = 4095;
+
 struct Plan {
     bool streaming;
     int bm, ksplit, max_tiles;
@@ -351,19 +372,80 @@ Plan make_plan(const moe_layer* L, int T) {
     return Plan{streaming, bm, ksplit, max_tiles, merge, weights_once};
 }
 
-ScatterOut scatter_out(const moe_layer* L, int32_t* counts, int32_t* offsets, int32_t* sorted) {
-    return ScatterOut{L->counts, L->offsets, L->tile_start, L->sorted_c, counts, offsets, sorted};
+// Routers wider than 16 columns (experts + shared gate) at decode batch sizes: the split gate.
+bool split_gate(const moe_layer* L, int T) {
+    const bool wide_router = L->E + (L->V > 0 ? 1 : 0) > 16;
+    const bool f32 = L->desc.expert_dtype == MOE_F32;
+    return wide_router && gate_split_fits(T, L->desc.top_k) && (f32 || T <= kGateSplitMaxT);
+}
+
+// ---- the static scratch of the allocation-free forward (moe_forward_noalloc)
+// One file-scope device array: every device the library runs on holds its own copy from
+// the module's load until the process ends, shared by every layer and call on that device.
+// In host code the name `scratch` is a host-side stand-in, not a device address: host code
+// takes the array's device address once per device (hipGetSymbolAddress, at the first
+// moe_layer_create on that device) and passes only that address to kernels.
+constexpr size_t kScratchBytes = MOE_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's device address on `dev` (the current device), looked up on first use.
+int scratch_on_device(int dev, char** out) {
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_EUNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        g_scratch_ptr[dev] = (char*)p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+// The workspace a forward of T tokens under plan pl reads and writes, laid out from `base`
+// into *W (each piece on a 256-byte boundary); returns its size. base == nullptr: size only.
+// Every byte a forward reads from it is written earlier in the same forward, so nothing
+// needs clearing between calls.
+size_t carve_work(const moe_layer* L, const Plan& pl, int T, char* base, Work* W) {
+    const moe_desc& d = L->desc;
+    const bool f32 = d.expert_dtype == MOE_F32;
+    const size_t Et = L->Et, P = (size_t)T * L->kt, dm = d.d_model, F = d.d_ff;
+    const size_t tiled_rows = (size_t)pl.max_tiles * pl.bm;  // padded rows of the tiled GEMM operands
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> char* {
+        char* p = base ? base + off : nullptr;
+        off += (bytes + 255) / 256 * 256;
+        return p;
+    };
+    Work w;
+    w.counts = (int32_t*)take((Et + 1) * 4);
+    w.offsets = (int32_t*)take((Et + 1) * 4);
+    w.tile_start = (int32_t*)take((Et + 1) * 4);
+    w.sorted_c = (int32_t*)take(P * 4);
+    w.gs = (float*)take((size_t)T * 4);
+    if (split_gate(L, T)) w.gate_part = (float*)take(gate_split_workspace(T, d.d_model, L->E, L->V > 0));
+    if (T * d.top_k > kScatterWideMin) w.scatter_work = (int32_t*)take(scatter_wide_workspace(T * d.top_k, L->E));
+    if (!f32 && !pl.streaming) w.xp = (bf16_t*)take(tiled_rows * dm * 2);
+    w.h = take((f32 || pl.streaming ? P : tiled_rows) * F * (f32 ? 4 : 2));
+    w.ow = (float*)take(P * pl.ksplit * dm * 4);
+    if (W) *W = w;
+    return off;
+}
+
+ScatterOut scatter_out(const Work& W, int32_t* counts, int32_t* offsets, int32_t* sorted) {
+    return ScatterOut{W.counts, W.offsets, W.tile_start, W.sorted_c, counts, offsets, sorted};
 }
 
 // Scatter of a routing already in device memory (idx [T][k]).
-int run_scatter(moe_layer* L, const int32_t* idx, int T, const Plan& pl, const ScatterOut& so, hipStream_t s) {
+int run_scatter(moe_layer* L, const Work& W, const int32_t* idx, int T, const Plan& pl, const ScatterOut& so,
+                hipStream_t s) {
     const int k = L->desc.top_k;
-#ifndef MOE_SCATTER_WIDE_MIN
-#define MOE_SCATTER_WIDE_MIN 4095
-#endif
     // many assignments: the scatter over many workgroups (three launches)
-    if (T * k > MOE_SCATTER_WIDE_MIN)
-        HIP_TRY(launch_scatter_wide(idx, T, L->E, k, L->V, pl.bm, so, L->scatter_work, s));
+    if (T * k > kScatterWideMin)
+        HIP_TRY(launch_scatter_wide(idx, T, L->E, k, L->V, pl.bm, so, W.scatter_work, s));
     else
         HIP_TRY(launch_scatter(idx, T, L->E, k, L->V, pl.bm, so, s));
     return MOE_OK;
@@ -371,25 +453,25 @@ int run_scatter(moe_layer* L, const int32_t* idx, int T, const Plan& pl, const S
 
 // Expert compute and Gather once the scatter tables are on the device: the gathering
 // of token rows for the tiled GEMMs, up, down, combine (with the per-stage events).
-int run_experts(moe_layer* L, const void* x, int T, void* y, const float* topk_w, const float* gs, const Plan& pl,
-                hipStream_t s) {
+int run_experts(moe_layer* L, const Work& W, const void* x, int T, void* y, const float* topk_w, const float* gs,
+                const Plan& pl, hipStream_t s) {
     const moe_desc& d = L->desc;
     const bool f32 = d.expert_dtype == MOE_F32;
     const bool i8 = d.expert_dtype == MOE_I8;
     const int wq = d.expert_dtype == MOE_I4 ? kWI4 : (i8 ? kWI8 : kWBf16);
     const int k = d.top_k;
     const bool prof = L->profiling;
-    const GemmArgs a{L->tile_start, L->offsets, L->sorted_c, L->Et, L->kt, k, pl.max_tiles, pl.bm, pl.ksplit,
-                     pl.merge ? 1 : 0, pl.weights_once ? 1 : 0, (const bf16_t*)x, L->xp, (bf16_t*)L->h, L->wgu, L->wdn, L->s_gate, L->s_up,
-                     L->s_down, topk_w, gs, L->ow, d.d_model, d.d_ff};
+    const GemmArgs a{W.tile_start, W.offsets, W.sorted_c, L->Et, L->kt, k, pl.max_tiles, pl.bm, pl.ksplit,
+                     pl.merge ? 1 : 0, pl.weights_once ? 1 : 0, (const bf16_t*)x, W.xp, (bf16_t*)W.h, L->wgu, L->wdn,
+                     L->s_gate, L->s_up, L->s_down, topk_w, gs, W.ow, d.d_model, d.d_ff};
     // the tiled GEMMs take the token rows already gathered into fragment order
     if (!f32 && !pl.streaming) HIP_TRY(launch_pack_a(a, s));
     if (prof) HIP_TRY(hipEventRecord(L->ev[2], s));
     if (f32) {
-        GemmF32Args af{L->tile_start, L->offsets, L->sorted_c, L->Et, L->kt, k, pl.max_tiles,
-                       (const float*)x, (float*)L->h, (const float*)L->wgu,
+        GemmF32Args af{W.tile_start, W.offsets, W.sorted_c, L->Et, L->kt, k, pl.max_tiles,
+                       (const float*)x, (float*)W.h, (const float*)L->wgu,
                        (const float*)L->wgu + (size_t)L->E * d.d_model * d.d_ff, (const float*)L->wdn,
-                       topk_w, gs, L->ow, d.d_model, d.d_ff};
+                       topk_w, gs, W.ow, d.d_model, d.d_ff};
         HIP_TRY(launch_expert_up_f32(af, s));
         if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));
         HIP_TRY(launch_expert_down_f32(af, s));
@@ -403,13 +485,63 @@ int run_experts(moe_layer* L, const void* x, int T, void* y, const float* topk_w
         HIP_TRY(launch_expert_down_tiled(a, wq, s));
     }
     if (prof) HIP_TRY(hipEventRecord(L->ev[4], s));
-    HIP_TRY(launch_combine(L->ow, T, (pl.merge ? k + 1 : L->kt) * pl.ksplit, L->kt * pl.ksplit, d.d_model, y, !f32,
+    HIP_TRY(launch_combine(W.ow, T, (pl.merge ? k + 1 : L->kt) * pl.ksplit, L->kt * pl.ksplit, d.d_model, y, !f32,
                            s));
     if (prof) {
         HIP_TRY(hipEventRecord(L->ev[5], s));
         L->ran = true;
     }
     return MOE_OK;
+}
+
+// Checks of a forward's arguments (before any HIP call).
+int check_forward(const moe_layer* L, const void* x, int32_t T, void* y, const moe_route_out* r) {
+    int rc = check_call(L, x, T, y);
+    if (rc || T == 0) return rc;
+    if (!r || !r->topk_idx || !r->topk_w) return fail(MOE_EINVAL, "route, route->topk_idx and route->topk_w are required");
+    const void* rp[] = {r->topk_idx, r->topk_w, r->expert_counts, r->expert_offsets, r->sorted_assign,
+                        r->shared_gate};
+    for (const void* q : rp)
+        if (q && !aligned(q, 4)) return fail(MOE_EINVAL, "route outputs must be 4-byte aligned");
+    return check_device(L);
+}
+
+// The forward on workspace W (the layer's own, or one carved out of the static scratch).
+int run_forward(moe_layer* L, const Work& W, const void* x, int32_t T, void* y, const moe_route_out* r,
+                const Plan& pl, hipStream_t s) {
+    int rc;
+    const moe_desc& d = L->desc;
+    const bool f32 = d.expert_dtype == MOE_F32;
+    const int k = d.top_k;
+    float* gs = r->shared_gate ? r->shared_gate : W.gs;
+    const bool prof = L->profiling;
+    const ScatterOut so = scatter_out(W, r->expert_counts, r->expert_offsets, r->sorted_assign);
+    if (prof) HIP_TRY(hipEventRecord(L->ev[0], s));
+
+    // Routing for decode batches: up to 16 router columns, one workgroup reads the whole
+    // router quickly enough (tiny batches fuse gate and scatter; larger ones run one gate
+    // workgroup per token, then the scatter); more columns spread the router over many
+    // workgroups (split gate, whose last launch also runs the scatter).
+    const bool wide_router = L->E + (L->V > 0 ? 1 : 0) > 16;
+    const int gflags = (L->V > 0 ? kGateShared : 0) | (d.gate_clamp ? kGateClamp : 0) |
+                       (d.gate_weighting == MOE_WEIGHT_RAW ? kGateRaw : 0);
+    if (!wide_router && gate_scatter_small_fits(T, d.d_model, L->E, L->V > 0, !f32)) {
+        // tiny batch: both stages in one workgroup (the scatter stage then times as empty)
+        HIP_TRY(launch_gate_scatter_small(x, !f32, L->wr_t, L->bias, T, d.d_model, L->E, gflags, k, r->topk_idx,
+                                          r->topk_w, gs, L->V, pl.bm, so, s));
+        if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
+    } else if (split_gate(L, T)) {
+        // decode batch: router dots on many workgroups, then top-k and scatter in one
+        HIP_TRY(launch_gate_split(x, !f32, L->wr_t, L->bias, T, d.d_model, L->E, gflags, k, r->topk_idx,
+                                  r->topk_w, gs, L->V, pl.bm, so, W.gate_part, s));
+        if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
+    } else {
+        HIP_TRY(launch_gate(x, !f32, L->wr_t, L->wr_planes, L->bias, T, d.d_model, L->E, gflags, k, r->topk_idx,
+                            r->topk_w, gs, s));
+        if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
+        if ((rc = run_scatter(L, W, r->topk_idx, T, pl, so, s))) return rc;
+    }
+    return run_experts(L, W, x, T, y, r->topk_w, gs, pl, s);
 }
 
 }  // namespace
@@ -449,49 +581,27 @@ int moe_layer_create(const moe_desc* desc, const moe_weights* weights, moe_layer
 
 int moe_forward(moe_layer* L, const void* x, int32_t T, void* y, const moe_route_out* r, void* stream) {
     g_err[0] = 0;
-    int rc = check_call(L, x, T, y);
+    int rc = check_forward(L, x, T, y, r);
     if (rc || T == 0) return rc;
-    if (!r || !r->topk_idx || !r->topk_w) return fail(MOE_EINVAL, "route, route->topk_idx and route->topk_w are required");
-    const void* rp[] = {r->topk_idx, r->topk_w, r->expert_counts, r->expert_offsets, r->sorted_assign,
-                        r->shared_gate};
-    for (const void* q : rp)
-        if (q && !aligned(q, 4)) return fail(MOE_EINVAL, "route outputs must be 4-byte aligned");
-    if ((rc = check_device(L))) return rc;
+    return run_forward(L, L->w, x, T, y, r, make_plan(L, T), (hipStream_t)stream);
+}
 
-    hipStream_t s = (hipStream_t)stream;
-    const moe_desc& d = L->desc;
-    const bool f32 = d.expert_dtype == MOE_F32;
-    const int k = d.top_k;
-    float* gs = r->shared_gate ? r->shared_gate : L->gs;
-    const bool prof = L->profiling;
+int moe_forward_noalloc(moe_layer* L, const void* x, int32_t T, void* y, const moe_route_out* r, void* stream) {
+    g_err[0] = 0;
+    int rc = check_forward(L, x, T, y, r);
+    if (rc || T == 0) return rc;
+    // the same plan as moe_forward, so the two give the same results
     const Plan pl = make_plan(L, T);
-    const ScatterOut so = scatter_out(L, r->expert_counts, r->expert_offsets, r->sorted_assign);
-    if (prof) HIP_TRY(hipEventRecord(L->ev[0], s));
-
-    // Routing for decode batches: up to 16 router columns, one workgroup reads the whole
-    // router quickly enough (tiny batches fuse gate and scatter; larger ones run one gate
-    // workgroup per token, then the scatter); more columns spread the router over many
-    // workgroups (split gate, whose last launch also runs the scatter).
-    const bool wide_router = L->E + (L->V > 0 ? 1 : 0) > 16;
-    const int gflags = (L->V > 0 ? kGateShared : 0) | (d.gate_clamp ? kGateClamp : 0) |
-                       (d.gate_weighting == MOE_WEIGHT_RAW ? kGateRaw : 0);
-    if (!wide_router && gate_scatter_small_fits(T, d.d_model, L->E, L->V > 0, !f32)) {
-        // tiny batch: both stages in one workgroup (the scatter stage then times as empty)
-        HIP_TRY(launch_gate_scatter_small(x, !f32, L->wr_t, L->bias, T, d.d_model, L->E, gflags, k, r->topk_idx,
-                                          r->topk_w, gs, L->V, pl.bm, so, s));
-        if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
-    } else if (wide_router && gate_split_fits(T, k) && (f32 || T <= kGateSplitMaxT)) {
-        // decode batch: router dots on many workgroups, then top-k and scatter in one
-        HIP_TRY(launch_gate_split(x, !f32, L->wr_t, L->bias, T, d.d_model, L->E, gflags, k, r->topk_idx,
-                                  r->topk_w, gs, L->V, pl.bm, so, L->gate_part, s));
-        if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
-    } else {
-        HIP_TRY(launch_gate(x, !f32, L->wr_t, L->wr_planes, L->bias, T, d.d_model, L->E, gflags, k, r->topk_idx,
-                            r->topk_w, gs, s));
-        if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
-        if ((rc = run_scatter(L, r->topk_idx, T, pl, so, s))) return rc;
-    }
-    return run_experts(L, x, T, y, r->topk_w, gs, pl, s);
+    const size_t need = carve_work(L, pl, T, nullptr, nullptr);
+    if (need > kScratchBytes)
+        return fail(MOE_EINVAL,
+                    "moe_forward_noalloc: T=%d on this layer needs %zu bytes of scratch; the static scratch "
+                    "holds %zu (moe_forward takes any T up to max_tokens)", T, need, kScratchBytes);
+    char* base = nullptr;
+    if ((rc = scratch_on_device(L->device, &base))) return rc;
+    Work W;
+    carve_work(L, pl, T, base, &W);
+    return run_forward(L, W, x, T, y, r, pl, (hipStream_t)stream);
 }
 
 int moe_forward_routed(moe_layer* L, const void* x, int32_t T, const int32_t* topk_idx, const float* topk_w,
@@ -511,14 +621,15 @@ int moe_forward_routed(moe_layer* L, const void* x, int32_t T, const int32_t* to
     hipStream_t s = (hipStream_t)stream;
     const bool prof = L->profiling;
     const Plan pl = make_plan(L, T);
-    const ScatterOut so = scatter_out(L, r ? r->expert_counts : nullptr, r ? r->expert_offsets : nullptr,
+    const Work& W = L->w;
+    const ScatterOut so = scatter_out(W, r ? r->expert_counts : nullptr, r ? r->expert_offsets : nullptr,
                                       r ? r->sorted_assign : nullptr);
     if (prof) HIP_TRY(hipEventRecord(L->ev[0], s));
     // the given routing, with ids outside [0, E) read as expert 0 at weight 0
-    HIP_TRY(launch_route_in(topk_idx, topk_w, T * L->desc.top_k, L->E, L->ridx, L->rw, s));
+    HIP_TRY(launch_route_in(topk_idx, topk_w, T * L->desc.top_k, L->E, W.ridx, W.rw, s));
     if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
-    if ((rc = run_scatter(L, L->ridx, T, pl, so, s))) return rc;
-    return run_experts(L, x, T, y, L->rw, shared_gate, pl, s);
+    if ((rc = run_scatter(L, W, W.ridx, T, pl, so, s))) return rc;
+    return run_experts(L, W, x, T, y, W.rw, shared_gate, pl, s);
 }
 
 int moe_set_profiling(moe_layer* L, int enable) {

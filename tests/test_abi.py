@@ -29,10 +29,18 @@ def _decl_comments():
 PAGE_CITE = re.compile(r"\[(0539edu|mhpq|hotelren|trdm|pptc) §\d+(\.\d+)*\]")
 
 
+# entry points that are not a step of the pages' method: their comment names the callers
+# they are for instead of a page passage
+NOT_FROM_THE_PAGES = {"moe_forward_noalloc": "callers that cannot allocate"}
+
+
 def test_every_declaration_cites_a_page_passage():
     com = _decl_comments()
     assert sorted(com) == _declared(), "every MOE_API declaration has a block comment right above it"
     for name, c in com.items():
+        if name in NOT_FROM_THE_PAGES:
+            assert NOT_FROM_THE_PAGES[name] in " ".join(c.split()), name
+            continue
         assert PAGE_CITE.search(c), f"{name}: its comment cites no page passage"
 
 
