@@ -18,6 +18,8 @@
 // Work item = (active expert, group of 4*NBW column blocks, K split); experts
 // without rows get no work items (the item count is read from the scatter's tile
 // table on the device).
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -119,120 +121,154 @@ __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
 #pragma unroll
         for (int j = 0; j < NBW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto step = [&](const u32x4 (&bb)[NBW], const u32x4 (&aa)[MB][KH], const float (&sc)[NBW]) {
-        if constexpr (INT4) {
-            // one scale group: its partial products (codes read as q + 136) and 136 * the
-            // rows' sums over the group, then acc += scale * (partial - 136 * sum)
-            const bf16x8 k136 = __builtin_bit_cast(bf16x8, u32x4{0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u});
-            f32x4 zr[MB], g[NBW][MB];
+    // The K loop runs with the number of row blocks that hold rows (MA <= MB) fixed at
+    // compile time and no other branch in its steady state: a branch inside it makes the
+    // compiler wait for every load in flight (vmcnt(0)) before the next round's loads and
+    // again before the MFMAs, which drains the two-round pipeline every round.
+    auto kloop = [&](auto ma) __attribute__((always_inline)) {
+        constexpr int MA = decltype(ma)::value;
+        auto step = [&](const u32x4 (&bb)[NBW], const u32x4 (&aa)[MB][KH], const float (&sc)[NBW])
+                        __attribute__((always_inline)) {
+            if constexpr (INT4) {
+                // one scale group: its partial products (codes read as q + 136) and 136 * the
+                // rows' sums over the group, then acc += scale * (partial - 136 * sum)
+                const bf16x8 k136 =
+                    __builtin_bit_cast(bf16x8, u32x4{0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u});
+                f32x4 zr[MA], g[NBW][MA];
 #pragma unroll
-            for (int kh = 0; kh < KH; ++kh) {
+                for (int kh = 0; kh < KH; ++kh) {
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    if (mb < mb_act)
+                    for (int mb = 0; mb < MA; ++mb)
                         zr[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aa[mb][kh]), k136,
-                                                                         kh ? zr[mb] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                                                                         kh ? zr[mb] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0,
+                                                                         0);
 #pragma unroll
-                for (int j = 0; j < NBW; ++j) {
-                    const bf16x8 bw = __builtin_bit_cast(bf16x8, i4x8_bf16(bb[j][kh], nib_mask));
+                    for (int j = 0; j < NBW; ++j) {
+                        const bf16x8 bw = __builtin_bit_cast(bf16x8, i4x8_bf16(bb[j][kh], nib_mask));
 #pragma unroll
-                    for (int mb = 0; mb < MB; ++mb)
-                        if (mb < mb_act)
+                        for (int mb = 0; mb < MA; ++mb)
                             g[j][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                                 __builtin_bit_cast(bf16x8, aa[mb][kh]), bw, kh ? g[j][mb] : f32x4{0.f, 0.f, 0.f, 0.f},
                                 0, 0, 0);
+                    }
                 }
+#pragma unroll
+                for (int j = 0; j < NBW; ++j)
+#pragma unroll
+                    for (int mb = 0; mb < MA; ++mb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            acc[mb][j][i] = fmaf(sc[j], g[j][mb][i] - zr[mb][i], acc[mb][j][i]);
+                return;
             }
 #pragma unroll
-            for (int j = 0; j < NBW; ++j)
+            for (int kh = 0; kh < KH; ++kh)
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    if (mb < mb_act)
+                for (int j = 0; j < NBW; ++j) {
+                    u32x4 bw;
+                    if constexpr (INT8) {
+                        const uint32_t lo = kh ? bb[j].z : bb[j].x, hi = kh ? bb[j].w : bb[j].y;
+                        bw = u32x4{i8x2_bf16(lo, 0), i8x2_bf16(lo, 16), i8x2_bf16(hi, 0), i8x2_bf16(hi, 16)};
+                    } else {
+                        bw = bb[j];
+                    }
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[mb][j][i] = fmaf(sc[j], g[j][mb][i] - zr[mb][i], acc[mb][j][i]);
-            return;
-        }
-#pragma unroll
-        for (int kh = 0; kh < KH; ++kh)
-#pragma unroll
-            for (int j = 0; j < NBW; ++j) {
-                u32x4 bw;
-                if constexpr (INT8) {
-                    const uint32_t lo = kh ? bb[j].z : bb[j].x, hi = kh ? bb[j].w : bb[j].y;
-                    bw = u32x4{i8x2_bf16(lo, 0), i8x2_bf16(lo, 16), i8x2_bf16(hi, 0), i8x2_bf16(hi, 16)};
-                } else {
-                    bw = bb[j];
-                }
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    if (mb < mb_act)
+                    for (int mb = 0; mb < MA; ++mb)
                         acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, aa[mb][kh]), __builtin_bit_cast(bf16x8, bw), acc[mb][j], 0, 0,
-                            0);
-            }
-    };
+                            __builtin_bit_cast(bf16x8, aa[mb][kh]), __builtin_bit_cast(bf16x8, bw), acc[mb][j], 0,
+                            0, 0);
+                }
+        };
 
-    // rounds of U K-steps, double-buffered: the loads of round r+1 are issued before the
-    // MFMAs of round r, so every wave always has a round of weight loads in flight
-    struct Round {
-        u32x4 bb[U][NBW];
-        u32x4 aa[U][MB][KH];
-        float sc[U][NBW];  // int4 only
-    };
-    auto load_round = [&](Round& R, int s0) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int j = 0; j < NBW; ++j) R.bb[u][j] = load_w<NT>(&bptr[j][(size_t)(s0 + u) * 64]);
-        if constexpr (INT4) {
+        // rounds of U K-steps, double-buffered: the loads of round r+1 are issued before the
+        // MFMAs of round r, so every wave always has a round of weight loads in flight
+        struct Round {
+            u32x4 bb[U][NBW];
+            u32x4 aa[U][MB][KH];
+            float sc[U][NBW];  // int4 only
+        };
+        auto load_round = [&](Round& R, int s0) __attribute__((always_inline)) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
-                for (int j = 0; j < NBW; ++j) R.sc[u][j] = sptr[j][(size_t)(s0 + u) * N];
+                for (int j = 0; j < NBW; ++j) R.bb[u][j] = load_w<NT>(&bptr[j][(size_t)(s0 + u) * 64]);
+            if constexpr (INT4) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int j = 0; j < NBW; ++j) R.sc[u][j] = sptr[j][(size_t)(s0 + u) * N];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int mb = 0; mb < MA; ++mb)
+#pragma unroll
+                    for (int kh = 0; kh < KH; ++kh)
+                        R.aa[u][mb][kh] = *reinterpret_cast<const u32x4*>(aptr[mb] + (s0 + u) * KSTEP + kh * 32);
+        };
+        auto compute_round = [&](const Round& R) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) step(R.bb[u], R.aa[u], R.sc[u]);
+        };
+        // the scheduler may not move a round's loads past the MFMAs of the round before
+        // (left to itself it sinks loads to shorten register lifetimes, and the waits
+        // then drain the queue)
+        auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+        const int nround = nsteps / U;
+        if (nround > 0) {
+            Round r0, r1;
+            load_round(r0, 0);
+            int r = 0;
+            for (; r + 2 < nround; r += 2) {  // steady state: two rounds always in flight
+                fence();
+                load_round(r1, (r + 1) * U);
+                fence();
+                compute_round(r0);
+                fence();
+                load_round(r0, (r + 2) * U);
+                fence();
+                compute_round(r1);
+            }
+            fence();
+            if (nround - r == 2) {
+                load_round(r1, (r + 1) * U);
+                fence();
+                compute_round(r0);
+                compute_round(r1);
+            } else {
+                compute_round(r0);
+            }
         }
+        for (int s = nround * U; s < nsteps; ++s) {
+            u32x4 bb[NBW];
+            u32x4 aa[MB][KH];
+            float sc[NBW] = {};
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+            for (int j = 0; j < NBW; ++j) bb[j] = load_w<NT>(&bptr[j][(size_t)s * 64]);
+            if constexpr (INT4) {
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
+                for (int j = 0; j < NBW; ++j) sc[j] = sptr[j][(size_t)s * N];
+            }
+#pragma unroll
+            for (int mb = 0; mb < MA; ++mb)
 #pragma unroll
                 for (int kh = 0; kh < KH; ++kh)
-                    R.aa[u][mb][kh] = mb < mb_act
-                                          ? *reinterpret_cast<const u32x4*>(aptr[mb] + (s0 + u) * KSTEP + kh * 32)
-                                          : u32x4{0u, 0u, 0u, 0u};
-    };
-    auto compute_round = [&](const Round& R) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) step(R.bb[u], R.aa[u], R.sc[u]);
-    };
-    const int nround = nsteps / U;
-    Round r0, r1;
-    if (nround > 0) load_round(r0, 0);
-    for (int r = 0; r < nround; r += 2) {
-        if (r + 1 < nround) load_round(r1, (r + 1) * U);
-        compute_round(r0);
-        if (r + 1 < nround) {
-            if (r + 2 < nround) load_round(r0, (r + 2) * U);
-            compute_round(r1);
+                    aa[mb][kh] = *reinterpret_cast<const u32x4*>(aptr[mb] + s * KSTEP + kh * 32);
+            step(bb, aa, sc);
         }
-    }
-    int s = nround * U;
-    for (; s < nsteps; ++s) {
-        u32x4 bb[NBW];
-        u32x4 aa[MB][KH];
-        float sc[NBW] = {};
-#pragma unroll
-        for (int j = 0; j < NBW; ++j) bb[j] = load_w<NT>(&bptr[j][(size_t)s * 64]);
-        if constexpr (INT4) {
-#pragma unroll
-            for (int j = 0; j < NBW; ++j) sc[j] = sptr[j][(size_t)s * N];
-        }
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int kh = 0; kh < KH; ++kh)
-                aa[mb][kh] = mb < mb_act ? *reinterpret_cast<const u32x4*>(aptr[mb] + s * KSTEP + kh * 32)
-                                         : u32x4{0u, 0u, 0u, 0u};
-        step(bb, aa, sc);
+    };
+    // row blocks holding rows: 1 .. MB (a work item always holds at least one row)
+    if constexpr (MB == 1) {
+        kloop(std::integral_constant<int, 1>{});
+    } else if constexpr (MB == 2) {
+        if (mb_act == 1) kloop(std::integral_constant<int, 1>{});
+        else kloop(std::integral_constant<int, 2>{});
+    } else {
+        static_assert(MB == 4, "row blocks per work item");
+        if (mb_act == 1) kloop(std::integral_constant<int, 1>{});
+        else if (mb_act == 2) kloop(std::integral_constant<int, 2>{});
+        else if (mb_act == 3) kloop(std::integral_constant<int, 3>{});
+        else kloop(std::integral_constant<int, 4>{});
     }
 
     // ---- epilogue (same fragment layout as the prefill kernels)
