@@ -39,8 +39,14 @@ constexpr float kGateClampAbs = 50.0f;
 // the chosen logits, and (with kGateShared) the shared-expert sigmoid gate read
 // from router column E. wr_t is the router weight transposed to [Ec][d].
 // planes: the router weight split into three bf16 planes in fragment order (bf16 tokens only).
+// part: at least gate_mfma_workspace(T, d, E, has_shared, x_bf16) bytes (part_cap: its size,
+// checked before the launch) for the partial logits of the MFMA gate (bf16 tokens past the
+// per-token decode gate), else unused. gate_mfma_workspace_max bounds that over T <= Tmax.
 hipError_t launch_gate(const void* x, bool x_bf16, const float* wr_t, const void* planes, const float* bias, int T,
-                       int d, int E, int gflags, int k, int32_t* idx, float* w, float* gs, hipStream_t s);
+                       int d, int E, int gflags, int k, int32_t* idx, float* w, float* gs, float* part,
+                       size_t part_cap, hipStream_t s);
+size_t gate_mfma_workspace(int T, int d, int E, bool has_shared, bool x_bf16);
+size_t gate_mfma_workspace_max(int Tmax, int E, bool has_shared);
 
 // Scatter: counts, offsets and the stable by-expert permutation of the T*k routed
 // assignments, V shared virtual experts appended (each takes every token), and the

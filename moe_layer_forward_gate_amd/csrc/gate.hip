@@ -11,7 +11,9 @@
 //   - gate_rowdot (T <= 64): one workgroup per token; the 256 threads split K and
 //     take the router rows eight at a time, so every load of the token and of the
 //     router weights is in flight at once (decode: latency is what counts);
-//   - gate_mfma (T > 64, bf16 tokens): 16 tokens per workgroup on bf16 MFMA. The
+//   - gate_mfma_part + gate_mfma_finish (T > 64, bf16 tokens): 128 tokens x a K
+//     slice per workgroup on bf16 MFMA, router and token fragments staged in LDS;
+//     the slices' partial logits are added in order by the finish launch. The
 //     fp32 router weight is carried as three bf16 planes w = hi + mid + lo (an
 //     exact split: each plane takes the next 8 significant bits), and a bf16
 //     token times a bf16 plane is exact in the fp32 accumulator, so the three
@@ -218,120 +220,176 @@ __global__ __launch_bounds__(256) void gate_rowdot(const XT* __restrict__ x, con
 }
 
 // ---------------------------------------------------------------- prefill path, bf16 tokens
-// 16*TB tokens per workgroup; NW waves split K (wave v takes the K steps
-// [v*(KS/NW), (v+1)*(KS/NW)), the last wave the rest) and each takes all 16-column
-// router blocks (NB = ceil(Ec/16) <= 9) for all TB token blocks, so every router
-// fragment it loads serves TB MFMAs (the router is re-read once per workgroup: TB sets
-// how many tokens share that read). One token block takes 16 waves (routers of up to 80
-// columns), two take 8 (up to 128 columns), four and wider routers take 4: the more waves
-// split K, the fewer K steps of dependent loads each waits through, as far as registers
-// and LDS allow. A fragments come straight from the token rows, B
-// fragments from the three packed planes ([plane][NB][d/32][64] lanes x 16 B, fragment
-// order). The wave partials are added in LDS one token block at a time, in a fixed order.
-template <int NB, int TB, int NW>
-__global__ __launch_bounds__(NW * 64) void gate_mfma(const bf16_t* __restrict__ x, const u32x4* __restrict__ planes,
-                                                     const float* __restrict__ bias, int T, int d, int E, int k,
-                                                     int gflags, int32_t* __restrict__ idx, float* __restrict__ w,
-                                                     float* __restrict__ gs) {
-    static_assert(NW == 4 || NW == 8 || NW == 16, "wave count");
-    const bool has_shared = (gflags & kGateShared) != 0;
-    constexpr int LP = NB * 16 + 1;
-    constexpr int NP = NW == 16 ? 8 : 4;  // partial slots: 8 or 16 waves fold pairwise first
-    __shared__ float part[NP][16 * LP];
-    __shared__ float logits[16 * TB * LP];
-    const int t0 = blockIdx.x * 16 * TB;
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+// Two launches. gate_mfma_part: workgroup (tile of 64*TPW tokens, K slice) of four waves,
+// wave w owning the tile's token blocks w*TPW .. w*TPW+TPW-1 (16 tokens each). Every K step
+// of 32 brings the three router planes' blocks (3*NB of 1 KB, fragment order) and the
+// tile's token fragments (4*TPW blocks of 16 rows x 32 K, gathered from the token rows)
+// into LDS by LDS-DMA, four steps in flight, so each router block is read once per 64*TPW
+// tokens and shared by the four waves (a workgroup per 16 or 32 tokens, each re-reading
+// the whole router, made the router reads the gate's cost). Each wave multiplies its
+// token blocks by the three planes (smallest first) and writes the slice's partial logits
+// to part[slice][token][NC]. gate_mfma_finish: one wave per token adds the slices in order
+// and the bias, then runs the top-k.
+constexpr int kGateTPW = 2;         // token blocks per wave: 128 tokens per workgroup
+constexpr int kGateStages = 4;
+constexpr int kGateMinSteps = 4;    // K steps per slice at least (pipeline fill)
+
+__host__ __device__ __forceinline__ int gate_mfma_tiles(int T) { return (T + 64 * kGateTPW - 1) / (64 * kGateTPW); }
+// K slices of kps steps each: enough (token tile, slice) workgroups to cover the CUs, each
+// slice at least kGateMinSteps K steps (but for K under that); the count is taken from kps so
+// that every slice holds at least one step: (slices - 1) * kps < KS
+__host__ __device__ __forceinline__ int gate_mfma_kps(int T, int d) {
     const int KS = d / 32;
-    const int ks0 = wave * (KS / NW), ks1 = (wave == NW - 1) ? KS : ks0 + KS / NW;
-    const bf16_t* xr[TB];
+    const int want = (256 + gate_mfma_tiles(T) - 1) / gate_mfma_tiles(T);
+    const int most = KS / kGateMinSteps > 0 ? KS / kGateMinSteps : 1;
+    const int S = want < most ? want : most;
+    return (KS + S - 1) / S;
+}
+__host__ __device__ __forceinline__ int gate_mfma_slices(int T, int d) {
+    const int kps = gate_mfma_kps(T, d);
+    return (d / 32 + kps - 1) / kps;
+}
+
+// one 16-byte LDS-DMA load per lane: LDS[block + 16*lane] = *src (block is wave-uniform)
+__device__ __forceinline__ void gate_dma16(const void* src, u32x4* lds_block) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_block, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt <= N and lgkmcnt 0 (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8): this wave's loads but the last N have landed and its LDS reads are done
+template <int N>
+__device__ __forceinline__ void gate_wait_vm_lds() {
+    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+template <int NB>
+__global__ __launch_bounds__(512, 1) void gate_mfma_part(const bf16_t* __restrict__ x, const u32x4* __restrict__ planes,
+                                                        int T, int d, int kps, float* __restrict__ part) {
+    constexpr int NW = 8;                      // waves: token group w % 4, column half w / 4
+    constexpr int TPW = kGateTPW;
+    constexpr int NB0 = (NB + 1) / 2;          // column blocks of the first half (the second takes the rest)
+    constexpr int NBL = 3 * NB;                // router blocks per K step
+    constexpr int LB = (NBL + NW - 1) / NW;    // router block loads per wave per step
+    constexpr int ABLK = 4 * TPW;              // token blocks per stage
+    static_assert(ABLK % NW == 0, "token blocks: a whole number per wave");
+    constexpr int LA = ABLK / NW;              // token block loads per wave per step
+    constexpr int L = LA + LB;                 // LDS-DMA loads per wave per step
+    constexpr int STAGE = ABLK + NW * LB;      // 1 KB blocks per stage
+    constexpr int STAGES = kGateStages;
+    constexpr int NC = NB * 16;
+    extern __shared__ u32x4 lds[];             // [STAGES][STAGE][64 lanes]
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int tg = wave % 4, ch = wave / 4;
+    const int KS = d / 32;
+    const int ks0 = blockIdx.y * kps;
+    const int nsteps = min(KS, ks0 + kps) - ks0;
+    const int t0 = blockIdx.x * 64 * TPW;
+    // token fragment loads: wave w fills token blocks w*LA .. (block b holds tokens
+    // t0 + 16b + 0..15); lane l loads row l%16, K 8*(l/16)..+7 of the step (rows past T repeat
+    // the last token)
+    const bf16_t* asrc[LA];
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-        const int tok = min(t0 + 16 * tb + lane % 16, T - 1);  // rows past T repeat the last token (dropped)
-        xr[tb] = x + (size_t)tok * d + 8 * (lane / 16);
+    for (int i = 0; i < LA; ++i) {
+        const int tok = min(t0 + 16 * (wave * LA + i) + lane % 16, T - 1);
+        asrc[i] = x + (size_t)tok * d + (size_t)ks0 * 32 + 8 * (lane / 16);
     }
+    // router block q = wave*LB + i (plane q / NB, column block q % NB); slots past NBL repeat
+    // the last block, so every wave issues the same number of loads
     const size_t plane_stride = (size_t)NB * KS * 64;
-    f32x4 acc[TB][NB];
+    const u32x4* bsrc[LB];
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[tb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // U K-steps per round, every load of the round issued before the first MFMA
-    // (16 waves: at most 64 registers of loads in flight, the budget of four waves per SIMD;
-    // 8 waves: at most ~110, two waves per SIMD)
-    constexpr int LR = TB + 3 * NB;  // 16-byte loads per K step
-    constexpr int U = NW == 4 ? (NB * TB <= 2 ? 8 : (NB * TB <= 4 ? 4 : (NB * TB <= 12 ? 2 : 1)))
-                              : NW == 8 ? (LR <= 6 ? 4 : (LR <= 13 ? 2 : 1))
-                                        : (LR <= 4 ? 4 : (LR <= 8 ? 2 : 1));
-    auto round = [&](int ks, auto uconst) {
-        constexpr int UU = decltype(uconst)::value;
-        u32x4 av[UU][TB], bv[UU][NB][3];
-#pragma unroll
-        for (int u = 0; u < UU; ++u) {
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb) av[u][tb] = *reinterpret_cast<const u32x4*>(xr[tb] + (ks + u) * 32);
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-#pragma unroll
-                for (int pl = 0; pl < 3; ++pl) bv[u][j][pl] = planes[pl * plane_stride + ((size_t)j * KS + ks + u) * 64 + lane];
-        }
-        __builtin_amdgcn_sched_barrier(0);  // keep the whole round's loads ahead of its MFMAs
-#pragma unroll
-        for (int u = 0; u < UU; ++u)
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-                for (int j = 0; j < NB; ++j)
-#pragma unroll
-                    for (int pl = 2; pl >= 0; --pl)  // smallest plane first
-                        acc[tb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, av[u][tb]), __builtin_bit_cast(bf16x8, bv[u][j][pl]),
-                            acc[tb][j], 0, 0, 0);
-    };
-    int ks = ks0;
-    for (; ks + U <= ks1; ks += U) round(ks, std::integral_constant<int, U>{});
-    for (; ks < ks1; ++ks) round(ks, std::integral_constant<int, 1>{});
-    // lane holds column 16*j + lane%16, tokens 4*(lane/16) + i of each token block
-    const int Ec = E + (has_shared ? 1 : 0);
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-        if constexpr (NW > NP) {
-            // waves NP..2NP-1 hand their partials to waves 0..NP-1, which add them to their own
-            if (wave >= NP) {
-#pragma unroll
-                for (int j = 0; j < NB; ++j)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        part[wave - NP][(4 * (lane / 16) + i) * LP + 16 * j + lane % 16] = acc[tb][j][i];
-            }
-            __syncthreads();
-            if (wave < NP) {
-#pragma unroll
-                for (int j = 0; j < NB; ++j)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        acc[tb][j][i] += part[wave][(4 * (lane / 16) + i) * LP + 16 * j + lane % 16];
-            }
-            __syncthreads();
-        }
-        if (wave < NP) {
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) part[wave][(4 * (lane / 16) + i) * LP + 16 * j + lane % 16] = acc[tb][j][i];
-        }
-        __syncthreads();
-        for (int q = tid; q < 16 * Ec; q += NW * 64) {
-            const int r = q / Ec, col = q - r * Ec;
-            const float b = (bias && col < E) ? bias[col] : 0.0f;
-            const int o = r * LP + col;
-            float sum = (part[0][o] + part[1][o]) + (part[2][o] + part[3][o]);
-            if constexpr (NP == 8) sum += (part[4][o] + part[5][o]) + (part[6][o] + part[7][o]);
-            logits[tb * 16 * LP + o] = sum + b;
-        }
-        __syncthreads();
+    for (int i = 0; i < LB; ++i) {
+        const int q = min(wave * LB + i, NBL - 1);
+        bsrc[i] = planes + (q / NB) * plane_stride + ((size_t)(q % NB) * KS + ks0) * 64 + lane;
     }
-    for (int r = wave; r < 16 * TB; r += NW)
-        if (t0 + r < T) wave_topk_write(logits + r * LP, E, k, gflags, t0 + r, idx, w, gs);
+    auto issue = [&](int st, int stage) __attribute__((always_inline)) {
+        u32x4* dst = lds + (size_t)stage * STAGE * 64;
+#pragma unroll
+        for (int i = 0; i < LA; ++i) gate_dma16(asrc[i] + (size_t)st * 32, dst + (wave * LA + i) * 64);
+#pragma unroll
+        for (int i = 0; i < LB; ++i) gate_dma16(bsrc[i] + (size_t)st * 64, dst + (ABLK + wave * LB + i) * 64);
+    };
+    // the K loop and the output of one column half: blocks [JB, JB + JN)
+    auto run = [&](auto jb, auto jn) __attribute__((always_inline)) {
+        constexpr int JB = decltype(jb)::value, JN = decltype(jn)::value;
+        f32x4 acc[TPW][JN > 0 ? JN : 1];
+#pragma unroll
+        for (int tb = 0; tb < TPW; ++tb)
+#pragma unroll
+            for (int j = 0; j < JN; ++j) acc[tb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(min(s0, nsteps - 1), s0);
+        gate_wait_vm_lds<(STAGES - 2) * L>();
+        asm volatile("s_barrier" ::: "memory");
+        for (int st = 0; st < nsteps; ++st) {
+            // refill the stage read in the previous step (every wave passed this step's barrier
+            // after its reads); past the last step it re-loads the last step into a stage that
+            // is never read, so the wait counts stay uniform
+            issue(min(st + STAGES - 1, nsteps - 1), (st + STAGES - 1) % STAGES);
+            if constexpr (JN > 0) {
+                const u32x4* sa = lds + (size_t)(st % STAGES) * STAGE * 64;
+                const u32x4* sb = sa + ABLK * 64;
+                bf16x8 af[TPW];
+#pragma unroll
+                for (int tb = 0; tb < TPW; ++tb) af[tb] = __builtin_bit_cast(bf16x8, sa[(tg * TPW + tb) * 64 + lane]);
+#pragma unroll
+                for (int pl = 2; pl >= 0; --pl) {  // smallest plane first
+                    bf16x8 bf[JN];
+#pragma unroll
+                    for (int j = 0; j < JN; ++j) bf[j] = __builtin_bit_cast(bf16x8, sb[(pl * NB + JB + j) * 64 + lane]);
+#pragma unroll
+                    for (int tb = 0; tb < TPW; ++tb)
+#pragma unroll
+                        for (int j = 0; j < JN; ++j)
+                            acc[tb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[tb], bf[j], acc[tb][j], 0, 0, 0);
+                }
+            }
+            gate_wait_vm_lds<(STAGES - 2) * L>();  // step st+1 has landed (this wave's loads)
+            asm volatile("s_barrier" ::: "memory");  // ... for every wave; stage st is free
+        }
+        gate_wait_vm_lds<0>();  // no LDS-DMA write may outlive the workgroup
+        // lane holds column 16*j + lane%16, tokens 4*(lane/16) + i of each block
+        float* out = part + ((size_t)blockIdx.y * T) * NC;
+#pragma unroll
+        for (int tb = 0; tb < TPW; ++tb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = t0 + 16 * (tg * TPW + tb) + 4 * (lane / 16) + i;
+                if (t < T)
+#pragma unroll
+                    for (int j = 0; j < JN; ++j) out[(size_t)t * NC + 16 * (JB + j) + lane % 16] = acc[tb][j][i];
+            }
+    };
+    if (ch == 0) run(std::integral_constant<int, 0>{}, std::integral_constant<int, NB0>{});
+    else run(std::integral_constant<int, NB0>{}, std::integral_constant<int, NB - NB0>{});
+}
+
+// One wave per token: logits = the slices' partial sums added in slice order, + bias.
+__global__ __launch_bounds__(256) void gate_mfma_finish(const float* __restrict__ part, int S, int NC, int T, int E,
+                                                       int Ec, const float* __restrict__ bias, int k, int gflags,
+                                                       int32_t* __restrict__ idx, float* __restrict__ w,
+                                                       float* __restrict__ gs) {
+    __shared__ float logits[4][kMaxExperts + 16];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int t = blockIdx.x * 4 + wave;
+    if (t < T) {
+        for (int c = lane; c < Ec; c += kWave) {
+            // eight slices' loads in flight at a time, added in slice order
+            const float* p = part + (size_t)t * NC + c;
+            float v = 0.0f;
+            for (int s0 = 0; s0 < S; s0 += 8) {
+                float u[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) u[i] = s0 + i < S ? p[(size_t)(s0 + i) * T * NC] : 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v += u[i];
+            }
+            logits[wave][c] = v + ((bias && c < E) ? bias[c] : 0.0f);
+        }
+    }
+    __syncthreads();
+    if (t < T) wave_topk_write(logits[wave], E, k, gflags, t, idx, w, gs);
 }
 
 // ---------------------------------------------------------------- prefill path, fp32 tokens
@@ -653,55 +711,59 @@ __global__ __launch_bounds__(1024) void gate_finish(const float* __restrict__ pa
     }
 }
 
-// largest router widths (16-column blocks) the 16-wave gate (one token block) and the
-// 8-wave gate (two token blocks) take: past them their loads and accumulators no longer
-// fit the registers of four and two waves per SIMD without spills
-constexpr int kGate16MaxNB = 5;
-constexpr int kGate8MaxNB = 8;
-
-template <int TB, int NW>
-hipError_t launch_gate_mfma_tb(int NB, const bf16_t* x, const u32x4* planes, const float* bias, int T, int d, int E,
-                               int k, int gflags, int32_t* idx, float* w, float* gs, hipStream_t s) {
-    dim3 grid((T + 16 * TB - 1) / (16 * TB));
-    switch (NB) {
-#define GATE_MFMA_CASE(J)                                                                                       \
-    case J:                                                                                                     \
-        if constexpr ((NW != 16 || J <= kGate16MaxNB) && (NW != 8 || J <= kGate8MaxNB)) {                      \
-            hipLaunchKernelGGL((gate_mfma<J, TB, NW>), grid, dim3(NW * 64), 0, s, x, planes, bias, T, d, E, k,   \
-                               gflags, idx, w, gs);                                                             \
-            break;                                                                                              \
-        } else {                                                                                                \
-            return hipErrorInvalidValue;                                                                        \
-        }
-        GATE_MFMA_CASE(1) GATE_MFMA_CASE(2) GATE_MFMA_CASE(3) GATE_MFMA_CASE(4) GATE_MFMA_CASE(5)
-        GATE_MFMA_CASE(6) GATE_MFMA_CASE(7) GATE_MFMA_CASE(8) GATE_MFMA_CASE(9)
-#undef GATE_MFMA_CASE
-        default:
-            return hipErrorInvalidValue;
+template <int NB>
+hipError_t launch_gate_mfma_nb(const bf16_t* x, const u32x4* planes, const float* bias, int T, int d, int E,
+                               int k, int gflags, int32_t* idx, float* w, float* gs, float* part, size_t part_cap,
+                               hipStream_t s) {
+    constexpr int LB = (3 * NB + 7) / 8;  // as in the kernel (8 waves)
+    constexpr size_t lds_bytes = (size_t)kGateStages * (4 * kGateTPW + 8 * LB) * 1024;
+    static_assert(lds_bytes <= 160 * 1024, "LDS");
+    auto kern = gate_mfma_part<NB>;
+    static bool attr_set = false;  // one-time opt-in above the default dynamic LDS limit
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)lds_bytes);
+        if (e != hipSuccess) return e;
+        attr_set = true;
     }
+    const int S = gate_mfma_slices(T, d), kps = gate_mfma_kps(T, d);
+    if (d % 32 || (S - 1) * kps >= d / 32) return hipErrorInvalidValue;
+    if ((size_t)S * T * NB * 16 * sizeof(float) > part_cap) return hipErrorInvalidValue;  // partial logits fit
+    hipLaunchKernelGGL(kern, dim3(gate_mfma_tiles(T), S), dim3(512), lds_bytes, s, x, planes, T, d, kps, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const bool has_shared = (gflags & kGateShared) != 0;
+    hipLaunchKernelGGL(gate_mfma_finish, dim3((T + 3) / 4), dim3(256), 0, s, (const float*)part, S, NB * 16, T, E,
+                       E + (has_shared ? 1 : 0), bias, k, gflags, idx, w, gs);
     return hipGetLastError();
 }
 
-hipError_t launch_gate_mfma_nb(int TB, int NB, const bf16_t* x, const u32x4* planes, const float* bias, int T, int d,
-                               int E, int k, int gflags, int32_t* idx, float* w, float* gs, hipStream_t s) {
-    if (TB == 4) return launch_gate_mfma_tb<4, 4>(NB, x, planes, bias, T, d, E, k, gflags, idx, w, gs, s);
-    if (TB == 2 && NB <= kGate8MaxNB) return launch_gate_mfma_tb<2, 8>(NB, x, planes, bias, T, d, E, k, gflags, idx, w, gs, s);
-    if (TB == 2) return launch_gate_mfma_tb<2, 4>(NB, x, planes, bias, T, d, E, k, gflags, idx, w, gs, s);
-    // one token block per workgroup: fewer than 512 workgroups take 16 waves each (every
-    // wave keeps at least one K step)
-    if (T < 16 * 512 && NB <= kGate16MaxNB && d / 32 >= 16)
-        return launch_gate_mfma_tb<1, 16>(NB, x, planes, bias, T, d, E, k, gflags, idx, w, gs, s);
-    return launch_gate_mfma_tb<1, 4>(NB, x, planes, bias, T, d, E, k, gflags, idx, w, gs, s);
+hipError_t launch_gate_mfma(int NB, const bf16_t* x, const u32x4* planes, const float* bias, int T, int d, int E,
+                            int k, int gflags, int32_t* idx, float* w, float* gs, float* part, size_t part_cap,
+                            hipStream_t s) {
+    switch (NB) {
+#define GATE_MFMA_CASE(J) \
+    case J: return launch_gate_mfma_nb<J>(x, planes, bias, T, d, E, k, gflags, idx, w, gs, part, part_cap, s);
+        GATE_MFMA_CASE(1) GATE_MFMA_CASE(2) GATE_MFMA_CASE(3) GATE_MFMA_CASE(4) GATE_MFMA_CASE(5)
+        GATE_MFMA_CASE(6) GATE_MFMA_CASE(7) GATE_MFMA_CASE(8) GATE_MFMA_CASE(9)
+#undef GATE_MFMA_CASE
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// per-token dots for decode batches, but routers wider than 16 columns with bf16 tokens
+// past kGateSplitMaxT tokens, which the MFMA path serves faster
+bool use_rowdot(int T, int d, int Ec, bool has_planes) {
+    return T <= 64 && d <= 2048 * kRowXC && (Ec <= 16 || !has_planes || T <= kGateSplitMaxT);
 }
 
 template <typename XT>
 hipError_t launch_gate_t(const XT* x, const float* wr_t, const u32x4* planes, const float* bias, int T, int d, int E,
-                         int gflags, int k, int32_t* idx, float* w, float* gs, hipStream_t s) {
+                         int gflags, int k, int32_t* idx, float* w, float* gs, float* part, size_t part_cap,
+                         hipStream_t s) {
     const bool has_shared = (gflags & kGateShared) != 0;
     const int Ec = E + (has_shared ? 1 : 0);
-    // per-token dots for decode batches, but routers wider than 16 columns with bf16 tokens
-    // past kGateSplitMaxT tokens, which the MFMA path below serves faster
-    if (T <= 64 && d <= 2048 * kRowXC && (Ec <= 16 || planes == nullptr || T <= kGateSplitMaxT)) {
+    if (use_rowdot(T, d, Ec, planes != nullptr)) {
         switch ((d + 2047) / 2048) {
 #define ROWDOT_CASE(C)                                                                                            \
     case C:                                                                                                       \
@@ -713,15 +775,10 @@ hipError_t launch_gate_t(const XT* x, const float* wr_t, const u32x4* planes, co
             default:
                 return hipErrorInvalidValue;
         }
-    } else if (planes != nullptr && (d / 32) >= 4) {
-        // token blocks per workgroup: as many as keep >= 256 workgroups (up to 4)
-#ifdef MOE_GATE_TB
-        const int TB = MOE_GATE_TB;
-#else
-        const int TB = T >= 16 * 4 * 256 ? 4 : (T >= 16 * 2 * 256 ? 2 : 1);
-#endif
-        return launch_gate_mfma_nb(TB, (Ec + 15) / 16, (const bf16_t*)x, planes, bias, T, d, E, k, gflags, idx, w,
-                                   gs, s);
+    } else if (planes != nullptr) {
+        if (part == nullptr) return hipErrorInvalidValue;
+        return launch_gate_mfma((Ec + 15) / 16, (const bf16_t*)x, planes, bias, T, d, E, k, gflags, idx, w, gs, part,
+                                part_cap, s);
     } else {
         const int EJ = (Ec + 15) / 16;
         dim3 grid((T + kTB - 1) / kTB);
@@ -790,12 +847,26 @@ hipError_t launch_gate_scatter_small(const void* x, bool x_bf16, const float* wr
     return hipGetLastError();
 }
 
+size_t gate_mfma_workspace(int T, int d, int E, bool has_shared, bool x_bf16) {
+    const int Ec = E + (has_shared ? 1 : 0);
+    if (T <= 0 || !x_bf16 || use_rowdot(T, d, Ec, true)) return 0;
+    return (size_t)gate_mfma_slices(T, d) * T * ((Ec + 15) / 16 * 16) * sizeof(float);
+}
+
+size_t gate_mfma_workspace_max(int Tmax, int E, bool has_shared) {
+    // slices <= ceil(256 / tiles) <= 256 / tiles + 1 and T <= tiles * (tokens per tile), so
+    // slices * T <= 256 * (tokens per tile) + T
+    const int Ec = E + (has_shared ? 1 : 0);
+    return ((size_t)256 * 64 * kGateTPW + (size_t)Tmax) * ((Ec + 15) / 16 * 16) * sizeof(float);
+}
+
 hipError_t launch_gate(const void* x, bool x_bf16, const float* wr_t, const void* planes, const float* bias, int T,
-                       int d, int E, int gflags, int k, int32_t* idx, float* w, float* gs, hipStream_t s) {
+                       int d, int E, int gflags, int k, int32_t* idx, float* w, float* gs, float* part,
+                       size_t part_cap, hipStream_t s) {
     if (x_bf16)
         return launch_gate_t<bf16_t>((const bf16_t*)x, wr_t, (const u32x4*)planes, bias, T, d, E, gflags, k, idx, w,
-                                     gs, s);
-    return launch_gate_t<float>((const float*)x, wr_t, nullptr, bias, T, d, E, gflags, k, idx, w, gs, s);
+                                     gs, part, part_cap, s);
+    return launch_gate_t<float>((const float*)x, wr_t, nullptr, bias, T, d, E, gflags, k, idx, w, gs, nullptr, 0, s);
 }
 
 }  // namespace moe

@@ -52,7 +52,8 @@ struct Work {
     float* gs = nullptr;
     int32_t* ridx = nullptr;  // a caller's routing, checked (moe_forward_routed)
     float* rw = nullptr;
-    float* gate_part = nullptr;  // partial router dots of the split decode gate
+    float* gate_part = nullptr;  // partial router dots of the split decode gate or the MFMA gate
+    size_t gate_part_bytes = 0;
     int32_t* scatter_work = nullptr;  // chunk counts and ranks of the multi-workgroup scatter
     bf16_t* xp = nullptr;  // tiled up operand (bf16/int8 experts)
     void* h = nullptr;
@@ -204,9 +205,13 @@ int create_impl(const moe_desc* desc, const moe_weights* w, moe_layer* L) {
     if ((rc = dev_alloc(&ws.gs, T * 4))) return rc;
     if ((rc = dev_alloc(&ws.ridx, T * d.top_k * 4))) return rc;
     if ((rc = dev_alloc(&ws.rw, T * d.top_k * 4))) return rc;
-    if ((rc = dev_alloc(&ws.gate_part, gate_split_workspace((int)std::min(T, (size_t)64), d.d_model, L->E,
-                                                             d.shared_d_ff > 0))))
-        return rc;
+    {
+        // the split decode gate's partial dots, or the MFMA gate's partial logits
+        const size_t split = gate_split_workspace((int)std::min(T, (size_t)64), d.d_model, L->E, d.shared_d_ff > 0);
+        const size_t mfma = f32 ? 0 : gate_mfma_workspace_max((int)T, L->E, d.shared_d_ff > 0);
+        ws.gate_part_bytes = std::max(split, mfma);
+        if ((rc = dev_alloc(&ws.gate_part, ws.gate_part_bytes))) return rc;
+    }
     if ((rc = dev_alloc(&ws.scatter_work, scatter_wide_workspace((int)(T * d.top_k), L->E)))) return rc;
     // the tiled GEMMs work on padded rows: at most P + (bm - 1) + Et*bm of them for bm <= 256
     const size_t R = P + (size_t)256 * (Et + 1);
@@ -426,7 +431,13 @@ size_t carve_work(const moe_layer* L, const Plan& pl, int T, char* base, Work* W
     w.tile_start = (int32_t*)take((Et + 1) * 4);
     w.sorted_c = (int32_t*)take(P * 4);
     w.gs = (float*)take((size_t)T * 4);
-    if (split_gate(L, T)) w.gate_part = (float*)take(gate_split_workspace(T, d.d_model, L->E, L->V > 0));
+    if (split_gate(L, T)) {
+        w.gate_part_bytes = gate_split_workspace(T, d.d_model, L->E, L->V > 0);
+        w.gate_part = (float*)take(w.gate_part_bytes);
+    } else if (const size_t gm = gate_mfma_workspace(T, d.d_model, L->E, L->V > 0, !f32)) {
+        w.gate_part_bytes = gm;
+        w.gate_part = (float*)take(gm);
+    }
     if (T * d.top_k > kScatterWideMin) w.scatter_work = (int32_t*)take(scatter_wide_workspace(T * d.top_k, L->E));
     if (!f32 && !pl.streaming) w.xp = (bf16_t*)take(tiled_rows * dm * 2);
     w.h = take((f32 || pl.streaming ? P : tiled_rows) * F * (f32 ? 4 : 2));
@@ -537,7 +548,7 @@ int run_forward(moe_layer* L, const Work& W, const void* x, int32_t T, void* y, 
         if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
     } else {
         HIP_TRY(launch_gate(x, !f32, L->wr_t, L->wr_planes, L->bias, T, d.d_model, L->E, gflags, k, r->topk_idx,
-                            r->topk_w, gs, s));
+                            r->topk_w, gs, W.gate_part, W.gate_part_bytes, s));
         if (prof) HIP_TRY(hipEventRecord(L->ev[1], s));
         if ((rc = run_scatter(L, W, r->topk_idx, T, pl, so, s))) return rc;
     }
