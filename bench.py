@@ -237,7 +237,7 @@ def summarize(cfg, res):
         rf = dict(bound="mfma", achieved=up["flops"] / (up_ms * 1e-3) / 1e12, peak=MFMA_BF16_PEAK_TFLOPS,
                   unit="TFLOP/s")
     rf["frac"] = rf["achieved"] / rf["peak"]
-    stream_max = 32 if cfg.expert_dtype in ("i8", "i4") else 64  # the library's launch plan
+    stream_max = 32 if cfg.expert_dtype == "i8" else 64  # the library's launch plan
     kern = ("expert_stream" if T <= stream_max else "expert_gemm") if cfg.expert_dtype != "f32" else "expert_f32"
     rf["kernel"] = f"{kern}<up>"
     rf["traffic"] = lookup_traffic(kern, f"up|{cfg.name}|T={T}") if kern in KERNEL_SOURCES else None

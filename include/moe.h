@@ -84,9 +84,9 @@ typedef enum moe_gate_weighting {
  * experts d_model % 128 == 0 and d_ff % 64 == 0; for I4 experts d_model % 128
  * == 0 and d_ff % 128 == 0; for F32 experts d_model % 64 == 0 and d_ff % 64 ==
  * 0. shared_d_ff > 0 adds a shared expert (BF16 experts only) and must be a
- * multiple of d_ff. Which kernels run is chosen per call from T: BF16 weights
- * stream from HBM for T <= 64 and run on the LDS-tiled MFMA GEMMs above; I8 and
- * I4 weights stream for T <= 32 and run tiled above (F32 experts always run on
+ * multiple of d_ff. Which kernels run is chosen per call from T: BF16 and I4
+ * weights stream from HBM for T <= 64 and run on the LDS-tiled MFMA GEMMs above;
+ * I8 weights stream for T <= 32 and run tiled above (F32 experts always run on
  * the fp32 kernels). */
 typedef struct moe_desc {
     int32_t d_model;
@@ -217,7 +217,7 @@ MOE_API int moe_forward_routed(moe_layer* layer, const void* x, int32_t T, const
  * device array of MOE_STATIC_SCRATCH_BYTES instead of the layer's own workspace; the call
  * allocates nothing and launches kernels only (no memset, copy or host wait). Arguments,
  * statuses and ownership as moe_forward, plus: EINVAL when the batch needs more scratch
- * than the array holds (decode batches fit: T <= 64 for BF16 experts, T <= 32 for I8/I4,
+ * than the array holds (decode batches fit: T <= 64 for BF16 and I4 experts, T <= 32 for I8,
  * on layers up to d_model 8192 and d_ff 16384; large prefill batches do not -- use
  * moe_forward), with the needed size in moe_last_error(). Every layer and every call on
  * one device shares that device's array, whatever the stream: calls that overlap in time

@@ -308,11 +308,10 @@ Plan make_plan(const moe_layer* L, int T) {
     const bool i8 = d.expert_dtype == MOE_I8;
     const bool i4 = d.expert_dtype == MOE_I4;
     const int k = d.top_k;
-    // quantised weights at 33-64 tokens: the tiled kernels are faster (8-expert 6144 x 16384
-    // layer, T = 64: int4 0.37 against 0.41 ms, int8 0.51 against 0.54 ms; T = 32: int4 0.31
-    // against 0.29 ms streaming, int8 equal); bf16 weights stream up to 64 (T = 64: 0.50
-    // against 0.58 ms tiled)
-    const bool streaming = !f32 && T <= ((i4 || i8) ? kStreamMaxT / 2 : kStreamMaxT);
+    // int8 weights at 33-64 tokens: the tiled kernels are faster (8-expert 6144 x 16384 layer,
+    // T = 64: 0.48 against 0.50 ms streaming); int4 and bf16 weights stream up to 64 (int4
+    // T = 64: 0.33 against 0.35 ms tiled; bf16 T = 64: 0.50 against 0.58 ms tiled)
+    const bool streaming = !f32 && T <= (i8 ? kStreamMaxT / 2 : kStreamMaxT);
     int bm, ksplit = 1;
     bool weights_once = true;
     if (f32) {

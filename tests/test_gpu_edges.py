@@ -182,3 +182,11 @@ def test_gate_raw_weighting(name, kw, Ts, clamp):
         if clamp:
             assert (w == 50.0).any()
     lay.close()
+
+
+@pytest.mark.parametrize("d,T", [(384, 65), (384, 300), (640, 129), (1664, 1000), (256, 7000)])
+def test_mfma_gate_slices(d, T):
+    # the MFMA gate's (128-token tile, K slice) grid: K of 12, 20, 52 and 8 steps of 32 split
+    # into slices of unequal counts, ragged last token tiles, and a shared gate column
+    cfg = synth.get_config("shared_fine_bf16", d_model=d, d_ff=128, n_experts=24, top_k=3, shared_d_ff=256)
+    _run(cfg, [T])

@@ -67,12 +67,13 @@ def test_int8_reduced():
 
 
 def test_int4_reduced():
-    # int4 group-wise weights: the streaming kernels up to T = 32 (row tiles of 16 and, with
-    # four experts, 32 rows), the LDS-tiled MFMA kernels past it (64-row tiles, several per
-    # expert, ragged last tiles holding one or two 16-row blocks per wave)
+    # int4 group-wise weights: the streaming kernels up to T = 64 (row tiles of 16 and 32 rows,
+    # with four experts several 32-row tiles per expert), the LDS-tiled MFMA kernels past it
+    # (64-row tiles, several per expert, ragged last tiles holding one or two 16-row blocks
+    # per wave)
     cfg = synth.get_config("int4_mixtral22b", d_model=512, d_ff=1024)
     _run(cfg, [1, 2, 16, 32, 33, 40, 64, 65, 256, 1000])
-    _run(synth.get_config("int4_mixtral22b", d_model=512, d_ff=1024, n_experts=4), [20, 32])
+    _run(synth.get_config("int4_mixtral22b", d_model=512, d_ff=1024, n_experts=4), [20, 32, 64])
 
 
 def test_quantised_partial_column_tiles():
