@@ -20,7 +20,9 @@ __device__ __forceinline__ float4 load_once(const float4* p) {
     return make_float4(t[0], t[1], t[2], t[3]);
 }
 
-template <bool BF16>
+// U rows are loaded at once (rows past kt are not loaded and not added), then added in
+// order, so every batch is one round trip to memory.
+template <bool BF16, int U>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ow, int T, int kt, int stride,
                                                       int d, void* __restrict__ y) {
     const int d4 = d / 4;
@@ -28,21 +30,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     if (i >= (size_t)T * d4) return;
     const int t = (int)(i / d4), c4 = (int)(i - (size_t)t * d4);
     const float4* src = reinterpret_cast<const float4*>(ow + (size_t)t * stride * d) + c4;
-    // rows are added in order 0, 1, 2, ...; loads go out 8 rows at a time
+    // rows are added in order 0, 1, 2, ...
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    int j = 0;
-    for (; j + 8 <= kt; j += 8) {
-        float4 v[8];
+    for (int j = 0; j < kt; j += U) {
+        float4 v[U];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = load_once(&src[(size_t)(j + u) * d4]);
+        for (int u = 0; u < U; ++u)
+            if (j + u < kt) v[u] = load_once(&src[(size_t)(j + u) * d4]);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
+        for (int u = 0; u < U; ++u) {
+            if (j + u < kt) {
+                s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
+            }
         }
-    }
-    for (; j < kt; ++j) {
-        const float4 v = load_once(&src[(size_t)j * d4]);
-        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
     }
     if (BF16) {
         uint2 o;
@@ -60,11 +60,22 @@ hipError_t launch_combine(const float* ow, int T, int nrow, int stride, int d, v
                           hipStream_t s) {
     if (nrow > stride) return hipErrorInvalidValue;
     const size_t n = (size_t)T * (d / 4);
-    dim3 grid((unsigned)((n + 255) / 256));
-    if (y_bf16)
-        hipLaunchKernelGGL((combine_kernel<true>), grid, dim3(256), 0, s, ow, T, nrow, stride, d, y);
-    else
-        hipLaunchKernelGGL((combine_kernel<false>), grid, dim3(256), 0, s, ow, T, nrow, stride, d, y);
+    // decode batches (under 2^18 threads): every row of a thread in one batch of up to 32
+    // loads, on 64-thread workgroups so the few thousand threads spread over many CUs;
+    // larger batches: 256-thread workgroups, 8 rows a batch (enough threads hide the latency)
+    if (n < (1u << 18)) {
+        dim3 grid((unsigned)((n + 63) / 64));
+        if (y_bf16)
+            hipLaunchKernelGGL((combine_kernel<true, 32>), grid, dim3(64), 0, s, ow, T, nrow, stride, d, y);
+        else
+            hipLaunchKernelGGL((combine_kernel<false, 32>), grid, dim3(64), 0, s, ow, T, nrow, stride, d, y);
+    } else {
+        dim3 grid((unsigned)((n + 255) / 256));
+        if (y_bf16)
+            hipLaunchKernelGGL((combine_kernel<true, 8>), grid, dim3(256), 0, s, ow, T, nrow, stride, d, y);
+        else
+            hipLaunchKernelGGL((combine_kernel<false, 8>), grid, dim3(256), 0, s, ow, T, nrow, stride, d, y);
+    }
     return hipGetLastError();
 }
 

@@ -423,7 +423,10 @@ __global__ __launch_bounds__(256) void gate_tiled(const XT* __restrict__ x, cons
 // one round trip instead of two or three), each wave folds its 64 partial dots with a
 // butterfly, the 16 wave partials are added in LDS in a fixed order, one wave per token
 // takes the top-k, and the same workgroup then runs the scatter ([0539edu §2.2], the
-// two stages back to back with no launch between them).
+// two stages back to back with no launch between them). All loads of one CU pass its
+// one address unit, so threads past d and tokens past T load nothing; the top-k results
+// stay in LDS until the scatter starts, when the other waves store them, so no wait of
+// the scatter's wave covers a store.
 template <typename XT>
 struct SmallGate {
     static constexpr int T = 4;  // tokens (register budget at 1024 threads)
@@ -442,7 +445,9 @@ __global__ __launch_bounds__(1024) void gate_scatter_small(const XT* __restrict_
     __shared__ float part[NW][MT * EC];
     __shared__ float logits[MT][EC + 1];
     __shared__ ScatterWaveSmem sm;
-    __shared__ int32_t ids[MT * kMaxTopK];  // the top-k ids again, for the scatter to read from LDS
+    __shared__ int32_t s_idx[MT * kMaxTopK];  // the top-k results, stored by the other waves
+    __shared__ float s_w[MT * kMaxTopK];
+    __shared__ float s_gs[MT];
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const bool has = tid * 8 < d;
     const int kc = has ? tid * 8 : 0;
@@ -453,18 +458,25 @@ __global__ __launch_bounds__(1024) void gate_scatter_small(const XT* __restrict_
     auto load_w = [&](int e0) {
 #pragma unroll
         for (int g = 0; g < EG; ++g) {
-            const u32x4* p = reinterpret_cast<const u32x4*>(wr_t + (size_t)(e0 + g < Ec ? e0 + g : 0) * d + kc);
-            wq[g][0] = p[0];
-            wq[g][1] = p[1];
+            wq[g][0] = wq[g][1] = u32x4{0u, 0u, 0u, 0u};
+            if (has && e0 + g < Ec) {
+                const u32x4* p = reinterpret_cast<const u32x4*>(wr_t + (size_t)(e0 + g) * d + kc);
+                wq[g][0] = p[0];
+                wq[g][1] = p[1];
+            }
         }
     };
     load_w(0);
     u32x4 xq[MT][XQ];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(x + (size_t)(t < T ? t : 0) * d + kc);
 #pragma unroll
-        for (int q = 0; q < XQ; ++q) xq[t][q] = p[q];
+        for (int q = 0; q < XQ; ++q) xq[t][q] = u32x4{0u, 0u, 0u, 0u};
+        if (has && t < T) {
+            const u32x4* p = reinterpret_cast<const u32x4*>(x + (size_t)t * d + kc);
+#pragma unroll
+            for (int q = 0; q < XQ; ++q) xq[t][q] = p[q];
+        }
     }
     for (int e0 = 0; e0 < Ec; e0 += EG) {
         if (e0 > 0) load_w(e0);
@@ -510,9 +522,18 @@ __global__ __launch_bounds__(1024) void gate_scatter_small(const XT* __restrict_
         }
     }
     __syncthreads();
-    if (wave < T) wave_topk_write(logits[wave], E, k, gflags, wave, idx, w, gs, ids);
+    if (wave < T) wave_topk_write(logits[wave], E, k, gflags, wave, s_idx, s_w, s_gs);
     __syncthreads();
-    if (wave == 0) scatter_wave(ids, T, E, k, V, bm, o, sm);  // at most 4 x 16 assignments
+    if (wave == 0) {
+        scatter_wave(s_idx, T, E, k, V, bm, o, sm);  // at most 4 x 16 assignments
+    } else {
+        const int i0 = tid - kWave, n = blockDim.x - kWave;
+        for (int i = i0; i < T * k; i += n) {
+            idx[i] = s_idx[i];
+            w[i] = s_w[i];
+        }
+        if ((gflags & kGateShared) && i0 < T) gs[i0] = s_gs[i0];
+    }
 }
 
 // ---------------------------------------------------------------- decode batches, split

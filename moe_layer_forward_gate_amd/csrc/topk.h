@@ -15,15 +15,39 @@ __device__ __forceinline__ uint64_t topk_key(float v, int e) {
     return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 
+// One DPP move of a 64-bit value (both halves with the same lane pattern).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Wave-wide maximum, the same in every lane. Inside each row of 16 lanes four DPP steps
+// pair every lane with one of each other group (quad swaps at distance 1 and 2, then the
+// mirror inside each half row and inside the row), so every lane ends with its row's
+// maximum; the four row maxima are then read into scalar registers and compared there.
+// All 64 lanes must be active. (DPP moves stay in the vector unit; a shuffle goes
+// through the LDS crossbar and waits on it at each of its steps.)
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    uint64_t o;
+    o = dpp_u64<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+    v = o > v ? o : v;
+    o = dpp_u64<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+    v = o > v ? o : v;
+    o = dpp_u64<0x141>(v);  // row_half_mirror
+    v = o > v ? o : v;
+    o = dpp_u64<0x140>(v);  // row_mirror
+    v = o > v ? o : v;
+    uint64_t m = 0;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        uint32_t lo = __shfl_xor((uint32_t)v, off, kWave);
-        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, kWave);
-        uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * r);
+        const uint64_t x = ((uint64_t)hi << 32) | lo;
+        m = x > m ? x : m;
     }
-    return v;
+    return m;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -86,10 +110,13 @@ __device__ void wave_topk_write(const float* logits, int E, int k, int gflags, i
         if (k1 == m) k1 = 0ull;
         if (lane == j) my_e = e;
     }
-    // softmax over the chosen logits, relative to slot 0 (the maximum)
-    float l0 = __shfl(my_e >= 0 ? logit(my_e) : 0.0f, 0, kWave);
-    float ex = lane < k ? expf(logit(my_e) - l0) : 0.0f;
-    float sum = wave_sum(ex);
+    // softmax over the chosen logits, relative to slot 0 (the maximum); the k terms are
+    // added in slot order
+    const float mine = my_e >= 0 ? logit(my_e) : 0.0f;
+    const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), 0));
+    const float ex = lane < k ? expf(mine - l0) : 0.0f;
+    float sum = 0.0f;
+    for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
     if (lane < k) {
         idx[(size_t)t * k + lane] = my_e;
         w[(size_t)t * k + lane] = raw ? logit(my_e) : ex / sum;
