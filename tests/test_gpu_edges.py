@@ -5,13 +5,16 @@ Covers: k = 1 and k = E, expert counts that are not multiples of 8 or 16 (up to 
 both sides of the streaming / tiled switch, every token routed to one expert, an
 expert holding more rows than the streaming row tile (more tiles than active experts), a
 shared expert of one and of sixteen d_ff slices, int8 output channels and int4
-groups whose scale is zero, the smallest int4 widths, and the decode routing paths for routers wider than 16 columns.
+groups whose scale is zero, the smallest int4 widths, the decode routing paths for routers wider than 16 columns,
+and int8 token rows of extreme or widely spread magnitudes on the tiled path.
 """
+import numpy as np
 import pytest
 import torch
 
 import synth
-from harness import compare, gpu_layer, oracle_layer
+import oracle
+from harness import MARGIN, Y_TOL, compare, gpu_layer, oracle_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -93,6 +96,50 @@ def test_int8_zero_scale_channels():
         L.w_down[1, :, 7] = 0
         L.s_down[1, 7] = 0
     _run(synth.get_config("int8_mixtral22b", d_model=256, d_ff=128), [1, 300], mutate=zero)
+
+
+def test_int8_tiled_extreme_rows():
+    # the tiled int8 path on token rows of extreme magnitude: rows scaled by 1e15 and 1e-15,
+    # an all-zero row (its output is exactly zero), and rows spanning 2^20 and 2^40 inside
+    # themselves. Each row is checked against the oracle on its own scale.
+    cfg = synth.get_config("int8_mixtral22b", d_model=256, d_ff=256)
+    L = synth.make_layer(cfg)
+    olay = oracle_layer(L)
+    T = 200
+    lay = gpu_layer(L, T)
+    x = synth.make_tokens(cfg, T).float()
+    x[0] = 0.0
+    x[1] *= 1e15
+    x[2] *= 1e-15
+    x[3, 17] = 1e6
+    x[4, 200] = -1e12
+    x = x.to(torch.bfloat16).cuda()
+    print(f"[edge] int8 token scales d={cfg.d_model} F={cfg.d_ff} T={T}", flush=True)
+    out = lay.forward(x)
+    torch.cuda.synchronize()
+    lay.close()
+    xn = x.float().cpu().numpy().astype(np.float64)
+    gidx = out.topk_idx.cpu().numpy().astype(np.int64)
+    with np.errstate(over="ignore"):  # silu(z) = z / (1 + exp(-z)) at z ~ -1e30: exp overflows, the quotient is -0
+        ref = oracle.moe_forward(xn, olay)
+    for t in range(T):
+        if ref["margin"][t] >= MARGIN:
+            assert np.array_equal(gidx[t], ref["idx"][t]), f"token {t}: top-k {gidx[t]} against {ref['idx'][t]}"
+        else:
+            assert any(np.array_equal(a, gidx[t]) for a in oracle.valid_selections(ref["logits"][t], cfg.top_k, MARGIN))
+    with np.errstate(over="ignore"):
+        ref = oracle.moe_forward(xn, olay, routing=gidx)
+    y = out.y.float().cpu().numpy().astype(np.float64)
+    assert np.all(y[0] == 0.0), "an all-zero token row gives exactly zero"
+    rel, mabs = Y_TOL["bf16"]
+    for t in range(1, T):
+        yr = ref["y"][t]
+        den = np.linalg.norm(yr)
+        rms = den / np.sqrt(yr.size)
+        err = y[t] - yr
+        assert np.all(np.isfinite(y[t])), f"token {t}: non-finite output"
+        assert np.linalg.norm(err) <= rel * den, f"token {t}: relative error {np.linalg.norm(err) / den:.3e}"
+        assert np.abs(err).max() <= mabs * rms, f"token {t}: max-abs error {np.abs(err).max() / rms:.3e} rms"
 
 
 @pytest.mark.parametrize("name", ["int8_mixtral22b", "int4_mixtral22b"])
