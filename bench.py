@@ -10,7 +10,9 @@ events off), the roofline of its dominant kernel (the expert up-projection GEMM;
 its average duration comes from libmoe's per-stage HIP events, recorded on the
 stream the kernels run on over a second pass of the same steps), the same
 figures for every other workload (each layer shape at each of its token counts,
-under "workloads"), and the CPU oracle timed on a bounded sample.
+under "workloads"), decode layers on 1 and 8 concurrent streams ("decode_concurrency"),
+eager against HIP-graph-replayed decode steps ("hip_graph_replay"), and the CPU oracle
+timed on a bounded sample.
 
   python bench.py [--steps K] [--warmup W] [--config NAME] [--tokens T] [--only-main]
 """
@@ -27,6 +29,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+# extra decode measurements of the default run: layers on concurrent streams, and HIP graph replay
+CONCURRENCY_CASES = (("mixtral_bf16", 1), ("int8_mixtral22b", 1))
+GRAPH_CASE = ("mixtral_bf16", 1)
 
 # HBM traffic per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (scaled by a
 # plain-copy calibration), keyed by kernel and workload, valid only while the kernel's
@@ -70,7 +75,8 @@ def parse():
     ap.add_argument("--tokens", type=int, default=None, help="main workload T (default: largest of the config)")
     ap.add_argument("--instances", type=int, default=4)
     ap.add_argument("--only-main", "--no-sweep", dest="only_main", action="store_true",
-                    help="time the main workload only (default: every layer shape at each of its token counts)")
+                    help="time the main workload only (default: also every layer shape at each of its token "
+                         "counts, decode layers on concurrent streams and HIP graph replay)")
     ap.add_argument("--no-measured-peaks", action="store_true",
                     help="leave out the measured HBM-read and MFMA rates (two microbenchmarks, ~0.3 s)")
     ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
@@ -466,6 +472,7 @@ def main():
     # every workload: each layer shape at each of its token counts (the main one included,
     # timed again in its turn), layers built once per shape
     workloads = []
+    graph_replay = None
     if not args.only_main:
         names = [cfg.name] + [n for n in synth.CONFIGS if n != cfg.name]
         for name in names:
@@ -482,6 +489,13 @@ def main():
                 s["config"] = c.name
                 workloads.append(s)
                 print(f"[bench] workload {c.name} T={Ts} {json.dumps(s)}", file=sys.stderr, flush=True)
+                if c.name == GRAPH_CASE[0] and Ts == GRAPH_CASE[1] and not args.graph:
+                    # the same steps captured once per instance and replayed
+                    rg = run_workload(c, Ts, max(args.steps, 50), args.warmup, lays, torch, synth, graph=True)
+                    re_ = run_workload(c, Ts, max(args.steps, 50), args.warmup, lays, torch, synth)
+                    graph_replay = dict(config=c.name, T=Ts, steps=max(args.steps, 50),
+                                        eager_ms=re_["ms_per_step"], graph_ms=rg["ms_per_step"])
+                    print(f"[bench] graph {json.dumps(graph_replay)}", file=sys.stderr, flush=True)
             if lays is not layers:
                 for lay in lays:
                     lay.close()
@@ -491,6 +505,18 @@ def main():
         lay.close()
     del layers
     torch.cuda.empty_cache()
+    # decode layers on concurrent streams: S independent layers, one per stream
+    concurrency = []
+    if not args.only_main:
+        for name, Tc in CONCURRENCY_CASES:
+            c = synth.get_config(name)
+            for S in (1, 8):
+                r = run_streams(c, Tc, max(args.steps, 20), args.warmup, S, torch, synth)
+                ach = r["step_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
+                concurrency.append(dict(config=name, T=Tc, streams=S, ms_per_step=r["ms_per_step"],
+                                        tokens_per_s=S * Tc / (r["ms_per_step"] * 1e-3),
+                                        layer_hbm_frac=ach / HBM_PEAK_GBS))
+                print(f"[bench] streams {json.dumps(concurrency[-1])}", file=sys.stderr, flush=True)
     cpu = None
     if want_cpu:
         n_tok = T if args.cpu_sample_tokens <= 0 else min(args.cpu_sample_tokens, T)
@@ -524,6 +550,8 @@ def main():
         "workloads": [{k: s[k] for k in ("config", "T", "tokens_per_s", "ms_per_step", "stage_ms", "layer_GBps",
                                          "layer_TFLOPs", "layer_hbm_frac", "layer_mfma_frac", "roofline",
                                          "target", "active_experts")} for s in workloads],
+        "decode_concurrency": concurrency,
+        "hip_graph_replay": graph_replay,
         "cpu_baseline": cpu,
         "measured_peaks": None if args.no_measured_peaks else measured_peaks(main_s["roofline"]),
     }
