@@ -319,8 +319,13 @@ __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
 template <int MB, int NBW, int WQ, bool UP>
 hipError_t launch_nbw(const GemmArgs& a, int S, hipStream_t s) {
     // K-steps per round (two rounds are in flight per wave); an int4 step holds four
-    // 32-K token fragments per row block, so wide row tiles take one step per round
-    constexpr int U = WQ == kWI4 ? (MB <= 1 ? 2 : 1) : WQ == kWI8 ? 2 : (MB <= 2 ? 4 : 2);
+    // 32-K token fragments per row block, so wide row tiles take one step per round. The
+    // bf16 up projection of one-block row tiles takes 8 (222 registers, two waves per SIMD,
+    // against 126 and three at 4: its grid has too few waves to hide HBM latency otherwise;
+    // 8-expert layer T = 1 up 80.9 -> 79.9 us, T = 8 270.5 -> 267.8 us). It runs without a K
+    // split, so its d / 32 steps are whole rounds when d % 256 == 0 (other widths finish in
+    // the per-step loop after the rounds); int8 with 3 steps: no change.
+    constexpr int U = WQ == kWI4 ? (MB <= 1 ? 2 : 1) : WQ == kWI8 ? 2 : (MB <= 1 && UP ? 8 : MB <= 2 ? 4 : 2);
     constexpr int KSTEP = WQ == kWI4 ? 128 : WQ == kWI8 ? 64 : 32;
     const int N = UP ? 2 * a.F : a.d;
     if (((UP ? a.d : a.F) / S) % KSTEP != 0) return hipErrorInvalidValue;  // whole K steps per split
