@@ -83,7 +83,8 @@ __device__ __forceinline__ float wave_sum_many(float (&v)[N]) {
     return r;
 }
 
-// One wave: top-k of logits[0..E) (bias already added), weights, shared gate.
+// One wave, all 64 lanes active (the maximum and the sums read other lanes through
+// DPP and readlanes): top-k of logits[0..E) (bias already added), weights, shared gate.
 // `logits` may live in LDS; E <= 128, k <= 64. With kGateClamp the routed logits are
 // first clamped to [-50, 50] ([0539edu §5.2]: the gate's clip option bounds the logits
 // before the softmax), so the top-k and the weights both see the clamped values. With
