@@ -6,7 +6,8 @@ both sides of the streaming / tiled switch, every token routed to one expert, an
 expert holding more rows than the streaming row tile (more tiles than active experts), a
 shared expert of one and of sixteen d_ff slices, int8 output channels and int4
 groups whose scale is zero, the smallest int4 widths, the decode routing paths for routers wider than 16 columns,
-and int8 token rows of extreme or widely spread magnitudes on the tiled path.
+int8 token rows of extreme or widely spread magnitudes on the tiled path, and decode K loops
+that end with steps after their last whole round.
 """
 import numpy as np
 import pytest
@@ -79,6 +80,16 @@ def test_streaming_expert_past_one_tile(name):
         b[3] = 2.0
         L.b_router = b
     _run(synth.get_config(name, d_model=256, d_ff=128), [32, 64], mutate=bias)
+
+
+@pytest.mark.parametrize("name,d", [("mixtral_bf16", 384), ("mixtral_bf16", 640), ("int8_mixtral22b", 384),
+                                    ("int4_mixtral22b", 640)])
+def test_streaming_partial_rounds(name, d):
+    # the decode streams run their K steps in rounds (8 steps of 32 for the bf16 up
+    # projection, 2 otherwise) and the steps left after the last round one at a time:
+    # d = 384 and 640 leave 4 steps after one or two bf16 up rounds
+    kw = dict(d_model=d, d_ff=256 if name == "int4_mixtral22b" else 128)
+    _run(synth.get_config(name, **kw), [1, 3, 16, 32])
 
 
 @pytest.mark.parametrize("slices", [1, 16])
