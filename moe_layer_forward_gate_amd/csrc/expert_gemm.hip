@@ -85,6 +85,10 @@ __device__ __forceinline__ u32x4 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 __device__ __forceinline__ void dma16(const void* src, u32x4* lds_block) {
     __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_block, 16, 0, 0);
 }
+// the same with the non-temporal cache policy: weight blocks no other row tile will read
+__device__ __forceinline__ void dma16_nt(const void* src, u32x4* lds_block) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_block, 16, 0, 2);
+}
 
 // s_waitcnt with vmcnt <= N (N < 64) and the other counters left alone (gfx9 encoding:
 // vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
@@ -220,8 +224,9 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
     // (wave + NW*i) / KH, read only by the waves of row group (that block) / MWB; a block
     // whose readers hold no rows (past the expert's last row) is not loaded. Blocks grow
     // with i, so the loads made are always a prefix.
-    auto issue = [&](int kt, int stage, auto na) __attribute__((always_inline)) {
+    auto issue = [&](int kt, int stage, auto na, auto nt) __attribute__((always_inline)) {
         constexpr int NA = decltype(na)::value;
+        constexpr bool NTB = decltype(nt)::value;
         u32x4* st = lds + (size_t)stage * STAGE * 64;
         size_t oa = 0, ob = 0;
         if constexpr (!UP) {
@@ -237,7 +242,9 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
             const int blk = wave * BW + j;  // bf16: n-block blk / KH, K half blk % KH; int8: n-block blk
             if constexpr (INT8 || INT4) {
                 const int nbg = min(tl.n * (BN / 16) + blk, NB16 - 1);
-                dma16(b_src + ob + ((size_t)nbg * (K / BK) + kt) * 64 + lane, st + (ABLK + blk) * 64);
+                const u32x4* src = b_src + ob + ((size_t)nbg * (K / BK) + kt) * 64 + lane;
+                if constexpr (NTB) dma16_nt(src, st + (ABLK + blk) * 64);
+                else dma16(src, st + (ABLK + blk) * 64);
             } else {
                 const int nb = blk / KH, kh = blk % KH;
                 const int nbg = min(tl.n * (BN / 16) + nb, NB16 - 1);
@@ -360,13 +367,13 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
         // In the ragged last row tile of an expert a wave reads and multiplies only its
         // row blocks that hold rows (MA of MWB; none when all its rows lie past the
         // expert's last row): it still loads its share of the tiles and meets every barrier.
-        auto run = [&](auto ma, auto nac) __attribute__((always_inline)) {
+        auto run = [&](auto ma, auto nac, auto nt) __attribute__((always_inline)) {
             constexpr bool C = decltype(ma)::value > 0;
             constexpr int L = decltype(nac)::value + BW + SBLK;  // LDS-DMA loads per stage of this wave
             auto step = [&](int k, auto& ca, auto& cb, auto& na, auto& nb) __attribute__((always_inline)) {
                 wait_vm_le<(STAGES - 3) * L>();    // stage k+1 has landed
                 lds_barrier();                     // ... for every wave; stage k-1 is free
-                issue(min(k + STAGES - 1, KT - 1), (k + STAGES - 1) % STAGES, nac);
+                issue(min(k + STAGES - 1, KT - 1), (k + STAGES - 1) % STAGES, nac, nt);
                 if constexpr (C && INT4) {
                     mfma_i4(k % STAGES, ma);
                 } else if constexpr (C) {
@@ -375,7 +382,7 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
                 }
             };
 #pragma unroll
-            for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(min(s0, KT - 1), s0, nac);
+            for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(min(s0, KT - 1), s0, nac, nt);
             wait_vm_le<(STAGES - 2) * L>();
             lds_barrier();
             if constexpr (C && !INT4) read_frags(0, fa[0], fb[0], ma);
@@ -405,13 +412,23 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
         using I1 = std::integral_constant<int, 1>;
         using I2 = std::integral_constant<int, AW>;  // == 2 when AW == 2
         using MF = std::integral_constant<int, MWB>;
+        using NT0 = std::false_type;
         if constexpr (INT8 || INT4) {
-            // row blocks holding rows: 0, 1, 2 or all (3 rounds up to all; int4 waves hold two)
+            // row blocks holding rows: 0, 1, 2 or all (3 rounds up to all; int4 waves hold two).
+            // An expert with one row tile is the only reader of its weights: they are loaded
+            // with the non-temporal policy (int8 T = 64 / 128 / 256 layers 478 / 532 / 653 ->
+            // 458 / 521 / 635 us); weights several row tiles read stay cached (the same policy
+            // for all of them made T = 1024 5% slower).
             const int rw = tl.rows - wm * MWB * 16;
+            const bool once = a.tile_start[tl.e + 1] - a.tile_start[tl.e] == 1;
             auto run_nac = [&](auto ma) __attribute__((always_inline)) {
-                if (nA == AW) run(ma, I2{});
-                else if (nA == 1) run(ma, I1{});
-                else run(ma, I0{});
+                auto go = [&](auto nt) __attribute__((always_inline)) {
+                    if (nA == AW) run(ma, I2{}, nt);
+                    else if (nA == 1) run(ma, I1{}, nt);
+                    else run(ma, I0{}, nt);
+                };
+                if (once) go(std::true_type{});
+                else go(NT0{});
             };
             if constexpr (MWB == 2) {
                 if (rw > 16) run_nac(MF{});
@@ -426,13 +443,13 @@ __global__ __launch_bounds__(NW * 64, 1) void expert_gemm(GemmArgs a) {
         } else if (has_rows) {
             // bf16 tiles are MFMA-bound and full but for each expert's last one, which is
             // bound by its weight loads: all or none of a wave's row blocks
-            if (nA == AW) run(MF{}, I2{});
-            else if (nA == 1) run(MF{}, I1{});
-            else run(MF{}, I0{});
+            if (nA == AW) run(MF{}, I2{}, NT0{});
+            else if (nA == 1) run(MF{}, I1{}, NT0{});
+            else run(MF{}, I0{}, NT0{});
         } else {
-            if (nA == AW) run(I0{}, I2{});
-            else if (nA == 1) run(I0{}, I1{});
-            else run(I0{}, I0{});
+            if (nA == AW) run(I0{}, I2{}, NT0{});
+            else if (nA == 1) run(I0{}, I1{}, NT0{});
+            else run(I0{}, I0{}, NT0{});
         }
         wait_vm_le<0>();  // no LDS-DMA write may outlive the workgroup
     }
