@@ -116,6 +116,7 @@ struct GemmArgs {
     const float* gs;            // [T] shared gate or null
     float* ow;                  // [T*kt*ksplit][d] weighted expert outputs (partial sums)
     int d, F;
+    int T;                      // tokens of the batch (a tile holds at most min(bm, T * k) rows)
 };
 // LDS-tiled MFMA GEMMs; wq: the weight kind (kWBf16, kWI8, kWI4), with a.bm 256, 128, 64
 hipError_t launch_expert_up_tiled(const GemmArgs& a, int wq, hipStream_t s);

@@ -18,6 +18,7 @@
 // Work item = (active expert, group of 4*NBW column blocks, K split); experts
 // without rows get no work items (the item count is read from the scatter's tile
 // table on the device).
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -26,6 +27,7 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr size_t kAStageBytes = 32 * 1024;  // LDS for a work item's token rows (see expert_stream)
 
 __device__ __forceinline__ uint32_t i8x2_bf16(uint32_t w, int sh) {
     const float f0 = (float)(int)(int8_t)(w >> sh);
@@ -56,7 +58,7 @@ __device__ __forceinline__ u32x4 load_w(const u32x4* p) {
 }
 
 // WQ: weight kind (kWBf16, kWI8, kWI4); NT: the weights are loaded non-temporally
-template <int MB, int NBW, int WQ, bool UP, int U, bool NT>
+template <int MB, int NBW, int WQ, bool UP, int U, bool NT, bool AL>
 __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
     constexpr bool INT8 = WQ == kWI8;
     constexpr bool INT4 = WQ == kWI4;
@@ -102,7 +104,8 @@ __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
         for (int j = 0; j < NBW; ++j)
             sptr[j] = (UP ? a.s_gate : a.s_down) + ((size_t)e * KB + kbase / KSTEP) * N + (nb0 + j) * 16 + lane % 16;
     }
-    // token rows as A fragments: lane holds row 16*mb + lane%16, K 8*(lane/16)..+7
+    // token rows as A fragments: lane holds row 16*mb + lane%16, K 8*(lane/16)..+7 (rows past
+    // the work item's last row repeat its first: their outputs are never stored)
     const bf16_t* aptr[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -111,6 +114,26 @@ __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
         const bf16_t* base = UP ? a.x + (size_t)(a.sorted_c[p] / a.kt) * a.d : a.h + (size_t)p * a.F;
         aptr[mb] = base + kbase + 8 * (lane / 16);
     }
+    // AL (int4, one row block, a few rows): the work item's rows over its K range are copied
+    // to LDS once, and the fragments are read from there, so the weight stream has more of
+    // the vector memory path (from global memory the four waves read the same rows, and 15
+    // of a fragment's 16 rows repeat the first when a tile holds one row)
+    extern __shared__ u32x4 arow[];  // AL: [rows][Kp / 8] 16-byte chunks
+    const int cpr = Kp / 8;
+    if constexpr (AL) {
+        static_assert(MB == 1, "LDS-staged rows: one row block");
+        for (int c = threadIdx.x; c < rows * cpr; c += kThreads) {
+            const int r = c / cpr, q = c - r * cpr;
+            const bf16_t* base = UP ? a.x + (size_t)(a.sorted_c[seg0 + r] / a.kt) * a.d : a.h + (size_t)(seg0 + r) * a.F;
+            arow[c] = *reinterpret_cast<const u32x4*>(base + kbase + 8 * q);
+        }
+        __syncthreads();
+    }
+    const int arr = lane % 16 < rows ? lane % 16 : 0;  // AL: the LDS row this lane reads
+    auto a_frag = [&](int mb, int s, int kh) __attribute__((always_inline)) -> u32x4 {
+        if constexpr (AL) return arow[arr * cpr + (s * KSTEP + kh * 32) / 8 + lane / 16];
+        else return *reinterpret_cast<const u32x4*>(aptr[mb] + s * KSTEP + kh * 32);
+    };
 
     uint32_t nib_mask = 0x000F000Fu;  // int4 unpacking (see i4x8_bf16)
     if constexpr (INT4) asm volatile("" : "+v"(nib_mask));
@@ -204,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
                 for (int mb = 0; mb < MA; ++mb)
 #pragma unroll
                     for (int kh = 0; kh < KH; ++kh)
-                        R.aa[u][mb][kh] = *reinterpret_cast<const u32x4*>(aptr[mb] + (s0 + u) * KSTEP + kh * 32);
+                        R.aa[u][mb][kh] = a_frag(mb, s0 + u, kh);
         };
         auto compute_round = [&](const Round& R) __attribute__((always_inline)) {
 #pragma unroll
@@ -253,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
             for (int mb = 0; mb < MA; ++mb)
 #pragma unroll
                 for (int kh = 0; kh < KH; ++kh)
-                    aa[mb][kh] = *reinterpret_cast<const u32x4*>(aptr[mb] + s * KSTEP + kh * 32);
+                    aa[mb][kh] = a_frag(mb, s, kh);
             step(bb, aa, sc);
         }
     };
@@ -335,10 +358,28 @@ hipError_t launch_nbw(const GemmArgs& a, int S, hipStream_t s) {
     // non-temporal weight loads when each expert's weights are read by one row tile; an int4
     // layer whose busiest expert needs several 32-row tiles streams them once per tile and
     // keeps them cached
+    // int4 one-row-block tiles whose rows over the K range fit kAStageBytes take them from
+    // LDS (an int4 K step reads four token fragments a block; int4 T = 1 79.4 -> 76.8 us).
+    // bf16 and int8 keep reading them from global memory: the copy and its barrier come
+    // before their weight stream starts (T = 1: 125.2 -> 127.8 and 109.3 -> 112.4 us). A
+    // tile holds at most min(bm, T * k) rows (a given routing may repeat an expert within a
+    // token; a shared slice holds T rows).
+    const size_t astage = (size_t)std::min(a.bm, a.T * a.k) * ((UP ? a.d : a.F) / S) * 2;
+    if constexpr (MB == 1 && WQ == kWI4) {
+        if (astage <= kAStageBytes) {
+            if (WQ != kWI4 || a.weights_once)
+                hipLaunchKernelGGL((expert_stream<MB, NBW, WQ, UP, U, true, true>), grid, dim3(kThreads), astage, s, a,
+                                   S);
+            else if constexpr (WQ == kWI4)
+                hipLaunchKernelGGL((expert_stream<MB, NBW, WQ, UP, U, false, true>), grid, dim3(kThreads), astage, s,
+                                   a, S);
+            return hipGetLastError();
+        }
+    }
     if (WQ != kWI4 || a.weights_once)
-        hipLaunchKernelGGL((expert_stream<MB, NBW, WQ, UP, U, true>), grid, dim3(kThreads), 0, s, a, S);
+        hipLaunchKernelGGL((expert_stream<MB, NBW, WQ, UP, U, true, false>), grid, dim3(kThreads), 0, s, a, S);
     else if constexpr (WQ == kWI4)
-        hipLaunchKernelGGL((expert_stream<MB, NBW, WQ, UP, U, false>), grid, dim3(kThreads), 0, s, a, S);
+        hipLaunchKernelGGL((expert_stream<MB, NBW, WQ, UP, U, false, false>), grid, dim3(kThreads), 0, s, a, S);
     return hipGetLastError();
 }
 

@@ -473,7 +473,7 @@ int run_experts(moe_layer* L, const Work& W, const void* x, int T, void* y, cons
     const bool prof = L->profiling;
     const GemmArgs a{W.tile_start, W.offsets, W.sorted_c, L->Et, L->kt, k, pl.max_tiles, pl.bm, pl.ksplit,
                      pl.merge ? 1 : 0, pl.weights_once ? 1 : 0, (const bf16_t*)x, W.xp, (bf16_t*)W.h, L->wgu, L->wdn,
-                     L->s_gate, L->s_up, L->s_down, topk_w, gs, W.ow, d.d_model, d.d_ff};
+                     L->s_gate, L->s_up, L->s_down, topk_w, gs, W.ow, d.d_model, d.d_ff, T};
     // the tiled GEMMs take the token rows already gathered into fragment order
     if (!f32 && !pl.streaming) HIP_TRY(launch_pack_a(a, s));
     if (prof) HIP_TRY(hipEventRecord(L->ev[2], s));
