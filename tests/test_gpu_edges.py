@@ -1,6 +1,6 @@
 """GPU parity on edge shapes and degenerate routings, at sizes the oracle evaluates in full.
 
-Covers: k = 1 and k = E, expert counts that are not multiples of 8 or 16 (up to the
+Covers: k = 1, k = E and k up to the 64-slot limit, expert counts that are not multiples of 8 or 16 (up to the
 128-expert limit), the smallest supported widths, T at the max_tokens bound and on
 both sides of the streaming / tiled switch, every token routed to one expert, an
 expert holding more rows than the streaming row tile (more tiles than active experts), a
@@ -40,6 +40,14 @@ def _run(cfg, Ts, max_tokens=None, mutate=None):
 def test_top_k_extremes(k):
     # k = 1: every weight is exactly 1; k = E = 8: the dense softmax mixture
     _run(synth.get_config("mixtral_bf16", d_model=256, d_ff=128, top_k=k), [1, 5, 70, 600])
+
+
+@pytest.mark.parametrize("E,k", [(64, 16), (64, 64), (128, 32), (128, 64)])
+def test_large_top_k(E, k):
+    # k up to the 64-slot limit: k rounds of the wave maximum over up to 128 keys (two a
+    # lane), the softmax over k slots, k*T assignments through the one-wave, one-workgroup
+    # and wide scatters
+    _run(synth.get_config("mixtral_bf16", d_model=128, d_ff=64, n_experts=E, top_k=k), [1, 3, 40, 300])
 
 
 @pytest.mark.parametrize("E,k", [(5, 2), (13, 3), (127, 4), (128, 1)])
