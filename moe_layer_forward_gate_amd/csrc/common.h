@@ -121,6 +121,10 @@ struct GemmArgs {
 // LDS-tiled MFMA GEMMs; wq: the weight kind (kWBf16, kWI8, kWI4), with a.bm 256, 128, 64
 hipError_t launch_expert_up_tiled(const GemmArgs& a, int wq, hipStream_t s);
 hipError_t launch_expert_down_tiled(const GemmArgs& a, int wq, hipStream_t s);
+// The same GEMMs for int8 and int4 weights with the weights streamed into registers and
+// the row tile staged in LDS (a.bm 64 or 128 for int8, 64 for int4; N % 256 == 0)
+hipError_t launch_expert_up_tstream(const GemmArgs& a, int wq, hipStream_t s);
+hipError_t launch_expert_down_tstream(const GemmArgs& a, int wq, hipStream_t s);
 // Token rows into the tiled up operand a.xp (padded rows past an expert's last row are
 // zero; shared virtual experts after the first are not written, the up kernel reads the
 // first one's rows for them). Reads the scatter's tile list on the device; writes

@@ -1,0 +1,398 @@
+// Expert compute for mid-size batches with quantised weights: row tiles in LDS,
+// weights streamed into registers.
+//
+// Between decode and prefill an int8 or int4 expert holds tens to a few hundred rows
+// and its weights are still most of the traffic ([hotelren §2.1]: the bottleneck is
+// moving data). Here each wave owns four 16-column weight blocks and streams them from
+// HBM over the whole K range as contiguous 1 KB chunks straight into MFMA operand
+// registers (no LDS round trip, each weight byte widened once), while the workgroup's
+// row tile (up to 128 rows) is staged in LDS by LDS-DMA, K step by K step, and read by
+// all four waves: every wave multiplies every row of the tile against its own columns.
+//   - Workgroup = (row tile, 256 columns, K split), 4 waves; the tile list, the padded
+//     A operand (xp for the up projection, packed H for the down projection) and the
+//     outputs are those of the LDS-tiled kernels, so the two are interchangeable.
+//   - R K steps of loads are in flight per wave (2 to 4, the most the registers hold beside
+//     the tile's accumulators; weights into a ring of R register sets, row blocks into R + 1
+//     LDS slots); one barrier per K step: after it, every wave's row blocks of this step
+//     have landed and the slot of the step before is free.
+//   - Only the row blocks that hold rows are loaded and multiplied (a compile-time count,
+//     one instantiation per count, so the K loop has no branch).
+// int8 chunks hold 16 columns x 64 K (bytes 0-7 the first 32-K half), widened to bf16 in
+// registers; int4 chunks 16 columns x 128 K (one scale group), unpacked as q + 136 with
+// 136 * sum(a) taken off per group, as in the other kernels.
+#include <type_traits>
+
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kNW = 4;                 // waves per workgroup
+constexpr int kThreads = kNW * kWave;
+constexpr int kNBW = 4;                // 16-column weight blocks per wave
+constexpr int kBN = kNW * kNBW * 16;   // columns per workgroup
+constexpr int kGN = 4, kGNAll = 6;     // column tiles per group (see decode_tile_at)
+constexpr int kChunk = 32;             // tiles dealt to the XCDs in chunks
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma16(const void* src, u32x4* lds_block) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_block, 16, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm_le() {
+    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t i8x2_bf16(uint32_t w, int sh) {
+    const float f0 = (float)(int)(int8_t)(w >> sh);
+    const float f1 = (float)(int)(int8_t)(w >> (sh + 8));
+    // the high halves of the two fp32 patterns (exact for |q| <= 128), by one byte permute
+    return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+}
+
+template <bool NT>
+__device__ __forceinline__ u32x4 load_w(const u32x4* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+// K steps in flight per wave for a tile of MA row blocks: as many as the registers left
+// beside the accumulators hold (two waves per SIMD: 256 registers a wave)
+template <int WQ>
+__host__ __device__ constexpr int ring_depth(int MA) {
+    return WQ == kWI4 ? (MA <= 2 ? 4 : MA == 3 ? 3 : 2) : (MA <= 4 ? 4 : MA <= 6 ? 3 : 2);
+}
+
+// LDS of the K loop: (R + 1) slots of MA * KH 1 KB blocks, the most over MA <= MB
+template <int WQ>
+__host__ __device__ constexpr int ring_blocks(int MB) {
+    int m = 0;
+    for (int ma = 1; ma <= MB; ++ma) {
+        const int b = (ring_depth<WQ>(ma) + 1) * ma * (WQ == kWI4 ? 4 : 2);
+        m = b > m ? b : m;
+    }
+    return m;
+}
+
+// MB: 16-row blocks per tile (a.bm = 16 MB); WQ: kWI8 or kWI4
+template <int MB, int WQ, bool UP>
+__global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
+    constexpr bool INT4 = WQ == kWI4;
+    static_assert(WQ == kWI8 || WQ == kWI4, "quantised weights");
+    constexpr int KSTEP = INT4 ? 128 : 64;  // K per weight chunk
+    constexpr int KH = KSTEP / 32;          // 32-K row-block fragments per K step
+
+    const int K = UP ? a.d : a.F;
+    const int N = UP ? 2 * a.F : a.d;
+    const int NT_ = N / kBN;
+    const int S = UP ? 1 : a.ksplit;
+    Tile tl;
+    int split = 0;
+    if (!decode_tile_split(a.tile_start, a.offsets, a.Et, NT_, NT_ <= kGNAll ? NT_ : kGN, MB * 16, S, tl, split,
+                           kChunk))
+        return;
+    const int Kp = K / S;
+    const int kbase = split * Kp;
+    const int nsteps = Kp / KSTEP;
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar addressing
+    const int nb0 = tl.n * (kBN / 16) + wave * kNBW;  // first owned column block
+
+    extern __shared__ u32x4 lds[];  // [R + 1][MA * KH][64]; the epilogue's patches afterwards
+
+    // weights: block nb's chunks are contiguous along K ([E][N/16][K/KSTEP][64][16 B])
+    // (uniform bases, per-lane offsets: the addresses take scalar registers)
+    const int KB = K / KSTEP;
+    const u32x4* bbase = reinterpret_cast<const u32x4*>(UP ? a.wgu : a.wdn) +
+                         ((size_t)tl.e * N * KB * 4 + (size_t)nb0 * KB * 64 + kbase / KSTEP * 64);
+    // int4: the column scales, [E][K/128][N]; lane reads its column's
+    const float* sbase = (UP ? a.s_gate : a.s_down) + ((size_t)tl.e * KB + kbase / KSTEP) * N + nb0 * 16;
+    // row blocks: the padded operand in fragment order ([R/16][K/32][64][8]); tile g owns
+    // row blocks g*MB .. g*MB + MB-1. Shared virtual experts past the first read the first
+    // one's token rows (the same tokens in the same order).
+    const int e0 = a.Et - a.kt + a.k;
+    const int ga = (UP && tl.e > e0) ? tl.g - a.tile_start[tl.e] + a.tile_start[e0] : tl.g;
+    const bf16_t* abase = (UP ? a.xp : a.h) + (((size_t)ga * MB * (K / 32) + kbase / 32) * 64 + lane) * 8;
+    const int mb_act = (tl.rows + 15) / 16;
+
+    f32x4 acc[MB][kNBW];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < kNBW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    uint32_t nib_mask = 0x000F000Fu;  // int4 unpacking: held in a register (one v_and_or_b32 a pair)
+    if constexpr (INT4) asm volatile("" : "+v"(nib_mask));
+
+    // MA: row blocks holding rows (compile time); NT: non-temporal weight loads, when the
+    // expert has one row tile (its weights are read once). AW: LDS-DMA loads per wave per
+    // step (the MA * KH blocks dealt to the waves in turn; a wave past the last block
+    // re-loads the last one, the same bytes to the same place, so that every wave makes the
+    // same number of loads per step and one wait count fits all).
+    auto kloop = [&](auto ma, auto nt) __attribute__((always_inline)) {
+        constexpr int MA = decltype(ma)::value;
+        constexpr bool NT = decltype(nt)::value;
+        constexpr int R = ring_depth<WQ>(MA);  // K steps in flight
+        constexpr int NS = R + 1;              // LDS slots
+        constexpr int SLOT = MA * KH;          // 1 KB blocks per slot
+        constexpr int AW = (MA * KH + kNW - 1) / kNW;
+        constexpr int X = kNBW + (INT4 ? kNBW : 0) + AW;  // vector memory loads per wave per step
+        static_assert((R - 1) * X < 64, "wait count");
+        size_t aoff[AW];
+        int aslot[AW];
+#pragma unroll
+        for (int i = 0; i < AW; ++i) {
+            const int b = min(wave + kNW * i, MA * KH - 1);  // block = mb * KH + kh
+            aoff[i] = ((size_t)(b / KH) * (K / 32) + b % KH) * 512;
+            aslot[i] = b;
+        }
+        struct Regs {
+            u32x4 b[kNBW];
+            float sc[kNBW];
+        };
+        Regs ring[R];
+        auto issue = [&](int s, Regs& rg, int slot) __attribute__((always_inline)) {
+#pragma unroll
+            for (int j = 0; j < kNBW; ++j) rg.b[j] = load_w<NT>(bbase + ((size_t)j * KB + s) * 64 + lane);
+            if constexpr (INT4) {
+#pragma unroll
+                for (int j = 0; j < kNBW; ++j) rg.sc[j] = sbase[(size_t)s * N + j * 16 + lane % 16];
+            }
+#pragma unroll
+            for (int i = 0; i < AW; ++i)
+                dma16(abase + aoff[i] + (size_t)s * KH * 512, lds + (size_t)(slot * SLOT + aslot[i]) * 64);
+        };
+        auto compute = [&](const Regs& rg, int slot) __attribute__((always_inline)) {
+            const u32x4* la = lds + (size_t)slot * SLOT * 64 + lane;
+            if constexpr (INT4) {
+                const bf16x8 k136 =
+                    __builtin_bit_cast(bf16x8, u32x4{0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u});
+                f32x4 zr[MA], g[MA][kNBW];
+#pragma unroll
+                for (int kh = 0; kh < KH; ++kh) {
+                    bf16x8 af[MA];
+#pragma unroll
+                    for (int mb = 0; mb < MA; ++mb) af[mb] = __builtin_bit_cast(bf16x8, la[(mb * KH + kh) * 64]);
+#pragma unroll
+                    for (int mb = 0; mb < MA; ++mb)
+                        zr[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], k136,
+                                                                         kh ? zr[mb] : f32x4{0.f, 0.f, 0.f, 0.f}, 0,
+                                                                         0, 0);
+#pragma unroll
+                    for (int j = 0; j < kNBW; ++j) {
+                        // word kh of the lane's chunk: K rows 32 kh + 8 (lane / 16) + 0..7 of its column
+                        const uint32_t w = rg.b[j][kh];
+                        const bf16x8 bw = __builtin_bit_cast(
+                            bf16x8, u32x4{(w & nib_mask) | 0x43004300u, ((w >> 4) & nib_mask) | 0x43004300u,
+                                          ((w >> 8) & nib_mask) | 0x43004300u, ((w >> 12) & nib_mask) | 0x43004300u});
+#pragma unroll
+                        for (int mb = 0; mb < MA; ++mb)
+                            g[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                af[mb], bw, kh ? g[mb][j] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < kNBW; ++j)
+#pragma unroll
+                    for (int mb = 0; mb < MA; ++mb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            acc[mb][j][i] = fmaf(rg.sc[j], g[mb][j][i] - zr[mb][i], acc[mb][j][i]);
+            } else {
+                // per 32-K half: the four widened weight fragments, then row block by row block
+                // (one row fragment live at a time)
+#pragma unroll
+                for (int kh = 0; kh < KH; ++kh) {
+                    bf16x8 bw[kNBW];
+#pragma unroll
+                    for (int j = 0; j < kNBW; ++j) {
+                        const uint32_t lo = kh ? rg.b[j].z : rg.b[j].x, hi = kh ? rg.b[j].w : rg.b[j].y;
+                        bw[j] = __builtin_bit_cast(
+                            bf16x8, u32x4{i8x2_bf16(lo, 0), i8x2_bf16(lo, 16), i8x2_bf16(hi, 0), i8x2_bf16(hi, 16)});
+                    }
+#pragma unroll
+                    for (int mb = 0; mb < MA; ++mb) {
+                        const bf16x8 af = __builtin_bit_cast(bf16x8, la[(mb * KH + kh) * 64]);
+#pragma unroll
+                        for (int j = 0; j < kNBW; ++j)
+                            acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bw[j], acc[mb][j], 0, 0, 0);
+                    }
+                }
+            }
+        };
+        // step s: its loads have landed for this wave (wait), and for every wave (barrier,
+        // which also frees the slot of step s-1); multiply; refill the ring entry and that
+        // slot with step s + R (past the last step the last one is loaded again and never
+        // used, so the loop has no branch)
+        auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+        auto step = [&](int s, Regs& rg) __attribute__((always_inline)) {
+            wait_vm_le<(R - 1) * X>();
+            lds_barrier();
+            fence();
+            compute(rg, s % NS);
+            fence();
+            issue(min(s + R, nsteps - 1), rg, (s + R) % NS);
+            fence();
+        };
+#pragma unroll
+        for (int u = 0; u < R; ++u) issue(min(u, nsteps - 1), ring[u], u);
+        int s = 0;
+        for (; s + R <= nsteps; s += R) {
+#pragma unroll
+            for (int u = 0; u < R; ++u) step(s + u, ring[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < R - 1; ++u)
+            if (s + u < nsteps) step(s + u, ring[u]);
+        wait_vm_le<0>();  // no LDS-DMA write may outlive the K loop
+    };
+    auto run = [&](auto nt) __attribute__((always_inline)) {
+        if constexpr (MB == 4) {
+            if (mb_act <= 1) kloop(std::integral_constant<int, 1>{}, nt);
+            else if (mb_act == 2) kloop(std::integral_constant<int, 2>{}, nt);
+            else if (mb_act == 3) kloop(std::integral_constant<int, 3>{}, nt);
+            else kloop(std::integral_constant<int, 4>{}, nt);
+        } else {
+            static_assert(MB == 8, "row blocks per tile");
+            switch (mb_act) {
+                case 0:
+                case 1: kloop(std::integral_constant<int, 1>{}, nt); break;
+                case 2: kloop(std::integral_constant<int, 2>{}, nt); break;
+                case 3: kloop(std::integral_constant<int, 3>{}, nt); break;
+                case 4: kloop(std::integral_constant<int, 4>{}, nt); break;
+                case 5: kloop(std::integral_constant<int, 5>{}, nt); break;
+                case 6: kloop(std::integral_constant<int, 6>{}, nt); break;
+                case 7: kloop(std::integral_constant<int, 7>{}, nt); break;
+                default: kloop(std::integral_constant<int, 8>{}, nt); break;
+            }
+        }
+    };
+    if (a.tile_start[tl.e + 1] - a.tile_start[tl.e] == 1) run(std::true_type{});
+    else run(std::false_type{});
+
+    // ---- epilogue: the LDS-tiled kernels' output layouts, through a per-wave LDS patch
+    const int col16 = lane % 16;
+    const int rq = 4 * (lane / 16);
+    __syncthreads();  // every wave is done with the row-block slots
+    if constexpr (UP) {
+        // H patch: 16 MB rows x 32 bf16 columns (the wave's two gate/up pairs); H goes out in
+        // the down operand's fragment order, every row of the tile (rows past the expert's
+        // last row are zero: zero inputs, or row blocks never multiplied)
+        constexpr int PW = 8 * kNBW;
+        bf16_t* patch = reinterpret_cast<bf16_t*>(lds) + (size_t)wave * (16 * MB) * PW;
+#pragma unroll
+        for (int q = 0; q < kNBW / 2; ++q) {
+            float sg = 1.f, su = 1.f;
+            if constexpr (!INT4) {
+                const int f = (nb0 / 2 + q) * 16 + col16;
+                sg = a.s_gate[(size_t)tl.e * a.F + f];
+                su = a.s_up[(size_t)tl.e * a.F + f];
+            }
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float g = acc[mb][2 * q][i] * sg;
+                    const float u = acc[mb][2 * q + 1][i] * su;
+                    patch[(mb * 16 + rq + i) * PW + q * 16 + col16] = f32_to_bf16(silu(g) * u);
+                }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the patch is written
+        static_assert(PW == 32, "one 32-column H block per wave");
+        const int fb = nb0 / 2 * 16 / 32;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(patch + (mb * 16 + lane % 16) * PW + 8 * (lane / 16));
+            const size_t blk = ((size_t)tl.g * MB + mb) * (a.F / 32) + fb;
+            *reinterpret_cast<u32x4*>(a.h + (blk * 64 + lane) * 8) = v;
+        }
+    } else {
+        // output patch: 16 MB rows x 32 fp32 columns, two 16-column blocks at a time
+        float* patch = reinterpret_cast<float*>(lds) + (size_t)wave * (16 * MB) * 32;
+#pragma unroll
+        for (int nh = 0; nh < kNBW / 2; ++nh) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) patch[(mb * 16 + rq + i) * 32 + j * 16 + col16] = acc[mb][2 * nh + j][i];
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+            const int n0 = (nb0 + 2 * nh) * 16;
+            for (int c = lane; c < 16 * MB * 8; c += kWave) {
+                const int r = c / 8, c4 = (c % 8) * 4;
+                if (r < tl.rows) {
+                    const int cs = a.sorted_c[tl.seg0 + tl.row0 + r];
+                    const int t = cs / a.kt, j = cs - t * a.kt;
+                    const float wgt = j < a.k ? a.topk_w[(size_t)t * a.k + j] : a.gs[t];
+                    f32x4 v = *reinterpret_cast<const f32x4*>(patch + r * 32 + c4) * wgt;
+                    if constexpr (!INT4) v *= *reinterpret_cast<const f32x4*>(a.s_down + (size_t)tl.e * a.d + n0 + c4);
+                    // partial sum `split` of slot cs: row cs*S + split of the combine buffer
+                    *reinterpret_cast<f32x4*>(a.ow + ((size_t)cs * S + split) * a.d + n0 + c4) = v;
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // patch reads done before the next half overwrites it
+        }
+    }
+}
+
+template <int MB, int WQ, bool UP>
+hipError_t launch_r(const GemmArgs& a, hipStream_t s) {
+    constexpr int KSTEP = WQ == kWI4 ? 128 : 64;
+    constexpr size_t ring = (size_t)ring_blocks<WQ>(MB) * 1024;
+    constexpr size_t patch = (size_t)kNW * 16 * MB * 32 * (UP ? 2 : 4);
+    constexpr size_t lds_bytes = ring > patch ? ring : patch;
+    static_assert(lds_bytes * (8 / kNW) <= 160 * 1024, "two waves per SIMD");
+    const int N = UP ? 2 * a.F : a.d;
+    const int S = UP ? 1 : a.ksplit;
+    const int Kp = (UP ? a.d : a.F) / S;
+    if (a.bm != MB * 16 || N % kBN != 0 || Kp % KSTEP != 0 || Kp < KSTEP) return hipErrorInvalidValue;
+    const int NT = N / kBN;
+    const int gn = NT <= kGNAll ? NT : kGN;
+    const int NTp = (NT + gn - 1) / gn * gn;
+    // the chunked deal needs the tile count rounded up to whole chunks per XCD
+    const size_t blocks = (size_t)a.max_tiles * NTp * S + kXcds * kChunk;
+    const dim3 grid((unsigned)((blocks + kXcds - 1) / kXcds * kXcds));
+    auto kern = expert_tstream<MB, WQ, UP>;
+    static bool attr_set = false;  // one-time opt-in above the default dynamic LDS limit
+    if (!attr_set) {
+        const hipError_t e =
+            hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds_bytes, s, a);
+    return hipGetLastError();
+}
+
+template <int WQ, bool UP>
+hipError_t launch_w(const GemmArgs& a, hipStream_t s) {
+    if constexpr (WQ == kWI4) {
+        if (a.bm == 64) return launch_r<4, WQ, UP>(a, s);
+    } else {
+        if (a.bm == 128) return launch_r<8, WQ, UP>(a, s);
+        if (a.bm == 64) return launch_r<4, WQ, UP>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_expert_up_tstream(const GemmArgs& a, int wq, hipStream_t s) {
+    if (wq == kWI8) return launch_w<kWI8, true>(a, s);
+    if (wq == kWI4) return launch_w<kWI4, true>(a, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_expert_down_tstream(const GemmArgs& a, int wq, hipStream_t s) {
+    if (wq == kWI8) return launch_w<kWI8, false>(a, s);
+    if (wq == kWI4) return launch_w<kWI4, false>(a, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace moe

@@ -219,7 +219,9 @@ int create_impl(const moe_desc* desc, const moe_weights* w, moe_layer* L) {
     if ((rc = dev_alloc(&ws.h, (f32 ? P : R) * F * (f32 ? 4 : 2)))) return rc;
     // combine buffer: one row per (token, slot, K split): 2 splits for large batches,
     // up to kStreamMaxSplit for batches the streaming kernels serve
-    L->ow_rows = std::max(P * 2, std::min(T, (size_t)kStreamMaxT) * L->kt * kStreamMaxSplit);
+    // (int8 and int4 layers: 4, so the tile-stream down projection can split K four ways at
+    // ~64 rows per expert; 8-expert int8 layer T = 512: 0.96 -> 0.89 ms)
+    L->ow_rows = std::max(P * (i8 || i4 ? 4 : 2), std::min(T, (size_t)kStreamMaxT) * L->kt * kStreamMaxSplit);
     if ((rc = dev_alloc(&ws.ow, L->ow_rows * dm * 4))) return rc;
     if (d.profile) {
         for (hipEvent_t& e : L->ev) HIP_TRY(hipEventCreate(&e));
@@ -290,8 +292,13 @@ int check_device(const moe_layer* L) {
 //  - small batches (T <= 64; int8 and int4 weights: T <= 32) stream the weights: row tiles
 //    of 16, 32 or 64 rows (int4: 16 or 32), sized so an active expert almost always fits one
 //    tile, the down projection's K split so ~1024 workgroups run;
-//  - larger batches use the LDS-tiled MFMA GEMMs (256-row tiles for bf16 weights, 128 for
-//    int8, 64 for int4), with the down projection's K split when that fills the CUs better.
+//  - larger batches of int8 and int4 weights (when both projections have whole 256-column
+//    tiles) take the tile-stream GEMMs: row tiles in LDS, each wave streaming its weight
+//    columns into registers (128-row tiles for int8, 64 when the experts average at most 32
+//    rows; 64 for int4);
+//  - other larger batches use the LDS-tiled MFMA GEMMs (256-row tiles for bf16 weights, 128
+//    for int8, 64 for int4);
+//  - in the last two the down projection's K is split when that fills the CUs better.
 // Past this many routed assignments the scatter runs over many workgroups.
 constexpr int kScatterWideMin = 4095;
 
@@ -300,6 +307,8 @@ struct Plan {
     int bm, ksplit, max_tiles;
     bool merge;         // tiled down projection of a multi-slice shared expert as one K loop
     bool weights_once;  // streaming: the busiest expert is expected to fit one row tile
+    bool tstream;       // quantised weights past the streaming sizes: row tiles in LDS, weights
+                        // streamed into registers (expert_tstream) instead of the LDS-tiled GEMMs
 };
 
 Plan make_plan(const moe_layer* L, int T) {
@@ -308,12 +317,13 @@ Plan make_plan(const moe_layer* L, int T) {
     const bool i8 = d.expert_dtype == MOE_I8;
     const bool i4 = d.expert_dtype == MOE_I4;
     const int k = d.top_k;
-    // int8 weights at 33-64 tokens: the tiled kernels are faster (8-expert 6144 x 16384 layer,
-    // T = 64: 0.48 against 0.50 ms streaming); int4 and bf16 weights stream up to 64 (int4
-    // T = 64: 0.33 against 0.35 ms tiled; bf16 T = 64: 0.50 against 0.58 ms tiled)
-    const bool streaming = !f32 && T <= (i8 ? kStreamMaxT / 2 : kStreamMaxT);
+    // int8 and int4 weights at 33-64 tokens: the tile-stream kernels are faster (8-expert
+    // 6144 x 16384 layer; int8 T = 64: 0.45 ms against 0.50 streaming, T = 24 and 32 stream
+    // faster; int4 T = 48: 0.30 against 0.31 streaming); bf16 weights stream up to 64 (T = 64:
+    // 0.50 against 0.58 ms tiled)
+    const bool streaming = !f32 && T <= (i8 || i4 ? kStreamMaxT / 2 : kStreamMaxT);
     int bm, ksplit = 1;
-    bool weights_once = true;
+    bool weights_once = true, tstream = false;
     if (f32) {
         bm = kBMf32;
     } else if (streaming) {
@@ -331,16 +341,22 @@ Plan make_plan(const moe_layer* L, int T) {
                (size_t)T * L->kt * ksplit * 2 <= L->ow_rows)
             ksplit *= 2;
     } else {
+        // int8 and int4: the tile-stream kernels (8-expert 6144 x 16384 layer, against the
+        // LDS-tiled ones: int8 T = 256 0.63 -> 0.57 ms, T = 1024 1.57 -> 1.40; int4 T = 256
+        // 0.70 -> 0.61, T = 1024 1.89 -> 1.61) when both projections have whole 256-column
+        // tiles
+        tstream = (i8 || i4) && (2 * d.d_ff) % 256 == 0 && d.d_model % 256 == 0;
         // bf16: 256-row tiles (the 256 x 256 workgroup tile reads the least LDS and L2 per MFMA
         // and outruns 128-row tiles even when most experts leave their last tile half empty);
-        // int8: 128-row tiles, 64 when the experts average at most 24 rows (T = 64 on the
-        // 8-expert layer: 0.48 against 0.51 ms; at 32 and 64 rows, T = 128 and 256, the
-        // 128-row tiles are faster); int4: 64-row tiles (see the GEMM launcher)
-        bm = i4 ? 64 : (i8 ? ((long long)T * k <= 24LL * L->E ? 64 : 128) : 256);
+        // int8: 128-row tiles, 64 when the experts average at most 24 rows (tile-stream: 32;
+        // LDS-tiled T = 64 on the 8-expert layer: 0.48 against 0.51 ms; tile-stream T = 128
+        // 0.48 against 0.49 ms, T = 256 0.66 against 0.57); int4: 64-row tiles (the
+        // registers of a 128-row tile do not fit)
+        bm = i4 ? 64 : (i8 ? ((long long)T * k <= (tstream ? 32LL : 24LL) * L->E ? 64 : 128) : 256);
         const int kq = i4 ? 128 : 64;  // every split a whole number of K steps
         // split the down projection's K (S = 2 or 4) when that fills the last round of
         // workgroups better: with W = tiles * column tiles * S workgroups, one per CU at a
-        // time, the busy fraction is W / (rounds * CUs); a split must gain 0.1 of it (the
+        // time (tile-stream: two), the busy fraction is W / (rounds * slots); a split must gain 0.1 of it (the
         // partial rows cost combine traffic), keep K >= 2048 per split and fit the combine
         // buffer. The tile count is its expectation under uniform routing: a routed expert
         // holds n ~ Binomial(T, k/E) rows (normal approximation) and needs
@@ -351,9 +367,10 @@ Plan make_plan(const moe_layer* L, int T) {
         for (int j = 0; j * bm < T; ++j) tiles_e += 0.5 * std::erfc((j * bm + 0.5 - mu) / (sd * std::sqrt(2.0)));
         const double est_tiles = L->E * tiles_e + L->V * (double)((T + bm - 1) / bm);
         const int nt_down = (d.d_model + 255) / 256;
+        const int slots = tstream ? 2 * L->cus : L->cus;  // workgroups one round runs
         auto busy = [&](int S) {
             const double w = est_tiles * nt_down * S;
-            return w / (std::ceil(w / L->cus) * L->cus);
+            return w / (std::ceil(w / slots) * slots);
         };
         double best = busy(1);
         for (int S = 2; S <= 4; S *= 2) {
@@ -373,7 +390,7 @@ Plan make_plan(const moe_layer* L, int T) {
     // tiled down projection of a shared expert in several slices: the slices of a row tile
     // are summed in one K loop (one partial row per token instead of one per slice)
     const bool merge = !f32 && !streaming && !i8 && !i4 && L->V > 1 && ksplit == 1;
-    return Plan{streaming, bm, ksplit, max_tiles, merge, weights_once};
+    return Plan{streaming, bm, ksplit, max_tiles, merge, weights_once, tstream};
 }
 
 // Routers wider than 16 columns (experts + shared gate) at decode batch sizes: the split gate.
@@ -489,6 +506,10 @@ int run_experts(moe_layer* L, const Work& W, const void* x, int T, void* y, cons
         HIP_TRY(launch_expert_up_stream(a, wq, s));
         if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));
         HIP_TRY(launch_expert_down_stream(a, wq, s));
+    } else if (pl.tstream) {
+        HIP_TRY(launch_expert_up_tstream(a, wq, s));
+        if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));
+        HIP_TRY(launch_expert_down_tstream(a, wq, s));
     } else {
         HIP_TRY(launch_expert_up_tiled(a, wq, s));
         if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));

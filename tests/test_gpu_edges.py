@@ -6,7 +6,7 @@ both sides of the streaming / tiled switch, every token routed to one expert, an
 expert holding more rows than the streaming row tile (more tiles than active experts), a
 shared expert of one and of sixteen d_ff slices, int8 output channels and int4
 groups whose scale is zero, the smallest int4 widths, the decode routing paths for routers wider than 16 columns,
-int8 token rows of extreme or widely spread magnitudes on the tiled path, and decode K loops
+int8 token rows of extreme or widely spread magnitudes on both mid-size paths, and decode K loops
 that end with steps after their last whole round.
 """
 import numpy as np
@@ -117,11 +117,14 @@ def test_int8_zero_scale_channels():
     _run(synth.get_config("int8_mixtral22b", d_model=256, d_ff=128), [1, 300], mutate=zero)
 
 
-def test_int8_tiled_extreme_rows():
-    # the tiled int8 path on token rows of extreme magnitude: rows scaled by 1e15 and 1e-15,
-    # an all-zero row (its output is exactly zero), and rows spanning 2^20 and 2^40 inside
-    # themselves. Each row is checked against the oracle on its own scale.
-    cfg = synth.get_config("int8_mixtral22b", d_model=256, d_ff=256)
+@pytest.mark.parametrize("d_model", [256, 384])
+def test_int8_extreme_rows(d_model):
+    # int8 experts past the streaming sizes on token rows of extreme magnitude: rows scaled
+    # by 1e15 and 1e-15, an all-zero row (its output is exactly zero), and rows spanning 2^20
+    # and 2^40 inside themselves. Each row is checked against the oracle on its own scale.
+    # d_model = 256: the tile-stream kernels; 384 (a partial last column tile): the
+    # LDS-tiled ones.
+    cfg = synth.get_config("int8_mixtral22b", d_model=d_model, d_ff=256)
     L = synth.make_layer(cfg)
     olay = oracle_layer(L)
     T = 200

@@ -52,12 +52,13 @@ def test_skewed_bf16_full():
 
 
 def test_int8_mixtral22b_full():
-    # T = 1, 16 on the streaming kernels; 64 (every row compared) and 256 on the tiled ones
-    _run("int8_mixtral22b", [1, 16, 64, 256])
+    # T = 1, 16 on the streaming kernels; 64, 256 and 512 on the tile-stream ones (512:
+    # experts over one 128-row tile, the down projection's K split four ways)
+    _run("int8_mixtral22b", [1, 16, 64, 256, 512])
 
 
 def test_int4_mixtral22b_full():
-    _run("int4_mixtral22b", [1, 16, 64, 256])
+    _run("int4_mixtral22b", [1, 16, 64, 256, 512])
 
 
 def test_mixtral_bf16_routed_full():

@@ -61,19 +61,30 @@ def test_skewed_many_experts_reduced_bf16():
 
 
 def test_int8_reduced():
-    # streaming kernels up to T = 32, tiled past it
+    # streaming kernels up to T = 32, tile-stream past it
     cfg = synth.get_config("int8_mixtral22b", d_model=512, d_ff=1024)
     _run(cfg, [1, 16, 32, 33, 64, 256, 1024, 3072])
 
 
 def test_int4_reduced():
-    # int4 group-wise weights: the streaming kernels up to T = 64 (row tiles of 16 and 32 rows,
-    # with four experts several 32-row tiles per expert), the LDS-tiled MFMA kernels past it
-    # (64-row tiles, several per expert, ragged last tiles holding one or two 16-row blocks
-    # per wave)
+    # int4 group-wise weights: the streaming kernels up to T = 32 (row tiles of 16 and 32 rows,
+    # with four experts several 32-row tiles per expert), the tile-stream kernels past it
+    # (64-row tiles, several per expert, ragged last tiles of one to four 16-row blocks)
     cfg = synth.get_config("int4_mixtral22b", d_model=512, d_ff=1024)
     _run(cfg, [1, 2, 16, 32, 33, 40, 64, 65, 256, 1000])
     _run(synth.get_config("int4_mixtral22b", d_model=512, d_ff=1024, n_experts=4), [20, 32, 64])
+
+
+@pytest.mark.parametrize("name,Ts", [
+    ("int8_mixtral22b", [40, 100, 130, 200, 260, 330, 400, 470, 520]),
+    ("int4_mixtral22b", [40, 80, 130, 200, 250, 520]),
+])
+def test_tile_stream_row_blocks(name, Ts):
+    # the tile-stream kernels over every count of 16-row blocks a tile can hold (int8: 64-row
+    # tiles up to 32 rows per expert on average, then 128; int4: 64), each count with its own
+    # number of K steps in flight (int8 up projection, 8 K steps: 4 in flight below 5 row
+    # blocks, 3 at 5-6 (a partial last round), 2 at 7-8), and experts over one tile
+    _run(synth.get_config(name, d_model=512, d_ff=1024), Ts)
 
 
 def test_quantised_partial_column_tiles():
