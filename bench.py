@@ -40,6 +40,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "expert_gemm": ["expert_gemm.hip", "common.h"],
     "expert_stream": ["expert_stream.hip", "common.h"],
+    "expert_tstream": ["expert_tstream.hip", "common.h"],
 }
 
 
@@ -243,8 +244,16 @@ def summarize(cfg, res):
         rf = dict(bound="mfma", achieved=up["flops"] / (up_ms * 1e-3) / 1e12, peak=MFMA_BF16_PEAK_TFLOPS,
                   unit="TFLOP/s")
     rf["frac"] = rf["achieved"] / rf["peak"]
-    stream_max = 32 if cfg.expert_dtype == "i8" else 64  # the library's launch plan
-    kern = ("expert_stream" if T <= stream_max else "expert_gemm") if cfg.expert_dtype != "f32" else "expert_f32"
+    # the up kernel the library's launch plan picks
+    quant = cfg.expert_dtype in ("i8", "i4")
+    if cfg.expert_dtype == "f32":
+        kern = "expert_f32"
+    elif T <= (32 if quant else 64):
+        kern = "expert_stream"
+    elif quant and (2 * cfg.d_ff) % 256 == 0 and cfg.d_model % 256 == 0:
+        kern = "expert_tstream"
+    else:
+        kern = "expert_gemm"
     rf["kernel"] = f"{kern}<up>"
     rf["traffic"] = lookup_traffic(kern, f"up|{cfg.name}|T={T}") if kern in KERNEL_SOURCES else None
     rf["avg_ms"] = up_ms
