@@ -84,10 +84,12 @@ typedef enum moe_gate_weighting {
  * experts d_model % 128 == 0 and d_ff % 64 == 0; for I4 experts d_model % 128
  * == 0 and d_ff % 128 == 0; for F32 experts d_model % 64 == 0 and d_ff % 64 ==
  * 0. shared_d_ff > 0 adds a shared expert (BF16 experts only) and must be a
- * multiple of d_ff. Which kernels run is chosen per call from T: BF16 and I4
- * weights stream from HBM for T <= 64 and run on the LDS-tiled MFMA GEMMs above;
- * I8 weights stream for T <= 32 and run tiled above (F32 experts always run on
- * the fp32 kernels). */
+ * multiple of d_ff. Which kernels run is chosen per call from T: BF16 weights
+ * stream from HBM for T <= 64 and run on the LDS-tiled MFMA GEMMs above; I8 and I4
+ * weights stream for T <= 32 and above it run on the tile-stream GEMMs (token rows
+ * staged in LDS, weights streamed into registers) when 2*d_ff and d_model are
+ * multiples of 256, else on the LDS-tiled GEMMs (F32 experts always run on the fp32
+ * kernels). */
 typedef struct moe_desc {
     int32_t d_model;
     int32_t n_experts;
