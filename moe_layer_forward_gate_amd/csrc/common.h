@@ -125,6 +125,9 @@ hipError_t launch_expert_down_tiled(const GemmArgs& a, int wq, hipStream_t s);
 // the row tile staged in LDS (a.bm 64 or 128 for int8, 64 for int4; N % 256 == 0)
 hipError_t launch_expert_up_tstream(const GemmArgs& a, int wq, hipStream_t s);
 hipError_t launch_expert_down_tstream(const GemmArgs& a, int wq, hipStream_t s);
+// The int8 tile-stream down projection takes two column blocks per wave (128 columns per
+// workgroup) while the experts average at most 64 rows (T * k routed rows over E experts).
+inline bool tstream_narrow_down(int T, int k, int E) { return (long long)T * k <= 64LL * E; }
 // Token rows into the tiled up operand a.xp (padded rows past an expert's last row are
 // zero; shared virtual experts after the first are not written, the up kernel reads the
 // first one's rows for them). Reads the scatter's tile list on the device; writes

@@ -3,12 +3,13 @@
 //
 // Between decode and prefill an int8 or int4 expert holds tens to a few hundred rows
 // and its weights are still most of the traffic ([hotelren §2.1]: the bottleneck is
-// moving data). Here each wave owns four 16-column weight blocks and streams them from
+// moving data). Here each wave owns four 16-column weight blocks (two in the int8 down
+// projection of 64-row tiles) and streams them from
 // HBM over the whole K range as contiguous 1 KB chunks straight into MFMA operand
 // registers (no LDS round trip, each weight byte widened once), while the workgroup's
 // row tile (up to 128 rows) is staged in LDS by LDS-DMA, K step by K step, and read by
 // all four waves: every wave multiplies every row of the tile against its own columns.
-//   - Workgroup = (row tile, 256 columns, K split), 4 waves; the tile list, the padded
+//   - Workgroup = (row tile, 256 or 128 columns, K split), 4 waves; the tile list, the padded
 //     A operand (xp for the up projection, packed H for the down projection) and the
 //     outputs are those of the LDS-tiled kernels, so the two are interchangeable.
 //   - R K steps of loads are in flight per wave (2 to 4, the most the registers hold beside
@@ -29,8 +30,6 @@ namespace {
 
 constexpr int kNW = 4;                 // waves per workgroup
 constexpr int kThreads = kNW * kWave;
-constexpr int kNBW = 4;                // 16-column weight blocks per wave
-constexpr int kBN = kNW * kNBW * 16;   // columns per workgroup
 constexpr int kGN = 4, kGNAll = 6;     // column tiles per group (see decode_tile_at)
 constexpr int kChunk = 32;             // tiles dealt to the XCDs in chunks
 
@@ -79,17 +78,20 @@ __host__ __device__ constexpr int ring_blocks(int MB) {
     return m;
 }
 
-// MB: 16-row blocks per tile (a.bm = 16 MB); WQ: kWI8 or kWI4
-template <int MB, int WQ, bool UP>
+// MB: 16-row blocks per tile (a.bm = 16 MB); WQ: kWI8 or kWI4; NBW: 16-column weight
+// blocks per wave (4; 2 for the int8 down projection of 64-row tiles)
+template <int MB, int WQ, bool UP, int NBW>
 __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
     constexpr bool INT4 = WQ == kWI4;
     static_assert(WQ == kWI8 || WQ == kWI4, "quantised weights");
     constexpr int KSTEP = INT4 ? 128 : 64;  // K per weight chunk
     constexpr int KH = KSTEP / 32;          // 32-K row-block fragments per K step
+    constexpr int BN = kNW * NBW * 16;      // columns per workgroup
+    static_assert(NBW == 4 || (!UP && NBW == 2), "the up epilogue writes 32-column H blocks");
 
     const int K = UP ? a.d : a.F;
     const int N = UP ? 2 * a.F : a.d;
-    const int NT_ = N / kBN;
+    const int NT_ = N / BN;
     const int S = UP ? 1 : a.ksplit;
     Tile tl;
     int split = 0;
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
     const int nsteps = Kp / KSTEP;
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar addressing
-    const int nb0 = tl.n * (kBN / 16) + wave * kNBW;  // first owned column block
+    const int nb0 = tl.n * (BN / 16) + wave * NBW;  // first owned column block
 
     extern __shared__ u32x4 lds[];  // [R + 1][MA * KH][64]; the epilogue's patches afterwards
 
@@ -120,11 +122,11 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
     const bf16_t* abase = (UP ? a.xp : a.h) + (((size_t)ga * MB * (K / 32) + kbase / 32) * 64 + lane) * 8;
     const int mb_act = (tl.rows + 15) / 16;
 
-    f32x4 acc[MB][kNBW];
+    f32x4 acc[MB][NBW];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int j = 0; j < kNBW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NBW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     uint32_t nib_mask = 0x000F000Fu;  // int4 unpacking: held in a register (one v_and_or_b32 a pair)
     if constexpr (INT4) asm volatile("" : "+v"(nib_mask));
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
         constexpr int NS = R + 1;              // LDS slots
         constexpr int SLOT = MA * KH;          // 1 KB blocks per slot
         constexpr int AW = (MA * KH + kNW - 1) / kNW;
-        constexpr int X = kNBW + (INT4 ? kNBW : 0) + AW;  // vector memory loads per wave per step
+        constexpr int X = NBW + (INT4 ? NBW : 0) + AW;  // vector memory loads per wave per step
         static_assert((R - 1) * X < 64, "wait count");
         size_t aoff[AW];
         int aslot[AW];
@@ -152,16 +154,16 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
             aslot[i] = b;
         }
         struct Regs {
-            u32x4 b[kNBW];
-            float sc[kNBW];
+            u32x4 b[NBW];
+            float sc[NBW];
         };
         Regs ring[R];
         auto issue = [&](int s, Regs& rg, int slot) __attribute__((always_inline)) {
 #pragma unroll
-            for (int j = 0; j < kNBW; ++j) rg.b[j] = load_w<NT>(bbase + ((size_t)j * KB + s) * 64 + lane);
+            for (int j = 0; j < NBW; ++j) rg.b[j] = load_w<NT>(bbase + ((size_t)j * KB + s) * 64 + lane);
             if constexpr (INT4) {
 #pragma unroll
-                for (int j = 0; j < kNBW; ++j) rg.sc[j] = sbase[(size_t)s * N + j * 16 + lane % 16];
+                for (int j = 0; j < NBW; ++j) rg.sc[j] = sbase[(size_t)s * N + j * 16 + lane % 16];
             }
 #pragma unroll
             for (int i = 0; i < AW; ++i)
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
                 constexpr int MH = MA <= 2 ? MA : (MA + 1) / 2;  // row blocks per pass
 #pragma unroll
                 for (int m0 = 0; m0 < MA; m0 += MH) {
-                    f32x4 zr[MH], g[MH][kNBW];
+                    f32x4 zr[MH], g[MH][NBW];
 #pragma unroll
                     for (int kh = 0; kh < KH; ++kh) {
                         bf16x8 af[MH];
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
                                                                                 kh ? zr[i] : f32x4{0.f, 0.f, 0.f, 0.f},
                                                                                 0, 0, 0);
 #pragma unroll
-                        for (int j = 0; j < kNBW; ++j) {
+                        for (int j = 0; j < NBW; ++j) {
                             const uint32_t w = rg.b[j][kh];
                             const bf16x8 bw = __builtin_bit_cast(
                                 bf16x8, u32x4{(w & nib_mask) | 0x43004300u, ((w >> 4) & nib_mask) | 0x43004300u,
@@ -208,7 +210,7 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
                         }
                     }
 #pragma unroll
-                    for (int j = 0; j < kNBW; ++j)
+                    for (int j = 0; j < NBW; ++j)
 #pragma unroll
                         for (int i = 0; i < MH; ++i)
                             if (m0 + i < MA)
@@ -221,9 +223,9 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
                 // (one row fragment live at a time)
 #pragma unroll
                 for (int kh = 0; kh < KH; ++kh) {
-                    bf16x8 bw[kNBW];
+                    bf16x8 bw[NBW];
 #pragma unroll
-                    for (int j = 0; j < kNBW; ++j) {
+                    for (int j = 0; j < NBW; ++j) {
                         const uint32_t lo = kh ? rg.b[j].z : rg.b[j].x, hi = kh ? rg.b[j].w : rg.b[j].y;
                         bw[j] = __builtin_bit_cast(
                             bf16x8, u32x4{i8x2_bf16(lo, 0), i8x2_bf16(lo, 16), i8x2_bf16(hi, 0), i8x2_bf16(hi, 16)});
@@ -232,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
                     for (int mb = 0; mb < MA; ++mb) {
                         const bf16x8 af = __builtin_bit_cast(bf16x8, la[(mb * KH + kh) * 64]);
 #pragma unroll
-                        for (int j = 0; j < kNBW; ++j)
+                        for (int j = 0; j < NBW; ++j)
                             acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bw[j], acc[mb][j], 0, 0, 0);
                     }
                 }
@@ -296,10 +298,10 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
         // H patch: 16 MB rows x 32 bf16 columns (the wave's two gate/up pairs); H goes out in
         // the down operand's fragment order, every row of the tile (rows past the expert's
         // last row are zero: zero inputs, or row blocks never multiplied)
-        constexpr int PW = 8 * kNBW;
+        constexpr int PW = 8 * NBW;
         bf16_t* patch = reinterpret_cast<bf16_t*>(lds) + (size_t)wave * (16 * MB) * PW;
 #pragma unroll
-        for (int q = 0; q < kNBW / 2; ++q) {
+        for (int q = 0; q < NBW / 2; ++q) {
             float sg = 1.f, su = 1.f;
             if constexpr (!INT4) {
                 const int f = (nb0 / 2 + q) * 16 + col16;
@@ -324,11 +326,34 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
             const size_t blk = ((size_t)tl.g * MB + mb) * (a.F / 32) + fb;
             *reinterpret_cast<u32x4*>(a.h + (blk * 64 + lane) * 8) = v;
         }
+    } else if constexpr (NBW == 2) {
+        // fp32 partial rows straight from the accumulators (no LDS patch, so more workgroups
+        // fit a CU): lane holds column lane%16 of each 16-column block, rows 4*(lane/16)+i,
+        // one 64-byte row piece per block and row
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = mb * 16 + rq + i;
+                if (r < tl.rows) {
+                    const int cs = a.sorted_c[tl.seg0 + tl.row0 + r];
+                    const int t = cs / a.kt, j = cs - t * a.kt;
+                    const float wgt = j < a.k ? a.topk_w[(size_t)t * a.k + j] : a.gs[t];
+                    float* orow = a.ow + ((size_t)cs * S + split) * a.d;
+#pragma unroll
+                    for (int jn = 0; jn < NBW; ++jn) {
+                        const int n = (nb0 + jn) * 16 + col16;
+                        float v = acc[mb][jn][i] * wgt;
+                        if constexpr (!INT4) v *= a.s_down[(size_t)tl.e * a.d + n];
+                        orow[n] = v;  // partial sum `split` of slot cs
+                    }
+                }
+            }
     } else {
         // output patch: 16 MB rows x 32 fp32 columns, two 16-column blocks at a time
         float* patch = reinterpret_cast<float*>(lds) + (size_t)wave * (16 * MB) * 32;
 #pragma unroll
-        for (int nh = 0; nh < kNBW / 2; ++nh) {
+        for (int nh = 0; nh < NBW / 2; ++nh) {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -354,24 +379,25 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
     }
 }
 
-template <int MB, int WQ, bool UP>
+template <int MB, int WQ, bool UP, int NBW>
 hipError_t launch_r(const GemmArgs& a, hipStream_t s) {
     constexpr int KSTEP = WQ == kWI4 ? 128 : 64;
+    constexpr int BN = kNW * NBW * 16;
     constexpr size_t ring = (size_t)ring_blocks<WQ>(MB) * 1024;
-    constexpr size_t patch = (size_t)kNW * 16 * MB * 32 * (UP ? 2 : 4);
+    constexpr size_t patch = UP ? (size_t)kNW * 16 * MB * 32 * 2 : NBW == 4 ? (size_t)kNW * 16 * MB * 32 * 4 : 0;
     constexpr size_t lds_bytes = ring > patch ? ring : patch;
     static_assert(lds_bytes * (8 / kNW) <= 160 * 1024, "two waves per SIMD");
     const int N = UP ? 2 * a.F : a.d;
     const int S = UP ? 1 : a.ksplit;
     const int Kp = (UP ? a.d : a.F) / S;
-    if (a.bm != MB * 16 || N % kBN != 0 || Kp % KSTEP != 0 || Kp < KSTEP) return hipErrorInvalidValue;
-    const int NT = N / kBN;
+    if (a.bm != MB * 16 || N % BN != 0 || Kp % KSTEP != 0 || Kp < KSTEP) return hipErrorInvalidValue;
+    const int NT = N / BN;
     const int gn = NT <= kGNAll ? NT : kGN;
     const int NTp = (NT + gn - 1) / gn * gn;
     // the chunked deal needs the tile count rounded up to whole chunks per XCD
     const size_t blocks = (size_t)a.max_tiles * NTp * S + kXcds * kChunk;
     const dim3 grid((unsigned)((blocks + kXcds - 1) / kXcds * kXcds));
-    auto kern = expert_tstream<MB, WQ, UP>;
+    auto kern = expert_tstream<MB, WQ, UP, NBW>;
     static bool attr_set = false;  // one-time opt-in above the default dynamic LDS limit
     if (!attr_set) {
         const hipError_t e =
@@ -385,11 +411,23 @@ hipError_t launch_r(const GemmArgs& a, hipStream_t s) {
 
 template <int WQ, bool UP>
 hipError_t launch_w(const GemmArgs& a, hipStream_t s) {
+    // The int8 down projection while the experts average at most 64 rows: two column blocks
+    // per wave (128 registers: four workgroups per CU with 64-row tiles, three with 128-row
+    // ones; 8-expert 6144 x 16384 layer: T = 64 down 166 -> 140 us, layer 451 -> 429 us;
+    // T = 192 519 against 528 us). With more rows, or int4 weights, the doubled row-fragment
+    // reads per weight byte cost more than the waves gain (int8 T = 384: 671 -> 688 us, T =
+    // 1024 down 493 -> 594 us).
     if constexpr (WQ == kWI4) {
-        if (a.bm == 64) return launch_r<4, WQ, UP>(a, s);
+        if (a.bm == 64) return launch_r<4, WQ, UP, 4>(a, s);
     } else {
-        if (a.bm == 128) return launch_r<8, WQ, UP>(a, s);
-        if (a.bm == 64) return launch_r<4, WQ, UP>(a, s);
+        if constexpr (!UP) {
+            if (tstream_narrow_down(a.T, a.k, a.Et)) {
+                if (a.bm == 128) return launch_r<8, WQ, UP, 2>(a, s);
+                if (a.bm == 64) return launch_r<4, WQ, UP, 2>(a, s);
+            }
+        }
+        if (a.bm == 128) return launch_r<8, WQ, UP, 4>(a, s);
+        if (a.bm == 64) return launch_r<4, WQ, UP, 4>(a, s);
     }
     return hipErrorInvalidValue;
 }

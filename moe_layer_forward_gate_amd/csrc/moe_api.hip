@@ -355,8 +355,8 @@ Plan make_plan(const moe_layer* L, int T) {
         bm = i4 ? 64 : (i8 ? ((long long)T * k <= (tstream ? 32LL : 24LL) * L->E ? 64 : 128) : 256);
         const int kq = i4 ? 128 : 64;  // every split a whole number of K steps
         // split the down projection's K (S = 2 or 4) when that fills the last round of
-        // workgroups better: with W = tiles * column tiles * S workgroups, one per CU at a
-        // time (tile-stream: two), the busy fraction is W / (rounds * slots); a split must gain 0.1 of it (the
+        // workgroups better: with W = tiles * column tiles * S workgroups and `slots` of them
+        // at a time, the busy fraction is W / (rounds * slots); a split must gain 0.1 of it (the
         // partial rows cost combine traffic), keep K >= 2048 per split and fit the combine
         // buffer. The tile count is its expectation under uniform routing: a routed expert
         // holds n ~ Binomial(T, k/E) rows (normal approximation) and needs
@@ -366,8 +366,12 @@ Plan make_plan(const moe_layer* L, int T) {
         double tiles_e = 0.0;
         for (int j = 0; j * bm < T; ++j) tiles_e += 0.5 * std::erfc((j * bm + 0.5 - mu) / (sd * std::sqrt(2.0)));
         const double est_tiles = L->E * tiles_e + L->V * (double)((T + bm - 1) / bm);
-        const int nt_down = (d.d_model + 255) / 256;
-        const int slots = tstream ? 2 * L->cus : L->cus;  // workgroups one round runs
+        // down-projection column tiles and the workgroups one round runs: 256 columns, one per
+        // CU (LDS-tiled) or two (tile-stream); the narrow int8 tile-stream down projection
+        // takes 128 columns, four per CU with 64-row tiles and three with 128-row ones
+        const bool narrow = tstream && i8 && tstream_narrow_down(T, k, L->E);
+        const int nt_down = (d.d_model + (narrow ? 127 : 255)) / (narrow ? 128 : 256);
+        const int slots = (narrow ? (bm == 64 ? 4 : 3) : tstream ? 2 : 1) * L->cus;
         auto busy = [&](int S) {
             const double w = est_tiles * nt_down * S;
             return w / (std::ceil(w / slots) * slots);
