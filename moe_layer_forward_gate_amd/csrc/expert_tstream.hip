@@ -4,14 +4,14 @@
 // Between decode and prefill an int8 or int4 expert holds tens to a few hundred rows
 // and its weights are still most of the traffic ([hotelren §2.1]: the bottleneck is
 // moving data). Here each wave owns four 16-column weight blocks (two in the int8 down
-// projection of 64-row tiles) and streams them from
-// HBM over the whole K range as contiguous 1 KB chunks straight into MFMA operand
-// registers (no LDS round trip, each weight byte widened once), while the workgroup's
-// row tile (up to 128 rows) is staged in LDS by LDS-DMA, K step by K step, and read by
-// all four waves: every wave multiplies every row of the tile against its own columns.
-//   - Workgroup = (row tile, 256 or 128 columns, K split), 4 waves; the tile list, the padded
-//     A operand (xp for the up projection, packed H for the down projection) and the
-//     outputs are those of the LDS-tiled kernels, so the two are interchangeable.
+// projection while the experts average at most 64 rows) and streams them from HBM over
+// the whole K range as contiguous 1 KB chunks straight into MFMA operand registers (no
+// LDS round trip, each weight byte widened once), while the workgroup's row tile (up to
+// 128 rows) is staged in LDS by LDS-DMA, K step by K step, and read by all four waves:
+// every wave multiplies every row of the tile against its own columns.
+//   - Workgroup = (row tile, 256 or 128 columns, K split), 4 waves; the tile list, the
+//     padded A operand (xp for the up projection, packed H for the down projection) and
+//     the outputs are those of the LDS-tiled kernels, so the two are interchangeable.
 //   - R K steps of loads are in flight per wave (2 to 4, the most the registers hold beside
 //     the tile's accumulators; weights into a ring of R register sets, row blocks into R + 1
 //     LDS slots); one barrier per K step: after it, every wave's row blocks of this step
@@ -79,7 +79,7 @@ __host__ __device__ constexpr int ring_blocks(int MB) {
 }
 
 // MB: 16-row blocks per tile (a.bm = 16 MB); WQ: kWI8 or kWI4; NBW: 16-column weight
-// blocks per wave (4; 2 for the int8 down projection of 64-row tiles)
+// blocks per wave (4; 2 for the int8 down projection of experts with few rows)
 template <int MB, int WQ, bool UP, int NBW>
 __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
     constexpr bool INT4 = WQ == kWI4;
@@ -290,7 +290,8 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
     if (a.tile_start[tl.e + 1] - a.tile_start[tl.e] == 1) run(std::true_type{});
     else run(std::false_type{});
 
-    // ---- epilogue: the LDS-tiled kernels' output layouts, through a per-wave LDS patch
+    // ---- epilogue: the LDS-tiled kernels' output layouts, through a per-wave LDS patch (the
+    // down projection with two column blocks per wave stores from the accumulators)
     const int col16 = lane % 16;
     const int rq = 4 * (lane / 16);
     __syncthreads();  // every wave is done with the row-block slots
