@@ -19,8 +19,8 @@
 //   - Only the row blocks that hold rows are loaded and multiplied (a compile-time count,
 //     one instantiation per count, so the K loop has no branch).
 // int8 chunks hold 16 columns x 64 K (bytes 0-7 the first 32-K half), widened to bf16 in
-// registers; int4 chunks 16 columns x 128 K (one scale group), unpacked as q + 136 with
-// 136 * sum(a) taken off per group, as in the other kernels.
+// registers; int4 chunks 16 columns x 128 K (one scale group), unpacked as q + 136, with
+// 136 * sum(a) taken off per group through the MFMA accumulator's starting value.
 #include <type_traits>
 
 #include "common.h"
@@ -172,30 +172,38 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
         auto compute = [&](const Regs& rg, int slot) __attribute__((always_inline)) {
             const u32x4* la = lds + (size_t)slot * SLOT * 64 + lane;
             if constexpr (INT4) {
-                const bf16x8 k136 =
-                    __builtin_bit_cast(bf16x8, u32x4{0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u});
-                // one scale group: its partial products (codes read as q + 136) and 136 * the
-                // rows' sums over the group, then acc += scale * (partial - 136 * sum); in
-                // passes of at most two row blocks, each unpacking the weights again, so that
-                // a pass's partials fit beside the accumulators with three K steps in flight
-                // (int4 T = 256-1024 on the 8-expert 6144 x 16384 layer: 1-3% faster than one
-                // pass with two in flight)
+                // one scale group: the MFMAs of the rows' fragments against the constant -136
+                // (bf16 0xC308) give -136 * the rows' sums over the group; the partial products
+                // of the codes (read as q + 136) accumulate onto that, so each partial comes out
+                // as sum(a * q), and acc += scale * partial is one FMA (8-expert 6144 x 16384
+                // layer: 2-5% faster than subtracting the sums after, T = 48-4096). In passes
+                // of at most two row blocks, each unpacking the weights again, so that a pass's
+                // fragments and partials fit beside the accumulators with three K steps in
+                // flight (1-3% over one pass with two).
+                const bf16x8 kneg136 =
+                    __builtin_bit_cast(bf16x8, u32x4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u});
                 constexpr int MH = MA <= 2 ? MA : (MA + 1) / 2;  // row blocks per pass
 #pragma unroll
                 for (int m0 = 0; m0 < MA; m0 += MH) {
-                    f32x4 zr[MH], g[MH][NBW];
+                    bf16x8 af[MH][KH];
+#pragma unroll
+                    for (int i = 0; i < MH; ++i)
+#pragma unroll
+                        for (int kh = 0; kh < KH; ++kh)
+                            if (m0 + i < MA) af[i][kh] = __builtin_bit_cast(bf16x8, la[((m0 + i) * KH + kh) * 64]);
+                    // -136 * the rows' sums over the group: the partials' starting value
+                    f32x4 zn[MH];
+#pragma unroll
+                    for (int i = 0; i < MH; ++i)
+                        if (m0 + i < MA) {
+                            zn[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int kh = 0; kh < KH; ++kh)
+                                zn[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i][kh], kneg136, zn[i], 0, 0, 0);
+                        }
+                    f32x4 g[MH][NBW];
 #pragma unroll
                     for (int kh = 0; kh < KH; ++kh) {
-                        bf16x8 af[MH];
-#pragma unroll
-                        for (int i = 0; i < MH; ++i)
-                            if (m0 + i < MA) af[i] = __builtin_bit_cast(bf16x8, la[((m0 + i) * KH + kh) * 64]);
-#pragma unroll
-                        for (int i = 0; i < MH; ++i)
-                            if (m0 + i < MA)
-                                zr[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], k136,
-                                                                                kh ? zr[i] : f32x4{0.f, 0.f, 0.f, 0.f},
-                                                                                0, 0, 0);
 #pragma unroll
                         for (int j = 0; j < NBW; ++j) {
                             const uint32_t w = rg.b[j][kh];
@@ -205,8 +213,8 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
 #pragma unroll
                             for (int i = 0; i < MH; ++i)
                                 if (m0 + i < MA)
-                                    g[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                        af[i], bw, kh ? g[i][j] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                                    g[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i][kh], bw,
+                                                                                      kh ? g[i][j] : zn[i], 0, 0, 0);
                         }
                     }
 #pragma unroll
@@ -216,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
                             if (m0 + i < MA)
 #pragma unroll
                                 for (int c = 0; c < 4; ++c)
-                                    acc[m0 + i][j][c] = fmaf(rg.sc[j], g[i][j][c] - zr[i][c], acc[m0 + i][j][c]);
+                                    acc[m0 + i][j][c] = fmaf(rg.sc[j], g[i][j][c], acc[m0 + i][j][c]);
                 }
             } else {
                 // per 32-K half: the four widened weight fragments, then row block by row block
