@@ -153,26 +153,30 @@ __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
         auto step = [&](const u32x4 (&bb)[NBW], const u32x4 (&aa)[MB][KH], const float (&sc)[NBW])
                         __attribute__((always_inline)) {
             if constexpr (INT4) {
-                // one scale group: its partial products (codes read as q + 136) and 136 * the
-                // rows' sums over the group, then acc += scale * (partial - 136 * sum)
-                const bf16x8 k136 =
-                    __builtin_bit_cast(bf16x8, u32x4{0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u});
-                f32x4 zr[MA], g[NBW][MA];
+                // one scale group: the MFMAs of the token fragments against the constant -136
+                // give -136 * the rows' sums over the group, the partial products of the codes
+                // (read as q + 136) accumulate onto that, so each partial comes out as
+                // sum(a * q), and acc += scale * partial is one FMA
+                const bf16x8 kneg136 =
+                    __builtin_bit_cast(bf16x8, u32x4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u});
+                f32x4 zn[MA], g[NBW][MA];
+#pragma unroll
+                for (int mb = 0; mb < MA; ++mb) {
+                    zn[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kh = 0; kh < KH; ++kh)
+                        zn[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aa[mb][kh]), kneg136,
+                                                                         zn[mb], 0, 0, 0);
+                }
 #pragma unroll
                 for (int kh = 0; kh < KH; ++kh) {
-#pragma unroll
-                    for (int mb = 0; mb < MA; ++mb)
-                        zr[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aa[mb][kh]), k136,
-                                                                         kh ? zr[mb] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0,
-                                                                         0);
 #pragma unroll
                     for (int j = 0; j < NBW; ++j) {
                         const bf16x8 bw = __builtin_bit_cast(bf16x8, i4x8_bf16(bb[j][kh], nib_mask));
 #pragma unroll
                         for (int mb = 0; mb < MA; ++mb)
                             g[j][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                __builtin_bit_cast(bf16x8, aa[mb][kh]), bw, kh ? g[j][mb] : f32x4{0.f, 0.f, 0.f, 0.f},
-                                0, 0, 0);
+                                __builtin_bit_cast(bf16x8, aa[mb][kh]), bw, kh ? g[j][mb] : zn[mb], 0, 0, 0);
                     }
                 }
 #pragma unroll
@@ -180,8 +184,7 @@ __global__ __launch_bounds__(kThreads) void expert_stream(GemmArgs a, int S) {
 #pragma unroll
                     for (int mb = 0; mb < MA; ++mb)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            acc[mb][j][i] = fmaf(sc[j], g[j][mb][i] - zr[mb][i], acc[mb][j][i]);
+                        for (int i = 0; i < 4; ++i) acc[mb][j][i] = fmaf(sc[j], g[j][mb][i], acc[mb][j][i]);
                 return;
             }
 #pragma unroll
