@@ -87,6 +87,17 @@ def test_tile_stream_row_blocks(name, Ts):
     _run(synth.get_config(name, d_model=512, d_ff=1024), Ts)
 
 
+@pytest.mark.parametrize("name,E,k,Ts", [
+    ("int8_mixtral22b", 64, 8, [40, 300]),
+    ("int4_mixtral22b", 128, 4, [40, 700]),
+])
+def test_tile_stream_many_experts(name, E, k, Ts):
+    # the tile-stream kernels over 64 and 128 experts: the workgroup's expert is found by
+    # ballots over the tile table 64 entries at a time (two passes for 128), most experts
+    # hold a few rows, some none
+    _run(synth.get_config(name, d_model=256, d_ff=512, n_experts=E, top_k=k), Ts)
+
+
 def test_quantised_partial_column_tiles():
     # d_model = 384: the down projections' last 256-column tile holds 128 columns (int4: its
     # group scales are read by lanes 0-31 only); d_ff = 192 (int8): the up projection's last
