@@ -82,7 +82,8 @@ def test_streaming_expert_past_one_tile(name):
     # a bias of 2 on expert 3 puts it in slot 0 of (nearly) every token while the slot-1
     # weights stay near 0.2: at T = 32 (and 64 for bf16 weights) expert 3 holds T rows, twice
     # the streaming row tile, so the tiles outnumber the active experts (9 against 8 for this
-    # draw); quantised weights take the tiled kernels at T = 64, with one expert over its tile
+    # draw); quantised weights take the tile-stream kernels at T = 64, with one expert over
+    # its 64-row tile
     def bias(L):
         b = torch.zeros(L.cfg.n_experts, dtype=torch.float32)
         b[3] = 2.0
@@ -224,7 +225,7 @@ def test_gate_clamp(name, kw, Ts):
     ("mixtral_bf16", dict(d_model=128, d_ff=64, n_experts=32, top_k=4), [16], False),  # split decode gate
     ("mixtral_bf16", dict(d_model=128, d_ff=64, n_experts=32, top_k=10), [8], False),  # per-token gate, k > 8
     ("shared_fine_bf16", dict(d_model=256, d_ff=128, shared_d_ff=512), [3, 16, 200], False),  # shared column
-    ("int8_mixtral22b", dict(d_model=256, d_ff=128), [2, 70], False),        # int8 streaming and tiled experts
+    ("int8_mixtral22b", dict(d_model=256, d_ff=128), [2, 70], False),        # int8 streaming and tile-stream experts
     ("mixtral_bf16", dict(d_model=256, d_ff=128), [1, 300], True),           # raw weights of clamped logits
 ])
 def test_gate_raw_weighting(name, kw, Ts, clamp):

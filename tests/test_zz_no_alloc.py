@@ -1,7 +1,8 @@
 """moe_forward_noalloc (the forward in the library's static device scratch) against
 moe_forward through the C ABI: the same launch plan, so every output must be
 bit-identical, on two calls in a row with the second batch smaller, for the tiled
-prefill path, the weight-streaming decode path and the split decode gate; and a
+prefill path, the quantised tile-stream path, the weight-streaming decode path and the
+split decode gate; and a
 batch too large for the scratch is refused before anything is written."""
 import ctypes
 
