@@ -117,6 +117,13 @@ struct GemmArgs {
     float* ow;                  // [T*kt*ksplit][d] weighted expert outputs (partial sums)
     int d, F;
     int T;                      // tokens of the batch (a tile holds at most min(bm, T * k) rows)
+    // The down projection's row tiling, which H follows: tile table [Et+1] and height (a
+    // multiple of 16). The same as tile_start / bm but for the int4 tile-stream GEMMs at
+    // 41-72 rows per expert, whose up projection takes 80-row tiles (an expert's weights
+    // streamed once) and down projection 64-row ones; launch_pack_a then fills
+    // tile_start_h from the offsets.
+    int32_t* tile_start_h;
+    int bm_h;
 };
 // LDS-tiled MFMA GEMMs; wq: the weight kind (kWBf16, kWI8, kWI4), with a.bm 256, 128, 64
 hipError_t launch_expert_up_tiled(const GemmArgs& a, int wq, hipStream_t s);

@@ -60,11 +60,11 @@ __device__ __forceinline__ u32x4 load_w(const u32x4* p) {
     else return *p;
 }
 
-// K steps in flight per wave for a tile of MA row blocks: as many as the registers left
-// beside the accumulators hold (two waves per SIMD: 256 registers a wave)
+// K steps in flight per wave for MA row blocks of a tile of MB: as many as the registers
+// left beside the accumulators hold (two waves per SIMD: 256 registers a wave)
 template <int WQ>
-__host__ __device__ constexpr int ring_depth(int MA) {
-    return WQ == kWI4 ? (MA <= 2 ? 4 : 3) : (MA <= 4 ? 4 : MA <= 6 ? 3 : 2);
+__host__ __device__ constexpr int ring_depth(int MA, int MB) {
+    return WQ == kWI4 ? (MB > 4 ? (MA <= 2 ? 3 : 2) : MA <= 2 ? 4 : 3) : (MA <= 4 ? 4 : MA <= 6 ? 3 : 2);
 }
 
 // LDS of the K loop: (R + 1) slots of MA * KH 1 KB blocks, the most over MA <= MB
@@ -72,7 +72,7 @@ template <int WQ>
 __host__ __device__ constexpr int ring_blocks(int MB) {
     int m = 0;
     for (int ma = 1; ma <= MB; ++ma) {
-        const int b = (ring_depth<WQ>(ma) + 1) * ma * (WQ == kWI4 ? 4 : 2);
+        const int b = (ring_depth<WQ>(ma, MB) + 1) * ma * (WQ == kWI4 ? 4 : 2);
         m = b > m ? b : m;
     }
     return m;
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
     auto kloop = [&](auto ma, auto nt) __attribute__((always_inline)) {
         constexpr int MA = decltype(ma)::value;
         constexpr bool NT = decltype(nt)::value;
-        constexpr int R = ring_depth<WQ>(MA);  // K steps in flight
+        constexpr int R = ring_depth<WQ>(MA, MB);  // K steps in flight
         constexpr int NS = R + 1;              // LDS slots
         constexpr int SLOT = MA * KH;          // 1 KB blocks per slot
         constexpr int AW = (MA * KH + kNW - 1) / kNW;
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
                 // flight (1-3% over one pass with two).
                 const bf16x8 kneg136 =
                     __builtin_bit_cast(bf16x8, u32x4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u});
-                constexpr int MH = MA <= 2 ? MA : (MA + 1) / 2;  // row blocks per pass
+                constexpr int MH = MA < 2 ? MA : 2;  // row blocks per pass
 #pragma unroll
                 for (int m0 = 0; m0 < MA; m0 += MH) {
                     bf16x8 af[MH][KH];
@@ -275,7 +275,13 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
         wait_vm_le<0>();  // no LDS-DMA write may outlive the K loop
     };
     auto run = [&](auto nt) __attribute__((always_inline)) {
-        if constexpr (MB == 4) {
+        if constexpr (MB == 5) {
+            if (mb_act <= 1) kloop(std::integral_constant<int, 1>{}, nt);
+            else if (mb_act == 2) kloop(std::integral_constant<int, 2>{}, nt);
+            else if (mb_act == 3) kloop(std::integral_constant<int, 3>{}, nt);
+            else if (mb_act == 4) kloop(std::integral_constant<int, 4>{}, nt);
+            else kloop(std::integral_constant<int, 5>{}, nt);
+        } else if constexpr (MB == 4) {
             if (mb_act <= 1) kloop(std::integral_constant<int, 1>{}, nt);
             else if (mb_act == 2) kloop(std::integral_constant<int, 2>{}, nt);
             else if (mb_act == 3) kloop(std::integral_constant<int, 3>{}, nt);
@@ -305,8 +311,8 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
     __syncthreads();  // every wave is done with the row-block slots
     if constexpr (UP) {
         // H patch: 16 MB rows x 32 bf16 columns (the wave's two gate/up pairs); H goes out in
-        // the down operand's fragment order, every row of the tile (rows past the expert's
-        // last row are zero: zero inputs, or row blocks never multiplied)
+        // the down operand's fragment order (rows past the expert's last row inside a block
+        // are zero: zero inputs)
         constexpr int PW = 8 * NBW;
         bf16_t* patch = reinterpret_cast<bf16_t*>(lds) + (size_t)wave * (16 * MB) * PW;
 #pragma unroll
@@ -329,11 +335,19 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the patch is written
         static_assert(PW == 32, "one 32-column H block per wave");
         const int fb = nb0 / 2 * 16 / 32;
+        // H row blocks in the down projection's tiling (tiles of bm_h rows from
+        // tile_start_h[e]): the block holding rows r0 .. r0+15 of expert e is
+        // tile_start_h[e] * bm_h / 16 + r0 / 16 (with bm_h == bm, tile g's block mb). Only
+        // blocks holding rows are written; the down kernel reads no others.
+        const int hb0 = a.tile_start_h[tl.e] * (a.bm_h / 16) + tl.row0 / 16;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(patch + (mb * 16 + lane % 16) * PW + 8 * (lane / 16));
-            const size_t blk = ((size_t)tl.g * MB + mb) * (a.F / 32) + fb;
-            *reinterpret_cast<u32x4*>(a.h + (blk * 64 + lane) * 8) = v;
+            if (mb * 16 < tl.rows) {
+                const u32x4 v =
+                    *reinterpret_cast<const u32x4*>(patch + (mb * 16 + lane % 16) * PW + 8 * (lane / 16));
+                const size_t blk = (size_t)(hb0 + mb) * (a.F / 32) + fb;
+                *reinterpret_cast<u32x4*>(a.h + (blk * 64 + lane) * 8) = v;
+            }
         }
     } else if constexpr (NBW == 2) {
         // fp32 partial rows straight from the accumulators (no LDS patch, so more workgroups
@@ -427,6 +441,9 @@ hipError_t launch_w(const GemmArgs& a, hipStream_t s) {
     // reads per weight byte cost more than the waves gain (int8 T = 384: 671 -> 688 us, T =
     // 1024 down 493 -> 594 us).
     if constexpr (WQ == kWI4) {
+        if constexpr (UP) {  // 80-row tiles: up projection only (its down projection tiles by 64, bm_h)
+            if (a.bm == 80) return launch_r<5, WQ, UP, 4>(a, s);
+        }
         if (a.bm == 64) return launch_r<4, WQ, UP, 4>(a, s);
     } else {
         if constexpr (!UP) {

@@ -48,6 +48,7 @@ struct Work {
     int32_t* counts = nullptr;
     int32_t* offsets = nullptr;
     int32_t* tile_start = nullptr;
+    int32_t* tile_start_h = nullptr;  // the down projection's tile table when its tiling differs
     int32_t* sorted_c = nullptr;
     float* gs = nullptr;
     int32_t* ridx = nullptr;  // a caller's routing, checked (moe_forward_routed)
@@ -90,7 +91,8 @@ void release(moe_layer* L) {
     if (!L) return;
     const Work& w = L->w;
     void* bufs[] = {L->wr_t, L->wr_planes, L->bias, L->wgu, L->wdn, L->s_gate, L->s_up, L->s_down, w.counts, w.offsets,
-                    w.tile_start, w.sorted_c, w.gs, w.ridx, w.rw, w.gate_part, w.scatter_work, w.xp, w.h, w.ow};
+                    w.tile_start, w.tile_start_h, w.sorted_c, w.gs, w.ridx, w.rw, w.gate_part, w.scatter_work,
+                    w.xp, w.h, w.ow};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
     for (hipEvent_t e : L->ev)
@@ -201,6 +203,7 @@ int create_impl(const moe_desc* desc, const moe_weights* w, moe_layer* L) {
     if ((rc = dev_alloc(&ws.counts, (Et + 1) * 4))) return rc;
     if ((rc = dev_alloc(&ws.offsets, (Et + 1) * 4))) return rc;
     if ((rc = dev_alloc(&ws.tile_start, (Et + 1) * 4))) return rc;
+    if ((rc = dev_alloc(&ws.tile_start_h, (Et + 1) * 4))) return rc;
     if ((rc = dev_alloc(&ws.sorted_c, P * 4))) return rc;
     if ((rc = dev_alloc(&ws.gs, T * 4))) return rc;
     if ((rc = dev_alloc(&ws.ridx, T * d.top_k * 4))) return rc;
@@ -309,6 +312,8 @@ struct Plan {
     bool weights_once;  // streaming: the busiest expert is expected to fit one row tile
     bool tstream;       // quantised weights past the streaming sizes: row tiles in LDS, weights
                         // streamed into registers (expert_tstream) instead of the LDS-tiled GEMMs
+    int bm_h, max_tiles_h;  // the down projection's row tiling (H follows it); == bm, max_tiles
+                            // but for the int4 tile-stream 80-row up tiles
 };
 
 Plan make_plan(const moe_layer* L, int T) {
@@ -322,7 +327,7 @@ Plan make_plan(const moe_layer* L, int T) {
     // faster; int4 T = 48: 0.30 against 0.31 streaming); bf16 weights stream up to 64 (T = 64:
     // 0.50 against 0.58 ms tiled)
     const bool streaming = !f32 && T <= (i8 || i4 ? kStreamMaxT / 2 : kStreamMaxT);
-    int bm, ksplit = 1;
+    int bm, ksplit = 1, bm_h = 0;
     bool weights_once = true, tstream = false;
     if (f32) {
         bm = kBMf32;
@@ -353,6 +358,15 @@ Plan make_plan(const moe_layer* L, int T) {
         // 0.48 against 0.49 ms, T = 256 0.66 against 0.57); int4: 64-row tiles (the
         // registers of a 128-row tile do not fit)
         bm = i4 ? 64 : (i8 ? ((long long)T * k <= (tstream ? 32LL : 24LL) * L->E ? 64 : 128) : 256);
+        // int4 tile-stream with 41-72 rows per expert on average: 80-row up tiles, so nearly
+        // every expert's weights stream once (not again for a ragged second tile of a few
+        // rows), and 64-row down tiles (an 80-row int4 down kernel spills, and the smaller
+        // tiles give more workgroups): 8-expert 6144 x 16384 layer, T = 256 0.608 -> 0.569
+        // ms, T = 288 0.659 -> 0.623 ms
+        if (tstream && i4 && (long long)T * k > 40LL * L->E && (long long)T * k <= 72LL * L->E) {
+            bm = 80;
+            bm_h = 64;
+        }
         const int kq = i4 ? 128 : 64;  // every split a whole number of K steps
         // split the down projection's K (S = 2 or 4) when that fills the last round of
         // workgroups better: with W = tiles * column tiles * S workgroups and `slots` of them
@@ -363,15 +377,16 @@ Plan make_plan(const moe_layer* L, int T) {
         // ceil(n / bm) = sum_j [n > j*bm] tiles; a shared slice holds all T rows.
         const double p_e = (double)k / L->E;
         const double mu = T * p_e, sd = std::sqrt(std::max(T * p_e * (1.0 - p_e), 1e-12));
+        const int bmd = bm_h ? bm_h : bm;  // the down projection's tile height
         double tiles_e = 0.0;
-        for (int j = 0; j * bm < T; ++j) tiles_e += 0.5 * std::erfc((j * bm + 0.5 - mu) / (sd * std::sqrt(2.0)));
-        const double est_tiles = L->E * tiles_e + L->V * (double)((T + bm - 1) / bm);
+        for (int j = 0; j * bmd < T; ++j) tiles_e += 0.5 * std::erfc((j * bmd + 0.5 - mu) / (sd * std::sqrt(2.0)));
+        const double est_tiles = L->E * tiles_e + L->V * (double)((T + bmd - 1) / bmd);
         // down-projection column tiles and the workgroups one round runs: 256 columns, one per
         // CU (LDS-tiled) or two (tile-stream); the narrow int8 tile-stream down projection
         // takes 128 columns, four per CU with 64-row tiles and three with 128-row ones
         const bool narrow = tstream && i8 && tstream_narrow_down(T, k, L->E);
         const int nt_down = (d.d_model + (narrow ? 127 : 255)) / (narrow ? 128 : 256);
-        const int slots = (narrow ? (bm == 64 ? 4 : 3) : tstream ? 2 : 1) * L->cus;
+        const int slots = (narrow ? (bmd == 64 ? 4 : 3) : tstream ? 2 : 1) * L->cus;
         auto busy = [&](int S) {
             const double w = est_tiles * nt_down * S;
             return w / (std::ceil(w / slots) * slots);
@@ -391,10 +406,12 @@ Plan make_plan(const moe_layer* L, int T) {
     // one tile (the streaming tile is sized to the expected busiest expert, not a bound)
     const int P = T * L->kt;
     const int max_tiles = std::min(L->Et, P) + (P - 1) / bm;
+    if (!bm_h) bm_h = bm;
+    const int max_tiles_h = std::min(L->Et, P) + (P - 1) / bm_h;
     // tiled down projection of a shared expert in several slices: the slices of a row tile
     // are summed in one K loop (one partial row per token instead of one per slice)
     const bool merge = !f32 && !streaming && !i8 && !i4 && L->V > 1 && ksplit == 1;
-    return Plan{streaming, bm, ksplit, max_tiles, merge, weights_once, tstream};
+    return Plan{streaming, bm, ksplit, max_tiles, merge, weights_once, tstream, bm_h, max_tiles_h};
 }
 
 // Routers wider than 16 columns (experts + shared gate) at decode batch sizes: the split gate.
@@ -449,6 +466,7 @@ size_t carve_work(const moe_layer* L, const Plan& pl, int T, char* base, Work* W
     w.counts = (int32_t*)take((Et + 1) * 4);
     w.offsets = (int32_t*)take((Et + 1) * 4);
     w.tile_start = (int32_t*)take((Et + 1) * 4);
+    w.tile_start_h = (int32_t*)take((Et + 1) * 4);
     w.sorted_c = (int32_t*)take(P * 4);
     w.gs = (float*)take((size_t)T * 4);
     if (split_gate(L, T)) {
@@ -460,7 +478,7 @@ size_t carve_work(const moe_layer* L, const Plan& pl, int T, char* base, Work* W
     }
     if (T * d.top_k > kScatterWideMin) w.scatter_work = (int32_t*)take(scatter_wide_workspace(T * d.top_k, L->E));
     if (!f32 && !pl.streaming) w.xp = (bf16_t*)take(tiled_rows * dm * 2);
-    w.h = take((f32 || pl.streaming ? P : tiled_rows) * F * (f32 ? 4 : 2));
+    w.h = take((f32 || pl.streaming ? P : (size_t)pl.max_tiles_h * pl.bm_h) * F * (f32 ? 4 : 2));
     w.ow = (float*)take(P * pl.ksplit * dm * 4);
     if (W) *W = w;
     return off;
@@ -494,8 +512,10 @@ int run_experts(moe_layer* L, const Work& W, const void* x, int T, void* y, cons
     const bool prof = L->profiling;
     const GemmArgs a{W.tile_start, W.offsets, W.sorted_c, L->Et, L->kt, k, pl.max_tiles, pl.bm, pl.ksplit,
                      pl.merge ? 1 : 0, pl.weights_once ? 1 : 0, (const bf16_t*)x, W.xp, (bf16_t*)W.h, L->wgu, L->wdn,
-                     L->s_gate, L->s_up, L->s_down, topk_w, gs, W.ow, d.d_model, d.d_ff, T};
-    // the tiled GEMMs take the token rows already gathered into fragment order
+                     L->s_gate, L->s_up, L->s_down, topk_w, gs, W.ow, d.d_model, d.d_ff, T,
+                     pl.bm_h != pl.bm ? W.tile_start_h : W.tile_start, pl.bm_h};
+    // the tiled GEMMs take the token rows already gathered into fragment order (and, with a
+    // separate down tiling, launch_pack_a also fills its tile table)
     if (!f32 && !pl.streaming) HIP_TRY(launch_pack_a(a, s));
     if (prof) HIP_TRY(hipEventRecord(L->ev[2], s));
     if (f32) {
@@ -513,7 +533,12 @@ int run_experts(moe_layer* L, const Work& W, const void* x, int T, void* y, cons
     } else if (pl.tstream) {
         HIP_TRY(launch_expert_up_tstream(a, wq, s));
         if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));
-        HIP_TRY(launch_expert_down_tstream(a, wq, s));
+        // the down projection on its own row tiling (the one H was written in)
+        GemmArgs ad = a;
+        ad.tile_start = a.tile_start_h;
+        ad.bm = pl.bm_h;
+        ad.max_tiles = pl.max_tiles_h;
+        HIP_TRY(launch_expert_down_tstream(ad, wq, s));
     } else {
         HIP_TRY(launch_expert_up_tiled(a, wq, s));
         if (prof) HIP_TRY(hipEventRecord(L->ev[3], s));

@@ -33,6 +33,23 @@ __global__ __launch_bounds__(64) void scatter_wave_kernel(const int32_t* __restr
 __global__ __launch_bounds__(256) void pack_a_kernel(GemmArgs a) {
     const int lane = threadIdx.x % kWave;
     const int u = blockIdx.x * 4 + threadIdx.x / kWave;
+    // a separate down-projection tiling: its tile table, tile_start_h[e] = sum over e' < e of
+    // ceil(n_e' / bm_h), by the first wave (a prefix sum 64 experts at a time)
+    if (a.tile_start_h != a.tile_start && u == 0) {
+        int carry = 0;
+        if (lane == 0) a.tile_start_h[0] = 0;
+        for (int j0 = 0; j0 < a.Et; j0 += kWave) {
+            const int e = j0 + lane;
+            int t = e < a.Et ? (a.offsets[e + 1] - a.offsets[e] + a.bm_h - 1) / a.bm_h : 0;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const int y = __shfl_up(t, o, kWave);
+                if (lane >= o) t += y;
+            }
+            if (e < a.Et) a.tile_start_h[e + 1] = carry + t;
+            carry += __shfl(t, kWave - 1, kWave);
+        }
+    }
     const int KC = a.d / 128;
     if (u >= a.tile_start[a.Et] * (a.bm / 16) * KC) return;
     const int mb = u / KC, kc = u - (u / KC) * KC;
