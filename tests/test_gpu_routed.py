@@ -95,6 +95,30 @@ def test_routed_with_own_routing_is_bit_identical(name, kw):
     lay.close()
 
 
+def test_routed_int4_tile_boundaries():
+    # int4 tile-stream at 41-72 rows per expert on average (T = 200, k = 2, E = 8: 50): 80-row
+    # up tiles and 64-row down tiles, H written in the down tiling. Experts holding exactly
+    # 64, 65, 80 and 81 rows (one tile or two in either tiling), 1 row, and none.
+    cfg = synth.get_config("int4_mixtral22b", d_model=256, d_ff=256)
+    T, k = 200, cfg.top_k
+    counts = [64, 65, 80, 81, 1, 0, 59, 50]
+    assert sum(counts) == T * k and len(counts) == cfg.n_experts
+    rng = np.random.default_rng(7)
+    ids = np.repeat(np.arange(cfg.n_experts), counts)
+    rng.shuffle(ids)
+    idx = torch.from_numpy(ids.reshape(T, k).astype(np.int32))
+    w = torch.from_numpy(rng.uniform(0.1, 1.0, size=(T, k)).astype(np.float32))
+    L = synth.make_layer(cfg)
+    olay = oracle_layer(L)
+    lay = gpu_layer(L, T)
+    x = synth.make_tokens(cfg, T)
+    print(f"[routed] int4 tile boundaries T={T} counts={counts}", flush=True)
+    out = lay.forward_routed(x.cuda(), idx.cuda(), w.cuda(), None, scatter=True)
+    torch.cuda.synchronize()
+    _check(cfg, olay, x, idx, w, None, out, "int4 tile boundaries")
+    lay.close()
+
+
 def test_routed_argument_checks():
     cfg = synth.get_config("shared_fine_bf16", d_model=256, d_ff=64, n_experts=8, top_k=2, shared_d_ff=128)
     lay = gpu_layer(synth.make_layer(cfg), 8)
