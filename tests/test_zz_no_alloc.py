@@ -39,7 +39,7 @@ def _poison(out):
     ("mixtral_bf16", dict(d_model=512, d_ff=1024), (300, 5)),                 # tiled GEMMs, then streaming
     ("int8_mixtral22b", dict(d_model=512, d_ff=1024), (40, 16, 3)),           # int8 tile-stream, streaming
     ("shared_fine_bf16", dict(d_model=256, d_ff=128, shared_d_ff=512), (20, 2)),  # split gate, shared expert
-    ("int4_mixtral22b", dict(d_model=512, d_ff=1024), (70, 9)),               # int4 tile-stream, streaming
+    ("int4_mixtral22b", dict(d_model=512, d_ff=1024), (250, 70, 9)),          # int4 80/64-row tile-stream, tile-stream, streaming
     ("tiny_f32", {}, (64, 7)),                                                # fp32 experts
 ])
 def test_noalloc_matches_forward(name, kw, Ts):
