@@ -64,7 +64,7 @@ __device__ __forceinline__ u32x4 load_w(const u32x4* p) {
 // left beside the accumulators hold (two waves per SIMD: 256 registers a wave)
 template <int WQ>
 __host__ __device__ constexpr int ring_depth(int MA, int MB) {
-    return WQ == kWI4 ? (MB > 4 ? (MA <= 2 ? 3 : 2) : MA <= 2 ? 4 : 3) : (MA <= 4 ? 4 : MA <= 6 ? 3 : 2);
+    return WQ == kWI4 ? (MB > 4 ? 3 : MA <= 2 ? 4 : 3) : (MA <= 4 ? 4 : MA <= 6 ? 3 : 2);
 }
 
 // LDS of the K loop: (R + 1) slots of MA * KH 1 KB blocks, the most over MA <= MB
@@ -177,12 +177,14 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
                 // of the codes (read as q + 136) accumulate onto that, so each partial comes out
                 // as sum(a * q), and acc += scale * partial is one FMA (8-expert 6144 x 16384
                 // layer: 2-5% faster than subtracting the sums after, T = 48-4096). In passes
-                // of at most two row blocks, each unpacking the weights again, so that a pass's
-                // fragments and partials fit beside the accumulators with three K steps in
-                // flight (1-3% over one pass with two).
+                // of at most two row blocks (one on 80-row tiles), each unpacking the weights
+                // again, so that a pass's fragments and partials fit beside the accumulators
+                // with three K steps in flight (64-row tiles: 1-3% over one pass with two
+                // steps; 80-row tiles: T = 256-288 up projection 3-6% over two-block passes
+                // with two steps, which also spilled).
                 const bf16x8 kneg136 =
                     __builtin_bit_cast(bf16x8, u32x4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u});
-                constexpr int MH = MA < 2 ? MA : 2;  // row blocks per pass
+                constexpr int MH = MB > 4 ? 1 : MA < 2 ? MA : 2;  // row blocks per pass
 #pragma unroll
                 for (int m0 = 0; m0 < MA; m0 += MH) {
                     bf16x8 af[MH][KH];
