@@ -360,9 +360,9 @@ Plan make_plan(const moe_layer* L, int T) {
         bm = i4 ? 64 : (i8 ? ((long long)T * k <= (tstream ? 32LL : 24LL) * L->E ? 64 : 128) : 256);
         // int4 tile-stream with 41-72 rows per expert on average: 80-row up tiles, so nearly
         // every expert's weights stream once (not again for a ragged second tile of a few
-        // rows), and 64-row down tiles (an 80-row int4 down kernel spills, and the smaller
-        // tiles give more workgroups): 8-expert 6144 x 16384 layer, T = 256 0.608 -> 0.569
-        // ms, T = 288 0.659 -> 0.623 ms
+        // rows), and 64-row down tiles (80-row down tiles measured within +-3% at T =
+        // 176-288, and the smaller tiles give more workgroups): 8-expert 6144 x 16384 layer,
+        // T = 256 0.608 -> 0.569 ms, T = 288 0.659 -> 0.623 ms
         if (tstream && i4 && (long long)T * k > 40LL * L->E && (long long)T * k <= 72LL * L->E) {
             bm = 80;
             bm_h = 64;
