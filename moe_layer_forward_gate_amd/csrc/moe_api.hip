@@ -371,8 +371,11 @@ Plan make_plan(const moe_layer* L, int T) {
         // split the down projection's K (S = 2 or 4) when that fills the last round of
         // workgroups better: with W = tiles * column tiles * S workgroups and `slots` of them
         // at a time, the busy fraction is W / (rounds * slots); a split must gain 0.1 of it (the
-        // partial rows cost combine traffic), keep K >= 2048 per split and fit the combine
-        // buffer. The tile count is its expectation under uniform routing: a routed expert
+        // partial rows cost combine traffic), keep K >= 2048 per split (4096 for a four-way
+        // split: the 8-expert bf16 layer's 14336-wide down projection ran as fast split in two
+        // as in four at T = 1024 and 2048, and the four-way split doubled the combine's
+        // partial rows, T = 2048 1.559 -> 1.530 ms) and fit the combine buffer. The tile
+        // count is its expectation under uniform routing: a routed expert
         // holds n ~ Binomial(T, k/E) rows (normal approximation) and needs
         // ceil(n / bm) = sum_j [n > j*bm] tiles; a shared slice holds all T rows.
         const double p_e = (double)k / L->E;
@@ -393,7 +396,7 @@ Plan make_plan(const moe_layer* L, int T) {
         };
         double best = busy(1);
         for (int S = 2; S <= 4; S *= 2) {
-            if (d.d_ff / S < 2048 || d.d_ff % (S * kq) != 0 || (size_t)T * L->kt * S > L->ow_rows) break;
+            if (d.d_ff / S < (S > 2 ? 4096 : 2048) || d.d_ff % (S * kq) != 0 || (size_t)T * L->kt * S > L->ow_rows) break;
             if (busy(S) > best + 0.1) {
                 best = busy(S);
                 ksplit = S;

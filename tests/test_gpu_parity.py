@@ -37,7 +37,8 @@ def test_tiny_f32_full():
 
 
 def test_mixtral_shape_reduced_bf16():
-    # T = 1024 splits the down projection's K in two; T = 3072 runs several full 256-row tiles per expert
+    # T = 1024 and 3072 run several 256-row tiles per expert (d_ff 1024 is too narrow to split
+    # the down projection's K)
     cfg = synth.get_config("mixtral_bf16", d_model=512, d_ff=1024)
     _run(cfg, [1, 8, 64, 300, 1024, 3072])
 
