@@ -250,7 +250,8 @@ def summarize(cfg, res):
         kern = "expert_f32"
     elif T <= (32 if quant else 64):
         kern = "expert_stream"
-    elif quant and (2 * cfg.d_ff) % 256 == 0 and cfg.d_model % 256 == 0:
+    elif (2 * cfg.d_ff) % 256 == 0 and cfg.d_model % 256 == 0 and (
+            quant or (cfg.shared_d_ff == 0 and T * cfg.top_k <= min(96 * cfg.n_experts, 4096))):
         kern = "expert_tstream"
     else:
         kern = "expert_gemm"

@@ -128,8 +128,9 @@ struct GemmArgs {
 // LDS-tiled MFMA GEMMs; wq: the weight kind (kWBf16, kWI8, kWI4), with a.bm 256, 128, 64
 hipError_t launch_expert_up_tiled(const GemmArgs& a, int wq, hipStream_t s);
 hipError_t launch_expert_down_tiled(const GemmArgs& a, int wq, hipStream_t s);
-// The same GEMMs for int8 and int4 weights with the weights streamed into registers and
-// the row tile staged in LDS (a.bm 64 or 128 for int8, 64 for int4; N % 256 == 0)
+// The same GEMMs with the weights streamed into registers and the row tile staged in LDS
+// (a.bm 128 for bf16, 64 or 128 for int8, 64 for int4 and 80 for its up projection;
+// N % 256 == 0)
 hipError_t launch_expert_up_tstream(const GemmArgs& a, int wq, hipStream_t s);
 hipError_t launch_expert_down_tstream(const GemmArgs& a, int wq, hipStream_t s);
 // The int8 tile-stream down projection takes two column blocks per wave (128 columns per

@@ -1,8 +1,7 @@
-// Expert compute for mid-size batches with quantised weights: row tiles in LDS,
-// weights streamed into registers.
+// Expert compute for mid-size batches: row tiles in LDS, weights streamed into registers.
 //
-// Between decode and prefill an int8 or int4 expert holds tens to a few hundred rows
-// and its weights are still most of the traffic ([hotelren §2.1]: the bottleneck is
+// Between decode and prefill an expert holds tens to a few hundred rows and its weights
+// are still most of the traffic ([hotelren §2.1]: the bottleneck is
 // moving data). Here each wave owns four 16-column weight blocks (two in the int8 down
 // projection while the experts average at most 64 rows) and streams them from HBM over
 // the whole K range as contiguous 1 KB chunks straight into MFMA operand registers (no
@@ -18,9 +17,10 @@
 //     have landed and the slot of the step before is free.
 //   - Only the row blocks that hold rows are loaded and multiplied (a compile-time count,
 //     one instantiation per count, so the K loop has no branch).
-// int8 chunks hold 16 columns x 64 K (bytes 0-7 the first 32-K half), widened to bf16 in
-// registers; int4 chunks 16 columns x 128 K (one scale group), unpacked as q + 136, with
-// 136 * sum(a) taken off per group through the MFMA accumulator's starting value.
+// bf16 chunks hold 16 columns x 32 K, the MFMA operand as it is; int8 chunks 16 columns x
+// 64 K (bytes 0-7 the first 32-K half), widened to bf16 in registers; int4 chunks 16
+// columns x 128 K (one scale group), unpacked as q + 136, with 136 * sum(a) taken off per
+// group through the MFMA accumulator's starting value.
 #include <type_traits>
 
 #include "common.h"
@@ -64,7 +64,7 @@ __device__ __forceinline__ u32x4 load_w(const u32x4* p) {
 // left beside the accumulators hold (two waves per SIMD: 256 registers a wave)
 template <int WQ>
 __host__ __device__ constexpr int ring_depth(int MA, int MB) {
-    return WQ == kWI4 ? (MB > 4 ? 3 : MA <= 2 ? 4 : 3) : (MA <= 4 ? 4 : MA <= 6 ? 3 : 2);
+    return WQ == kWBf16 ? 4 : WQ == kWI4 ? (MB > 4 ? 3 : MA <= 2 ? 4 : 3) : (MA <= 4 ? 4 : MA <= 6 ? 3 : 2);
 }
 
 // LDS of the K loop: (R + 1) slots of MA * KH 1 KB blocks, the most over MA <= MB
@@ -72,19 +72,18 @@ template <int WQ>
 __host__ __device__ constexpr int ring_blocks(int MB) {
     int m = 0;
     for (int ma = 1; ma <= MB; ++ma) {
-        const int b = (ring_depth<WQ>(ma, MB) + 1) * ma * (WQ == kWI4 ? 4 : 2);
+        const int b = (ring_depth<WQ>(ma, MB) + 1) * ma * (WQ == kWI4 ? 4 : WQ == kWI8 ? 2 : 1);
         m = b > m ? b : m;
     }
     return m;
 }
 
-// MB: 16-row blocks per tile (a.bm = 16 MB); WQ: kWI8 or kWI4; NBW: 16-column weight
-// blocks per wave (4; 2 for the int8 down projection of experts with few rows)
+// MB: 16-row blocks per tile (a.bm = 16 MB); WQ: kWBf16, kWI8 or kWI4; NBW: 16-column
+// weight blocks per wave (4; 2 for the int8 down projection of experts with few rows)
 template <int MB, int WQ, bool UP, int NBW>
 __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
-    constexpr bool INT4 = WQ == kWI4;
-    static_assert(WQ == kWI8 || WQ == kWI4, "quantised weights");
-    constexpr int KSTEP = INT4 ? 128 : 64;  // K per weight chunk
+    constexpr bool INT4 = WQ == kWI4, BF16 = WQ == kWBf16;
+    constexpr int KSTEP = INT4 ? 128 : BF16 ? 32 : 64;  // K per weight chunk
     constexpr int KH = KSTEP / 32;          // 32-K row-block fragments per K step
     constexpr int BN = kNW * NBW * 16;      // columns per workgroup
     static_assert(NBW == 4 || (!UP && NBW == 2), "the up epilogue writes 32-column H blocks");
@@ -228,6 +227,16 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
                                 for (int c = 0; c < 4; ++c)
                                     acc[m0 + i][j][c] = fmaf(rg.sc[j], g[i][j][c], acc[m0 + i][j][c]);
                 }
+            } else if constexpr (BF16) {
+                // the weight chunks are the MFMA operands as they are; row block by row block
+#pragma unroll
+                for (int mb = 0; mb < MA; ++mb) {
+                    const bf16x8 af = __builtin_bit_cast(bf16x8, la[mb * 64]);
+#pragma unroll
+                    for (int j = 0; j < NBW; ++j)
+                        acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8, rg.b[j]),
+                                                                            acc[mb][j], 0, 0, 0);
+                }
             } else {
                 // per 32-K half: the four widened weight fragments, then row block by row block
                 // (one row fragment live at a time)
@@ -320,7 +329,7 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
 #pragma unroll
         for (int q = 0; q < NBW / 2; ++q) {
             float sg = 1.f, su = 1.f;
-            if constexpr (!INT4) {
+            if constexpr (WQ == kWI8) {
                 const int f = (nb0 / 2 + q) * 16 + col16;
                 sg = a.s_gate[(size_t)tl.e * a.F + f];
                 su = a.s_up[(size_t)tl.e * a.F + f];
@@ -369,7 +378,7 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
                     for (int jn = 0; jn < NBW; ++jn) {
                         const int n = (nb0 + jn) * 16 + col16;
                         float v = acc[mb][jn][i] * wgt;
-                        if constexpr (!INT4) v *= a.s_down[(size_t)tl.e * a.d + n];
+                        if constexpr (WQ == kWI8) v *= a.s_down[(size_t)tl.e * a.d + n];
                         orow[n] = v;  // partial sum `split` of slot cs
                     }
                 }
@@ -394,7 +403,7 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
                     const int t = cs / a.kt, j = cs - t * a.kt;
                     const float wgt = j < a.k ? a.topk_w[(size_t)t * a.k + j] : a.gs[t];
                     f32x4 v = *reinterpret_cast<const f32x4*>(patch + r * 32 + c4) * wgt;
-                    if constexpr (!INT4) v *= *reinterpret_cast<const f32x4*>(a.s_down + (size_t)tl.e * a.d + n0 + c4);
+                    if constexpr (WQ == kWI8) v *= *reinterpret_cast<const f32x4*>(a.s_down + (size_t)tl.e * a.d + n0 + c4);
                     // partial sum `split` of slot cs: row cs*S + split of the combine buffer
                     *reinterpret_cast<f32x4*>(a.ow + ((size_t)cs * S + split) * a.d + n0 + c4) = v;
                 }
@@ -406,7 +415,7 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
 
 template <int MB, int WQ, bool UP, int NBW>
 hipError_t launch_r(const GemmArgs& a, hipStream_t s) {
-    constexpr int KSTEP = WQ == kWI4 ? 128 : 64;
+    constexpr int KSTEP = WQ == kWI4 ? 128 : WQ == kWI8 ? 64 : 32;
     constexpr int BN = kNW * NBW * 16;
     constexpr size_t ring = (size_t)ring_blocks<WQ>(MB) * 1024;
     constexpr size_t patch = UP ? (size_t)kNW * 16 * MB * 32 * 2 : NBW == 4 ? (size_t)kNW * 16 * MB * 32 * 4 : 0;
@@ -442,7 +451,9 @@ hipError_t launch_w(const GemmArgs& a, hipStream_t s) {
     // T = 192 519 against 528 us). With more rows, or int4 weights, the doubled row-fragment
     // reads per weight byte cost more than the waves gain (int8 T = 384: 671 -> 688 us, T =
     // 1024 down 493 -> 594 us).
-    if constexpr (WQ == kWI4) {
+    if constexpr (WQ == kWBf16) {
+        if (a.bm == 128) return launch_r<8, WQ, UP, 4>(a, s);
+    } else if constexpr (WQ == kWI4) {
         if constexpr (UP) {  // 80-row tiles: up projection only (its down projection tiles by 64, bm_h)
             if (a.bm == 80) return launch_r<5, WQ, UP, 4>(a, s);
         }
@@ -463,12 +474,14 @@ hipError_t launch_w(const GemmArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_expert_up_tstream(const GemmArgs& a, int wq, hipStream_t s) {
+    if (wq == kWBf16) return launch_w<kWBf16, true>(a, s);
     if (wq == kWI8) return launch_w<kWI8, true>(a, s);
     if (wq == kWI4) return launch_w<kWI4, true>(a, s);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_expert_down_tstream(const GemmArgs& a, int wq, hipStream_t s) {
+    if (wq == kWBf16) return launch_w<kWBf16, false>(a, s);
     if (wq == kWI8) return launch_w<kWI8, false>(a, s);
     if (wq == kWI4) return launch_w<kWI4, false>(a, s);
     return hipErrorInvalidValue;

@@ -119,6 +119,30 @@ def test_routed_int4_tile_boundaries():
     lay.close()
 
 
+def test_routed_bf16_tile_stream_tiles():
+    # bf16 tile-stream (128-row tiles; T = 214, k = 2 over 8 experts: 53.5 rows on average):
+    # experts at 150 (a second tile of 22 rows), 128, 129 (a second tile of one row), 1 and no rows
+    cfg = synth.get_config("mixtral_bf16", d_model=256, d_ff=256)
+    T, k = 214, cfg.top_k
+    counts = [150, 128, 0, 1, 129, 0, 20, 0]
+    assert sum(counts) == T * k and len(counts) == cfg.n_experts
+    rng = np.random.default_rng(11)
+    ids = np.repeat(np.arange(cfg.n_experts), counts)
+    rng.shuffle(ids)
+    ids = ids.reshape(T, k)
+    idx = torch.from_numpy(ids.astype(np.int32))
+    w = torch.from_numpy(rng.uniform(0.1, 1.0, size=(T, k)).astype(np.float32))
+    L = synth.make_layer(cfg)
+    olay = oracle_layer(L)
+    lay = gpu_layer(L, T)
+    x = synth.make_tokens(cfg, T)
+    print(f"[routed] bf16 tile-stream tiles T={T} counts={counts}", flush=True)
+    out = lay.forward_routed(x.cuda(), idx.cuda(), w.cuda(), None, scatter=True)
+    torch.cuda.synchronize()
+    _check(cfg, olay, x, idx, w, None, out, "bf16 tile-stream tiles")
+    lay.close()
+
+
 def test_routed_argument_checks():
     cfg = synth.get_config("shared_fine_bf16", d_model=256, d_ff=64, n_experts=8, top_k=2, shared_d_ff=128)
     lay = gpu_layer(synth.make_layer(cfg), 8)
