@@ -1,13 +1,13 @@
 // Expert compute for mid-size batches: row tiles in LDS, weights streamed into registers.
 //
 // Between decode and prefill an expert holds tens to a few hundred rows and its weights
-// are still most of the traffic ([hotelren §2.1]: the bottleneck is
-// moving data). Here each wave owns four 16-column weight blocks (two in the int8 down
-// projection while the experts average at most 64 rows) and streams them from HBM over
-// the whole K range as contiguous 1 KB chunks straight into MFMA operand registers (no
-// LDS round trip, each weight byte widened once), while the workgroup's row tile (up to
-// 128 rows) is staged in LDS by LDS-DMA, K step by K step, and read by all four waves:
-// every wave multiplies every row of the tile against its own columns.
+// are still most of the traffic ([hotelren §2.1]: the bottleneck is moving data). Here
+// each wave owns four 16-column weight blocks (two in the int8 down projection while the
+// experts average at most 64 rows) and streams them from HBM over the whole K range as
+// contiguous 1 KB chunks straight into MFMA operand registers (no LDS round trip; a
+// quantised weight byte is widened once), while the workgroup's row tile (up to 128 rows)
+// is staged in LDS by LDS-DMA, K step by K step, and read by all four waves: every wave
+// multiplies every row of the tile against its own columns.
 //   - Workgroup = (row tile, 256 or 128 columns, K split), 4 waves; the tile list, the
 //     padded A operand (xp for the up projection, packed H for the down projection) and
 //     the outputs are those of the LDS-tiled kernels, so the two are interchangeable.
