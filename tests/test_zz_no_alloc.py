@@ -1,8 +1,8 @@
 """moe_forward_noalloc (the forward in the library's static device scratch) against
 moe_forward through the C ABI: the same launch plan, so every output must be
-bit-identical, on two calls in a row with the second batch smaller, for the tiled
-prefill path, the quantised tile-stream path, the weight-streaming decode path and the
-split decode gate; and a
+bit-identical, on two calls in a row with the second batch smaller, for the LDS-tiled
+prefill path, the tile-stream path (bf16 and quantised), the weight-streaming decode path
+and the split decode gate; and a
 batch too large for the scratch is refused before anything is written."""
 import ctypes
 
@@ -36,7 +36,7 @@ def _poison(out):
 
 
 @pytest.mark.parametrize("name,kw,Ts", [
-    ("mixtral_bf16", dict(d_model=512, d_ff=1024), (300, 5)),                 # tiled GEMMs, then streaming
+    ("mixtral_bf16", dict(d_model=512, d_ff=1024), (600, 300, 5)),            # LDS-tiled, tile-stream, streaming
     ("int8_mixtral22b", dict(d_model=512, d_ff=1024), (40, 16, 3)),           # int8 tile-stream, streaming
     ("shared_fine_bf16", dict(d_model=256, d_ff=128, shared_d_ff=512), (20, 2)),  # split gate, shared expert
     ("int4_mixtral22b", dict(d_model=512, d_ff=1024), (250, 70, 9)),          # int4 80/64-row tile-stream, tile-stream, streaming
