@@ -62,7 +62,8 @@ def test_smallest_widths():
 
 
 def test_max_tokens_bound():
-    # T == max_tokens on both sides of the streaming / tiled switch (T <= 64 streams)
+    # T == max_tokens on both sides of the streaming / tiled switch (T <= 64 streams, past it
+    # the bf16 tile-stream GEMMs)
     cfg = synth.get_config("mixtral_bf16", d_model=256, d_ff=256)
     _run(cfg, [64], max_tokens=64)
     _run(cfg, [65, 300], max_tokens=300)

@@ -55,7 +55,8 @@ def test_routed_f32():
 
 
 def test_routed_bf16():
-    # streaming (T <= 64), tiled, and the multi-workgroup scatter (T * k > 4095)
+    # streaming (T <= 64), tile-stream (65), LDS-tiled (700, 2100), and the multi-workgroup
+    # scatter (T * k > 4095)
     _run(synth.get_config("mixtral_bf16", d_model=256, d_ff=256), [1, 5, 64, 65, 700, 2100])
 
 
@@ -83,7 +84,7 @@ def test_routed_with_own_routing_is_bit_identical(name, kw):
     cfg = synth.get_config(name, **kw)
     L = synth.make_layer(cfg)
     lay = gpu_layer(L, 300)
-    for T in (1, 3, 64, 300):  # fused tiny gate, per-token gate, streaming, tiled
+    for T in (1, 3, 64, 300):  # fused tiny gate, per-token gate, streaming, tiled (tile-stream or LDS-tiled)
         x = synth.make_tokens(cfg, T).cuda()
         a = lay.forward(x, scatter=True)
         b = lay.forward_routed(x, a.topk_idx, a.topk_w, a.shared_gate, scatter=True)
