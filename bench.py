@@ -251,7 +251,7 @@ def summarize(cfg, res):
     elif T <= (32 if quant else 64):
         kern = "expert_stream"
     elif (2 * cfg.d_ff) % 256 == 0 and cfg.d_model % 256 == 0 and (
-            quant or (cfg.shared_d_ff == 0 and T * cfg.top_k <= min(96 * cfg.n_experts, 4096))):
+            quant or (cfg.shared_d_ff == 0 and T * cfg.top_k <= min(128 * cfg.n_experts, 4096))):
         kern = "expert_tstream"
     else:
         kern = "expert_gemm"

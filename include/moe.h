@@ -87,7 +87,7 @@ typedef enum moe_gate_weighting {
  * multiple of d_ff. Which kernels run is chosen per call from T: BF16 weights
  * stream from HBM for T <= 64; above it they run on the tile-stream GEMMs (token rows
  * staged in LDS, weights streamed into registers) while the experts average at most
- * 96 rows and T*top_k <= 4096 (no shared expert), else on the LDS-tiled MFMA GEMMs;
+ * 128 rows and T*top_k <= 4096 (no shared expert), else on the LDS-tiled MFMA GEMMs;
  * I8 and I4 weights stream for T <= 32 and above it run on the tile-stream GEMMs.
  * The tile-stream GEMMs need 2*d_ff and d_model to be multiples of 256; otherwise
  * the LDS-tiled GEMMs run (F32 experts always run on the fp32 kernels). */

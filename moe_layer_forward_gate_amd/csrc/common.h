@@ -129,7 +129,7 @@ struct GemmArgs {
 hipError_t launch_expert_up_tiled(const GemmArgs& a, int wq, hipStream_t s);
 hipError_t launch_expert_down_tiled(const GemmArgs& a, int wq, hipStream_t s);
 // The same GEMMs with the weights streamed into registers and the row tile staged in LDS
-// (a.bm 128 for bf16, 64 or 128 for int8, 64 for int4 and 80 for its up projection;
+// (a.bm 128 or 160 for bf16, 64 or 128 for int8, 64 for int4 and 80 for its up projection;
 // N % 256 == 0)
 hipError_t launch_expert_up_tstream(const GemmArgs& a, int wq, hipStream_t s);
 hipError_t launch_expert_down_tstream(const GemmArgs& a, int wq, hipStream_t s);

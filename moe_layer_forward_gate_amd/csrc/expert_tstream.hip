@@ -61,10 +61,11 @@ __device__ __forceinline__ u32x4 load_w(const u32x4* p) {
 }
 
 // K steps in flight per wave for MA row blocks of a tile of MB: as many as the registers
-// left beside the accumulators hold (two waves per SIMD: 256 registers a wave)
+// left beside the accumulators hold (two waves per SIMD: 256 registers a wave; bf16 160-row
+// tiles: 3)
 template <int WQ>
 __host__ __device__ constexpr int ring_depth(int MA, int MB) {
-    return WQ == kWBf16 ? 4 : WQ == kWI4 ? (MB > 4 ? 3 : MA <= 2 ? 4 : 3) : (MA <= 4 ? 4 : MA <= 6 ? 3 : 2);
+    return WQ == kWBf16 ? (MB > 8 ? 3 : 4) : WQ == kWI4 ? (MB > 4 ? 3 : MA <= 2 ? 4 : 3) : (MA <= 4 ? 4 : MA <= 6 ? 3 : 2);
 }
 
 // LDS of the K loop: (R + 1) slots of MA * KH 1 KB blocks, the most over MA <= MB
@@ -297,6 +298,20 @@ __global__ __launch_bounds__(kThreads, 2) void expert_tstream(GemmArgs a) {
             else if (mb_act == 2) kloop(std::integral_constant<int, 2>{}, nt);
             else if (mb_act == 3) kloop(std::integral_constant<int, 3>{}, nt);
             else kloop(std::integral_constant<int, 4>{}, nt);
+        } else if constexpr (MB == 10) {
+            switch (mb_act) {
+                case 0:
+                case 1: kloop(std::integral_constant<int, 1>{}, nt); break;
+                case 2: kloop(std::integral_constant<int, 2>{}, nt); break;
+                case 3: kloop(std::integral_constant<int, 3>{}, nt); break;
+                case 4: kloop(std::integral_constant<int, 4>{}, nt); break;
+                case 5: kloop(std::integral_constant<int, 5>{}, nt); break;
+                case 6: kloop(std::integral_constant<int, 6>{}, nt); break;
+                case 7: kloop(std::integral_constant<int, 7>{}, nt); break;
+                case 8: kloop(std::integral_constant<int, 8>{}, nt); break;
+                case 9: kloop(std::integral_constant<int, 9>{}, nt); break;
+                default: kloop(std::integral_constant<int, 10>{}, nt); break;
+            }
         } else {
             static_assert(MB == 8, "row blocks per tile");
             switch (mb_act) {
@@ -452,7 +467,9 @@ hipError_t launch_w(const GemmArgs& a, hipStream_t s) {
     // reads per weight byte cost more than the waves gain (int8 T = 384: 671 -> 688 us, T =
     // 1024 down 493 -> 594 us).
     if constexpr (WQ == kWBf16) {
+        // 128-row tiles, or 160 rows when the experts average 97-128 (one tile for most)
         if (a.bm == 128) return launch_r<8, WQ, UP, 4>(a, s);
+        if (a.bm == 160) return launch_r<10, WQ, UP, 4>(a, s);
     } else if constexpr (WQ == kWI4) {
         if constexpr (UP) {  // 80-row tiles: up projection only (its down projection tiles by 64, bm_h)
             if (a.bm == 80) return launch_r<5, WQ, UP, 4>(a, s);

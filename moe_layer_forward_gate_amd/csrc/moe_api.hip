@@ -350,14 +350,16 @@ Plan make_plan(const moe_layer* L, int T) {
         // LDS-tiled ones: int8 T = 256 0.63 -> 0.57 ms, T = 1024 1.57 -> 1.40; int4 T = 256
         // 0.70 -> 0.61, T = 1024 1.89 -> 1.61) when both projections have whole 256-column
         // tiles
-        // bf16 (no shared expert) while the experts average at most 96 rows, on 128-row tiles:
-        // 8-expert 4096 x 14336 layer, T = 80-256 12-15% faster than the LDS-tiled 256-row
-        // tiles (T = 128 0.596 -> 0.512 ms), T = 384 9%; at T = 512 most experts spill into a
-        // second 128-row tile that streams the weights again (0.69 -> 0.78 ms). With uneven
-        // routing the average misleads (128-expert Zipf-biased layer: 5% faster at T = 256,
-        // even at 1024, 5-9% slower at 2048-3072, where a few experts hold most rows), so at
-        // most 4096 routed rows.
-        const bool bf16_ts = !i8 && !i4 && L->V == 0 && (long long)T * k <= 96LL * L->E && (long long)T * k <= 4096;
+        // bf16 (no shared expert) while the experts average at most 128 rows: 128-row tiles up
+        // to 96, 160-row ones past it (most experts then fit one tile, 160 being about three
+        // standard deviations past 128 rows). 8-expert 4096 x 14336 layer against the
+        // LDS-tiled 256-row tiles: T = 80-256 12-15% faster (T = 128 0.596 -> 0.512 ms), T =
+        // 384 9%, 448 and 512 7-8% (160-row tiles; 128-row ones at 512: 0.69 -> 0.78 ms, most
+        // experts spilling into a second tile that streams the weights again); T = 576 2%
+        // slower. With uneven routing the average misleads (128-expert Zipf-biased layer: 5%
+        // faster at T = 256, even at 1024, 5-9% slower at 2048-3072, where a few experts hold
+        // most rows), so at most 4096 routed rows.
+        const bool bf16_ts = !i8 && !i4 && L->V == 0 && (long long)T * k <= 128LL * L->E && (long long)T * k <= 4096;
         tstream = (i8 || i4 || bf16_ts) && (2 * d.d_ff) % 256 == 0 && d.d_model % 256 == 0;
         // bf16: 256-row tiles (the 256 x 256 workgroup tile reads the least LDS and L2 per MFMA
         // and outruns 128-row tiles even when most experts leave their last tile half empty);
@@ -365,7 +367,8 @@ Plan make_plan(const moe_layer* L, int T) {
         // LDS-tiled T = 64 on the 8-expert layer: 0.48 against 0.51 ms; tile-stream T = 128
         // 0.48 against 0.49 ms, T = 256 0.66 against 0.57); int4: 64-row tiles (the
         // registers of a 128-row tile do not fit)
-        bm = i4 ? 64 : (i8 ? ((long long)T * k <= (tstream ? 32LL : 24LL) * L->E ? 64 : 128) : tstream ? 128 : 256);
+        bm = i4 ? 64 : (i8 ? ((long long)T * k <= (tstream ? 32LL : 24LL) * L->E ? 64 : 128)
+                           : tstream ? ((long long)T * k <= 96LL * L->E ? 128 : 160) : 256);
         // int4 tile-stream with 41-72 rows per expert on average: 80-row up tiles, so nearly
         // every expert's weights stream once (not again for a ragged second tile of a few
         // rows), and 64-row down tiles (80-row down tiles measured within +-3% at T =

@@ -39,9 +39,9 @@ def _run(name, Ts):
 
 
 def test_mixtral_bf16_full():
-    # T <= 64 on the streaming kernels, 128 and 384 on the tile-stream ones (128-row tiles),
-    # 4096 on the LDS-tiled GEMMs
-    _run("mixtral_bf16", [1, 8, 32, 64, 128, 384, 4096])
+    # T <= 64 on the streaming kernels, 128 and 384 on the tile-stream ones with 128-row
+    # tiles, 512 with 160-row tiles, 4096 on the LDS-tiled GEMMs
+    _run("mixtral_bf16", [1, 8, 32, 64, 128, 384, 512, 4096])
 
 
 def test_shared_fine_bf16_full():

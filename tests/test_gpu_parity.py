@@ -79,15 +79,15 @@ def test_int4_reduced():
 @pytest.mark.parametrize("name,Ts", [
     ("int8_mixtral22b", [40, 100, 130, 200, 260, 330, 400, 470, 520]),
     ("int4_mixtral22b", [40, 80, 130, 200, 250, 520]),
-    ("mixtral_bf16", [65, 80, 130, 200, 260, 330, 384, 385]),
+    ("mixtral_bf16", [65, 80, 130, 200, 260, 330, 384, 385, 450, 512, 513]),
 ])
 def test_tile_stream_row_blocks(name, Ts):
     # the tile-stream kernels over every count of 16-row blocks a tile can hold (int8: 64-row
     # tiles up to 32 rows per expert on average, then 128; int4: 64, 80-row up tiles at 41-72;
-    # bf16: 128-row tiles from 65 tokens while the experts average at most 96 rows, so T = 385
-    # runs the LDS-tiled kernel), each count with its own number of K steps in flight (int8 up
-    # projection, 8 K steps: 4 in flight below 5 row blocks, 3 at 5-6 (a partial last round),
-    # 2 at 7-8), and experts over one tile
+    # bf16: 128-row tiles from 65 tokens while the experts average at most 96 rows, 160-row
+    # ones up to 128, so T = 513 runs the LDS-tiled kernel), each count with its own number of
+    # K steps in flight (int8 up projection, 8 K steps: 4 in flight below 5 row blocks, 3 at
+    # 5-6 (a partial last round), 2 at 7-8), and experts over one tile
     _run(synth.get_config(name, d_model=512, d_ff=1024), Ts)
 
 
