@@ -434,13 +434,16 @@ struct SmallGate {
     static constexpr int EG = 8;                       // columns per load round
 };
 
-template <typename XT>
+// MT: token slots (1 for a single token, whose instantiation holds a quarter of the dot
+// code: its instructions are fetched cold at every decode step)
+template <typename XT, int MT>
 __global__ __launch_bounds__(1024) void gate_scatter_small(const XT* __restrict__ x, const float* __restrict__ wr_t,
                                                            const float* __restrict__ bias, int T, int d, int E,
                                                            int Ec, int k, int gflags, int32_t* __restrict__ idx,
                                                            float* __restrict__ w, float* __restrict__ gs, int V,
                                                            int bm, ScatterOut o) {
-    constexpr int MT = SmallGate<XT>::T, EC = SmallGate<XT>::EC, EG = SmallGate<XT>::EG;
+    static_assert(MT == 1 || MT == SmallGate<XT>::T, "token slots");
+    constexpr int EC = SmallGate<XT>::EC, EG = SmallGate<XT>::EG;
     constexpr int NW = 16;
     __shared__ float part[NW][MT * EC];
     __shared__ float logits[MT][EC + 1];
@@ -765,12 +768,15 @@ hipError_t launch_gate_scatter_small(const void* x, bool x_bf16, const float* wr
     const bool has_shared = (gflags & kGateShared) != 0;
     if (!gate_scatter_small_fits(T, d, E, has_shared, x_bf16) || E + V > kMaxEt) return hipErrorInvalidValue;
     const int Ec = E + (has_shared ? 1 : 0);
-    if (x_bf16)
-        hipLaunchKernelGGL(gate_scatter_small<bf16_t>, dim3(1), dim3(1024), 0, s, (const bf16_t*)x, wr_t, bias, T, d,
-                           E, Ec, k, gflags, idx, w, gs, V, bm, o);
-    else
-        hipLaunchKernelGGL(gate_scatter_small<float>, dim3(1), dim3(1024), 0, s, (const float*)x, wr_t, bias, T, d,
-                           E, Ec, k, gflags, idx, w, gs, V, bm, o);
+    if (x_bf16) {
+        auto kern = T == 1 ? gate_scatter_small<bf16_t, 1> : gate_scatter_small<bf16_t, SmallGate<bf16_t>::T>;
+        hipLaunchKernelGGL(kern, dim3(1), dim3(1024), 0, s, (const bf16_t*)x, wr_t, bias, T, d, E, Ec, k, gflags,
+                           idx, w, gs, V, bm, o);
+    } else {
+        auto kern = T == 1 ? gate_scatter_small<float, 1> : gate_scatter_small<float, SmallGate<float>::T>;
+        hipLaunchKernelGGL(kern, dim3(1), dim3(1024), 0, s, (const float*)x, wr_t, bias, T, d, E, Ec, k, gflags, idx,
+                           w, gs, V, bm, o);
+    }
     return hipGetLastError();
 }
 
