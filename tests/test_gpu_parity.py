@@ -110,6 +110,15 @@ def test_quantised_partial_column_tiles():
     _run(synth.get_config("int8_mixtral22b", d_model=384, d_ff=192), [70, 200])
 
 
+def test_bf16_mid_batches_without_whole_column_tiles():
+    # bf16 batches in the tile-stream range whose widths leave a half 256-column tile (d_model
+    # 384: the down projection; d_ff 192: the up projection's 384 gate/up columns) run the
+    # LDS-tiled GEMMs instead; d_model 512, d_ff 640: both whole, the tile-stream kernels
+    _run(synth.get_config("mixtral_bf16", d_model=384, d_ff=512), [80, 200])
+    _run(synth.get_config("mixtral_bf16", d_model=512, d_ff=192), [80, 200])
+    _run(synth.get_config("mixtral_bf16", d_model=512, d_ff=640), [80, 200, 500])
+
+
 def test_tiny_batches_single_workgroup_route():
     # T <= 4 with at most 16 router columns: gate and scatter run in one workgroup
     _run(synth.get_config("mixtral_bf16", d_model=512, d_ff=1024), [1, 2, 3, 4, 5])
