@@ -94,11 +94,12 @@ def test_tile_stream_row_blocks(name, Ts):
 @pytest.mark.parametrize("name,E,k,Ts", [
     ("int8_mixtral22b", 64, 8, [40, 300]),
     ("int4_mixtral22b", 128, 4, [40, 700]),
+    ("mixtral_bf16", 128, 4, [80, 1000]),
 ])
 def test_tile_stream_many_experts(name, E, k, Ts):
-    # the tile-stream kernels over 64 and 128 experts: the workgroup's expert is found by
-    # ballots over the tile table 64 entries at a time (two passes for 128), most experts
-    # hold a few rows, some none
+    # the tile-stream kernels (int8, int4, bf16) over 64 and 128 experts: the workgroup's
+    # expert is found by ballots over the tile table 64 entries at a time (two passes for
+    # 128), most experts hold a few rows, some none
     _run(synth.get_config(name, d_model=256, d_ff=512, n_experts=E, top_k=k), Ts)
 
 
