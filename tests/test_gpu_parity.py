@@ -182,6 +182,7 @@ def test_forward_argument_errors():
 
 @pytest.mark.parametrize("name,kw", [
     ("shared_fine_bf16", dict(d_model=256, d_ff=128, shared_d_ff=512)),
+    ("mixtral_bf16", dict(d_model=256, d_ff=256)),
     ("int8_mixtral22b", dict(d_model=256, d_ff=128)),
     ("int4_mixtral22b", dict(d_model=256, d_ff=256)),
 ])
@@ -189,7 +190,8 @@ def test_hip_graph_replays_match_eager(name, kw):
     # moe_forward only enqueues kernels (no allocation, no host sync, no memset nodes), so it
     # can be captured in a HIP graph; every replay, with eager work and synchronisations in
     # between, must reproduce the eager result bit for bit (prefill and decode plans of the
-    # bf16, int8 and int4 kernels)
+    # bf16, int8 and int4 kernels: T = 300 runs the LDS-tiled GEMMs on the shared + fine
+    # layer, the tile-stream ones on the others)
     cfg = synth.get_config(name, **kw)
     L = synth.make_layer(cfg)
     lay = gpu_layer(L, 300)
