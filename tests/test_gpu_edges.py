@@ -61,6 +61,14 @@ def test_smallest_widths():
     _run(synth.get_config("int8_mixtral22b", d_model=128, d_ff=64), [1, 100])
 
 
+@pytest.mark.parametrize("name,d", [("mixtral_bf16", 8192), ("mixtral_bf16", 8320), ("tiny_f32", 8192), ("tiny_f32", 8320)])
+def test_small_gate_width_limit(name, d):
+    # the one-workgroup decode gate takes d_model <= 8192 (1024 threads x 8 elements: at 8192
+    # every thread loads); 8320 runs the per-token gate instead. T = 1 (the one-token
+    # instantiation) and 3 (four token slots)
+    _run(synth.get_config(name, d_model=d, d_ff=64, n_experts=8, top_k=2), [1, 3])
+
+
 def test_max_tokens_bound():
     # T == max_tokens on both sides of the streaming / tiled switch (T <= 64 streams, past it
     # the bf16 tile-stream GEMMs)
